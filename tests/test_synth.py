@@ -1,0 +1,49 @@
+"""Generator contract: determinism per seed, the top-k gap, the Zipf skew."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import LayerConfig, make_layer, make_tokens
+
+
+def test_deterministic_per_seed():
+    a = make_layer("c0", cache=False)
+    b = make_layer("c0", cache=False)
+    assert np.array_equal(a.gate_up.codes, b.gate_up.codes)
+    assert np.array_equal(a.down.block_scales, b.down.block_scales)
+    assert np.array_equal(make_tokens(a, 16), make_tokens(b, 16))
+    assert not np.array_equal(make_tokens(a, 16, stream=1), make_tokens(a, 16))
+
+
+def test_topk_gap_holds_in_fp64():
+    lay = make_layer("c0")
+    x = make_tokens(lay, 16)
+    lg = oracle.router_logits(lay, oracle.bf16_to_f64(x))
+    top = -np.sort(-lg, axis=1)[:, :lay.top_k + 1]
+    assert (top[:, :-1] - top[:, 1:]).min() >= 1e-3
+
+
+def test_token_prefix_stable():
+    lay = make_layer("c0")
+    assert np.array_equal(make_tokens(lay, 16)[:4], make_tokens(lay, 4))
+
+
+def test_zipf_bias_skews_load():
+    cfg = LayerConfig("z", (4096,), 64, 16, 2, 32, "fp8", act="fp8", zipf_s=1.1, zipf_ratio=4.0, seed=7)
+    lay = make_layer(cfg, cache=False)
+    assert abs(lay.extra["calibration_ratio"] - 4.0) < 0.3
+    x = make_tokens(lay, 4096)
+    ids = oracle.select_topk(oracle.router_logits(lay, oracle.bf16_to_f64(x)), 2)
+    c = np.bincount(ids.ravel(), minlength=16)
+    assert 3.0 < c.max() / c.mean() < 5.0
+
+
+def test_bf16_rounding_is_nearest_even():
+    v = np.array([1.0, 1.00390625, 1.0078125 + 2 ** -9, -3.14159, 1 + 2 ** -8], np.float32)
+    b = synth.f32_to_bf16_bits(v)
+    back = synth.bf16_bits_to_f32(b)
+    assert back[0] == 1.0
+    assert back[1] == 1.0           # exact tie 1 + 2^-8 -> even (1.0)
+    assert back[4] == 1.0
+    assert back[2] == np.float32(1.0078125)  # a quarter ulp above rounds down
