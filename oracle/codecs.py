@@ -79,23 +79,30 @@ def _unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+# Value of every code, for decoding whole matrices by table lookup (the same
+# values as the decoders above, looked up instead of recomputed per element).
+_E2M1_TABLE = e2m1_decode(np.arange(16))
+_E8M0_TABLE = e8m0_decode(np.arange(256))
+_E4M3_TABLE = e4m3_decode(np.arange(256))
+
+
 def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """W[n,k] = E2M1(code[n,k]) * 2^(S[n, k//32] - 127), float64."""
-    el = e2m1_decode(_unpack_nibbles(codes))
-    sc = e8m0_decode(scales)
-    return el * np.repeat(sc, 32, axis=-1)
+    el = _E2M1_TABLE[_unpack_nibbles(codes)]
+    sc = _E8M0_TABLE[np.asarray(scales, np.uint8)]
+    return (el.reshape(*el.shape[:-1], -1, 32) * sc[..., None]).reshape(el.shape)
 
 
 def dequant_nvfp4(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
     """W[n,k] = E2M1(code[n,k]) * E4M3(S[n, k//16]) * g, float64."""
-    el = e2m1_decode(_unpack_nibbles(codes))
-    sc = e4m3_decode(scales)
-    return el * np.repeat(sc, 16, axis=-1) * np.float64(g)
+    el = _E2M1_TABLE[_unpack_nibbles(codes)]
+    sc = _E4M3_TABLE[np.asarray(scales, np.uint8)] * np.float64(g)
+    return (el.reshape(*el.shape[:-1], -1, 16) * sc[..., None]).reshape(el.shape)
 
 
 def dequant_fp8(codes: np.ndarray, s: float) -> np.ndarray:
     """W[n,k] = E4M3(code[n,k]) * s, float64."""
-    return e4m3_decode(codes) * np.float64(s)
+    return _E4M3_TABLE[np.asarray(codes, np.uint8)] * np.float64(s)
 
 
 def dequant(qw, e: int) -> np.ndarray:

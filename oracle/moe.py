@@ -271,19 +271,26 @@ def forward_tokens(lay, x_bits: np.ndarray, tokens, s_h=None) -> np.ndarray:
     xq = quant_act_per_tensor(xf)[0] if fp8 else xf
     k = lay.cfg.top_k
     out = np.zeros((len(tokens), xf.shape[1]))
+    cache = {}
+
+    def W(qw, e):
+        key = (id(qw), e)
+        if key not in cache:
+            cache[key] = dequant(qw, e)
+        return cache[key]
+
     for r, t in enumerate(tokens):
         acc = np.zeros(xf.shape[1])
         for j in range(k):
             e = int(ids[t, j])
-            wgu, wd = dequant(lay.gate_up, e), dequant(lay.down, e)
+            wgu, wd = W(lay.gate_up, e), W(lay.down, e)
             h = swiglu_expert(wgu, wd, xq[t])[0]
             if fp8:
                 s = np.float32(s_h)
                 h = e4m3_decode(e4m3_encode_nearest(h.astype(np.float32) / s)) * np.float64(s)
             acc = acc + w[t, j] * (wd @ h)
         if sg is not None:
-            acc = acc + sg[t] * swiglu_expert(dequant(lay.shared_gate_up, 0),
-                                              dequant(lay.shared_down, 0), xq[t])[1]
+            acc = acc + sg[t] * swiglu_expert(W(lay.shared_gate_up, 0), W(lay.shared_down, 0), xq[t])[1]
         out[r] = acc
     return out
 
