@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer forward (ftmoe_forward) on one MI355X.
+
+One step = one ftmoe_forward call (router GEMM + softmax top-k, align,
+gate_up GEMM + SwiGLU, down GEMM, weighted combine) over one batch of
+synthetic tokens, with the inputs already resident in HBM.
+
+Default workload: the decode configuration of the 30B-A3B-class layer
+(T = 8 tokens, hidden 2048, 128 experts, top-8, intermediate 768, MXFP4
+experts).  Its metric is the selected-expert weight bytes streamed per second
+(each distinct selected expert's packed bytes counted once per step).  To
+keep the 256 MB Infinity Cache from serving those bytes, consecutive steps
+cycle through several device copies of the layer (a model's consecutive MoE
+layers) and through different token batches.
+
+Prints one JSON line (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
+METRIC = "MoE-layer tokens/s (prefill) + decode expert-weight GB/s, % of MI355X roofline"
+
+WORKLOADS = {
+    # name: (config, T, kind)
+    "c1": ("c1", 8, "decode"),
+    "c1-t1": ("c1", 1, "decode"),
+    "c3-t1": ("c3", 1, "decode"),
+    "c2": ("c2", 4096, "prefill"),
+    "c3": ("c3", 8192, "prefill"),
+    "c4": ("c4", 16384, "prefill"),
+}
+
+
+def describe(cfg, T):
+    s = (f"{cfg.name}: T={T}, hidden {cfg.hidden}, {cfg.num_experts} experts, top-{cfg.top_k}, "
+         f"intermediate {cfg.inter}, {cfg.fmt.upper()} experts")
+    if cfg.shared_inter:
+        s += f", shared expert (intermediate {cfg.shared_inter})"
+    if cfg.act == "fp8":
+        s += ", per-tensor E4M3 activations"
+    if cfg.zipf_s:
+        s += f", Zipf({cfg.zipf_s}) router bias"
+    return s
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
+    ap.add_argument("--ring", type=int, default=None, help="device copies of the layer cycled over steps")
+    ap.add_argument("--batches", type=int, default=16, help="distinct token batches cycled over steps")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the layer forward is not sharded across "
+                                   "GPUs here, so --gpus above 1 is not supported"}), flush=True)
+        return 2
+
+    import torch
+    import block_scaled_fp4_router_amd as ft
+    import synth
+
+    name, T, kind = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[name]
+    lay = synth.make_layer(name)
+    ring = args.ring or (4 if kind == "decode" else 1)
+    dev = "cuda"
+    dlays = [ft.DeviceLayer.from_host(lay, dev, path=args.path) for _ in range(ring)]
+    descs = [d.desc() for d in dlays]
+    nb = args.batches if kind == "decode" else 2
+    xs_host = [synth.make_tokens(lay, T, stream=100 + b) for b in range(nb)]
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs_host]
+    ws = ft.alloc_workspace(dlays[0], T)
+    y = torch.empty((T, cfg.hidden), dtype=torch.int16, device=dev)
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # Routing of every batch (for the byte count of the selected experts).
+    sel_bytes = []
+    for b in range(nb):
+        ft.forward(dlays[0], xs[b], T, ws, y, ids, w, desc=descs[0])
+        torch.cuda.synchronize()
+        sel_bytes.append(dlays[0].selected_expert_bytes(ids.cpu().numpy()))
+
+    def step(i):
+        ft.forward(dlays[i % ring], xs[i % nb], T, ws, y, ids, w, stream=stream, desc=descs[i % ring])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    mean_bytes = float(np.mean([sel_bytes[i % nb] for i in range(args.steps)]))
+
+    # Same steps again with every kernel bracketed by HIP events on its stream.
+    ft.timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = ft.timing_collect()
+    ft.timing_enable(False)
+    kernel_us = {k: 1e3 * v[0] / v[1] for k, v in kern.items()}
+
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    if kind == "decode":
+        value = mean_bytes / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        dom = max((n for n in kernel_us if n.startswith("decode_")), key=lambda n: kernel_us[n])
+        # Algorithmic bytes of the dominant kernel: its matrix's packed bytes of
+        # every distinct selected expert (shared expert for the shared kernels).
+        def per_expert(q):
+            b = q.codes[0].nbytes
+            if q.block_scales is not None:
+                b += q.block_scales[0].nbytes
+            if q.tensor_scales is not None:
+                b += 4
+            return b
+        gu_b, dn_b = per_expert(lay.gate_up), per_expert(lay.down)
+        shared_b = per_expert(lay.shared_gate_up) + per_expert(lay.shared_down) if cfg.shared_inter else 0
+        mean_unique = (mean_bytes - shared_b) / (gu_b + dn_b)
+        unit_bytes = {"decode_gateup": gu_b * mean_unique, "decode_down": dn_b * mean_unique,
+                      "decode_shared_gateup": per_expert(lay.shared_gate_up) if cfg.shared_inter else 0,
+                      "decode_shared_down": per_expert(lay.shared_down) if cfg.shared_inter else 0}[dom]
+        achieved = unit_bytes / (kernel_us[dom] * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": int(unit_bytes), "avg_launch_us": round(kernel_us[dom], 3)}
+    else:
+        value = T / (ms * 1e-3)
+        unit = "tokens/s"
+        dom = "gemm_gateup"
+        flops = 2.0 * T * k * H * 2 * I
+        achieved = flops / (kernel_us[dom] * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS["fp8" if cfg.act == "fp8" else "bf16"]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_flops_per_launch": flops, "avg_launch_us": round(kernel_us[dom], 3)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": ("fp8-e4m3" if cfg.act == "fp8" else "bf16") + "-mfma/fp32-acc",
+        "data": "synthetic (seeded generator; random-init weights quantised to the named format)",
+        "config": {"workload": describe(cfg, T), "kind": kind, "tokens": T, "layer_copies_cycled": ring,
+                   "token_batches_cycled": nb, "path": args.path,
+                   "selected_expert_bytes_per_step": int(mean_bytes)},
+        "roofline": roof,
+        "kernel_avg_us": {k2: round(v, 3) for k2, v in sorted(kernel_us.items())},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(lay, xs_host[0], kind, T, args.cpu_sample_tokens, sel_bytes[0])
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(lay, x, kind, T, sample_tokens, bytes0):
+    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
+    same workload, timed on this host's cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    if kind == "decode":
+        t0 = time.perf_counter()
+        oracle.forward(lay, x)
+        dt = time.perf_counter() - t0
+        return {"value": round(bytes0 / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"one full decode step (T={T}) of the same layer, per-token oracle loop",
+                "seconds": round(dt, 2)}
+    n = sample_tokens or 16
+    tok = np.arange(n)
+    s_h = None
+    t0 = time.perf_counter()
+    if lay.cfg.act == "fp8":
+        s_h = 1.0  # the sample measures the per-token arithmetic; the h scale only sets magnitudes
+    oracle.forward_tokens(lay, x, tok, s_h=s_h)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of the {T} tokens through the per-token oracle loop", "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

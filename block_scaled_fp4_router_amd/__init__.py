@@ -1,0 +1,296 @@
+"""Python binding of libftmoe.so: the routed MoE layer forward over
+block-quantised experts (MXFP4 / NVFP4 / FP8) on MI355X.
+
+The binding only marshals arguments: every step of the forward runs in the
+library's HIP kernels.  Tensors are torch device tensors (torch provides
+device memory and streams); their pointers and the current HIP stream are
+passed through the C ABI declared in ``include/ftmoe.h``.  Every entry point
+fails loudly when the library has not been built; there is no fallback
+implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libftmoe.so")
+
+# ftmoe_status
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+# ftmoe_wfmt
+W_MXFP4, W_NVFP4, W_FP8_E4M3 = 1, 2, 3
+# ftmoe_afmt
+ACT_BF16, ACT_FP8_PER_TENSOR = 0, 1
+# ftmoe_path
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+
+FMT_CODES = {"mxfp4": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8_E4M3}
+ACT_CODES = {"bf16": ACT_BF16, "fp8": ACT_FP8_PER_TENSOR}
+PATH_CODES = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL}
+
+# Every symbol include/ftmoe.h declares.
+EXPORTS = (
+    "ftmoe_workspace_size", "ftmoe_align_max_padded", "ftmoe_align_workspace_size", "ftmoe_route",
+    "ftmoe_align", "ftmoe_experts_forward", "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor",
+    "ftmoe_timing_enable", "ftmoe_timing_collect", "ftmoe_status_string", "ftmoe_last_error", "ftmoe_version",
+)
+
+
+class FtmoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class QWeightDesc(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p), ("tensor_scales", ctypes.c_void_p),
+    ]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("act", ctypes.c_int32), ("path", ctypes.c_int32),
+        ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("gate_up", QWeightDesc), ("down", QWeightDesc),
+        ("shared_inter", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("shared_gate_up", QWeightDesc), ("shared_down", QWeightDesc),
+        ("shared_gate_w", ctypes.c_void_p),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libftmoe.so (once).  Raises if it is missing: build it with
+    ``python -m block_scaled_fp4_router_amd.build``."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first "
+                           "(python -m block_scaled_fp4_router_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.ftmoe_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
+    lib.ftmoe_align_max_padded.argtypes = [i32, i32, i32, i32]
+    lib.ftmoe_align_max_padded.restype = i32
+    lib.ftmoe_align_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.ftmoe_align_workspace_size.restype = sz
+    lib.ftmoe_route.argtypes = [P(LayerDesc), vp, i32, vp, sz, vp, vp, vp, vp]
+    lib.ftmoe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ftmoe_experts_forward.argtypes = [P(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp, vp]
+    lib.ftmoe_forward.argtypes = [P(LayerDesc), vp, i32, vp, sz, vp, vp, vp, vp]
+    lib.ftmoe_quantize_fp8_per_tensor.argtypes = [vp, i64, vp, vp, vp, sz, vp]
+    lib.ftmoe_status_string.argtypes = [i32]
+    lib.ftmoe_status_string.restype = ctypes.c_char_p
+    lib.ftmoe_last_error.argtypes = []
+    lib.ftmoe_last_error.restype = ctypes.c_char_p
+    lib.ftmoe_version.restype = i32
+    lib.ftmoe_timing_enable.argtypes = [i32]
+    lib.ftmoe_timing_enable.restype = None
+    lib.ftmoe_timing_collect.argtypes = [i32, ctypes.c_char_p, P(ctypes.c_double), P(i64)]
+    lib.ftmoe_timing_collect.restype = i32
+    for name in ("ftmoe_workspace_size", "ftmoe_route", "ftmoe_align", "ftmoe_experts_forward",
+                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _status_name(st: int) -> str:
+    try:
+        return load().ftmoe_status_string(st).decode()
+    except Exception:  # library missing: still say something useful
+        return f"status {st}"
+
+
+def _check(st: int) -> None:
+    if st != OK:
+        raise FtmoeError(st, load().ftmoe_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# --------------------------------------------------------------- layer ----
+
+
+@dataclass
+class DeviceQWeight:
+    fmt: str
+    num_experts: int
+    n: int
+    k: int
+    codes: object
+    block_scales: object = None
+    tensor_scales: object = None
+
+    def desc(self) -> QWeightDesc:
+        return QWeightDesc(FMT_CODES[self.fmt], self.num_experts, self.n, self.k, _ptr(self.codes),
+                           _ptr(self.block_scales), _ptr(self.tensor_scales))
+
+
+class DeviceLayer:
+    """A layer whose tensors live on the GPU, plus its C descriptor.
+
+    ``from_host`` copies a host layer (numpy arrays with the attribute names
+    of the generator's layers: router_w, router_b, gate_up, down, shared_*)
+    to ``device``."""
+
+    def __init__(self, hidden, inter, num_experts, top_k, router_w, gate_up: DeviceQWeight,
+                 down: DeviceQWeight, router_bias=None, act="bf16", path="auto", shared_inter=0,
+                 shared_gate_up: Optional[DeviceQWeight] = None, shared_down: Optional[DeviceQWeight] = None,
+                 shared_gate_w=None):
+        self.hidden, self.inter, self.num_experts, self.top_k = hidden, inter, num_experts, top_k
+        self.router_w, self.router_bias = router_w, router_bias
+        self.gate_up, self.down = gate_up, down
+        self.act, self.path = act, path
+        self.shared_inter = shared_inter
+        self.shared_gate_up, self.shared_down, self.shared_gate_w = shared_gate_up, shared_down, shared_gate_w
+
+    @classmethod
+    def from_host(cls, lay, device="cuda", path="auto") -> "DeviceLayer":
+        import torch
+
+        def t(a):
+            return None if a is None else torch.from_numpy(a).to(device)
+
+        def qw(q):
+            if q is None:
+                return None
+            return DeviceQWeight(q.fmt, q.num_experts, q.n, q.k, t(q.codes), t(q.block_scales), t(q.tensor_scales))
+
+        cfg = lay.cfg
+        return cls(cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, t(lay.router_w), qw(lay.gate_up),
+                   qw(lay.down), router_bias=t(lay.router_b), act=cfg.act, path=path,
+                   shared_inter=cfg.shared_inter, shared_gate_up=qw(lay.shared_gate_up),
+                   shared_down=qw(lay.shared_down), shared_gate_w=t(lay.shared_gate_w))
+
+    def desc(self) -> LayerDesc:
+        d = LayerDesc()
+        d.hidden, d.inter, d.num_experts, d.top_k = self.hidden, self.inter, self.num_experts, self.top_k
+        d.act, d.path = ACT_CODES[self.act], PATH_CODES[self.path]
+        d.router_w, d.router_bias = _ptr(self.router_w), _ptr(self.router_bias)
+        d.gate_up, d.down = self.gate_up.desc(), self.down.desc()
+        d.shared_inter = self.shared_inter
+        if self.shared_inter:
+            d.shared_gate_up, d.shared_down = self.shared_gate_up.desc(), self.shared_down.desc()
+            d.shared_gate_w = _ptr(self.shared_gate_w)
+        return d
+
+    def with_path(self, path: str) -> "DeviceLayer":
+        import copy
+        c = copy.copy(self)
+        c.path = path
+        return c
+
+    def selected_expert_bytes(self, ids) -> int:
+        """Bytes of packed weights (codes + block scales + tensor scales) of
+        the distinct experts in ``ids`` plus the shared expert."""
+        import numpy as np
+        u = np.unique(np.asarray(ids)).size
+
+        def per_expert(q):
+            b = q.codes[0].numel() * q.codes.element_size()
+            if q.block_scales is not None:
+                b += q.block_scales[0].numel()
+            if q.tensor_scales is not None:
+                b += 4
+            return b
+
+        total = u * (per_expert(self.gate_up) + per_expert(self.down))
+        if self.shared_inter:
+            total += per_expert(self.shared_gate_up) + per_expert(self.shared_down)
+        return total
+
+
+# ----------------------------------------------------------- entry points --
+
+
+def workspace_size(layer: DeviceLayer, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    d = layer.desc()
+    _check(load().ftmoe_workspace_size(ctypes.byref(d), T, ctypes.byref(n)))
+    return n.value
+
+
+def align_max_padded(T: int, k: int, E: int, block_m: int) -> int:
+    return load().ftmoe_align_max_padded(T, k, E, block_m)
+
+
+def align_workspace_size(T: int, k: int, E: int, block_m: int) -> int:
+    return load().ftmoe_align_workspace_size(T, k, E, block_m)
+
+
+def alloc_workspace(layer: DeviceLayer, T: int, device="cuda"):
+    import torch
+    n = max(256, workspace_size(layer, T))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(layer: DeviceLayer, x, T: int, ws, topk_ids, topk_w, shared_gate=None, stream=None) -> None:
+    d = layer.desc()
+    _check(load().ftmoe_route(ctypes.byref(d), _ptr(x), T, _ptr(ws), ws.numel(), _ptr(topk_ids), _ptr(topk_w),
+                              _ptr(shared_gate), _stream(stream)))
+
+
+def align(topk_ids, T: int, k: int, E: int, block_m: int, counts, offsets, sorted_ids, block_expert, num_padded,
+          ws=None, stream=None) -> None:
+    _check(load().ftmoe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(counts), _ptr(offsets), _ptr(sorted_ids),
+                              _ptr(block_expert), _ptr(num_padded), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)))
+
+
+def experts_forward(layer: DeviceLayer, x, T: int, topk_ids, topk_w, shared_gate, ws, y, stream=None) -> None:
+    d = layer.desc()
+    _check(load().ftmoe_experts_forward(ctypes.byref(d), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(shared_gate), _ptr(ws), ws.numel(), _ptr(y), _stream(stream)))
+
+
+def forward(layer: DeviceLayer, x, T: int, ws, y, topk_ids=None, topk_w=None, stream=None, desc=None) -> None:
+    d = desc if desc is not None else layer.desc()
+    _check(load().ftmoe_forward(ctypes.byref(d), _ptr(x), T, _ptr(ws), ws.numel(), _ptr(y), _ptr(topk_ids),
+                                _ptr(topk_w), _stream(stream)))
+
+
+def quantize_fp8_per_tensor(x, n: int, q, scale, ws, stream=None) -> None:
+    _check(load().ftmoe_quantize_fp8_per_tensor(_ptr(x), n, _ptr(q), _ptr(scale), _ptr(ws), ws.numel(),
+                                                _stream(stream)))
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every kernel this thread enqueues with HIP events."""
+    load().ftmoe_timing_enable(1 if on else 0)
+
+
+def timing_collect(max_entries: int = 64) -> dict:
+    """{kernel name: (total ms, launches)} since the last collect."""
+    names = ctypes.create_string_buffer(32 * max_entries)
+    ms = (ctypes.c_double * max_entries)()
+    cnt = (ctypes.c_int64 * max_entries)()
+    n = load().ftmoe_timing_collect(max_entries, names, ms, cnt)
+    out = {}
+    for i in range(min(n, max_entries)):
+        name = names.raw[32 * i:32 * i + 32].split(b"\0", 1)[0].decode()
+        out[name] = (ms[i], cnt[i])
+    return out
+
+
+def version() -> int:
+    return load().ftmoe_version()

@@ -1,0 +1,121 @@
+// Device-side helpers shared by the ftmoe kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ftmoe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kWave = 64;
+
+// Weight format tags (values match ftmoe_wfmt).
+constexpr int kMXFP4 = 1;
+constexpr int kNVFP4 = 2;
+constexpr int kFP8 = 3;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: weights are read once per use).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------- bf16 ----
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ------------------------------------------------------------- codecs -----
+
+// E8M0 scale code -> the fp32 whose exponent field is that code.  The gfx950
+// scaled conversions read only the exponent field of their scale operand, so
+// this encodes 2^(code - 127) for every code 0..254 (code 0 included).
+__device__ __forceinline__ float e8m0_as_scale(uint32_t code) {
+  return __uint_as_float(code << 23);
+}
+
+// E4M3FN byte -> fp32 value (exact; hardware decode of the OCP format).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code & 0xFFu, 1.0f, false);
+  return v[0];
+}
+
+// Eight packed E2M1 nibbles (one dword, element 0 in the low nibble) times a
+// power-of-two scale given as an E8M0-style float -> four bf16 pairs.
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t w, float scale, uint32_t out[4]) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  out[0] = __builtin_bit_cast(uint32_t, p0);
+  out[1] = __builtin_bit_cast(uint32_t, p1);
+  out[2] = __builtin_bit_cast(uint32_t, p2);
+  out[3] = __builtin_bit_cast(uint32_t, p3);
+}
+
+// Eight E2M1 nibbles times an arbitrary fp32 factor -> four bf16 pairs.
+// Used for NVFP4, whose E4M3 block scale is not a power of two: the product
+// of a 2-bit and a 4-bit significand fits bf16's 8 bits, so it is exact.
+__device__ __forceinline__ void fp4x8_to_bf16_mul(uint32_t w, float factor, uint32_t out[4]) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = pack_bf16x2(v0[0] * factor, v0[1] * factor);
+  out[1] = pack_bf16x2(v1[0] * factor, v1[1] * factor);
+  out[2] = pack_bf16x2(v2[0] * factor, v2[1] * factor);
+  out[3] = pack_bf16x2(v3[0] * factor, v3[1] * factor);
+}
+
+// fp32 -> E4M3FN code: round to nearest even, saturate to +-448.  The
+// hardware conversion rounds to nearest even but does not saturate, so the
+// input is clamped first.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------ wave ops ----
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+// silu(g) * u in fp32.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace ftmoe

@@ -1,0 +1,492 @@
+// C ABI of the ftmoe library: argument validation, workspace carving and the
+// fixed kernel sequence of each entry point.  See include/ftmoe.h.
+#include <stdarg.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/ftmoe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace ftmoe;
+
+thread_local std::string g_last_error;
+
+ftmoe_status fail(ftmoe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ftmoe_status fail(ftmoe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ftmoe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FTMOE_OK;
+  return fail(FTMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FT_TRY(expr)                          \
+  do {                                        \
+    const ftmoe_status st_ = (expr);          \
+    if (st_ != FTMOE_OK) return st_;          \
+  } while (0)
+
+#define FT_HIP(expr, what)                                 \
+  do {                                                     \
+    const hipError_t e_ = (expr);                          \
+    if (e_ != hipSuccess) return hip_status(e_, what);     \
+  } while (0)
+
+// ---- optional per-kernel timing (diagnostics) ----
+// When enabled on this thread, each launch is bracketed by two HIP events on
+// its stream; ftmoe_timing_collect() waits for them and sums durations per
+// kernel name.  Events come from a pool that is reused after each collect.
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t a, b;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_pending;
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_timing) return launch();
+  TimedLaunch t{name, pool_event(), pool_event()};
+  if (t.a) hipEventRecord(t.a, s);
+  const hipError_t e = launch();
+  if (t.b) hipEventRecord(t.b, s);
+  if (t.a && t.b) g_pending.push_back(t);
+  return e;
+}
+
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTokens = 1 << 20;
+constexpr int kDecodeAutoMaxT = 16;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ftmoe_status check_qweight(const ftmoe_qweight& q, const char* name, int fmt, int E, int n, int k) {
+  if (q.fmt != fmt)
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.fmt=%d but the layer's routed experts use %d", name, q.fmt, fmt);
+  if (q.num_experts != E || q.n != n || q.k != k)
+    return fail(FTMOE_ERR_INVALID_ARG, "%s is [%d][%d][%d], expected [%d][%d][%d]", name, q.num_experts, q.n, q.k,
+                E, n, k);
+  if (!q.codes) return fail(FTMOE_ERR_INVALID_ARG, "%s.codes is NULL", name);
+  if (!aligned16(q.codes)) return fail(FTMOE_ERR_INVALID_ARG, "%s.codes is not 16-byte aligned", name);
+  if (fmt == FTMOE_W_MXFP4 || fmt == FTMOE_W_NVFP4) {
+    if (!q.block_scales) return fail(FTMOE_ERR_INVALID_ARG, "%s.block_scales is NULL", name);
+    if (!aligned16(q.block_scales))
+      return fail(FTMOE_ERR_INVALID_ARG, "%s.block_scales is not 16-byte aligned", name);
+  }
+  if (fmt == FTMOE_W_NVFP4 || fmt == FTMOE_W_FP8_E4M3) {
+    if (!q.tensor_scales) return fail(FTMOE_ERR_INVALID_ARG, "%s.tensor_scales is NULL", name);
+  }
+  return FTMOE_OK;
+}
+
+ftmoe_status check_layer(const ftmoe_layer* L) {
+  if (!L) return fail(FTMOE_ERR_INVALID_ARG, "layer is NULL");
+  if (L->hidden <= 0 || L->hidden % 128)
+    return fail(FTMOE_ERR_UNSUPPORTED, "hidden=%d must be a positive multiple of 128", L->hidden);
+  if (L->inter <= 0 || L->inter % 128)
+    return fail(FTMOE_ERR_UNSUPPORTED, "inter=%d must be a positive multiple of 128", L->inter);
+  if (L->top_k < 1 || L->top_k > kMaxTopK)
+    return fail(FTMOE_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", L->top_k, kMaxTopK);
+  if (L->num_experts < L->top_k || L->num_experts > kMaxExperts)
+    return fail(FTMOE_ERR_UNSUPPORTED, "num_experts=%d outside [top_k=%d, %d]", L->num_experts, L->top_k,
+                kMaxExperts);
+  if (L->act != FTMOE_ACT_BF16 && L->act != FTMOE_ACT_FP8_PER_TENSOR)
+    return fail(FTMOE_ERR_INVALID_ARG, "act=%d is not an ftmoe_afmt", L->act);
+  if (L->path != FTMOE_PATH_AUTO && L->path != FTMOE_PATH_DECODE && L->path != FTMOE_PATH_PREFILL)
+    return fail(FTMOE_ERR_INVALID_ARG, "path=%d is not an ftmoe_path", L->path);
+  if (!L->router_w) return fail(FTMOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (!aligned16(L->router_w)) return fail(FTMOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
+  const int fmt = L->gate_up.fmt;
+  if (fmt != FTMOE_W_MXFP4 && fmt != FTMOE_W_NVFP4 && fmt != FTMOE_W_FP8_E4M3)
+    return fail(FTMOE_ERR_INVALID_ARG, "gate_up.fmt=%d is not an ftmoe_wfmt", fmt);
+  if (L->act == FTMOE_ACT_FP8_PER_TENSOR && fmt != FTMOE_W_FP8_E4M3)
+    return fail(FTMOE_ERR_UNSUPPORTED, "FP8 per-tensor activations need FP8 weights");
+  FT_TRY(check_qweight(L->gate_up, "gate_up", fmt, L->num_experts, 2 * L->inter, L->hidden));
+  FT_TRY(check_qweight(L->down, "down", fmt, L->num_experts, L->hidden, L->inter));
+  if (L->shared_inter < 0) return fail(FTMOE_ERR_INVALID_ARG, "shared_inter=%d is negative", L->shared_inter);
+  if (L->shared_inter > 0) {
+    if (L->shared_inter % 128)
+      return fail(FTMOE_ERR_UNSUPPORTED, "shared_inter=%d must be a multiple of 128", L->shared_inter);
+    if (L->act == FTMOE_ACT_FP8_PER_TENSOR)
+      return fail(FTMOE_ERR_UNSUPPORTED, "a shared expert with FP8 per-tensor activations is not supported");
+    FT_TRY(check_qweight(L->shared_gate_up, "shared_gate_up", fmt, 1, 2 * L->shared_inter, L->hidden));
+    FT_TRY(check_qweight(L->shared_down, "shared_down", fmt, 1, L->hidden, L->shared_inter));
+    if (!L->shared_gate_w) return fail(FTMOE_ERR_INVALID_ARG, "shared_gate_w is NULL");
+    if (!aligned16(L->shared_gate_w))
+      return fail(FTMOE_ERR_INVALID_ARG, "shared_gate_w is not 16-byte aligned");
+  }
+  return FTMOE_OK;
+}
+
+ftmoe_status check_tokens(int32_t T) {
+  if (T < 0 || T > kMaxTokens) return fail(FTMOE_ERR_INVALID_ARG, "T=%d outside [0, %d]", T, kMaxTokens);
+  return FTMOE_OK;
+}
+
+int max_padded(int T, int k, int E, int BM) {
+  const long long n = static_cast<long long>(T) * k;
+  const long long p = n + std::min<long long>(E, n) * (BM - 1);
+  return static_cast<int>((p + BM - 1) / BM * BM);
+}
+
+size_t up256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+struct Plan {
+  bool decode = false;
+  int BM = 0, P = 0, nblocks = 0, shared_rows = 0, shared_blocks = 0;
+  size_t logits = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
+         scal = 0, ascratch = 0, xq = 0, h = 0, o = 0, hs = 0, s = 0, total = 0;
+};
+
+Plan make_plan(const ftmoe_layer* L, int T) {
+  Plan p;
+  const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
+  p.decode = L->path == FTMOE_PATH_DECODE || (L->path == FTMOE_PATH_AUTO && T <= kDecodeAutoMaxT);
+  p.BM = p.decode ? kDecodeBM : kPrefillBM;
+  p.P = max_padded(T, k, E, p.BM);
+  p.nblocks = p.P / p.BM;
+  p.shared_blocks = (T + p.BM - 1) / p.BM;
+  p.shared_rows = p.shared_blocks * p.BM;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  const size_t tk = static_cast<size_t>(T) * k;
+  p.logits = take(static_cast<size_t>(T) * (E + 1) * 4);
+  p.ids = take(tk * 4);
+  p.w = take(tk * 4);
+  p.sg = take(static_cast<size_t>(T) * 4);
+  p.counts = take(static_cast<size_t>(E) * 4);
+  p.offsets = take(static_cast<size_t>(E + 1) * 4);
+  p.sorted = take(static_cast<size_t>(p.P) * 4);
+  p.bexp = take(static_cast<size_t>(p.nblocks) * 4);
+  p.npad = take(4);
+  p.scal = take(256);
+  p.ascratch = take(align_scratch_bytes(T, k, E, p.BM));
+  p.xq = take(L->act == FTMOE_ACT_FP8_PER_TENSOR ? static_cast<size_t>(T) * H : 0);
+  p.h = take(static_cast<size_t>(p.P) * I * 2);
+  p.o = take(tk * H * 2);
+  if (L->shared_inter > 0) {
+    p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
+    p.s = take(static_cast<size_t>(T) * H * 2);
+  }
+  p.total = off;
+  return p;
+}
+
+QW to_qw(const ftmoe_qweight& q) {
+  QW w;
+  w.fmt = q.fmt;
+  w.n = q.n;
+  w.k = q.k;
+  w.codes = static_cast<const uint8_t*>(q.codes);
+  w.scales = static_cast<const uint8_t*>(q.block_scales);
+  w.tscale = q.tensor_scales;
+  return w;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+ftmoe_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (ws_bytes < p.total)
+    return fail(FTMOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, p.total);
+  if (p.total > 0 && !ws) return fail(FTMOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(FTMOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return FTMOE_OK;
+}
+
+ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const Plan& p, void* ws, int32_t* ids,
+                           float* w, float* sg, hipStream_t s) {
+  const bool shared = L->shared_inter > 0;
+  float* logits = at<float>(ws, p.logits);
+  FT_HIP(timed("router_logits", s,
+               [&] {
+                 return launch_router_logits(x, T, L->hidden, L->router_w, L->num_experts,
+                                             shared ? L->shared_gate_w : nullptr, logits, s);
+               }),
+         "router logits launch");
+  FT_HIP(timed("topk", s,
+               [&] { return launch_topk(logits, T, L->num_experts, L->top_k, L->router_bias, shared, ids, w, sg, s); }),
+         "top-k launch");
+  return FTMOE_OK;
+}
+
+ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, const int32_t* ids, const float* w,
+                             const float* sg, const Plan& p, void* ws, uint16_t* y, hipStream_t s) {
+  const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
+  const bool fp8act = L->act == FTMOE_ACT_FP8_PER_TENSOR;
+  uint32_t* scal = at<uint32_t>(ws, p.scal);
+  uint32_t* amax_x = scal + 0;
+  uint32_t* amax_h = scal + 1;
+  int32_t* sorted = at<int32_t>(ws, p.sorted);
+  int32_t* bexp = at<int32_t>(ws, p.bexp);
+  FT_HIP(timed("align", s,
+               [&] {
+                 return launch_align(ids, T, k, E, p.BM, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                     sorted, bexp, at<int32_t>(ws, p.npad), at<void>(ws, p.ascratch), scal,
+                                     fp8act ? 2 : 0, s);
+               }),
+         "align launch");
+  const uint8_t* xq = nullptr;
+  if (fp8act) {
+    FT_HIP(timed("amax_x", s, [&] { return launch_amax_bf16(x, static_cast<int64_t>(T) * H, amax_x, s); }),
+           "amax launch");
+    FT_HIP(timed("quant_x", s,
+                 [&] {
+                   return launch_quant_fp8(x, static_cast<int64_t>(T) * H, amax_x, at<uint8_t>(ws, p.xq), nullptr, s);
+                 }),
+           "quantise launch");
+    xq = at<uint8_t>(ws, p.xq);
+  }
+  Rows rr;
+  rr.sorted_ids = sorted;
+  rr.block_expert = bexp;
+  rr.n_flat = T * k;
+  rr.top_k = k;
+  rr.num_blocks = p.nblocks;
+  const QW gu = to_qw(L->gate_up), dn = to_qw(L->down);
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  uint16_t* o = at<uint16_t>(ws, p.o);
+  const uint32_t* ax = fp8act ? amax_x : nullptr;
+  uint32_t* ah = fp8act ? amax_h : nullptr;
+  const bool shared = L->shared_inter > 0;
+  Rows rs;
+  rs.sorted_ids = nullptr;
+  rs.block_expert = nullptr;
+  rs.n_flat = T;
+  rs.top_k = 1;
+  rs.num_blocks = p.shared_blocks;
+  uint16_t* hs = shared ? at<uint16_t>(ws, p.hs) : nullptr;
+  uint16_t* sh = shared ? at<uint16_t>(ws, p.s) : nullptr;
+  if (p.decode) {
+    FT_HIP(timed("decode_gateup", s,
+                 [&] { return launch_decode_gateup(gu, rr, x, xq, ax, H, I, h, ah, std::min(T, kDecodeBM), s); }),
+           "decode gate_up launch");
+    FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(dn, rr, h, ah, H, I, o, s); }),
+           "decode down launch");
+    if (shared) {
+      FT_HIP(timed("decode_shared_gateup", s,
+                   [&] {
+                     return launch_decode_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
+                                                 hs, nullptr, std::min(T, kDecodeBM), s);
+                   }),
+             "decode shared gate_up launch");
+      FT_HIP(timed("decode_shared_down", s,
+                   [&] { return launch_decode_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
+             "decode shared down launch");
+    }
+  } else {
+    FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ah, s); }),
+           "gate_up GEMM launch");
+    FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, ah, H, I, o, s); }), "down GEMM launch");
+    if (shared) {
+      FT_HIP(timed("gemm_shared_gateup", s,
+                   [&] {
+                     return launch_gemm_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
+                                               hs, nullptr, s);
+                   }),
+             "shared gate_up GEMM launch");
+      FT_HIP(timed("gemm_shared_down", s,
+                   [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
+             "shared down GEMM launch");
+    }
+  }
+  FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),
+         "combine launch");
+  return FTMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ftmoe_status ftmoe_workspace_size(const ftmoe_layer* layer, int32_t T, size_t* bytes) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  FT_TRY(check_tokens(T));
+  if (!bytes) return fail(FTMOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_plan(layer, T).total;
+  return FTMOE_OK;
+}
+
+int32_t ftmoe_align_max_padded(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || T > kMaxTokens || k < 1 || k > kMaxTopK || E < 1 || E > kMaxExperts || block_m < 1 ||
+      block_m > 1024)
+    return -1;
+  return max_padded(T, k, E, block_m);
+}
+
+size_t ftmoe_align_workspace_size(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (ftmoe_align_max_padded(T, k, E, block_m) < 0) return 0;
+  return align_scratch_bytes(T, k, E, block_m);
+}
+
+ftmoe_status ftmoe_route(const ftmoe_layer* layer, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                         int32_t* topk_ids, float* topk_w, float* shared_gate, void* stream) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  FT_TRY(check_tokens(T));
+  if (T == 0) return FTMOE_OK;
+  if (!x || !topk_ids || !topk_w) return fail(FTMOE_ERR_INVALID_ARG, "x, topk_ids and topk_w must be non-NULL");
+  if (!aligned16(x)) return fail(FTMOE_ERR_INVALID_ARG, "x is not 16-byte aligned");
+  if (layer->shared_inter > 0 && !shared_gate)
+    return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
+  const Plan p = make_plan(layer, T);
+  FT_TRY(check_ws(p, ws, ws_bytes));
+  return enqueue_route(layer, x, T, p, ws, topk_ids, topk_w, shared_gate, static_cast<hipStream_t>(stream));
+}
+
+ftmoe_status ftmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                         void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (ftmoe_align_max_padded(T, k, E, block_m) < 0)
+    return fail(FTMOE_ERR_INVALID_ARG, "bad sizes T=%d k=%d E=%d block_m=%d", T, k, E, block_m);
+  if (T == 0) return FTMOE_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_ids || !block_expert || !num_padded)
+    return fail(FTMOE_ERR_INVALID_ARG, "align: every array must be non-NULL");
+  const size_t need = align_scratch_bytes(T, k, E, block_m);
+  if (ws_bytes < need) return fail(FTMOE_ERR_WORKSPACE, "align needs %zu bytes of workspace", need);
+  if (need > 0 && (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+    return fail(FTMOE_ERR_WORKSPACE, "align workspace must be non-NULL and 256-byte aligned");
+  return hip_status(launch_align(topk_ids, T, k, E, block_m, counts, offsets, sorted_ids, block_expert, num_padded,
+                                 ws, nullptr, 0, static_cast<hipStream_t>(stream)),
+                    "align launch");
+}
+
+ftmoe_status ftmoe_experts_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T, const int32_t* topk_ids,
+                                   const float* topk_w, const float* shared_gate, void* ws, size_t ws_bytes,
+                                   uint16_t* y, void* stream) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  FT_TRY(check_tokens(T));
+  if (T == 0) return FTMOE_OK;
+  if (!x || !topk_ids || !topk_w || !y)
+    return fail(FTMOE_ERR_INVALID_ARG, "x, topk_ids, topk_w and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if (layer->shared_inter > 0 && !shared_gate)
+    return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
+  const Plan p = make_plan(layer, T);
+  FT_TRY(check_ws(p, ws, ws_bytes));
+  return enqueue_experts(layer, x, T, topk_ids, topk_w, shared_gate, p, ws, y, static_cast<hipStream_t>(stream));
+}
+
+ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                           uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  FT_TRY(check_tokens(T));
+  if (T == 0) return FTMOE_OK;
+  if (!x || !y) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  const Plan p = make_plan(layer, T);
+  FT_TRY(check_ws(p, ws, ws_bytes));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
+  float* sg = at<float>(ws, p.sg);
+  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, s));
+  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, s);
+}
+
+ftmoe_status ftmoe_quantize_fp8_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(FTMOE_ERR_INVALID_ARG, "n=%lld is negative", static_cast<long long>(n));
+  if (n == 0) return FTMOE_OK;
+  if (!x || !q || !scale) return fail(FTMOE_ERR_INVALID_ARG, "x, q and scale must be non-NULL");
+  if (!aligned16(x) || !aligned16(q)) return fail(FTMOE_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+  if (!ws || ws_bytes < 256 || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(FTMOE_ERR_WORKSPACE, "quantiser needs 256 bytes of 256-byte aligned workspace");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  FT_HIP(launch_zero_u32(amax, 1, s), "zero launch");
+  FT_HIP(launch_amax_bf16(x, n, amax, s), "amax launch");
+  FT_HIP(launch_quant_fp8(x, n, amax, q, scale, s), "quantise launch");
+  return FTMOE_OK;
+}
+
+void ftmoe_timing_enable(int32_t on) { g_timing = on != 0; }
+
+int32_t ftmoe_timing_collect(int32_t max_entries, char* names, double* total_ms, int64_t* counts) {
+  std::vector<std::string> keys;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+  for (const TimedLaunch& t : g_pending) {
+    float m = 0.f;
+    hipEventSynchronize(t.b);
+    if (hipEventElapsedTime(&m, t.a, t.b) != hipSuccess) m = 0.f;
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != t.name) ++i;
+    if (i == keys.size()) {
+      keys.emplace_back(t.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += m;
+    cnt[i] += 1;
+    g_event_pool.push_back(t.a);
+    g_event_pool.push_back(t.b);
+  }
+  g_pending.clear();
+  const int32_t n = static_cast<int32_t>(keys.size());
+  for (int32_t i = 0; i < n && i < max_entries; ++i) {
+    if (names) {
+      strncpy(names + 32 * i, keys[i].c_str(), 31);
+      names[32 * i + 31] = 0;
+    }
+    if (total_ms) total_ms[i] = ms[i];
+    if (counts) counts[i] = cnt[i];
+  }
+  return n;
+}
+
+const char* ftmoe_status_string(ftmoe_status st) {
+  switch (st) {
+    case FTMOE_OK: return "FTMOE_OK";
+    case FTMOE_ERR_INVALID_ARG: return "FTMOE_ERR_INVALID_ARG";
+    case FTMOE_ERR_UNSUPPORTED: return "FTMOE_ERR_UNSUPPORTED";
+    case FTMOE_ERR_WORKSPACE: return "FTMOE_ERR_WORKSPACE";
+    case FTMOE_ERR_HIP: return "FTMOE_ERR_HIP";
+  }
+  return "FTMOE_UNKNOWN_STATUS";
+}
+
+const char* ftmoe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ftmoe_version(void) { return 100; }
+
+}  // extern "C"

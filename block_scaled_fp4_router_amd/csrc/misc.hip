@@ -1,0 +1,137 @@
+// Per-tensor E4M3 activation quantisation and the weighted combine.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ftmoe {
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s) {
+  zero_u32_kernel<<<1, 64, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ amax(|x|) ---
+// Non-negative floats order like their bit patterns, so the running maximum
+// is an unsigned atomicMax on the bits.
+__global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                        uint32_t* amax_bits) {
+  const int64_t n8 = n / 8;
+  float m = 0.f;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(w[j] & 0xFFFF)));
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(w[j] >> 16)));
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += blockDim.x)
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(x[i])));
+  m = wave_max(m);
+  if (lane_id() == 0) atomicMax(amax_bits, __float_as_uint(m));
+}
+
+// s = amax / 448 (1 when amax is 0), the dequantisation scale.
+__device__ __forceinline__ float fp8_scale_from_amax(uint32_t bits) {
+  const float a = __uint_as_float(bits);
+  return a > 0.f ? a / 448.0f : 1.0f;
+}
+
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                        const uint32_t* __restrict__ amax_bits,
+                                                        uint8_t* __restrict__ q, float* scale_out) {
+  const float s = fp8_scale_from_amax(*amax_bits);
+  const int64_t n8 = n / 8;
+  const int64_t i0 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i0 == 0 && scale_out) *scale_out = s;
+  for (int64_t i = i0; i < n8; i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t lo = f32x2_to_e4m3x2(bf16_to_f32(w[2 * j] & 0xFFFF) / s, bf16_to_f32(w[2 * j] >> 16) / s);
+      const uint32_t hi = f32x2_to_e4m3x2(bf16_to_f32(w[2 * j + 1] & 0xFFFF) / s, bf16_to_f32(w[2 * j + 1] >> 16) / s);
+      out[j] = lo | (hi << 16);
+    }
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(out[0], out[1]);
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += blockDim.x)
+      q[i] = static_cast<uint8_t>(f32x2_to_e4m3x2(bf16_to_f32(x[i]) / s, 0.f) & 0xFF);
+}
+
+static int elementwise_grid(int64_t n8) {
+  int64_t g = (n8 + 255) / 256;
+  if (g > 4096) g = 4096;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* amax_bits, hipStream_t s) {
+  amax_bf16_kernel<<<elementwise_grid(n / 8), 256, 0, s>>>(x, n, amax_bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, const uint32_t* amax_bits, uint8_t* q,
+                            float* scale_out, hipStream_t s) {
+  quant_fp8_kernel<<<elementwise_grid(n / 8), 256, 0, s>>>(x, n, amax_bits, q, scale_out);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- combine ---
+// One thread per 8 outputs: y[t, n:n+8] = sum_j w[t,j] o[t*k+j, n:n+8]
+// (+ sg[t] * sh[t, n:n+8]), fp32 sums in ascending j, bf16 nearest-even.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o,
+                                                      const float* __restrict__ w, int T, int k, int H,
+                                                      const float* __restrict__ sg,
+                                                      const uint16_t* __restrict__ sh,
+                                                      uint16_t* __restrict__ y) {
+  const int per_row = H / 8;
+  const int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (idx >= static_cast<int64_t>(T) * per_row) return;
+  const int t = static_cast<int>(idx / per_row);
+  const int c = static_cast<int>(idx % per_row) * 8;
+  float acc[8] = {};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[static_cast<size_t>(t) * k + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(o + (static_cast<size_t>(t) * k + j) * H + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(wj, bf16_to_f32(u[i] & 0xFFFF), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(wj, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    }
+  }
+  if (sg) {
+    const float g = sg[t];
+    const uint4 v = *reinterpret_cast<const uint4*>(sh + static_cast<size_t>(t) * H + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, bf16_to_f32(u[i] & 0xFFFF), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    }
+  }
+  uint4 r;
+  r.x = pack_bf16x2(acc[0], acc[1]);
+  r.y = pack_bf16x2(acc[2], acc[3]);
+  r.z = pack_bf16x2(acc[4], acc[5]);
+  r.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(y + static_cast<size_t>(t) * H + c) = r;
+}
+
+hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H, const float* sg,
+                          const uint16_t* sh, uint16_t* y, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(T) * (H / 8);
+  combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(o, w, T, k, H, sg, sh, y);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -1,0 +1,226 @@
+/*
+ * ftmoe.h -- routed Mixture-of-Experts layer forward over block-quantised
+ * expert weights (MXFP4, NVFP4, FP8 E4M3) on AMD Instinct MI355X (gfx950).
+ *
+ * The FreeToken README ("About": an edge-native Mixture-of-Experts serving
+ * engine; "Broad MoE & Ecosystem Support": MXFP4, NVFP4, FP8, BF16 formats)
+ * names the layer and its weight formats but never writes its arithmetic.
+ * This library computes the standard routed SwiGLU MoE layer:
+ *
+ *   l[t,e]   = x_t . W_r[e] + b[e]                       router GEMM
+ *   ids_t    = k largest l[t,:], descending, ties -> lower expert index
+ *   w_t      = softmax of the k selected logits          renormalised weights
+ *   h_tj     = silu(Wg[e] x_t) * (Wu[e] x_t),  e = ids_t[j]     gate_up + SwiGLU
+ *   y_t      = sum_j w_tj Wd[e] h_tj   (j ascending)    down + weighted combine
+ *   y_t     += sigmoid(x_t . w_sg) * shared_mlp(x_t)    optional shared expert
+ *
+ * With per-tensor FP8 activations, x and h are each quantised to E4M3 with
+ * one scale amax/448 over the whole GEMM input (all T rows of x; all T*k rows
+ * of h) before their GEMM.
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers owned by the caller.  Structs
+ *    (ftmoe_layer, ftmoe_qweight) live in HOST memory and are only read
+ *    during the call.  The library never allocates, frees or synchronises
+ *    device memory; scratch comes from the caller's workspace, sized by
+ *    ftmoe_workspace_size().
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on it, enqueue a fixed sequence of kernels whose
+ *    grid sizes depend only on the arguments (never on device data), and
+ *    issue no host synchronisation, so they can be captured in a HIP graph.
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    error nothing is enqueued and no output is written; the status says why
+ *    (ftmoe_last_error() gives a message).  A failed kernel launch returns
+ *    FTMOE_ERR_HIP.  No C++ exception crosses this interface.
+ *  - No mutable global state is touched by the compute entry points, so
+ *    concurrent calls on different streams with different workspaces are
+ *    safe.  Two calls sharing one workspace must be ordered by the caller.
+ *  - Layouts are row-major with the last index contiguous.  bf16 tensors are
+ *    passed as uint16_t bit patterns.
+ */
+#ifndef FTMOE_H
+#define FTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FTMOE_OK = 0,
+  FTMOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, ... */
+  FTMOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle */
+  FTMOE_ERR_WORKSPACE = 3,    /* workspace missing or too small            */
+  FTMOE_ERR_HIP = 4           /* HIP runtime reported an error             */
+} ftmoe_status;
+
+/* Expert weight formats (FreeToken README, "Broad MoE & Ecosystem Support").
+ *  MXFP4: OCP Microscaling v1.0.  E2M1 codes, two per byte (element 2i in the
+ *         low nibble), one E8M0 scale byte (2^(s-127)) per 32 elements along K.
+ *  NVFP4: E2M1 codes as above, one E4M3FN scale byte per 16 elements along K,
+ *         and one fp32 multiplier per matrix: w = e2m1 * e4m3(s_blk) * g.
+ *  FP8:   one E4M3FN (OCP: bias 7, max 448, no inf) byte per element and one
+ *         fp32 multiplier per matrix: w = e4m3 * g.                       */
+typedef enum {
+  FTMOE_W_MXFP4 = 1,
+  FTMOE_W_NVFP4 = 2,
+  FTMOE_W_FP8_E4M3 = 3
+} ftmoe_wfmt;
+
+/* Activation format fed to the expert GEMMs.  FP8_PER_TENSOR is the W8A8
+ * scheme of the FreeToken commit message on per-tensor FP8 projections: one
+ * dynamic E4M3 scale per GEMM input.  It requires FP8 weights.            */
+typedef enum {
+  FTMOE_ACT_BF16 = 0,
+  FTMOE_ACT_FP8_PER_TENSOR = 1
+} ftmoe_afmt;
+
+/* Expert-kernel family.  AUTO picks the bandwidth-bound decode kernels for
+ * small token counts and the MFMA grouped GEMMs otherwise; the other values
+ * force one for A/B comparisons (both compute the same function).        */
+typedef enum {
+  FTMOE_PATH_AUTO = 0,
+  FTMOE_PATH_DECODE = 1,
+  FTMOE_PATH_PREFILL = 2
+} ftmoe_path;
+
+/* One stacked set of expert matrices, [E][N][K], K contiguous.
+ *  codes:         FP4: [E][N][K/2] bytes.  FP8: [E][N][K] bytes.
+ *  block_scales:  MXFP4: [E][N][K/32] E8M0.  NVFP4: [E][N][K/16] E4M3.  FP8: NULL.
+ *  tensor_scales: NVFP4, FP8: [E] fp32 dequantisation multipliers.  MXFP4: NULL.
+ * All three must be 16-byte aligned.                                       */
+typedef struct {
+  int32_t fmt;          /* ftmoe_wfmt */
+  int32_t num_experts;
+  int32_t n;
+  int32_t k;
+  const void* codes;
+  const void* block_scales;
+  const float* tensor_scales;
+} ftmoe_qweight;
+
+/* One MoE layer.
+ *  router_w     [E][H] fp32.   router_bias [E] fp32 or NULL (added to the
+ *               logits before both selection and weighting).
+ *  gate_up      N = 2*inter, K = hidden: rows [0, inter) are the gate
+ *               projection, rows [inter, 2*inter) the up projection.
+ *  down         N = hidden, K = inter.
+ *  shared_inter 0 for no shared expert; otherwise shared_gate_up (E = 1,
+ *               N = 2*shared_inter, K = hidden), shared_down (E = 1,
+ *               N = hidden, K = shared_inter) in the routed experts' format,
+ *               and shared_gate_w [H] fp32: the shared expert's output is
+ *               scaled by sigmoid(x . shared_gate_w) and added after the
+ *               routed combine.
+ * Limits: hidden and inter multiples of 128; 1 <= top_k <= 16;
+ * top_k <= num_experts <= 1024.                                            */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t act;          /* ftmoe_afmt */
+  int32_t path;         /* ftmoe_path */
+  const float* router_w;
+  const float* router_bias;
+  ftmoe_qweight gate_up;
+  ftmoe_qweight down;
+  int32_t shared_inter;
+  int32_t reserved0;
+  ftmoe_qweight shared_gate_up;
+  ftmoe_qweight shared_down;
+  const float* shared_gate_w;
+} ftmoe_layer;
+
+/* Bytes of workspace that ftmoe_forward / ftmoe_experts_forward /
+ * ftmoe_route need for T tokens of this layer (T >= 0).  The workspace must
+ * be 256-byte aligned; its contents need no initialisation and are
+ * meaningless after a call.                                               */
+ftmoe_status ftmoe_workspace_size(const ftmoe_layer* layer, int32_t T, size_t* bytes);
+
+/* Capacity of the padded expert-sorted row list written by ftmoe_align:
+ * roundup(T*k + min(E, T*k)*(block_m - 1), block_m).  Returns -1 on bad
+ * arguments.                                                              */
+int32_t ftmoe_align_max_padded(int32_t T, int32_t k, int32_t E, int32_t block_m);
+
+/* Scratch bytes ftmoe_align needs (device, 256-byte aligned).             */
+size_t ftmoe_align_workspace_size(int32_t T, int32_t k, int32_t E, int32_t block_m);
+
+/* Router: logits, softmax top-k with renormalised weights, and the shared
+ * expert's sigmoid gate.
+ *  x           [T][H] bf16.
+ *  topk_ids    [T][k] int32 out: experts by descending logit.
+ *  topk_w      [T][k] fp32 out: softmax over the k selected logits.
+ *  shared_gate [T] fp32 out, or NULL; required when the layer has a shared
+ *              expert.
+ *  ws          scratch of ftmoe_workspace_size(layer, T) bytes.          */
+ftmoe_status ftmoe_route(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
+                         void* ws, size_t ws_bytes,
+                         int32_t* topk_ids, float* topk_w, float* shared_gate,
+                         void* stream);
+
+/* Token-to-expert alignment (count, prefix-sum, padded scatter).
+ * Flat row i = t*k + j goes to expert topk_ids[i] (each in [0, E)).
+ *  counts       [E]     rows per expert.
+ *  offsets      [E+1]   exclusive prefix sum of counts rounded up to block_m.
+ *  sorted_ids   [P]     P = ftmoe_align_max_padded(T, k, E, block_m): each
+ *               expert's rows in ascending i at [offsets[e], offsets[e+1]),
+ *               padded with the sentinel T*k; entries >= num_padded are T*k.
+ *  block_expert [P/block_m] expert of each block of block_m rows, -1 past
+ *               num_padded.
+ *  num_padded   [1]     offsets[E].
+ *  ws           ftmoe_align_workspace_size() bytes of scratch.
+ * The result is unique (stable order), hence bit-reproducible.           */
+ftmoe_status ftmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                         int32_t* block_expert, int32_t* num_padded,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Experts given a routing: align, gate_up GEMM with fused SwiGLU, down GEMM,
+ * weighted combine and the optional gated shared expert.
+ *  topk_ids, topk_w  as written by ftmoe_route.
+ *  shared_gate       [T] fp32 sigmoid gate, required iff shared_inter > 0.
+ *  y                 [T][H] bf16 out (round to nearest even).             */
+ftmoe_status ftmoe_experts_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
+                                   const int32_t* topk_ids, const float* topk_w,
+                                   const float* shared_gate,
+                                   void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
+/* The whole layer: ftmoe_route then ftmoe_experts_forward.
+ *  topk_ids_out / topk_w_out: optional [T][k] copies of the routing (NULL
+ *  to keep it in the workspace only).                                    */
+ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
+                           void* ws, size_t ws_bytes, uint16_t* y,
+                           int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
+/* Per-tensor E4M3 activation quantiser used by FTMOE_ACT_FP8_PER_TENSOR,
+ * exposed for testing: scale[0] = amax(|x|)/448 (1 if amax is 0, fp32) and
+ * q = E4M3(x / scale) rounded to nearest even and saturated to +-448.
+ *  x [n] bf16 in; q [n] bytes out; scale [1] fp32 out; ws >= 256 bytes.  */
+ftmoe_status ftmoe_quantize_fp8_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,
+                                           void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostics: per-kernel timing.  While enabled on the calling thread,
+ * every kernel the entry points enqueue is bracketed by two HIP events on its
+ * stream (not for use under graph capture; the events are host objects the
+ * library creates and reuses).  ftmoe_timing_collect waits for the recorded
+ * events, writes up to max_entries rows -- kernel name (32-byte slots in
+ * `names`), summed milliseconds and launch count -- clears the record and
+ * returns the number of distinct kernels seen.  Any output may be NULL.    */
+void ftmoe_timing_enable(int32_t on);
+int32_t ftmoe_timing_collect(int32_t max_entries, char* names, double* total_ms, int64_t* counts);
+
+/* Human-readable name of a status, and the message of the last error seen
+ * by this thread (empty if none).                                         */
+const char* ftmoe_status_string(ftmoe_status s);
+const char* ftmoe_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch.                     */
+int32_t ftmoe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FTMOE_H */

@@ -1,0 +1,171 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and its host-side argument checks return the documented statuses
+before anything touches a GPU (validation never dereferences the device
+pointers, so placeholders stand in for them here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_router_amd as ft
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ftmoe.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(ft.LIB_PATH), reason="libftmoe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ftmoe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("ftmoe_route", "ftmoe_align", "ftmoe_experts_forward", "ftmoe_forward"):
+        assert n in names
+    assert set(names) == set(ft.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ft.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+@needs_lib
+@pytest.mark.parametrize("T,k,E,BM", [(0, 2, 8, 16), (1, 8, 128, 16), (8, 8, 128, 16), (16, 2, 8, 64),
+                                      (4096, 8, 128, 64), (16384, 8, 128, 64), (37, 3, 5, 7)])
+def test_align_capacity_matches_oracle(T, k, E, BM):
+    assert ft.align_max_padded(T, k, E, BM) == oracle.align_max_padded(T, k, E, BM)
+
+
+@needs_lib
+def test_align_capacity_rejects_bad_sizes():
+    for args in [(-1, 2, 8, 16), (4, 0, 8, 16), (4, 17, 32, 16), (4, 2, 0, 16), (4, 2, 8, 0), (4, 2, 2000, 16)]:
+        assert ft.align_max_padded(*args) == -1
+
+
+FAKE = 1 << 20  # an aligned placeholder address; never dereferenced by validation
+
+
+def _qw(fmt, E, n, k):
+    return ft.QWeightDesc(fmt, E, n, k, FAKE, FAKE, FAKE)
+
+
+def good_layer():
+    d = ft.LayerDesc()
+    d.hidden, d.inter, d.num_experts, d.top_k = 256, 128, 8, 2
+    d.act, d.path = ft.ACT_BF16, ft.PATH_AUTO
+    d.router_w, d.router_bias = FAKE, None
+    d.gate_up = _qw(ft.W_MXFP4, 8, 256, 256)
+    d.down = _qw(ft.W_MXFP4, 8, 256, 128)
+    return d
+
+
+def _ws_status(d, T=16):
+    n = ctypes.c_size_t(0)
+    return ft.load().ftmoe_workspace_size(ctypes.byref(d), T, ctypes.byref(n)), n.value
+
+
+@needs_lib
+def test_workspace_size_of_a_valid_layer():
+    st, n = _ws_status(good_layer())
+    assert st == ft.OK and n > 0 and n % 256 == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden", 100, ft.ERR_UNSUPPORTED),
+    ("inter", 0, ft.ERR_UNSUPPORTED),
+    ("top_k", 0, ft.ERR_UNSUPPORTED),
+    ("top_k", 9, ft.ERR_UNSUPPORTED),
+    ("num_experts", 2000, ft.ERR_UNSUPPORTED),
+    ("act", 7, ft.ERR_INVALID_ARG),
+    ("path", 9, ft.ERR_INVALID_ARG),
+    ("router_w", None, ft.ERR_INVALID_ARG),
+    ("router_w", FAKE + 4, ft.ERR_INVALID_ARG),
+    ("act", ft.ACT_FP8_PER_TENSOR, ft.ERR_UNSUPPORTED),   # FP8 activations need FP8 weights
+])
+def test_layer_validation(field, value, status):
+    d = good_layer()
+    setattr(d, field, value)
+    assert _ws_status(d)[0] == status
+    assert ft.load().ftmoe_last_error().decode() != ""
+
+
+@needs_lib
+def test_weight_shape_and_format_validation():
+    d = good_layer()
+    d.down = _qw(ft.W_MXFP4, 8, 256, 256)          # K must equal inter
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    d = good_layer()
+    d.down = _qw(ft.W_NVFP4, 8, 256, 128)          # mixed formats
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    d = good_layer()
+    d.gate_up.block_scales = None
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    d = good_layer()
+    d.gate_up.fmt = d.down.fmt = 9
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    d = good_layer()
+    d.shared_inter = 128                           # shared expert without its tensors
+    d.shared_gate_up = ft.QWeightDesc(ft.W_MXFP4, 1, 256, 256, None, None, None)
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_tokens_and_workspace_validation():
+    d = good_layer()
+    lib = ft.load()
+    assert _ws_status(d, T=-1)[0] == ft.ERR_INVALID_ARG
+    n = _ws_status(d, T=16)[1]
+    # too small a workspace is refused before anything is enqueued
+    st = lib.ftmoe_forward(ctypes.byref(d), FAKE, 16, FAKE, n - 256, FAKE, None, None, None)
+    assert st == ft.ERR_WORKSPACE
+    st = lib.ftmoe_forward(ctypes.byref(d), FAKE, 16, FAKE + 16, n, FAKE, None, None, None)
+    assert st == ft.ERR_WORKSPACE                  # not 256-byte aligned
+    st = lib.ftmoe_forward(ctypes.byref(d), None, 16, FAKE, n, FAKE, None, None, None)
+    assert st == ft.ERR_INVALID_ARG
+    st = lib.ftmoe_forward(ctypes.byref(d), FAKE + 2, 16, FAKE, n, FAKE, None, None, None)
+    assert st == ft.ERR_INVALID_ARG                # misaligned x
+    # T = 0 is a valid no-op that touches nothing
+    assert lib.ftmoe_forward(ctypes.byref(d), None, 0, None, 0, None, None, None, None) == ft.OK
+
+
+@needs_lib
+def test_shared_expert_needs_gate_output():
+    d = good_layer()
+    d.shared_inter = 128
+    d.shared_gate_up = _qw(ft.W_MXFP4, 1, 256, 256)
+    d.shared_down = _qw(ft.W_MXFP4, 1, 256, 128)
+    d.shared_gate_w = FAKE
+    st, n = _ws_status(d)
+    assert st == ft.OK
+    lib = ft.load()
+    assert lib.ftmoe_route(ctypes.byref(d), FAKE, 16, FAKE, n, FAKE, FAKE, None, None) == ft.ERR_INVALID_ARG
+    assert lib.ftmoe_experts_forward(ctypes.byref(d), FAKE, 16, FAKE, FAKE, None, FAKE, n, FAKE,
+                                     None) == ft.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_align_validation():
+    lib = ft.load()
+    assert lib.ftmoe_align(None, 4, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ft.ERR_INVALID_ARG
+    assert lib.ftmoe_align(FAKE, 4, 2, 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ft.ERR_INVALID_ARG
+    need = ft.align_workspace_size(4096, 8, 128, 64)
+    assert need > 0
+    assert lib.ftmoe_align(FAKE, 4096, 8, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+                           None) == ft.ERR_WORKSPACE
+
+
+@needs_lib
+def test_status_strings():
+    lib = ft.load()
+    assert lib.ftmoe_status_string(ft.ERR_WORKSPACE) == b"FTMOE_ERR_WORKSPACE"
+    assert lib.ftmoe_status_string(99) == b"FTMOE_UNKNOWN_STATUS"
+    assert ft.version() >= 100
