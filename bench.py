@@ -137,9 +137,10 @@ def main() -> int:
         gu_b, dn_b = per_expert(lay.gate_up), per_expert(lay.down)
         shared_b = per_expert(lay.shared_gate_up) + per_expert(lay.shared_down) if cfg.shared_inter else 0
         mean_unique = (mean_bytes - shared_b) / (gu_b + dn_b)
-        unit_bytes = {"decode_gateup": gu_b * mean_unique, "decode_down": dn_b * mean_unique,
-                      "decode_shared_gateup": per_expert(lay.shared_gate_up) if cfg.shared_inter else 0,
-                      "decode_shared_down": per_expert(lay.shared_down) if cfg.shared_inter else 0}[dom]
+        sgu_b = per_expert(lay.shared_gate_up) if cfg.shared_inter else 0
+        sdn_b = per_expert(lay.shared_down) if cfg.shared_inter else 0
+        unit_bytes = {"decode_gateup": gu_b * mean_unique + sgu_b,
+                      "decode_down": dn_b * mean_unique + sdn_b}[dom]
         achieved = unit_bytes / (kernel_us[dom] * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

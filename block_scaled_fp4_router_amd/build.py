@@ -21,7 +21,7 @@ ARCH = "gfx950"
 # compiler forms them from ordinary float code, and this code base does not
 # rely on them.
 HIPFLAGS = [
-    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-I", os.path.join(ROOT, "include"),
 ]

@@ -12,68 +12,19 @@
 // per-chunk stable scatter where a wave ranks equal experts with lane reads.
 #include <algorithm>
 
+#include "align_dev.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace ftmoe {
 
 constexpr int kAlignSmallN = 1024;
-constexpr int kAlignMaxE = 1024;
 constexpr int kAlignChunk = 1024;
 
 static inline int max_padded(int T, int k, int E, int BM) {
   const long long n = static_cast<long long>(T) * k;
   const long long p = n + std::min<long long>(E, n) * (BM - 1);
   return static_cast<int>((p + BM - 1) / BM * BM);
-}
-
-// Exclusive scan of `v` over a 1024-thread block (thread e holds v for expert e).
-__device__ int block_exclusive_scan_1024(int v, int* tmp /* 32 ints */) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) tmp[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int s = lane < 16 ? tmp[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(s, o, kWave);
-      if (lane >= o) s += y;
-    }
-    if (lane < 16) tmp[16 + lane] = s;
-  }
-  __syncthreads();
-  const int base = wv > 0 ? tmp[16 + wv - 1] : 0;
-  return base + x - v;
-}
-
-// Writes offsets, counts, num_padded, block ids and sentinels given counts in
-// `cnt` (thread e handles expert e; blockDim = 1024, E <= 1024).
-__device__ void finish_layout(int e, int E, int c, int BM, int n, int P, int32_t* counts,
-                              int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert,
-                              int32_t* num_padded, int* tmp, int* off_out, int* total_out) {
-  const int padded = e < E ? (c + BM - 1) / BM * BM : 0;
-  const int off = block_exclusive_scan_1024(padded, tmp);
-  const int total = tmp[16 + 15];
-  if (e < E) {
-    counts[e] = c;
-    offsets[e] = off;
-    for (int p = off + c; p < off + padded; ++p) sorted_ids[p] = n;
-    for (int b = off / BM; b < (off + padded) / BM; ++b) block_expert[b] = e;
-  }
-  if (e == 0) {
-    offsets[E] = total;
-    num_padded[0] = total;
-  }
-  for (int p = total + threadIdx.x; p < P; p += blockDim.x) sorted_ids[p] = n;
-  for (int b = total / BM + threadIdx.x; b < P / BM; b += blockDim.x) block_expert[b] = -1;
-  *off_out = off;
-  *total_out = total;
 }
 
 // ---------------------------------------------------------- small table ---
@@ -86,7 +37,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
   __shared__ int ids_s[kAlignSmallN];
   __shared__ int tmp[32];
   const int e = threadIdx.x;
-  if (e < n_zero) zero_words[e] = 0u;
+  for (int i = e; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
   cnt[e] = 0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) ids_s[i] = ids[i];
   __syncthreads();
@@ -109,7 +60,8 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
                                                          uint32_t* zero_words, int n_zero) {
   __shared__ int cnt[kAlignMaxE];
   const int c = blockIdx.x;
-  if (c == 0 && static_cast<int>(threadIdx.x) < n_zero) zero_words[threadIdx.x] = 0u;
+  if (c == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   const int i0 = c * kAlignChunk, i1 = min(n, i0 + kAlignChunk);

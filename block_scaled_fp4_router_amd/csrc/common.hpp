@@ -113,6 +113,86 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
+// DPP lane permutations within 16-lane rows (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16 lanes
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Wave-wide reductions with a fixed combination order (deterministic): DPP
+// within each 16-lane row, then the four row results in lane order.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = __builtin_fmaxf(v, dpp_f<kDppXor1>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppXor2>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppMirror>(v));
+  return __builtin_fmaxf(__builtin_fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+                         __builtin_fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Wave argmax: the largest value, equal values resolved to the lowest index.
+// Every lane gets (value, index).
+__device__ __forceinline__ void wave_argmax(float v, int idx, float* best_v, int* best_i) {
+  const float m = wave_max_fast(v);
+  const unsigned long long mask = __ballot(v == m);
+  int wi;
+  if (__popcll(mask) == 1) {
+    wi = __builtin_amdgcn_readlane(idx, __ffsll(static_cast<long long>(mask)) - 1);
+  } else {
+    wi = wave_min_int(v == m ? idx : 0x7FFFFFFF);
+  }
+  *best_v = m;
+  *best_i = wi;
+}
+
+// Per-call maximum of |h| for the FP8 per-tensor scale.  Many workgroups
+// contribute, and atomics on one address serialise, so each workgroup first
+// reduces in LDS and then updates one of kAmaxSlots words kAmaxStride words
+// apart (different cache lines); a one-wave pass folds the slots afterwards.
+constexpr int kAmaxSlots = 64;
+constexpr int kAmaxStride = 32;
+
+// All threads of the workgroup must call it.  `red` is >= 16 floats of LDS.
+__device__ __forceinline__ void wg_amax_to_slots(float m, uint32_t* slots, float* red) {
+  m = wave_max_fast(m);
+  const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  if (lane_id() == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = 0.f;
+    for (int i = 0; i < nw; ++i) r = __builtin_fmaxf(r, red[i]);
+    const unsigned slot = (blockIdx.x + blockIdx.y * gridDim.x) % kAmaxSlots;
+    atomicMax(slots + slot * kAmaxStride, __float_as_uint(r));
+  }
+}
+
 // silu(g) * u in fp32.
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

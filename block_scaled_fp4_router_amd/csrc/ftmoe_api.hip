@@ -83,7 +83,7 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTokens = 1 << 20;
-constexpr int kDecodeAutoMaxT = 16;
+constexpr int kDecodeAutoMaxT = kDecodeMaxT;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -159,21 +159,27 @@ int max_padded(int T, int k, int E, int BM) {
 size_t up256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct Plan {
-  bool decode = false;
-  int BM = 0, P = 0, nblocks = 0, shared_rows = 0, shared_blocks = 0;
-  size_t logits = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
+  bool decode = false;    // bandwidth-bound decode kernels
+  bool small_route = false;  // router via H-sliced partials + fused top-k (T <= kDecodeMaxT)
+  int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0;
+  size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
          scal = 0, ascratch = 0, xq = 0, h = 0, o = 0, hs = 0, s = 0, total = 0;
 };
 
 Plan make_plan(const ftmoe_layer* L, int T) {
   Plan p;
   const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
+  const bool shared = L->shared_inter > 0;
   p.decode = L->path == FTMOE_PATH_DECODE || (L->path == FTMOE_PATH_AUTO && T <= kDecodeAutoMaxT);
+  p.small_route = T <= kDecodeMaxT;
   p.BM = p.decode ? kDecodeBM : kPrefillBM;
   p.P = max_padded(T, k, E, p.BM);
   p.nblocks = p.P / p.BM;
-  p.shared_blocks = (T + p.BM - 1) / p.BM;
-  p.shared_rows = p.shared_blocks * p.BM;
+  p.nb_shared = shared ? (T + p.BM - 1) / p.BM : 0;
+  p.shared_rows = p.nb_shared * p.BM;
+  p.S = router_splits(H);
+  p.tiles = decode_down_tiles(H);
+  p.n_zero = 2 + kAmaxSlots * kAmaxStride;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -181,7 +187,11 @@ Plan make_plan(const ftmoe_layer* L, int T) {
     return at;
   };
   const size_t tk = static_cast<size_t>(T) * k;
-  p.logits = take(static_cast<size_t>(T) * (E + 1) * 4);
+  const size_t obytes = p.decode ? 4 : 2;
+  if (p.small_route)
+    p.part = take(static_cast<size_t>(p.S) * T * (E + 1) * 4);
+  else
+    p.logits = take(static_cast<size_t>(T) * (E + 1) * 4);
   p.ids = take(tk * 4);
   p.w = take(tk * 4);
   p.sg = take(static_cast<size_t>(T) * 4);
@@ -190,14 +200,14 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   p.sorted = take(static_cast<size_t>(p.P) * 4);
   p.bexp = take(static_cast<size_t>(p.nblocks) * 4);
   p.npad = take(4);
-  p.scal = take(256);
+  p.scal = take(static_cast<size_t>(p.n_zero) * 4);
   p.ascratch = take(align_scratch_bytes(T, k, E, p.BM));
   p.xq = take(L->act == FTMOE_ACT_FP8_PER_TENSOR ? static_cast<size_t>(T) * H : 0);
   p.h = take(static_cast<size_t>(p.P) * I * 2);
-  p.o = take(tk * H * 2);
-  if (L->shared_inter > 0) {
+  p.o = take(tk * H * obytes);
+  if (shared) {
     p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
-    p.s = take(static_cast<size_t>(T) * H * 2);
+    p.s = take(static_cast<size_t>(T) * H * obytes);
   }
   p.total = off;
   return p;
@@ -228,38 +238,64 @@ ftmoe_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
   return FTMOE_OK;
 }
 
+// Router.  With `align` (decode plans with few tokens) the fused top-k kernel
+// also writes the block alignment and clears the per-call counters, so the
+// experts stage can skip its own align launch.
 ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const Plan& p, void* ws, int32_t* ids,
-                           float* w, float* sg, hipStream_t s) {
+                           float* w, float* sg, bool align, hipStream_t s) {
   const bool shared = L->shared_inter > 0;
+  const int E = L->num_experts, k = L->top_k;
+  if (p.small_route) {
+    float* part = at<float>(ws, p.part);
+    FT_HIP(timed("router_partial", s,
+                 [&] {
+                   return launch_router_partial(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
+                                                part, s);
+                 }),
+           "router launch");
+    FT_HIP(timed("topk_align", s,
+                 [&] {
+                   return launch_topk_align_decode(part, p.S, T, E, k, L->router_bias, shared, ids, w, sg,
+                                                   at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                                   at<int32_t>(ws, p.sorted), at<int32_t>(ws, p.bexp),
+                                                   at<int32_t>(ws, p.npad), align ? p.P : 0,
+                                                   at<uint32_t>(ws, p.scal), align ? p.n_zero : 0, s);
+                 }),
+           "top-k launch");
+    return FTMOE_OK;
+  }
   float* logits = at<float>(ws, p.logits);
   FT_HIP(timed("router_logits", s,
                [&] {
-                 return launch_router_logits(x, T, L->hidden, L->router_w, L->num_experts,
-                                             shared ? L->shared_gate_w : nullptr, logits, s);
+                 return launch_router_logits(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
+                                             logits, s);
                }),
          "router logits launch");
-  FT_HIP(timed("topk", s,
-               [&] { return launch_topk(logits, T, L->num_experts, L->top_k, L->router_bias, shared, ids, w, sg, s); }),
+  FT_HIP(timed("topk", s, [&] { return launch_topk(logits, T, E, k, L->router_bias, shared, ids, w, sg, s); }),
          "top-k launch");
   return FTMOE_OK;
 }
 
 ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, const int32_t* ids, const float* w,
-                             const float* sg, const Plan& p, void* ws, uint16_t* y, hipStream_t s) {
+                             const float* sg, const Plan& p, void* ws, uint16_t* y, bool aligned, hipStream_t s) {
   const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
   const bool fp8act = L->act == FTMOE_ACT_FP8_PER_TENSOR;
+  const bool shared = L->shared_inter > 0;
   uint32_t* scal = at<uint32_t>(ws, p.scal);
   uint32_t* amax_x = scal + 0;
   uint32_t* amax_h = scal + 1;
+  uint32_t* amax_slots = scal + 2;
   int32_t* sorted = at<int32_t>(ws, p.sorted);
   int32_t* bexp = at<int32_t>(ws, p.bexp);
-  FT_HIP(timed("align", s,
-               [&] {
-                 return launch_align(ids, T, k, E, p.BM, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
-                                     sorted, bexp, at<int32_t>(ws, p.npad), at<void>(ws, p.ascratch), scal,
-                                     fp8act ? 2 : 0, s);
-               }),
-         "align launch");
+  if (!aligned) {
+    FT_HIP(timed("align", s,
+                 [&] {
+                   return launch_align(ids, T, k, E, p.BM, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                       sorted, bexp, at<int32_t>(ws, p.npad), at<void>(ws, p.ascratch), scal,
+                                       p.n_zero, s);
+                 }),
+           "align launch");
+  }
   const uint8_t* xq = nullptr;
   if (fp8act) {
     FT_HIP(timed("amax_x", s, [&] { return launch_amax_bf16(x, static_cast<int64_t>(T) * H, amax_x, s); }),
@@ -271,58 +307,77 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
            "quantise launch");
     xq = at<uint8_t>(ws, p.xq);
   }
+  const QW gu = to_qw(L->gate_up), dn = to_qw(L->down);
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  const uint32_t* ax = fp8act ? amax_x : nullptr;
+  uint32_t* ah = fp8act ? amax_h : nullptr;
+  uint32_t* ahs = fp8act ? amax_slots : nullptr;
+  uint16_t* hs = shared ? at<uint16_t>(ws, p.hs) : nullptr;
+
+  if (p.decode) {
+    DecodeArgs a{};
+    a.gu = gu;
+    a.dn = dn;
+    if (shared) {
+      a.sgu = to_qw(L->shared_gate_up);
+      a.sdn = to_qw(L->shared_down);
+    }
+    a.sorted_ids = sorted;
+    a.block_expert = bexp;
+    a.T = T;
+    a.k = k;
+    a.H = H;
+    a.I = I;
+    a.Is = shared ? L->shared_inter : 0;
+    a.nb_routed = p.nblocks;
+    a.nb_shared = p.nb_shared;
+    a.x = x;
+    a.xq = xq;
+    a.amax_x = ax;
+    a.h = h;
+    a.hs = hs;
+    a.amax_slots = ahs;
+    a.amax_h = ah;
+    a.o32 = at<float>(ws, p.o);
+    a.s32 = shared ? at<float>(ws, p.s) : nullptr;
+    a.w = w;
+    a.sg = shared ? sg : nullptr;
+    a.y = y;
+    FT_HIP(timed("decode_gateup", s, [&] { return launch_decode_gateup(a, s); }), "decode gate_up launch");
+    if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
+    FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(a, s); }), "decode down launch");
+    FT_HIP(timed("combine", s, [&] { return launch_decode_combine(a, s); }), "combine launch");
+    return FTMOE_OK;
+  }
+
   Rows rr;
   rr.sorted_ids = sorted;
   rr.block_expert = bexp;
   rr.n_flat = T * k;
   rr.top_k = k;
   rr.num_blocks = p.nblocks;
-  const QW gu = to_qw(L->gate_up), dn = to_qw(L->down);
-  uint16_t* h = at<uint16_t>(ws, p.h);
-  uint16_t* o = at<uint16_t>(ws, p.o);
-  const uint32_t* ax = fp8act ? amax_x : nullptr;
-  uint32_t* ah = fp8act ? amax_h : nullptr;
-  const bool shared = L->shared_inter > 0;
   Rows rs;
   rs.sorted_ids = nullptr;
   rs.block_expert = nullptr;
   rs.n_flat = T;
   rs.top_k = 1;
-  rs.num_blocks = p.shared_blocks;
-  uint16_t* hs = shared ? at<uint16_t>(ws, p.hs) : nullptr;
+  rs.num_blocks = p.nb_shared;
+  uint16_t* o = at<uint16_t>(ws, p.o);
   uint16_t* sh = shared ? at<uint16_t>(ws, p.s) : nullptr;
-  if (p.decode) {
-    FT_HIP(timed("decode_gateup", s,
-                 [&] { return launch_decode_gateup(gu, rr, x, xq, ax, H, I, h, ah, std::min(T, kDecodeBM), s); }),
-           "decode gate_up launch");
-    FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(dn, rr, h, ah, H, I, o, s); }),
-           "decode down launch");
-    if (shared) {
-      FT_HIP(timed("decode_shared_gateup", s,
-                   [&] {
-                     return launch_decode_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
-                                                 hs, nullptr, std::min(T, kDecodeBM), s);
-                   }),
-             "decode shared gate_up launch");
-      FT_HIP(timed("decode_shared_down", s,
-                   [&] { return launch_decode_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
-             "decode shared down launch");
-    }
-  } else {
-    FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ah, s); }),
-           "gate_up GEMM launch");
-    FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, ah, H, I, o, s); }), "down GEMM launch");
-    if (shared) {
-      FT_HIP(timed("gemm_shared_gateup", s,
-                   [&] {
-                     return launch_gemm_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
-                                               hs, nullptr, s);
-                   }),
-             "shared gate_up GEMM launch");
-      FT_HIP(timed("gemm_shared_down", s,
-                   [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
-             "shared down GEMM launch");
-    }
+  FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ahs, s); }),
+         "gate_up GEMM launch");
+  if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
+  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, ah, H, I, o, s); }), "down GEMM launch");
+  if (shared) {
+    FT_HIP(timed("gemm_shared_gateup", s,
+                 [&] {
+                   return launch_gemm_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
+                                             hs, nullptr, s);
+                 }),
+           "shared gate_up GEMM launch");
+    FT_HIP(timed("gemm_shared_down", s,
+                 [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
+           "shared down GEMM launch");
   }
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),
          "combine launch");
@@ -366,7 +421,7 @@ ftmoe_status ftmoe_route(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
     return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
   const Plan p = make_plan(layer, T);
   FT_TRY(check_ws(p, ws, ws_bytes));
-  return enqueue_route(layer, x, T, p, ws, topk_ids, topk_w, shared_gate, static_cast<hipStream_t>(stream));
+  return enqueue_route(layer, x, T, p, ws, topk_ids, topk_w, shared_gate, false, static_cast<hipStream_t>(stream));
 }
 
 ftmoe_status ftmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m, int32_t* counts,
@@ -401,7 +456,8 @@ ftmoe_status ftmoe_experts_forward(const ftmoe_layer* layer, const uint16_t* x, 
     return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
   const Plan p = make_plan(layer, T);
   FT_TRY(check_ws(p, ws, ws_bytes));
-  return enqueue_experts(layer, x, T, topk_ids, topk_w, shared_gate, p, ws, y, static_cast<hipStream_t>(stream));
+  return enqueue_experts(layer, x, T, topk_ids, topk_w, shared_gate, p, ws, y, false,
+                         static_cast<hipStream_t>(stream));
 }
 
 ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
@@ -418,8 +474,9 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
   float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
   float* sg = at<float>(ws, p.sg);
-  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, s));
-  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, s);
+  const bool fused_align = p.decode && p.small_route;
+  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, s));
+  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, s);
 }
 
 ftmoe_status ftmoe_quantize_fp8_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale, void* ws,

@@ -228,8 +228,8 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(QW w, Rows rows, const
     h[static_cast<size_t>(p) * I + n0 + wn * 32 + j] = f32_to_bf16(v);
   }
   if constexpr (FP8ACT) {
-    m = wave_max(m);
-    if (lane == 0) atomicMax(amax_h, __float_as_uint(m));
+    __shared__ float red[16];
+    wg_amax_to_slots(m, amax_h, red);
   }
 }
 

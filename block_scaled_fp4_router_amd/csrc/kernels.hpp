@@ -47,22 +47,57 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, const uint32_t* amax_bits, uint8_t* q,
                             float* scale_out, hipStream_t s);
+// Max over the kAmaxSlots partial maxima written by the gate_up kernels.
+hipError_t launch_amax_fold(const uint32_t* slots, uint32_t* out, hipStream_t s);
 
-// ---- decode experts (small token counts; bandwidth-bound) ----
+// ---- decode path (T <= kDecodeMaxT; bandwidth-bound) ----
 constexpr int kDecodeBM = 16;
-// h[p][0..inter) for every row p of every block (identity rows when
-// rows.sorted_ids == NULL).  act_q: fp8 activations (x_q + amax_x) or NULL.
-hipError_t launch_decode_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
-                                const uint32_t* amax_x, int H, int inter, uint16_t* h,
-                                uint32_t* amax_h, int max_tokens_per_block, hipStream_t s);
-hipError_t launch_decode_down(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h,
-                              int H, int inter, uint16_t* o, hipStream_t s);
+constexpr int kDecodeMaxT = 16;
+// Router partial logits part[s][t][row], s over H-slices of 256 columns.
+int router_splits(int H);
+hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* router_w, int E,
+                                 const float* shared_gate_w, float* part, hipStream_t s);
+// Sums the partial logits, top-k + softmax (+ sigmoid gate), aligns the T*k
+// rows into blocks of kDecodeBM and zeroes `zero_words`.  One workgroup.
+hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int k, const float* bias,
+                                    bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
+                                    int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert,
+                                    int32_t* num_padded, int P, uint32_t* zero_words, int n_zero,
+                                    hipStream_t s);
+
+struct DecodeArgs {
+  QW gu, dn;                  // routed experts
+  QW sgu, sdn;                // shared expert (used when Is > 0)
+  const int32_t* sorted_ids;  // [nb_routed * kDecodeBM]
+  const int32_t* block_expert;
+  int T, k, H, I, Is;
+  int nb_routed, nb_shared;   // grid blocks: routed blocks, then shared blocks
+  const uint16_t* x;
+  const uint8_t* xq;          // FP8 activations or NULL
+  const uint32_t* amax_x;
+  uint16_t* h;                // [nb_routed * 16][I] bf16
+  uint16_t* hs;               // [nb_shared * 16][Is] bf16
+  uint32_t* amax_slots;       // FP8 activations: gate_up partial maxima of |h| (or NULL)
+  const uint32_t* amax_h;     // FP8 activations: folded max of |h| read by down (or NULL)
+  float* o32;                 // [T*k][H] fp32
+  float* s32;                 // [T][H] fp32
+  const float* w;             // [T*k]
+  const float* sg;            // [T] or NULL
+  uint16_t* y;                // [T][H] bf16
+};
+int decode_down_tiles(int H);
+hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s);
+// Down projection of every block into fp32 rows o32 / s32.
+hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
+// y = routed rows summed in ascending slot order j, then the gated shared expert.
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill experts (grouped GEMMs on MFMA) ----
 constexpr int kPrefillBM = 64;
+// amax_slots: FP8 activations only, the kAmaxSlots partial maxima of |h|.
 hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
                               const uint32_t* amax_x, int H, int inter, uint16_t* h,
-                              uint32_t* amax_h, hipStream_t s);
+                              uint32_t* amax_slots, hipStream_t s);
 hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h,
                             int H, int inter, uint16_t* o, hipStream_t s);
 

@@ -33,8 +33,28 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restri
   if (blockIdx.x == 0)
     for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += blockDim.x)
       m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(x[i])));
-  m = wave_max(m);
-  if (lane_id() == 0) atomicMax(amax_bits, __float_as_uint(m));
+  __shared__ float red[16];
+  m = wave_max_fast(m);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = 0.f;
+    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) r = __builtin_fmaxf(r, red[i]);
+    atomicMax(amax_bits, __float_as_uint(r));
+  }
+}
+
+// Folds the kAmaxSlots partial maxima into one word.
+__global__ void amax_fold_kernel(const uint32_t* __restrict__ slots, uint32_t* __restrict__ out) {
+  const int l = lane_id();
+  uint32_t v = l < kAmaxSlots ? slots[l * kAmaxStride] : 0u;
+  const float m = wave_max_fast(__uint_as_float(v));
+  if (l == 0) *out = __float_as_uint(m);
+}
+
+hipError_t launch_amax_fold(const uint32_t* slots, uint32_t* out, hipStream_t s) {
+  amax_fold_kernel<<<1, 64, 0, s>>>(slots, out);
+  return hipGetLastError();
 }
 
 // s = amax / 448 (1 when amax is 0), the dequantisation scale.
@@ -67,15 +87,15 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
       q[i] = static_cast<uint8_t>(f32x2_to_e4m3x2(bf16_to_f32(x[i]) / s, 0.f) & 0xFF);
 }
 
-static int elementwise_grid(int64_t n8) {
+static int elementwise_grid(int64_t n8, int64_t cap = 4096) {
   int64_t g = (n8 + 255) / 256;
-  if (g > 4096) g = 4096;
+  if (g > cap) g = cap;
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* amax_bits, hipStream_t s) {
-  amax_bf16_kernel<<<elementwise_grid(n / 8), 256, 0, s>>>(x, n, amax_bits);
+  amax_bf16_kernel<<<elementwise_grid(n / 8, 512), 256, 0, s>>>(x, n, amax_bits);
   return hipGetLastError();
 }
 

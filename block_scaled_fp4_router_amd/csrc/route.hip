@@ -1,6 +1,7 @@
 // Router: logits l[t,e] = x_t . W_r[e] (fp32 accumulation of exact bf16 x
 // and fp32 W_r), then per-token softmax top-k with renormalised weights and
 // the shared expert's sigmoid gate.
+#include "align_dev.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -135,15 +136,67 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
 }
 
 // ---------------------------------------------------------------- top-k ---
-// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a wave
-// argmax (larger value wins, equal values go to the lower index) remove the
-// winner each round.  Weights: softmax over the k selected logits.
+// One wave per token.  Lane l holds the logits of experts l, l+64, ... (SLOTS
+// of them) and sorts them once, descending (equal values: lower expert
+// first).  Each of the k rounds is then a wave argmax over the lanes' heads
+// (DPP reductions; equal values go to the lower expert index) after which the
+// winning lane drops its head.  Weights: softmax over the k selected logits.
 constexpr int kTopkMaxPerLane = 16;  // E <= 1024
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// v[i] holds the logit of expert lane + 64 i (-inf past E).  On return lane
+// j < k holds the j-th selected expert and its renormalised weight.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_softmax(float (&v)[SLOTS], int k, int* sel_id, float* sel_w) {
+  const int lane = lane_id();
+  int id[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) id[i] = lane + i * kWave;
+  // odd-even transposition sort, descending
+#pragma unroll
+  for (int pass = 0; pass < SLOTS; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < SLOTS; i += 2) {
+      if (better(v[i + 1], id[i + 1], v[i], id[i])) {
+        const float tv = v[i];
+        v[i] = v[i + 1];
+        v[i + 1] = tv;
+        const int ti = id[i];
+        id[i] = id[i + 1];
+        id[i + 1] = ti;
+      }
+    }
+  }
+  float sel_v = 0.f;
+  int sel_i = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv;
+    int bi;
+    wave_argmax(v[0], id[0], &bv, &bi);
+    if (lane == j) {
+      sel_v = bv;
+      sel_i = bi;
+    }
+    if ((bi & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i + 1 < SLOTS; ++i) {
+        v[i] = v[i + 1];
+        id[i] = id[i + 1];
+      }
+      v[SLOTS - 1] = -__builtin_inff();
+    }
+  }
+  const float m = readlane_f(sel_v, 0);
+  const float ex = lane < k ? expf(sel_v - m) : 0.f;
+  const float sum = wave_sum_fixed(ex);
+  *sel_id = sel_i;
+  *sel_w = ex / sum;
+}
+
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    const float* __restrict__ bias, int has_shared,
                                                    int32_t* __restrict__ ids, float* __restrict__ w,
@@ -152,44 +205,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   const int lane = lane_id();
   const float* row = logits + static_cast<size_t>(t) * (E + 1);
-  float v[kTopkMaxPerLane];
+  float v[SLOTS];
 #pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+  for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + i * kWave;
     v[i] = -__builtin_inff();
     if (e < E) v[i] = row[e] + (bias ? bias[e] : 0.f);
   }
-  float sel_v = 0.f;   // lane j < k keeps the j-th selected logit
-  int sel_i = 0;
-  for (int j = 0; j < k; ++j) {
-    // local best
-    float bv = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (e < E && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-    }
-    // wave argmax
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == j) { sel_v = bv; sel_i = bi; }
-    if ((bi & (kWave - 1)) == lane) {
-#pragma unroll
-      for (int i = 0; i < kTopkMaxPerLane; ++i)
-        if (lane + i * kWave == bi) v[i] = -__builtin_inff();
-    }
-  }
-  const float m = __shfl(sel_v, 0, kWave);
-  const float ex = lane < k ? expf(sel_v - m) : 0.f;
-  const float sum = wave_sum(ex);
+  int sel_i;
+  float sel_w;
+  wave_topk_softmax<SLOTS>(v, k, &sel_i, &sel_w);
   if (lane < k) {
     ids[static_cast<size_t>(t) * k + lane] = sel_i;
-    w[static_cast<size_t>(t) * k + lane] = ex / sum;
+    w[static_cast<size_t>(t) * k + lane] = sel_w;
   }
   if (has_shared && lane == 0) {
     const float g = row[E];
@@ -197,11 +225,151 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
+// Calls f.template operator()<SLOTS>() with the smallest SLOTS covering E.
+template <class F>
+static hipError_t with_slots(int E, F&& f) {
+  if (E <= 64) return f.template operator()<1>();
+  if (E <= 128) return f.template operator()<2>();
+  if (E <= 256) return f.template operator()<4>();
+  if (E <= 512) return f.template operator()<8>();
+  return f.template operator()<16>();
+}
+
 hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool has_shared,
                        int32_t* ids, float* w, float* sgate, hipStream_t s) {
   dim3 grid((T + 3) / 4);
-  topk_kernel<<<grid, 256, 0, s>>>(logits, T, E, k, bias, has_shared ? 1 : 0, ids, w, sgate);
+  return with_slots(E, [&]<int SL>() {
+    topk_kernel<SL><<<grid, 256, 0, s>>>(logits, T, E, k, bias, has_shared ? 1 : 0, ids, w, sgate);
+    return hipGetLastError();
+  });
+}
+
+// ======================================================= decode router ====
+// Few tokens (T <= 16).  The router matrix (E x H fp32, 1-4 MiB) is read by
+// many workgroups at once: workgroup (r, s) reads rows 4r..4r+3 over the
+// H-slice [256 s, 256 s + 256) -- one 16-byte load per lane -- and writes
+// partial logits part[s][t][row].  The fused top-k kernel adds the S slices
+// in order, so the logits do not depend on scheduling.
+constexpr int kSliceH = 256;
+
+int router_splits(int H) { return (H + kSliceH - 1) / kSliceH; }
+
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                             const float* __restrict__ router_w, int E,
+                                                             const float* __restrict__ shared_gate_w,
+                                                             float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kDecodeMaxT][kSliceH];
+  const int rows = E + (shared_gate_w ? 1 : 0);
+  const int s = blockIdx.y, h0 = s * kSliceH;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  // Issue this wave's weight load first.
+  float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool have_row = row < rows;
+  const int hl = h0 + lane * 4;
+  if (have_row && hl < H) {
+    const float* wrow = row < E ? router_w + static_cast<size_t>(row) * H : shared_gate_w;
+    wv = *reinterpret_cast<const float4*>(wrow + hl);
+  }
+  // Stage the x slice of every token: T x 256 bf16, 16 bytes per thread.
+  for (int i = threadIdx.x; i < T * (kSliceH / 8); i += blockDim.x) {
+    const int t = i / (kSliceH / 8), c = (i % (kSliceH / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h0 + c < H) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h0 + c);
+    *reinterpret_cast<uint4*>(&xs[t][c]) = v;
+  }
+  __syncthreads();
+  if (!have_row) return;
+  for (int t = 0; t < T; ++t) {
+    const uint2 xv = *reinterpret_cast<const uint2*>(&xs[t][lane * 4]);
+    float acc = bf16_to_f32(xv.x & 0xFFFF) * wv.x;
+    acc = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc);
+    acc = fmaf(bf16_to_f32(xv.y & 0xFFFF), wv.z, acc);
+    acc = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc);
+    const float v = wave_sum_fixed(acc);
+    if (lane == 0) part[(static_cast<size_t>(s) * T + t) * rows + row] = v;
+  }
+}
+
+hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* router_w, int E,
+                                 const float* shared_gate_w, float* part, hipStream_t s) {
+  const int rows = E + (shared_gate_w ? 1 : 0);
+  dim3 grid((rows + 3) / 4, router_splits(H));
+  router_partial_kernel<<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, part);
   return hipGetLastError();
+}
+
+// Fused decode top-k + align: one workgroup of 1024 threads.  Wave t < T sums
+// token t's partial logits (slices in order), adds the bias and runs k rounds
+// of wave argmax (DPP reductions); then the whole workgroup aligns the T*k
+// routed rows into blocks of kDecodeBM (stable counting sort in LDS).
+template <int SLOTS>
+__global__ __launch_bounds__(1024) void topk_align_decode_kernel(
+    const float* __restrict__ part, int S, int T, int E, int k, const float* __restrict__ bias, int has_shared,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ sgate, int32_t* counts, int32_t* offsets,
+    int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, int P, uint32_t* zero_words, int n_zero) {
+  __shared__ int ids_s[kDecodeMaxT * 16];
+  __shared__ int cnt[kAlignMaxE];
+  __shared__ int tmp[32];
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int rows = E + (has_shared ? 1 : 0);
+  for (int i = tid; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
+  cnt[tid] = 0;
+  if (wv < T) {
+    const int t = wv;
+    float v[SLOTS];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int e = lane + i * kWave;
+      float acc = -__builtin_inff();
+      if (e < E) {
+        acc = 0.f;
+        for (int sl = 0; sl < S; ++sl) acc += part[(static_cast<size_t>(sl) * T + t) * rows + e];
+        if (bias) acc += bias[e];
+      }
+      v[i] = acc;
+    }
+    int sel_i;
+    float sel_w;
+    wave_topk_softmax<SLOTS>(v, k, &sel_i, &sel_w);
+    if (lane < k) {
+      ids[t * k + lane] = sel_i;
+      w[t * k + lane] = sel_w;
+      ids_s[t * k + lane] = sel_i;
+    }
+    if (has_shared && lane == 0) {
+      float g = 0.f;
+      for (int sl = 0; sl < S; ++sl) g += part[(static_cast<size_t>(sl) * T + t) * rows + E];
+      sgate[t] = 1.0f / (1.0f + expf(-g));
+    }
+  }
+  if (P == 0) return;  // routing only
+  __syncthreads();
+  const int n = T * k;
+  for (int i = tid; i < n; i += blockDim.x) atomicAdd(&cnt[ids_s[i]], 1);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  int off, total;
+  finish_layout(tid, E, c, kDecodeBM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off,
+                &total);
+  if (tid < E && c > 0) {
+    int pos = off;
+    for (int i = 0; i < n; ++i)
+      if (ids_s[i] == tid) sorted_ids[pos++] = i;
+  }
+}
+
+hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int k, const float* bias,
+                                    bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
+                                    int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert,
+                                    int32_t* num_padded, int P, uint32_t* zero_words, int n_zero,
+                                    hipStream_t s) {
+  return with_slots(E, [&]<int SL>() {
+    topk_align_decode_kernel<SL><<<1, 1024, 0, s>>>(part, S, T, E, k, bias, has_shared ? 1 : 0, ids, w, sg, counts,
+                                                    offsets, sorted_ids, block_expert, num_padded, P, zero_words,
+                                                    n_zero);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace ftmoe
