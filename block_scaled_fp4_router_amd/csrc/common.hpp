@@ -97,6 +97,69 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
 
+// ------------------------------------------- split FP8 activation blocks ----
+// For the MX-scaled MFMA (FP8 activations x MXFP4 weights) a block of 32
+// activations is carried as two E4M3 vectors sharing one power-of-two scale
+// 2^e:  x ~= 2^e * (hi + lo / 16)  with  hi = E4M3(x / 2^e) and
+// lo = E4M3(16 (x / 2^e - hi)).  e = floor(log2 amax) - 7 keeps |x / 2^e| below
+// 256 (no saturation), so the pair keeps about 8 significant bits -- the
+// precision of the bf16 input -- while the weights stay as 4-bit codes.
+// The scale is returned as its E8M0 code (e + 127, clamped to [0, 254]).
+__device__ __forceinline__ uint32_t mx_split_scale_code(float amax) {
+  const int ebits = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
+  int code = ebits - 7;
+  code = code < 0 ? 0 : (code > 254 ? 254 : code);
+  return static_cast<uint32_t>(code);
+}
+
+// 2^(127 - code): multiplying by it divides by the block scale exactly.
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
+// hi and lo E4M3 codes of two adjacent values already divided by the scale.
+__device__ __forceinline__ void mx_split_pair(float a, float b, uint32_t* hi2, uint32_t* lo2) {
+  const uint32_t h = f32x2_to_e4m3x2(a, b);
+  const f32x2 dh = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 1.0f, false);
+  *hi2 = h;
+  *lo2 = f32x2_to_e4m3x2((a - dh[0]) * 16.0f, (b - dh[1]) * 16.0f);
+}
+
+// Splits one 32-block of bf16 values (4 vectors of 8) into 32 hi codes, 32
+// lo codes (16-byte aligned destinations, global or LDS) and the scale code.
+__device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi, uint8_t* lo, uint8_t* sc) {
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[i] & 0xFFFF)));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[i] >> 16)));
+    }
+  }
+  const uint32_t code = mx_split_scale_code(amax);
+  const float inv = mx_inv_scale(code);
+  uint32_t hw[8], lw[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      uint32_t h0, l0, h1, l1;
+      mx_split_pair(bf16_to_f32(w[i] & 0xFFFF) * inv, bf16_to_f32(w[i] >> 16) * inv, &h0, &l0);
+      mx_split_pair(bf16_to_f32(w[i + 1] & 0xFFFF) * inv, bf16_to_f32(w[i + 1] >> 16) * inv, &h1, &l1);
+      hw[2 * q + i / 2] = h0 | (h1 << 16);
+      lw[2 * q + i / 2] = l0 | (l1 << 16);
+    }
+  }
+  reinterpret_cast<uint4*>(hi)[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  reinterpret_cast<uint4*>(hi)[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+  reinterpret_cast<uint4*>(lo)[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  reinterpret_cast<uint4*>(lo)[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  *sc = static_cast<uint8_t>(code);
+}
+
 // ------------------------------------------------------------ wave ops ----
 
 __device__ __forceinline__ float wave_sum(float v) {

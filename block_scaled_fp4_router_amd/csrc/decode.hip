@@ -1,86 +1,426 @@
 // Decode experts: few tokens per expert, so the work is streaming each
 // selected expert's packed weights from HBM exactly once.
 //
-// Work unit: (block b, row group).  A block is one selected expert with its
-// (up to 16) routed rows -- or, after the routed blocks, 16 tokens of the
-// shared expert.  Each wave owns 16 weight rows and runs 16x16 MFMA tiles
-// whose 16 columns are those rows and whose 16 rows are the block's token
-// slots (absent slots are zero).  Lane l reads the 16-byte slice [32g, 32g+32)
-// (g = l/16) of every 128-element K chunk of weight row l%16 -- one MXFP4
-// block with its one E8M0 scale, or two NVFP4 blocks -- and all of a row's
-// chunks are requested before any is used, so a wave has its whole share in
-// flight at once.  Weights are dequantised in registers (gfx950 scaled
-// FP4->bf16 conversion) into v_mfma_f32_16x16x32_bf16; FP8 weights with FP8
-// activations go straight to v_mfma_scale_f32_16x16x128_f8f6f4.  The token
-// rows are staged in LDS while the weight loads are in flight.
+// Work unit: (block b, group of 16 weight rows per wave).  A block is one
+// selected expert with its (up to 16) routed rows -- or, after the routed
+// blocks, 16 tokens of the shared expert.  Each wave runs 16x16 MFMA tiles
+// whose 16 columns are its weight rows and whose 16 rows are token slots
+// (absent slots are zero).
 //
-// gate_up writes h = silu(gate) * up; down writes fp32 outputs per routed
-// row, and the combine sums each token's rows in ascending slot order j, then
-// adds the gated shared expert.
+// Prologue: the token rows a workgroup multiplies are copied HBM/L2 -> LDS
+// by LDS DMA (global_load_lds_dwordx4: no registers, so nothing to spill),
+// then every wave issues its whole weight stream into registers, and one
+// barrier later the MFMA work runs out of registers and LDS.  Rows in LDS are
+// stored with their 16-byte vectors XOR-swizzled by (row & 7), so the eight
+// lanes of a ds_read_b128 phase that read one K offset of eight different
+// rows hit eight different bank groups.
+//
+// MXFP4 weights go to v_mfma_scale_f32_16x16x128_f8f6f4 as raw E2M1 codes
+// with their E8M0 block scales, against activations carried as split E4M3
+// pairs (common.hpp); no weight is dequantised.  The gate_up workgroup covers one 32-block of h per token slot, so it writes
+// h directly in the split form the down kernel consumes.
+//
+// NVFP4 (E4M3 block scales, not expressible as E8M0) and FP8 weights with
+// bf16 activations are dequantised to bf16 in registers for
+// v_mfma_f32_16x16x32_bf16; FP8 weights with FP8 activations use the f8f6f4
+// MFMA with unit scales.
+//
+// Operand layout of the scaled 16x16x128 MFMA (checked on gfx950): lane
+// (n, g) of a 4-bit operand holds elements [32g, 32g+32) of the 128-wide K
+// window and its scale applies to exactly that block; lane (i, g) of an 8-bit
+// operand holds [16g, 16g+16) in bytes 0-15 and [64+16g, 64+16g+16) in bytes
+// 16-31, and the scale register of lane (i, g) is the one of K block g.  With
+// unit scales (FP8 x FP8) any consistent K assignment of the two operands is
+// valid, so that path keeps 32 contiguous elements per lane.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace ftmoe {
 
-constexpr int kDownWaves = 4;   // waves per down workgroup: a 64-column tile of y
+constexpr int kGateWaves = 4;   // MXFP4 gate_up workgroup: 4 x 8 intermediate indices = one 32-block of h
+constexpr int kDownWaves = 4;   // waves per down workgroup: a 64-column tile of the output
 constexpr int kDownTileN = 16 * kDownWaves;
 
 int decode_down_tiles(int H) { return (H + kDownTileN - 1) / kDownTileN; }
 
-// Per-lane weight slice of one 128-element K chunk.
-struct WSlice {
-  uint4 c0, c1;      // codes: FP4 uses c0 only
-  uint32_t sc;       // block scale byte(s)
+__host__ __device__ constexpr int decode_rows(int T) { return T < kDecodeBM ? T : kDecodeBM; }
+
+using lds_void = __attribute__((address_space(3))) void;
+
+// ------------------------------------------------------------ staging -----
+// (row, vector) of sequence element i: floor(i / per_row) through fp32 is
+// exact here (i < 2^20, per_row <= 2^10: the product's error stays below
+// 2^-3 / per_row, inside the 0.5 / per_row margin to the next integer).
+__device__ __forceinline__ void split_index(int i, int per_row, float inv, int& r, int& q) {
+  r = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+  q = i - r * per_row;
+}
+
+// Position of vector q of LDS row r (rows of a multiple of 8 vectors).
+__device__ __forceinline__ int swz(int r, int q) { return q ^ (r & 7); }
+
+__device__ __forceinline__ i32x8 u4x2(const uint4& p, const uint4& q) {
+  return i32x8{static_cast<int>(p.x), static_cast<int>(p.y), static_cast<int>(p.z), static_cast<int>(p.w),
+               static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w)};
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* row, int r, int q) {
+  return *reinterpret_cast<const uint4*>(row + 16 * swz(r, q));
+}
+
+// DMA of nvec 16-byte vectors into LDS: vector v lands at lds + 16 v and is
+// read from src(v).  Wave w issues the 1 KB chunks w, w + waves, ...; every
+// lane of the wave evaluates src (it may shuffle), only lanes v < nvec load.
+// Completion is awaited by the caller's __syncthreads (its release fence
+// waits for every outstanding vector memory operation).
+template <class Src>
+__device__ __forceinline__ void dma_stage(uint8_t* lds, int nvec, Src src) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = lane_id();
+  for (int c = wave; c * 64 < nvec; c += nw) {
+    const int v = c * 64 + lane;
+    const void* p = src(v < nvec ? v : nvec - 1);
+    if (v < nvec) __builtin_amdgcn_global_load_lds(p, (lds_void*)(lds + c * 1024), 16, 0, 0);
+  }
+}
+
+// DMA of `rows` rows of `rowvec` vectors each, swizzled; row_src(r) is the
+// global address of row r.
+template <class RowSrc>
+__device__ __forceinline__ void dma_rows(uint8_t* lds, int rows, int rowvec, RowSrc row_src) {
+  const float inv = 1.0f / static_cast<float>(rowvec);
+  dma_stage(lds, rows * rowvec, [&](int v) -> const void* {
+    int r, s;
+    split_index(v, rowvec, inv, r, s);
+    return static_cast<const uint8_t*>(row_src(r)) + 16 * swz(r, s);
+  });
+}
+
+// DMA of split rows: hi [rows][K], lo [rows][K] (swizzled) and the scale rows
+// [rows][spitch] (plain), consecutive in LDS.  Row r of the source is row
+// src_row(r) of hi / lo ([.][K]) and of sc ([.][spitch]).
+template <class SrcRow>
+__device__ __forceinline__ void dma_split_rows(uint8_t* lds, int rows, int K, int spitch, const uint8_t* hi,
+                                               const uint8_t* lo, const uint8_t* sc, SrcRow src_row) {
+  const int hv = K / 16, sv = spitch / 16, nh = rows * hv;
+  const float inv_h = 1.0f / static_cast<float>(hv), inv_s = 1.0f / static_cast<float>(sv);
+  dma_stage(lds, 2 * nh + rows * sv, [&](int v) -> const void* {
+    int r, s;
+    if (v < 2 * nh) {
+      const bool is_lo = v >= nh;
+      split_index(is_lo ? v - nh : v, hv, inv_h, r, s);
+      const uint8_t* base = is_lo ? lo : hi;
+      return base + static_cast<size_t>(src_row(r)) * K + 16 * swz(r, s);
+    }
+    split_index(v - 2 * nh, sv, inv_s, r, s);
+    return sc + static_cast<size_t>(src_row(r)) * spitch + 16 * s;
+  });
+}
+
+// ------------------------------------------------------------ blocks ------
+// A routed block's LDS holds every token of the batch when T <= kAllRowsT
+// (its DMA needs nothing from the slot table), else the block's 16 slot rows.
+constexpr int kAllRowsT = 8;
+
+// This lane's token slot (lane & 15) of block b: token row, flat row, valid.
+struct LaneSlot {
+  int tok, flat;
+  bool valid;
 };
 
-template <int WFMT>
-__device__ __forceinline__ WSlice load_wslice(const QW& w, size_t row, int K, int kb) {
-  WSlice s;
-  if constexpr (WFMT == kFP8) {
-    const uint8_t* p = w.codes + row * K + kb;
-    s.c0 = load_nt(p);
-    s.c1 = load_nt(p + 16);
-    s.sc = 0;
+__device__ __forceinline__ LaneSlot lane_slot(const DecodeArgs& a, int b, bool shared, int p0) {
+  const int j = lane_id() & 15;
+  LaneSlot s;
+  if (shared) {
+    s.flat = p0 + j;
+    s.tok = s.flat;
+    s.valid = s.flat < a.T;
   } else {
-    s.c0 = load_nt(w.codes + row * (K / 2) + kb / 2);
-    s.c1 = make_uint4(0, 0, 0, 0);
-    if constexpr (WFMT == kMXFP4)
-      s.sc = w.scales[row * (K / 32) + kb / 32];
-    else
-      s.sc = *reinterpret_cast<const uint16_t*>(w.scales + row * (K / 16) + kb / 16);
+    s.flat = a.sorted_ids[b * kDecodeBM + j];
+    s.valid = s.flat < a.T * a.k;
+    s.tok = s.valid ? s.flat / a.k : 0;
   }
   return s;
 }
 
-// bf16 operand (8 values) for MFMA step `st` (0..3) of a weight slice.
-template <int WFMT>
-__device__ __forceinline__ bf16x8 wslice_bf16(const WSlice& s, int st) {
-  uint32_t o[4];
-  if constexpr (WFMT == kMXFP4) {
-    const uint32_t word = st == 0 ? s.c0.x : st == 1 ? s.c0.y : st == 2 ? s.c0.z : s.c0.w;
-    fp4x8_to_bf16(word, e8m0_as_scale(s.sc), o);
-  } else if constexpr (WFMT == kNVFP4) {
-    const uint32_t word = st == 0 ? s.c0.x : st == 1 ? s.c0.y : st == 2 ? s.c0.z : s.c0.w;
-    fp4x8_to_bf16_mul(word, e4m3_to_f32((s.sc >> (st < 2 ? 0 : 8)) & 0xFF), o);
+// ======================================================== MXFP4 kernels ====
+// Split rows in LDS: hi / lo codes [rows][K] (swizzled), scales [rows][spitch].
+struct MxRows {
+  const uint8_t* hi;
+  const uint8_t* lo;
+  const uint8_t* sc;
+  int K, spitch;
+};
+
+__device__ __forceinline__ MxRows mx_rows(const uint8_t* base, int K, int spitch, int rows) {
+  return MxRows{base, base + rows * K, base + 2 * rows * K, K, spitch};
+}
+
+__host__ __device__ constexpr size_t mx_rows_bytes(int K, int spitch, int rows) {
+  return static_cast<size_t>(rows) * (2 * K + spitch);
+}
+
+// Weight stream of NB chunks of one row: lane group g holds K block 4u + g
+// of chunk u (16 code bytes at 64u + 16g: each load instruction reads 64
+// contiguous bytes of each of the wave's 16 rows) and its E8M0 scale: with
+// PACK (nch a multiple of 4) the row's 16 scale bytes of 4 chunks come as one
+// 16-byte load, else one byte per chunk.
+template <int NB, bool PACK>
+struct MxW {
+  uint4 c[NB];
+  uint32_t s[NB];
+};
+
+template <int NB, bool PACK>
+__device__ __forceinline__ void mx_wload(MxW<NB, PACK>& w, const uint8_t* codes, const uint8_t* scales, int u0,
+                                         int nch, int g) {
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (u0 + u < nch) w.c[u] = load_nt(codes + 64 * (u0 + u) + 16 * g);
+  if constexpr (PACK) {
+#pragma unroll
+    for (int m = 0; m < NB / 4; ++m)
+      if (u0 + 4 * m < nch) {
+        const uint4 v = *reinterpret_cast<const uint4*>(scales + 4 * (u0 + 4 * m));
+        w.s[4 * m] = v.x;
+        w.s[4 * m + 1] = v.y;
+        w.s[4 * m + 2] = v.z;
+        w.s[4 * m + 3] = v.w;
+      }
   } else {
-    const uint4 c = st < 2 ? s.c0 : s.c1;
-    const uint32_t w0 = (st & 1) ? c.z : c.x, w1 = (st & 1) ? c.w : c.y;
-    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
-    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
-    const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
-    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
-    o[0] = pack_bf16x2(a[0], a[1]);
-    o[1] = pack_bf16x2(b[0], b[1]);
-    o[2] = pack_bf16x2(c2[0], c2[1]);
-    o[3] = pack_bf16x2(d[0], d[1]);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (u0 + u < nch) w.s[u] = scales[4 * (u0 + u) + g];
   }
+}
+
+template <int NB, bool PACK>
+__device__ __forceinline__ int mx_wscale(const MxW<NB, PACK>& w, int u, int g) {
+  if constexpr (PACK)
+    return static_cast<int>((w.s[u] >> (8 * g)) & 0xFF);
+  else
+    return static_cast<int>(w.s[u]);
+}
+
+// MFMA chunk u (K [128u, 128u + 128)): A from LDS row r (zero unless
+// `valid`), hi then lo with the scale lowered by 2^4.
+__device__ __forceinline__ void mx_mma(const MxRows& m, int r, bool valid, int u, int g, const uint4& wc, int sb,
+                                       f32x4& acc) {
+  i32x8 ah = {}, al = {};
+  int sa = 0;
+  if (valid) {
+    const int q0 = 8 * u + g, q1 = q0 + 4;
+    const uint8_t* rh = m.hi + r * m.K;
+    const uint8_t* rl = m.lo + r * m.K;
+    ah = u4x2(lds16(rh, r, q0), lds16(rh, r, q1));
+    al = u4x2(lds16(rl, r, q0), lds16(rl, r, q1));
+    sa = m.sc[r * m.spitch + 4 * u + g];
+  }
+  const int sa_lo = sa >= 4 ? sa - 4 : 0;
+  const i32x8 b = {static_cast<int>(wc.x), static_cast<int>(wc.y), static_cast<int>(wc.z), static_cast<int>(wc.w),
+                   0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, acc, 0, 4, 0, sa, 0, sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc, 0, 4, 0, sa_lo, 0, sb);
+}
+
+// Streams one weight row (nch chunks) against LDS rows; the first NB chunks
+// are already loaded.
+template <int NB, bool PACK>
+__device__ __forceinline__ void mx_row_dot(MxW<NB, PACK>& wt, const uint8_t* codes, const uint8_t* scales,
+                                           const MxRows& m, int r, bool valid, int nch, int g, f32x4& acc) {
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (u < nch) mx_mma(m, r, valid, u, g, wt.c[u], mx_wscale(wt, u, g), acc);
+  for (int u0 = NB; u0 < nch; u0 += NB) {
+    mx_wload(wt, codes, scales, u0, nch, g);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (u0 + u < nch) mx_mma(m, r, valid, u0 + u, g, wt.c[u], mx_wscale(wt, u, g), acc);
+  }
+}
+
+// Split h rows of a block: routed rows [nb_routed * 16][I] first, then the
+// shared expert's [nb_shared * 16][Is]; scale rows share one pitch.
+struct HSplit {
+  uint8_t* hi;
+  uint8_t* lo;
+  uint8_t* sc;
+  int K;
+};
+
+__device__ __forceinline__ HSplit h_split_rows(const DecodeArgs& a, bool shared, int row0) {
+  const size_t routed = static_cast<size_t>(a.nb_routed) * kDecodeBM;
+  const size_t off = shared ? routed * a.I + static_cast<size_t>(row0) * a.Is : static_cast<size_t>(row0) * a.I;
+  const size_t srow = shared ? routed + row0 : row0;
+  return HSplit{a.hhi + off, a.hlo + off, a.hsc + srow * a.hsc_pitch, shared ? a.Is : a.I};
+}
+
+// gate_up: 4 waves, each on 8 intermediate indices (8 gate + 8 up rows); the
+// token rows arrive already split (xhi / xlo / xsc).
+template <int NB, bool PACK, bool ALLROWS>
+__global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float red[kGateWaves][kDecodeBM];
+  const int b = blockIdx.y;
+  const bool shared = b >= a.nb_routed;
+  const int I = shared ? a.Is : a.I;
+  const int c0 = blockIdx.x * 8 * kGateWaves;
+  if (c0 >= I) return;
+  const int e = shared ? 0 : a.block_expert[b];
+  if (e < 0) return;
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const QW& w = shared ? a.sgu : a.gu;
+  const int H = a.H, nch = H / 128;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int i0 = c0 + wave * 8;
+  const int j = lane & 15, g = lane >> 4;
+  const size_t wrow = static_cast<size_t>(e) * (2 * I) + (j < 8 ? i0 + j : I + i0 + (j - 8));
+  const int rows = ALLROWS ? a.T : kDecodeBM;
+  const MxRows m = mx_rows(smem, H, a.xsc_pitch, rows);
+  LaneSlot ls;
+  if constexpr (!ALLROWS) ls = lane_slot(a, b, shared, p0);
+
+  // 1. token rows -> LDS
+  dma_split_rows(smem, rows, H, a.xsc_pitch, a.xhi, a.xlo, a.xsc, [&](int r) {
+    if constexpr (ALLROWS)
+      return r;
+    else
+      return __shfl(ls.tok, r, kWave);
+  });
+  // 2. the weight stream
+  const uint8_t* codes = w.codes + wrow * (H / 2);
+  const uint8_t* scales = w.scales + wrow * (H / 32);
+  MxW<NB, PACK> wt;
+  mx_wload(wt, codes, scales, 0, nch, g);
+  if constexpr (ALLROWS) ls = lane_slot(a, b, shared, p0);
+  __syncthreads();
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mx_row_dot(wt, codes, scales, m, ALLROWS ? ls.tok : j, j < count, nch, g, acc);
+
+  // 3. h = SwiGLU(gate, up) rounded to bf16, then split per 32-block: lanes
+  //    j < 8 hold column i0 + j of slots 4g + r; the 32-block of a slot spans
+  //    the 4 waves.
+  float hv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float up = __shfl_xor(acc[r], 8, kWave);
+    const float v = bf16_to_f32(f32_to_bf16(swiglu(acc[r], up)));
+    hv[r] = j < 8 ? v : 0.f;
+    float mx = __builtin_fabsf(hv[r]);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, kWave));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2, kWave));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4, kWave));
+    if (j == 0) red[wave][4 * g + r] = mx;
+  }
+  __syncthreads();
+  const HSplit hs = h_split_rows(a, shared, p0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = 4 * g + r;
+    if (j < 8 && slot < count) {
+      float amax = red[0][slot];
+#pragma unroll
+      for (int q = 1; q < kGateWaves; ++q) amax = __builtin_fmaxf(amax, red[q][slot]);
+      const uint32_t code = mx_split_scale_code(amax);
+      uint32_t h2, l2;
+      mx_split_pair(hv[r] * mx_inv_scale(code), 0.f, &h2, &l2);
+      const size_t o = static_cast<size_t>(slot) * hs.K + i0 + j;
+      hs.hi[o] = static_cast<uint8_t>(h2 & 0xFF);
+      hs.lo[o] = static_cast<uint8_t>(l2 & 0xFF);
+      if (wave == 0 && j == 0) hs.sc[static_cast<size_t>(slot) * a.hsc_pitch + c0 / 32] = static_cast<uint8_t>(code);
+    }
+  }
+}
+
+// down: 16 output rows per wave against the block's split h rows.
+template <int NB, bool PACK>
+__global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = blockIdx.y;
+  const bool shared = b >= a.nb_routed;
+  const int e = shared ? 0 : a.block_expert[b];
+  if (e < 0) return;
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const QW& w = shared ? a.sdn : a.dn;
+  const int K = shared ? a.Is : a.I;
+  const int H = a.H, nch = K / 128;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int n0 = blockIdx.x * kDownTileN + wave * 16;
+  const int j = lane & 15, g = lane >> 4;
+  const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
+  const int rows = decode_rows(a.T);  // rows past the block's count are stale and unused
+  const MxRows m = mx_rows(smem, K, a.hsc_pitch, rows);
+  const HSplit hs = h_split_rows(a, shared, p0);
+
+  dma_split_rows(smem, rows, K, a.hsc_pitch, hs.hi, hs.lo, hs.sc, [](int r) { return r; });
+  const uint8_t* codes = w.codes + wrow * (K / 2);
+  const uint8_t* scales = w.scales + wrow * (K / 32);
+  MxW<NB, PACK> wt;
+  mx_wload(wt, codes, scales, 0, nch, g);
+  const LaneSlot ls = lane_slot(a, b, shared, p0);
+  __syncthreads();
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mx_row_dot(wt, codes, scales, m, j, j < count, nch, g, acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = 4 * g + r;
+    const int flat = __shfl(ls.flat, slot, kWave);
+    if (slot < count) {
+      if (shared)
+        a.s32[static_cast<size_t>(p0 + slot) * H + n0 + j] = acc[r];
+      else
+        a.o32[static_cast<size_t>(flat) * H + n0 + j] = acc[r];
+    }
+  }
+}
+
+// ================================================ bf16 / FP8 kernels ======
+// Per-lane weight slice of one 128-element K chunk (elements [32g, 32g+32)).
+struct WSlice4 {   // NVFP4: 16 bytes of codes + two E4M3 block scales
+  uint4 c;
+  uint32_t sc;
+};
+struct WSlice8 {   // FP8: 32 bytes of codes
+  uint4 c0, c1;
+};
+template <int WFMT> struct WSliceT { using type = WSlice4; };
+template <> struct WSliceT<kFP8> { using type = WSlice8; };
+
+template <int WFMT>
+__device__ __forceinline__ typename WSliceT<WFMT>::type load_wslice(const QW& w, size_t row, int K, int kb) {
+  typename WSliceT<WFMT>::type s;
+  if constexpr (WFMT == kFP8) {
+    const uint8_t* p = w.codes + row * K + kb;
+    s.c0 = load_nt(p);
+    s.c1 = load_nt(p + 16);
+  } else {
+    s.c = load_nt(w.codes + row * (K / 2) + kb / 2);
+    s.sc = *reinterpret_cast<const uint16_t*>(w.scales + row * (K / 16) + kb / 16);
+  }
+  return s;
+}
+
+// bf16 operand (8 values) for MFMA step `st` (0..3) of an NVFP4 slice.
+__device__ __forceinline__ bf16x8 nvfp4_bf16(const WSlice4& s, int st) {
+  uint32_t o[4];
+  const uint32_t word = st == 0 ? s.c.x : st == 1 ? s.c.y : st == 2 ? s.c.z : s.c.w;
+  fp4x8_to_bf16_mul(word, e4m3_to_f32((s.sc >> (st < 2 ? 0 : 8)) & 0xFF), o);
   return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-__device__ __forceinline__ i32x8 wslice_i32x8(const WSlice& s) {
-  return i32x8{static_cast<int>(s.c0.x), static_cast<int>(s.c0.y), static_cast<int>(s.c0.z),
-               static_cast<int>(s.c0.w), static_cast<int>(s.c1.x), static_cast<int>(s.c1.y),
-               static_cast<int>(s.c1.z), static_cast<int>(s.c1.w)};
+// bf16 operand (8 values) for MFMA step `st` (0..3) of an FP8 slice.
+__device__ __forceinline__ bf16x8 fp8_bf16(const WSlice8& s, int st) {
+  const uint4 c = st < 2 ? s.c0 : s.c1;
+  const uint32_t w0 = (st & 1) ? c.z : c.x, w1 = (st & 1) ? c.w : c.y;
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
+  const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]),
+                                               pack_bf16x2(c2[0], c2[1]), pack_bf16x2(d[0], d[1])));
 }
 
 __device__ __forceinline__ float scale_from_amax(const uint32_t* bits) {
@@ -88,135 +428,117 @@ __device__ __forceinline__ float scale_from_amax(const uint32_t* bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
-// Token slots of block b: LDS tok[16] (token index, or -1) and the count of
-// valid slots (a prefix).  Also returns flat row ids for routed blocks.
-struct SlotTable {
-  int tok[kDecodeBM];
-  int flat[kDecodeBM];
-  int count;
-};
-
-__device__ __forceinline__ void fill_slots(const DecodeArgs& a, int b, bool shared, SlotTable* st) {
-  if (threadIdx.x < kWave) {
-    const int r = lane_id();
-    bool valid = false;
-    int tok = -1, flat = -1;
-    if (r < kDecodeBM) {
-      if (shared) {
-        tok = (b - a.nb_routed) * kDecodeBM + r;
-        flat = tok;
-        valid = tok < a.T;
-      } else {
-        flat = a.sorted_ids[b * kDecodeBM + r];
-        valid = flat < a.T * a.k;
-        tok = flat / a.k;
-      }
-    }
-    const unsigned long long m = __ballot(valid);
-    if (r < kDecodeBM) {
-      st->tok[r] = valid ? tok : -1;
-      st->flat[r] = valid ? flat : -1;
-    }
-    if (r == 0) st->count = __popcll(m);
-  }
+// 8 bf16 -> 8 E4M3 codes of v / sh (fp32 quotient, round to nearest even).
+__device__ __forceinline__ uint2 bf16x8_to_e4m3(const uint4& v, float sh) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = f32x2_to_e4m3x2(bf16_to_f32(w[i] & 0xFFFF) / sh, bf16_to_f32(w[i] >> 16) / sh);
+  return make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
 }
 
-// A operand: 8 bf16 (or 32 FP8 bytes) of slot row j at element kb from LDS.
-__device__ __forceinline__ bf16x8 lds_row_bf16(const uint8_t* xs, int pitch, int j, int count, int kb) {
-  if (j >= count) return bf16x8{};
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + j * pitch + kb * 2));
-}
-__device__ __forceinline__ i32x8 lds_row_fp8(const uint8_t* xs, int pitch, int j, int count, int kb) {
-  if (j >= count) return i32x8{};
-  const uint4 p = *reinterpret_cast<const uint4*>(xs + j * pitch + kb);
-  const uint4 q = *reinterpret_cast<const uint4*>(xs + j * pitch + kb + 16);
-  return i32x8{static_cast<int>(p.x), static_cast<int>(p.y), static_cast<int>(p.z), static_cast<int>(p.w),
-               static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w)};
-}
-
-// MFMA work of one batch of NB chunks held in registers.
-template <int WFMT, bool FP8ACT, int NB>
-__device__ __forceinline__ void mma_batch(const WSlice* ws, int kc0, int K, int g, const uint8_t* xs, int pitch,
-                                          int j, int count, f32x4& acc) {
+// A operand rows in LDS, swizzled: bf16 rows (ABF16) or FP8 rows.
+// ABF16 + FP8 MFMA (down with FP8 activations) quantises with sh on the fly.
+template <int WFMT, bool FP8MMA, bool ABF16, int NB>
+__device__ __forceinline__ void mma_batch(const typename WSliceT<WFMT>::type* ws, int kc0, int K, int g,
+                                          const uint8_t* xs, int row_bytes, int r, bool valid, float sh,
+                                          f32x4& acc) {
+  const uint8_t* row = xs + r * row_bytes;
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     if (kc0 + u * 128 >= K) break;
     const int kb = kc0 + u * 128 + g * 32;
-    if constexpr (FP8ACT) {
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lds_row_fp8(xs, pitch, j, count, kb),
-                                                             wslice_i32x8(ws[u]), acc, 0, 0, 0, 127, 0, 127);
+    if constexpr (FP8MMA) {
+      i32x8 av = {};
+      if (valid) {
+        if constexpr (ABF16) {
+          uint2 p[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) p[q] = bf16x8_to_e4m3(lds16(row, r, kb / 8 + q), sh);
+          av = i32x8{static_cast<int>(p[0].x), static_cast<int>(p[0].y), static_cast<int>(p[1].x),
+                     static_cast<int>(p[1].y), static_cast<int>(p[2].x), static_cast<int>(p[2].y),
+                     static_cast<int>(p[3].x), static_cast<int>(p[3].y)};
+        } else {
+          av = u4x2(lds16(row, r, kb / 16), lds16(row, r, kb / 16 + 1));
+        }
+      }
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, u4x2(ws[u].c0, ws[u].c1), acc, 0, 0, 0, 127, 0,
+                                                             127);
     } else {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_bf16(xs, pitch, j, count, kb + st * 8),
-                                                      wslice_bf16<WFMT>(ws[u], st), acc, 0, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 bw;
+        if constexpr (WFMT == kFP8)
+          bw = fp8_bf16(ws[u], st);
+        else
+          bw = nvfp4_bf16(ws[u], st);
+        const bf16x8 av = valid ? __builtin_bit_cast(bf16x8, lds16(row, r, kb / 8 + st)) : bf16x8{};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc, 0, 0, 0);
+      }
     }
   }
 }
 
-// ------------------------------------------------------------- gate_up ----
-// WPB waves per workgroup, each on 8 adjacent intermediate indices (their 8
-// gate rows and 8 up rows); the workgroup shares one LDS copy of its tokens.
-template <int WFMT, bool FP8ACT, int NB, int WPB>
+template <int WFMT, bool FP8ACT, int NB, int WPB, bool ALLROWS>
 __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-  __shared__ SlotTable slots;
+  __shared__ float red[16];
   const int b = blockIdx.y;
   const bool shared = b >= a.nb_routed;
+  const int e = shared ? 0 : a.block_expert[b];
+  if (e < 0) return;
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const QW& w = shared ? a.sgu : a.gu;
   const int I = shared ? a.Is : a.I;
   const int H = a.H;
-  const int e = shared ? 0 : a.block_expert[b];
-  if (e < 0) return;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int i0 = (blockIdx.x * WPB + wave) * 8;
   const bool active = i0 < I;
   const int j = lane & 15, g = lane >> 4;
   const size_t wrow = static_cast<size_t>(e) * (2 * I) + (j < 8 ? i0 + j : I + i0 + (j - 8));
-  const int pitch = (FP8ACT ? H : 2 * H) + 16;
+  const int row_bytes = FP8ACT ? H : 2 * H;
+  const int rows = ALLROWS ? a.T : kDecodeBM;
+  LaneSlot ls;
+  if constexpr (!ALLROWS) ls = lane_slot(a, b, shared, p0);
 
-  WSlice ws[NB];
+  dma_rows(xs, rows, row_bytes / 16, [&](int r) -> const void* {
+    size_t t;
+    if constexpr (ALLROWS)
+      t = static_cast<size_t>(r);
+    else
+      t = static_cast<size_t>(__shfl(ls.tok, r, kWave));
+    return FP8ACT ? a.xq + t * H : reinterpret_cast<const uint8_t*>(a.x + t * H);
+  });
+  typename WSliceT<WFMT>::type ws[NB];
   if (active) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
       if (u * 128 < H) ws[u] = load_wslice<WFMT>(w, wrow, H, u * 128 + g * 32);
   }
-  fill_slots(a, b, shared, &slots);
-  __syncthreads();
-  const int count = slots.count;
-  // Stage the block's token rows (x, or its FP8 codes) in LDS.
-  {
-    const int row_vec = (FP8ACT ? H : 2 * H) / 16;
-    for (int i = threadIdx.x; i < count * row_vec; i += blockDim.x) {
-      const int r = i / row_vec, c = i % row_vec;
-      const size_t t = static_cast<size_t>(slots.tok[r]);
-      const uint4 v = FP8ACT ? reinterpret_cast<const uint4*>(a.xq + t * H)[c]
-                             : reinterpret_cast<const uint4*>(a.x + t * H)[c];
-      *reinterpret_cast<uint4*>(xs + r * pitch + c * 16) = v;
-    }
-  }
+  if constexpr (ALLROWS) ls = lane_slot(a, b, shared, p0);
   __syncthreads();
   if constexpr (!FP8ACT) {
     if (!active) return;
   }
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
 
+  const int arow = ALLROWS ? ls.tok : j;
+  const bool aval = j < count;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
-    mma_batch<WFMT, FP8ACT, NB>(ws, 0, H, g, xs, pitch, j, count, acc);
+    mma_batch<WFMT, FP8ACT, false, NB>(ws, 0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
     for (int kc0 = NB * 128; kc0 < H; kc0 += NB * 128) {
 #pragma unroll
       for (int u = 0; u < NB; ++u)
         if (kc0 + u * 128 < H) ws[u] = load_wslice<WFMT>(w, wrow, H, kc0 + u * 128 + g * 32);
-      mma_batch<WFMT, FP8ACT, NB>(ws, kc0, H, g, xs, pitch, j, count, acc);
+      mma_batch<WFMT, FP8ACT, false, NB>(ws, kc0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
     }
   }
 
-  float f = 1.0f;
-  if constexpr (WFMT != kMXFP4) f = w.tscale[e];
+  float f = w.tscale[e];
   if constexpr (FP8ACT) f *= scale_from_amax(a.amax_x);
   uint16_t* h = shared ? a.hs : a.h;
-  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
-  float m = 0.f;
+  float mx = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float up = __shfl_xor(acc[r], 8, kWave);
@@ -224,90 +546,64 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
     if (active && j < 8 && slot < count) {
       const float v = swiglu(acc[r] * f, up * f);
       h[static_cast<size_t>(p0 + slot) * I + i0 + j] = f32_to_bf16(v);
-      m = __builtin_fmaxf(m, __builtin_fabsf(v));
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
     }
   }
-  if constexpr (FP8ACT) {
-    __shared__ float red[16];
-    wg_amax_to_slots(m, a.amax_slots, red);
-  }
+  if constexpr (FP8ACT) wg_amax_to_slots(mx, a.amax_slots, red);
 }
 
-// ----------------------------------------------------- down + combine ----
 template <int WFMT, bool FP8ACT, int NB>
 __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t hsm[];
-  __shared__ SlotTable slots;
   const int b = blockIdx.y;
   const bool shared = b >= a.nb_routed;
+  const int e = shared ? 0 : a.block_expert[b];
+  if (e < 0) return;
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const QW& w = shared ? a.sdn : a.dn;
   const int K = shared ? a.Is : a.I;
   const int H = a.H;
-  const int e = shared ? 0 : a.block_expert[b];
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int tile = blockIdx.x;
-  const int n0 = tile * kDownTileN + wave * 16;
+  const int n0 = blockIdx.x * kDownTileN + wave * 16;
   const int j = lane & 15, g = lane >> 4;
+  const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
+  const uint16_t* hsrc = shared ? a.hs : a.h;
+  const int rows = decode_rows(a.T);  // rows past the block's count are stale and unused
 
-  if (e < 0) return;
-  {
-    const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
-    const int kmax = a.Is > a.I ? a.Is : a.I;
-    const int pitch = (FP8ACT ? kmax : 2 * kmax) + 16;
-    WSlice ws[NB];
+  dma_rows(hsm, rows, K / 8, [&](int r) -> const void* { return hsrc + static_cast<size_t>(p0 + r) * K; });
+  typename WSliceT<WFMT>::type ws[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, u * 128 + g * 32);
+  const LaneSlot ls = lane_slot(a, b, shared, p0);
+  float sh = 1.0f;
+  if constexpr (FP8ACT) sh = scale_from_amax(a.amax_h);
+  __syncthreads();
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  const bool aval = j < count;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mma_batch<WFMT, FP8ACT, true, NB>(ws, 0, K, g, hsm, 2 * K, j, aval, sh, acc);
+  for (int kc0 = NB * 128; kc0 < K; kc0 += NB * 128) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, u * 128 + g * 32);
-    fill_slots(a, b, shared, &slots);
-    __syncthreads();
-    const int count = slots.count;
-    float sh = 1.0f;
-    if constexpr (FP8ACT) sh = scale_from_amax(a.amax_h);
-    // Stage the block's h rows (quantised to E4M3 with the h scale for FP8).
-    {
-      const uint16_t* hsrc = shared ? a.hs : a.h;
-      const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
-      const int row_vec = K / 8;  // 8 bf16 per 16-byte load
-      for (int i = threadIdx.x; i < count * row_vec; i += blockDim.x) {
-        const int r = i / row_vec, c = i % row_vec;
-        const uint4 v = reinterpret_cast<const uint4*>(hsrc + static_cast<size_t>(p0 + r) * K)[c];
-        if constexpr (FP8ACT) {
-          const uint32_t lo = f32x2_to_e4m3x2(bf16_to_f32(v.x & 0xFFFF) / sh, bf16_to_f32(v.x >> 16) / sh);
-          const uint32_t hi = f32x2_to_e4m3x2(bf16_to_f32(v.y & 0xFFFF) / sh, bf16_to_f32(v.y >> 16) / sh);
-          const uint32_t lo2 = f32x2_to_e4m3x2(bf16_to_f32(v.z & 0xFFFF) / sh, bf16_to_f32(v.z >> 16) / sh);
-          const uint32_t hi2 = f32x2_to_e4m3x2(bf16_to_f32(v.w & 0xFFFF) / sh, bf16_to_f32(v.w >> 16) / sh);
-          *reinterpret_cast<uint2*>(hsm + r * pitch + c * 8) = make_uint2(lo | (hi << 16), lo2 | (hi2 << 16));
-        } else {
-          *reinterpret_cast<uint4*>(hsm + r * pitch + c * 16) = v;
-        }
-      }
-    }
-    __syncthreads();
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma_batch<WFMT, FP8ACT, NB>(ws, 0, K, g, hsm, pitch, j, count, acc);
-    for (int kc0 = NB * 128; kc0 < K; kc0 += NB * 128) {
+      if (kc0 + u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, kc0 + u * 128 + g * 32);
+    mma_batch<WFMT, FP8ACT, true, NB>(ws, kc0, K, g, hsm, 2 * K, j, aval, sh, acc);
+  }
+  const float f = w.tscale[e] * sh;
 #pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (kc0 + u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, kc0 + u * 128 + g * 32);
-      mma_batch<WFMT, FP8ACT, NB>(ws, kc0, K, g, hsm, pitch, j, count, acc);
-    }
-    float f = 1.0f;
-    if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-    if constexpr (FP8ACT) f *= sh;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int slot = 4 * g + r;
-      if (slot < count) {
-        if (shared)
-          a.s32[static_cast<size_t>(slots.tok[slot]) * H + n0 + j] = acc[r] * f;
-        else
-          a.o32[static_cast<size_t>(slots.flat[slot]) * H + n0 + j] = acc[r] * f;
-      }
+  for (int r = 0; r < 4; ++r) {
+    const int slot = 4 * g + r;
+    const int flat = __shfl(ls.flat, slot, kWave);
+    if (slot < count) {
+      if (shared)
+        a.s32[static_cast<size_t>(p0 + slot) * H + n0 + j] = acc[r] * f;
+      else
+        a.o32[static_cast<size_t>(flat) * H + n0 + j] = acc[r] * f;
     }
   }
-
 }
 
+// ============================================================ combine =====
 // y[t] = sum_j w[t,j] o[t*k+j] (ascending j) + sg[t] s[t], from the fp32
 // partial outputs; one thread per 4 columns.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
@@ -326,18 +622,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     acc.w = fmaf(wj, v.w, acc.w);
   }
   if (a.sg) {
-    const float g = a.sg[t];
+    const float gt = a.sg[t];
     const float4 v = *reinterpret_cast<const float4*>(a.s32 + static_cast<size_t>(t) * a.H + c);
-    acc.x = fmaf(g, v.x, acc.x);
-    acc.y = fmaf(g, v.y, acc.y);
-    acc.z = fmaf(g, v.z, acc.z);
-    acc.w = fmaf(g, v.w, acc.w);
+    acc.x = fmaf(gt, v.x, acc.x);
+    acc.y = fmaf(gt, v.y, acc.y);
+    acc.z = fmaf(gt, v.z, acc.z);
+    acc.w = fmaf(gt, v.w, acc.w);
   }
   *reinterpret_cast<uint2*>(a.y + static_cast<size_t>(t) * a.H + c) =
       make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
 }
 
-// Kernels that may need more than 64 KB of dynamic LDS opt in once.
+// ========================================================= x split prep ===
+// xhi / xlo [T][H] and xsc [T][xsc_pitch] of bf16 x: one thread per 32-block.
+__global__ __launch_bounds__(256) void x_split_kernel(const uint16_t* __restrict__ x, int T, int H, int xsc_pitch,
+                                                      uint8_t* __restrict__ xhi, uint8_t* __restrict__ xlo,
+                                                      uint8_t* __restrict__ xsc) {
+  const int nb = H / 32;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * nb) return;
+  const int t = i / nb, blk = i % nb;
+  const uint4* p = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + blk * 32);
+  uint4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = p[q];
+  mx_split_block(v, xhi + static_cast<size_t>(t) * H + blk * 32, xlo + static_cast<size_t>(t) * H + blk * 32,
+                 xsc + static_cast<size_t>(t) * xsc_pitch + blk);
+}
+
+hipError_t launch_x_split(const uint16_t* x, int T, int H, int xsc_pitch, uint8_t* xhi, uint8_t* xlo,
+                          uint8_t* xsc, hipStream_t s) {
+  const int n = T * (H / 32);
+  x_split_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, T, H, xsc_pitch, xhi, xlo, xsc);
+  return hipGetLastError();
+}
+
+// ============================================================ launches ====
+// Kernels that may need more than 64 KB of dynamic LDS opt in.
 template <class Kern>
 static hipError_t allow_lds(Kern kernel, size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
@@ -346,33 +667,65 @@ static hipError_t allow_lds(Kern kernel, size_t bytes) {
                              static_cast<int>(bytes));
 }
 
-template <int WFMT, bool FP8ACT, int WPB>
-static hipError_t run_decode_gateup_w(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NB = WFMT == kFP8 ? 8 : 16;
+template <bool PACK, bool ALLROWS>
+static hipError_t run_gateup_mx_r(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NB = 16;
   const int imax = a.Is > a.I ? a.Is : a.I;
-  const int rows = a.T < kDecodeBM ? a.T : kDecodeBM;
-  const size_t lds = static_cast<size_t>(rows) * ((FP8ACT ? a.H : 2 * a.H) + 16);
-  dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
-  const hipError_t e = allow_lds(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB>, lds);
+  const size_t lds = mx_rows_bytes(a.H, a.xsc_pitch, ALLROWS ? a.T : kDecodeBM);
+  dim3 grid(imax / (8 * kGateWaves), a.nb_routed + a.nb_shared);
+  const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK, ALLROWS>, lds);
   if (e != hipSuccess) return e;
-  decode_gateup_kernel<WFMT, FP8ACT, NB, WPB><<<grid, 64 * WPB, lds, s>>>(a);
+  decode_gateup_mx_kernel<NB, PACK, ALLROWS><<<grid, 64 * kGateWaves, lds, s>>>(a);
   return hipGetLastError();
 }
 
-// One-token batches touch few experts: single-wave workgroups spread them over
-// every CU.  Larger batches share each LDS token copy among 8 waves.
-template <int WFMT, bool FP8ACT>
-static hipError_t run_decode_gateup(const DecodeArgs& a, hipStream_t s) {
-  if (a.T <= 2) return run_decode_gateup_w<WFMT, FP8ACT, 1>(a, s);
-  return run_decode_gateup_w<WFMT, FP8ACT, 8>(a, s);
+static hipError_t run_gateup_mx(const DecodeArgs& a, hipStream_t s) {
+  const bool pack = (a.H / 128) % 4 == 0;
+  if (a.T <= kAllRowsT) return pack ? run_gateup_mx_r<true, true>(a, s) : run_gateup_mx_r<false, true>(a, s);
+  return pack ? run_gateup_mx_r<true, false>(a, s) : run_gateup_mx_r<false, false>(a, s);
+}
+
+template <int WFMT, bool FP8ACT, int WPB, bool ALLROWS>
+static hipError_t run_gateup_r(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NB = WFMT == kFP8 ? 8 : 16;
+  const int imax = a.Is > a.I ? a.Is : a.I;
+  const size_t lds = static_cast<size_t>(ALLROWS ? a.T : kDecodeBM) * (FP8ACT ? a.H : 2 * a.H);
+  dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
+  const hipError_t e = allow_lds(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB, ALLROWS>, lds);
+  if (e != hipSuccess) return e;
+  decode_gateup_kernel<WFMT, FP8ACT, NB, WPB, ALLROWS><<<grid, 64 * WPB, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int WFMT, bool FP8ACT, int WPB>
+static hipError_t run_gateup(const DecodeArgs& a, hipStream_t s) {
+  return a.T <= kAllRowsT ? run_gateup_r<WFMT, FP8ACT, WPB, true>(a, s)
+                          : run_gateup_r<WFMT, FP8ACT, WPB, false>(a, s);
+}
+
+template <bool PACK>
+static hipError_t run_down_mx_p(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NB = 8;
+  const int kmax = a.Is > a.I ? a.Is : a.I;
+  const size_t lds = mx_rows_bytes(kmax, a.hsc_pitch, decode_rows(a.T));
+  dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
+  const hipError_t e = allow_lds(decode_down_mx_kernel<NB, PACK>, lds);
+  if (e != hipSuccess) return e;
+  decode_down_mx_kernel<NB, PACK><<<grid, 64 * kDownWaves, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+static hipError_t run_down_mx(const DecodeArgs& a, hipStream_t s) {
+  // PACK needs every K of the launch (routed and shared) to hold whole dwords of scales
+  const bool pack = (a.I / 128) % 4 == 0 && (a.Is / 128) % 4 == 0;
+  return pack ? run_down_mx_p<true>(a, s) : run_down_mx_p<false>(a, s);
 }
 
 template <int WFMT, bool FP8ACT>
-static hipError_t run_decode_down(const DecodeArgs& a, hipStream_t s) {
+static hipError_t run_down(const DecodeArgs& a, hipStream_t s) {
   constexpr int NB = WFMT == kFP8 ? 4 : 8;
   const int kmax = a.Is > a.I ? a.Is : a.I;
-  const int rows = a.T < kDecodeBM ? a.T : kDecodeBM;
-  const size_t lds = static_cast<size_t>(rows) * ((FP8ACT ? kmax : 2 * kmax) + 16);
+  const size_t lds = static_cast<size_t>(decode_rows(a.T)) * 2 * kmax;
   dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
   const hipError_t e = allow_lds(decode_down_kernel<WFMT, FP8ACT, NB>, lds);
   if (e != hipSuccess) return e;
@@ -380,12 +733,28 @@ static hipError_t run_decode_down(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// bf16 / FP8 gate_up: one-token batches touch few experts, so single-wave
+// workgroups spread them over every CU; larger batches share each LDS token
+// copy among 4 waves.
 hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
   const bool fp8act = a.xq != nullptr;
+  const bool small = a.T <= 2;
   switch (a.gu.fmt) {
-    case kMXFP4: return run_decode_gateup<kMXFP4, false>(a, s);
-    case kNVFP4: return run_decode_gateup<kNVFP4, false>(a, s);
-    case kFP8: return fp8act ? run_decode_gateup<kFP8, true>(a, s) : run_decode_gateup<kFP8, false>(a, s);
+    case kMXFP4: return run_gateup_mx(a, s);
+    case kNVFP4: return small ? run_gateup<kNVFP4, false, 1>(a, s) : run_gateup<kNVFP4, false, 4>(a, s);
+    case kFP8:
+      if (fp8act) return small ? run_gateup<kFP8, true, 1>(a, s) : run_gateup<kFP8, true, 4>(a, s);
+      return small ? run_gateup<kFP8, false, 1>(a, s) : run_gateup<kFP8, false, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
+  const bool fp8act = a.amax_h != nullptr;
+  switch (a.dn.fmt) {
+    case kMXFP4: return run_down_mx(a, s);
+    case kNVFP4: return run_down<kNVFP4, false>(a, s);
+    case kFP8: return fp8act ? run_down<kFP8, true>(a, s) : run_down<kFP8, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -394,16 +763,6 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   const int n = a.T * (a.H / 4);
   decode_combine_kernel<<<(n + 255) / 256, 256, 0, s>>>(a);
   return hipGetLastError();
-}
-
-hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
-  const bool fp8act = a.amax_h != nullptr;
-  switch (a.dn.fmt) {
-    case kMXFP4: return run_decode_down<kMXFP4, false>(a, s);
-    case kNVFP4: return run_decode_down<kNVFP4, false>(a, s);
-    case kFP8: return fp8act ? run_decode_down<kFP8, true>(a, s) : run_decode_down<kFP8, false>(a, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace ftmoe

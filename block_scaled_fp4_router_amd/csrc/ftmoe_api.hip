@@ -81,6 +81,7 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 }
 
 constexpr int kMaxTopK = 16;
+constexpr int kMaxDim = 4096;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTokens = 1 << 20;
 constexpr int kDecodeAutoMaxT = kDecodeMaxT;
@@ -108,10 +109,11 @@ ftmoe_status check_qweight(const ftmoe_qweight& q, const char* name, int fmt, in
 
 ftmoe_status check_layer(const ftmoe_layer* L) {
   if (!L) return fail(FTMOE_ERR_INVALID_ARG, "layer is NULL");
-  if (L->hidden <= 0 || L->hidden % 128)
-    return fail(FTMOE_ERR_UNSUPPORTED, "hidden=%d must be a positive multiple of 128", L->hidden);
-  if (L->inter <= 0 || L->inter % 128)
-    return fail(FTMOE_ERR_UNSUPPORTED, "inter=%d must be a positive multiple of 128", L->inter);
+  if (L->hidden <= 0 || L->hidden % 128 || L->hidden > kMaxDim)
+    return fail(FTMOE_ERR_UNSUPPORTED, "hidden=%d must be a positive multiple of 128, at most %d", L->hidden,
+                kMaxDim);
+  if (L->inter <= 0 || L->inter % 128 || L->inter > kMaxDim)
+    return fail(FTMOE_ERR_UNSUPPORTED, "inter=%d must be a positive multiple of 128, at most %d", L->inter, kMaxDim);
   if (L->top_k < 1 || L->top_k > kMaxTopK)
     return fail(FTMOE_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", L->top_k, kMaxTopK);
   if (L->num_experts < L->top_k || L->num_experts > kMaxExperts)
@@ -132,8 +134,9 @@ ftmoe_status check_layer(const ftmoe_layer* L) {
   FT_TRY(check_qweight(L->down, "down", fmt, L->num_experts, L->hidden, L->inter));
   if (L->shared_inter < 0) return fail(FTMOE_ERR_INVALID_ARG, "shared_inter=%d is negative", L->shared_inter);
   if (L->shared_inter > 0) {
-    if (L->shared_inter % 128)
-      return fail(FTMOE_ERR_UNSUPPORTED, "shared_inter=%d must be a multiple of 128", L->shared_inter);
+    if (L->shared_inter % 128 || L->shared_inter > kMaxDim)
+      return fail(FTMOE_ERR_UNSUPPORTED, "shared_inter=%d must be a multiple of 128, at most %d", L->shared_inter,
+                  kMaxDim);
     if (L->act == FTMOE_ACT_FP8_PER_TENSOR)
       return fail(FTMOE_ERR_UNSUPPORTED, "a shared expert with FP8 per-tensor activations is not supported");
     FT_TRY(check_qweight(L->shared_gate_up, "shared_gate_up", fmt, 1, 2 * L->shared_inter, L->hidden));
@@ -163,7 +166,10 @@ struct Plan {
   bool small_route = false;  // router via H-sliced partials + fused top-k (T <= kDecodeMaxT)
   int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0;
   size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
-         scal = 0, ascratch = 0, xq = 0, h = 0, o = 0, hs = 0, s = 0, total = 0;
+         scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
+         hsc = 0, total = 0;
+  int hsc_pitch = 0;
+  bool mx_split = false;  // MXFP4: activations travel as split E4M3 pairs
 };
 
 Plan make_plan(const ftmoe_layer* L, int T) {
@@ -203,12 +209,26 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   p.scal = take(static_cast<size_t>(p.n_zero) * 4);
   p.ascratch = take(align_scratch_bytes(T, k, E, p.BM));
   p.xq = take(L->act == FTMOE_ACT_FP8_PER_TENSOR ? static_cast<size_t>(T) * H : 0);
-  p.h = take(static_cast<size_t>(p.P) * I * 2);
-  p.o = take(tk * H * obytes);
-  if (shared) {
-    p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
-    p.s = take(static_cast<size_t>(T) * H * obytes);
+  p.mx_split = p.decode && L->gate_up.fmt == FTMOE_W_MXFP4;
+  if (p.mx_split) {
+    p.xhi = take(static_cast<size_t>(T) * H);
+    p.xlo = take(static_cast<size_t>(T) * H);
+    p.xsc = take(static_cast<size_t>(T) * xsc_pitch_of(H));
   }
+  if (p.mx_split) {
+    // h in the split form the MXFP4 down kernel multiplies
+    const int imax = shared && L->shared_inter > I ? L->shared_inter : I;
+    const size_t hbytes = static_cast<size_t>(p.P) * I + static_cast<size_t>(p.shared_rows) * L->shared_inter;
+    p.hsc_pitch = xsc_pitch_of(imax);
+    p.hhi = take(hbytes);
+    p.hlo = take(hbytes);
+    p.hsc = take(static_cast<size_t>(p.P + p.shared_rows) * p.hsc_pitch);
+  } else {
+    p.h = take(static_cast<size_t>(p.P) * I * 2);
+    if (shared) p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
+  }
+  p.o = take(tk * H * obytes);
+  if (shared) p.s = take(static_cast<size_t>(T) * H * obytes);
   p.total = off;
   return p;
 }
@@ -247,10 +267,13 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
   const int E = L->num_experts, k = L->top_k;
   if (p.small_route) {
     float* part = at<float>(ws, p.part);
+    const bool split = align && p.mx_split;  // the experts stage of this call reads the split x
     FT_HIP(timed("router_partial", s,
                  [&] {
                    return launch_router_partial(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
-                                                part, s);
+                                                part, split ? at<uint8_t>(ws, p.xhi) : nullptr,
+                                                split ? at<uint8_t>(ws, p.xlo) : nullptr,
+                                                split ? at<uint8_t>(ws, p.xsc) : nullptr, xsc_pitch_of(L->hidden), s);
                  }),
            "router launch");
     FT_HIP(timed("topk_align", s,
@@ -315,6 +338,15 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   uint16_t* hs = shared ? at<uint16_t>(ws, p.hs) : nullptr;
 
   if (p.decode) {
+    if (p.mx_split && !aligned) {
+      // the router of this call did not produce the split x
+      FT_HIP(timed("x_split", s,
+                   [&] {
+                     return launch_x_split(x, T, H, xsc_pitch_of(H), at<uint8_t>(ws, p.xhi), at<uint8_t>(ws, p.xlo),
+                                           at<uint8_t>(ws, p.xsc), s);
+                   }),
+             "x split launch");
+    }
     DecodeArgs a{};
     a.gu = gu;
     a.dn = dn;
@@ -332,10 +364,22 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     a.nb_routed = p.nblocks;
     a.nb_shared = p.nb_shared;
     a.x = x;
+    if (p.mx_split) {
+      a.xhi = at<uint8_t>(ws, p.xhi);
+      a.xlo = at<uint8_t>(ws, p.xlo);
+      a.xsc = at<uint8_t>(ws, p.xsc);
+      a.xsc_pitch = xsc_pitch_of(H);
+    }
     a.xq = xq;
     a.amax_x = ax;
     a.h = h;
     a.hs = hs;
+    if (p.mx_split) {
+      a.hhi = at<uint8_t>(ws, p.hhi);
+      a.hlo = at<uint8_t>(ws, p.hlo);
+      a.hsc = at<uint8_t>(ws, p.hsc);
+      a.hsc_pitch = p.hsc_pitch;
+    }
     a.amax_slots = ahs;
     a.amax_h = ah;
     a.o32 = at<float>(ws, p.o);

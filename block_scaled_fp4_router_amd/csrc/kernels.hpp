@@ -53,10 +53,17 @@ hipError_t launch_amax_fold(const uint32_t* slots, uint32_t* out, hipStream_t s)
 // ---- decode path (T <= kDecodeMaxT; bandwidth-bound) ----
 constexpr int kDecodeBM = 16;
 constexpr int kDecodeMaxT = 16;
-// Router partial logits part[s][t][row], s over H-slices of 256 columns.
+// Router partial logits part[t][row][s], s over S = router_splits(H) slices
+// of H (a multiple of 4).  With xhi non-NULL the kernel also writes the split
+// E4M3 form of x (xhi / xlo [T][H], xsc [T][xsc_pitch]) for the MXFP4 MFMA.
 int router_splits(int H);
 hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                 const float* shared_gate_w, float* part, hipStream_t s);
+                                 const float* shared_gate_w, float* part, uint8_t* xhi, uint8_t* xlo,
+                                 uint8_t* xsc, int xsc_pitch, hipStream_t s);
+// Split E4M3 form of x without the router (one thread per 32-block).
+hipError_t launch_x_split(const uint16_t* x, int T, int H, int xsc_pitch, uint8_t* xhi, uint8_t* xlo,
+                          uint8_t* xsc, hipStream_t s);
+inline int xsc_pitch_of(int H) { return (H / 32 + 15) / 16 * 16; }
 // Sums the partial logits, top-k + softmax (+ sigmoid gate), aligns the T*k
 // rows into blocks of kDecodeBM and zeroes `zero_words`.  One workgroup.
 hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int k, const float* bias,
@@ -73,10 +80,18 @@ struct DecodeArgs {
   int T, k, H, I, Is;
   int nb_routed, nb_shared;   // grid blocks: routed blocks, then shared blocks
   const uint16_t* x;
+  const uint8_t* xhi;         // MXFP4: split activations [T][H] (hi codes)
+  const uint8_t* xlo;         //        [T][H] (lo codes)
+  const uint8_t* xsc;         //        [T][xsc_pitch] E8M0 scale per 32-block
+  int xsc_pitch;
   const uint8_t* xq;          // FP8 activations or NULL
   const uint32_t* amax_x;
-  uint16_t* h;                // [nb_routed * 16][I] bf16
-  uint16_t* hs;               // [nb_shared * 16][Is] bf16
+  uint16_t* h;                // [nb_routed * 16][I] bf16 (NVFP4 / FP8)
+  uint16_t* hs;               // [nb_shared * 16][Is] bf16 (NVFP4 / FP8)
+  uint8_t* hhi;               // MXFP4: split h, routed rows [nb_routed * 16][I] then shared [nb_shared * 16][Is]
+  uint8_t* hlo;               //        (lo codes, same layout)
+  uint8_t* hsc;               //        [(nb_routed + nb_shared) * 16][hsc_pitch] E8M0 scales
+  int hsc_pitch;
   uint32_t* amax_slots;       // FP8 activations: gate_up partial maxima of |h| (or NULL)
   const uint32_t* amax_h;     // FP8 activations: folded max of |h| read by down (or NULL)
   float* o32;                 // [T*k][H] fp32

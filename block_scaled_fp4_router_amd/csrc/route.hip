@@ -247,63 +247,95 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bi
 // ======================================================= decode router ====
 // Few tokens (T <= 16).  The router matrix (E x H fp32, 1-4 MiB) is read by
 // many workgroups at once: workgroup (r, s) reads rows 4r..4r+3 over the
-// H-slice [256 s, 256 s + 256) -- one 16-byte load per lane -- and writes
-// partial logits part[s][t][row].  The fused top-k kernel adds the S slices
-// in order, so the logits do not depend on scheduling.
-constexpr int kSliceH = 256;
+// H-slice [256 s, 256 s + 256) -- at most one 16-byte load per lane -- and
+// writes partial logits part[t][row][s] (S is rounded up to a multiple of 4;
+// slices past H contribute zero).  The fused top-k kernel adds the S slices
+// in order, so the logits do not depend on scheduling.  The workgroups of
+// row block 0 also write the split E4M3 form of their x slice when asked.
+int router_splits(int H) {
+  const int s = (H + 255) / 256;
+  return (s + 3) / 4 * 4;
+}
 
-int router_splits(int H) { return (H + kSliceH - 1) / kSliceH; }
-
-__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x, int T, int H,
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x, int T, int H, int S,
                                                              const float* __restrict__ router_w, int E,
                                                              const float* __restrict__ shared_gate_w,
-                                                             float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kDecodeMaxT][kSliceH];
+                                                             float* __restrict__ part, uint8_t* __restrict__ xhi,
+                                                             uint8_t* __restrict__ xlo, uint8_t* __restrict__ xsc,
+                                                             int xsc_pitch) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kDecodeMaxT][256];
   const int rows = E + (shared_gate_w ? 1 : 0);
-  const int s = blockIdx.y, h0 = s * kSliceH;
+  const int s = blockIdx.y;
+  const int h0 = s * 256;
+  const int L = H - h0 < 0 ? 0 : (H - h0 > 256 ? 256 : H - h0);  // a multiple of 128
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
-  // Issue this wave's weight load first.
   float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
   const bool have_row = row < rows;
-  const int hl = h0 + lane * 4;
-  if (have_row && hl < H) {
+  if (have_row && lane * 4 < L) {
     const float* wrow = row < E ? router_w + static_cast<size_t>(row) * H : shared_gate_w;
-    wv = *reinterpret_cast<const float4*>(wrow + hl);
+    wv = *reinterpret_cast<const float4*>(wrow + h0 + lane * 4);
   }
-  // Stage the x slice of every token: T x 256 bf16, 16 bytes per thread.
-  for (int i = threadIdx.x; i < T * (kSliceH / 8); i += blockDim.x) {
-    const int t = i / (kSliceH / 8), c = (i % (kSliceH / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h0 + c < H) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h0 + c);
-    *reinterpret_cast<uint4*>(&xs[t][c]) = v;
+  // Stage the x slice of every token (T x L bf16) in 16-byte pieces.
+  for (int i = threadIdx.x; i < T * (L / 8); i += blockDim.x) {
+    const int t = i / (L / 8), c = (i % (L / 8)) * 8;
+    *reinterpret_cast<uint4*>(&xs[t][c]) = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h0 + c);
   }
   __syncthreads();
+  if (xhi && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < T * (L / 32); i += blockDim.x) {
+      const int t = i / (L / 32), blk = i % (L / 32);
+      uint4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4*>(&xs[t][blk * 32 + q * 8]);
+      const size_t o = static_cast<size_t>(t) * H + h0 + blk * 32;
+      mx_split_block(v, xhi + o, xlo + o, xsc + static_cast<size_t>(t) * xsc_pitch + (h0 / 32) + blk);
+    }
+  }
   if (!have_row) return;
   for (int t = 0; t < T; ++t) {
-    const uint2 xv = *reinterpret_cast<const uint2*>(&xs[t][lane * 4]);
-    float acc = bf16_to_f32(xv.x & 0xFFFF) * wv.x;
-    acc = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc);
-    acc = fmaf(bf16_to_f32(xv.y & 0xFFFF), wv.z, acc);
-    acc = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc);
+    float acc = 0.f;
+    if (lane * 4 < L) {
+      const uint2 xv = *reinterpret_cast<const uint2*>(&xs[t][lane * 4]);
+      acc = bf16_to_f32(xv.x & 0xFFFF) * wv.x;
+      acc = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc);
+      acc = fmaf(bf16_to_f32(xv.y & 0xFFFF), wv.z, acc);
+      acc = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc);
+    }
     const float v = wave_sum_fixed(acc);
-    if (lane == 0) part[(static_cast<size_t>(s) * T + t) * rows + row] = v;
+    if (lane == 0) part[(static_cast<size_t>(t) * rows + row) * S + s] = v;
   }
 }
 
 hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                 const float* shared_gate_w, float* part, hipStream_t s) {
+                                 const float* shared_gate_w, float* part, uint8_t* xhi, uint8_t* xlo, uint8_t* xsc,
+                                 int xsc_pitch, hipStream_t s) {
   const int rows = E + (shared_gate_w ? 1 : 0);
-  dim3 grid((rows + 3) / 4, router_splits(H));
-  router_partial_kernel<<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, part);
+  const int S = router_splits(H);
+  dim3 grid((rows + 3) / 4, S);
+  router_partial_kernel<<<grid, 256, 0, s>>>(x, T, H, S, router_w, E, shared_gate_w, part, xhi, xlo, xsc,
+                                             xsc_pitch);
   return hipGetLastError();
+}
+
+// Logit of (token t, row e): the S partials, added in slice order.
+template <int SQ>
+__device__ __forceinline__ float sum_partials(const float* part, size_t base) {
+  float4 v[SQ];
+  const float4* p = reinterpret_cast<const float4*>(part + base);
+#pragma unroll
+  for (int q = 0; q < SQ; ++q) v[q] = p[q];
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < SQ; ++q) acc = ((acc + v[q].x) + v[q].y + v[q].z) + v[q].w;
+  return acc;
 }
 
 // Fused decode top-k + align: one workgroup of 1024 threads.  Wave t < T sums
 // token t's partial logits (slices in order), adds the bias and runs k rounds
 // of wave argmax (DPP reductions); then the whole workgroup aligns the T*k
 // routed rows into blocks of kDecodeBM (stable counting sort in LDS).
-template <int SLOTS>
+template <int SLOTS, int SQ>
 __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
     const float* __restrict__ part, int S, int T, int E, int k, const float* __restrict__ bias, int has_shared,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ sgate, int32_t* counts, int32_t* offsets,
@@ -323,8 +355,7 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
       const int e = lane + i * kWave;
       float acc = -__builtin_inff();
       if (e < E) {
-        acc = 0.f;
-        for (int sl = 0; sl < S; ++sl) acc += part[(static_cast<size_t>(sl) * T + t) * rows + e];
+        acc = sum_partials<SQ>(part, (static_cast<size_t>(t) * rows + e) * S);
         if (bias) acc += bias[e];
       }
       v[i] = acc;
@@ -338,8 +369,7 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
       ids_s[t * k + lane] = sel_i;
     }
     if (has_shared && lane == 0) {
-      float g = 0.f;
-      for (int sl = 0; sl < S; ++sl) g += part[(static_cast<size_t>(sl) * T + t) * rows + E];
+      const float g = sum_partials<SQ>(part, (static_cast<size_t>(t) * rows + E) * S);
       sgate[t] = 1.0f / (1.0f + expf(-g));
     }
   }
@@ -365,10 +395,23 @@ hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int 
                                     int32_t* num_padded, int P, uint32_t* zero_words, int n_zero,
                                     hipStream_t s) {
   return with_slots(E, [&]<int SL>() {
-    topk_align_decode_kernel<SL><<<1, 1024, 0, s>>>(part, S, T, E, k, bias, has_shared ? 1 : 0, ids, w, sg, counts,
-                                                    offsets, sorted_ids, block_expert, num_padded, P, zero_words,
-                                                    n_zero);
-    return hipGetLastError();
+    auto go = [&]<int SQ>() {
+      topk_align_decode_kernel<SL, SQ><<<1, 1024, 0, s>>>(part, S, T, E, k, bias, has_shared ? 1 : 0, ids, w, sg,
+                                                          counts, offsets, sorted_ids, block_expert, num_padded, P,
+                                                          zero_words, n_zero);
+      return hipGetLastError();
+    };
+    switch (S / 4) {
+      case 1: return go.template operator()<1>();
+      case 2: return go.template operator()<2>();
+      case 3: return go.template operator()<3>();
+      case 4: return go.template operator()<4>();
+      case 5: return go.template operator()<5>();
+      case 6: return go.template operator()<6>();
+      case 7: return go.template operator()<7>();
+      case 8: return go.template operator()<8>();
+      default: return hipErrorInvalidValue;
+    }
   });
 }
 

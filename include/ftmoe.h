@@ -113,8 +113,8 @@ typedef struct {
  *               and shared_gate_w [H] fp32: the shared expert's output is
  *               scaled by sigmoid(x . shared_gate_w) and added after the
  *               routed combine.
- * Limits: hidden and inter multiples of 128; 1 <= top_k <= 16;
- * top_k <= num_experts <= 1024.                                            */
+ * Limits: hidden, inter and shared_inter multiples of 128 and at most 4096;
+ * 1 <= top_k <= 16; top_k <= num_experts <= 1024.                          */
 typedef struct {
   int32_t hidden;
   int32_t inter;
