@@ -63,6 +63,10 @@ def main() -> int:
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="decode: oracle steps run until this much time")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a known-size kernel for "
+                         "scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -89,6 +93,14 @@ def main() -> int:
     ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
     w = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Routing of every batch (for the byte count of the selected experts).
     sel_bytes = []
@@ -168,34 +180,79 @@ def main() -> int:
         "kernel_avg_us": {k2: round(v, 3) for k2, v in sorted(kernel_us.items())},
     }
 
+    traffic = measured_traffic(roof["kernel"], args.workload)
+    if traffic is not None:
+        roof["traffic"] = traffic
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(lay, xs_host[0], kind, T, args.cpu_sample_tokens, sel_bytes[0])
+        out["cpu_baseline"] = cpu_baseline(lay, xs_host, kind, T, args.cpu_sample_tokens, sel_bytes,
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def cpu_baseline(lay, x, kind, T, sample_tokens, bytes0):
+PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64}
+
+
+def cpu_baseline(lay, xs, kind, T, sample_tokens, sel_bytes, seconds):
     """The oracle (float64 NumPy, as it stands) on a bounded sample of the
     same workload, timed on this host's cores."""
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     if kind == "decode":
+        # whole decode steps over the same token batches, until `seconds` have passed
+        done, nbytes = 0, 0.0
         t0 = time.perf_counter()
-        oracle.forward(lay, x)
-        dt = time.perf_counter() - t0
-        return {"value": round(bytes0 / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                "sample": f"one full decode step (T={T}) of the same layer, per-token oracle loop",
-                "seconds": round(dt, 2)}
-    n = sample_tokens or 16
+        while True:
+            b = done % len(xs)
+            oracle.forward(lay, xs[b])
+            nbytes += sel_bytes[b]
+            done += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds or done >= 256:
+                break
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{done} full decode steps (T={T}) of the same layer and token batches, per-token "
+                          f"oracle loop", "seconds": round(dt, 2)}
+    n = sample_tokens or PREFILL_SAMPLE.get(lay.cfg.name, 32)
     tok = np.arange(n)
     s_h = None
-    t0 = time.perf_counter()
     if lay.cfg.act == "fp8":
         s_h = 1.0  # the sample measures the per-token arithmetic; the h scale only sets magnitudes
-    oracle.forward_tokens(lay, x, tok, s_h=s_h)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(lay, xs[0], tok, s_h=s_h)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of the {T} tokens through the per-token oracle loop", "seconds": round(dt, 2)}
+            "sample": f"{n} of the {T} tokens through the per-token oracle loop (experts dequantised once "
+                      f"each, included)", "seconds": round(dt, 2)}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a known-size copy), or None when
+    there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m_b or not m_h:
+        return None
+    return int(m_b.group(1)) if m_h.group(1) == kernel_source_sha() else None
+
+
+def kernel_source_sha():
+    """Hash of the HIP sources the expert kernels are built from."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_scaled_fp4_router_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(root)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(root, name), "rb").read())
+    return h.hexdigest()
 
 
 if __name__ == "__main__":
