@@ -178,7 +178,7 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   const bool shared = L->shared_inter > 0;
   p.decode = L->path == FTMOE_PATH_DECODE || (L->path == FTMOE_PATH_AUTO && T <= kDecodeAutoMaxT);
   p.small_route = T <= kDecodeMaxT;
-  p.BM = p.decode ? kDecodeBM : kPrefillBM;
+  p.BM = p.decode ? kDecodeBM : gemm_block_m(T, k, E);
   p.P = max_padded(T, k, E, p.BM);
   p.nblocks = p.P / p.BM;
   p.nb_shared = shared ? (T + p.BM - 1) / p.BM : 0;
@@ -397,15 +397,21 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   Rows rr;
   rr.sorted_ids = sorted;
   rr.block_expert = bexp;
+  rr.counts = at<int32_t>(ws, p.counts);
+  rr.offsets = at<int32_t>(ws, p.offsets);
   rr.n_flat = T * k;
   rr.top_k = k;
   rr.num_blocks = p.nblocks;
+  rr.block_m = p.BM;
   Rows rs;
   rs.sorted_ids = nullptr;
   rs.block_expert = nullptr;
+  rs.counts = nullptr;
+  rs.offsets = nullptr;
   rs.n_flat = T;
   rs.top_k = 1;
   rs.num_blocks = p.nb_shared;
+  rs.block_m = p.BM;
   uint16_t* o = at<uint16_t>(ws, p.o);
   uint16_t* sh = shared ? at<uint16_t>(ws, p.s) : nullptr;
   FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ahs, s); }),

@@ -21,9 +21,12 @@ struct QW {
 struct Rows {
   const int32_t* sorted_ids;   // [P] flat row ids t*k+j, sentinel = n_flat; NULL = identity
   const int32_t* block_expert; // [P/BM]
+  const int32_t* counts;       // [E] rows per expert (routed) or NULL
+  const int32_t* offsets;      // [E+1] padded segment starts (routed) or NULL
   int32_t n_flat;              // T*k (routed) or T (identity)
   int32_t top_k;               // flat id -> token divisor (1 for identity)
-  int32_t num_blocks;          // grid extent in blocks of BM rows
+  int32_t num_blocks;          // grid extent in blocks of block_m rows
+  int32_t block_m;             // rows per block: 64 or 128
 };
 
 // ---- router ----
@@ -108,7 +111,8 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill experts (grouped GEMMs on MFMA) ----
-constexpr int kPrefillBM = 64;
+// Rows per block of the prefill GEMMs for a layer routing T*k rows over E experts.
+int gemm_block_m(int T, int k, int E);
 // amax_slots: FP8 activations only, the kAmaxSlots partial maxima of |h|.
 hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
                               const uint32_t* amax_x, int H, int inter, uint16_t* h,
