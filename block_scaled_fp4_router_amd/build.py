@@ -47,6 +47,16 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_resolved(lib: str) -> None:
+    """A kernel whose host stub the compiler dropped shows up as an undefined
+    ftmoe symbol: refuse such a library instead of failing at load time."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-u", "-C", lib], capture_output=True, text=True)
+    bad = [ln.strip() for ln in r.stdout.splitlines() if "ftmoe::" in ln]
+    if bad:
+        raise RuntimeError("libftmoe.so has unresolved ftmoe symbols:\n" + "\n".join(bad[:20]))
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -58,6 +68,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_resolved(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")

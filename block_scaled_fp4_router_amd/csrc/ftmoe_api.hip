@@ -167,7 +167,7 @@ struct Plan {
   int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0;
   size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
          scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
-         hsc = 0, total = 0;
+         hsc = 0, hq = 0, total = 0;
   int hsc_pitch = 0;
   bool mx_split = false;  // MXFP4: activations travel as split E4M3 pairs
 };
@@ -178,7 +178,7 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   const bool shared = L->shared_inter > 0;
   p.decode = L->path == FTMOE_PATH_DECODE || (L->path == FTMOE_PATH_AUTO && T <= kDecodeAutoMaxT);
   p.small_route = T <= kDecodeMaxT;
-  p.BM = p.decode ? kDecodeBM : gemm_block_m(T, k, E);
+  p.BM = p.decode ? kDecodeBM : gemm_block_m(T, k, E, L->gate_up.fmt);
   p.P = max_padded(T, k, E, p.BM);
   p.nblocks = p.P / p.BM;
   p.nb_shared = shared ? (T + p.BM - 1) / p.BM : 0;
@@ -226,6 +226,8 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   } else {
     p.h = take(static_cast<size_t>(p.P) * I * 2);
     if (shared) p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
+    // FP8 activations, prefill: h quantised once for the down GEMM
+    if (!p.decode && L->act == FTMOE_ACT_FP8_PER_TENSOR) p.hq = take(static_cast<size_t>(p.P) * I);
   }
   p.o = take(tk * H * obytes);
   if (shared) p.s = take(static_cast<size_t>(T) * H * obytes);
@@ -417,7 +419,15 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ahs, s); }),
          "gate_up GEMM launch");
   if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
-  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, ah, H, I, o, s); }), "down GEMM launch");
+  uint8_t* hq = nullptr;
+  if (fp8act) {
+    hq = at<uint8_t>(ws, p.hq);
+    FT_HIP(timed("quant_h", s,
+                 [&] { return launch_quant_fp8(h, static_cast<int64_t>(p.P) * I, ah, hq, nullptr, s); }),
+           "quantise launch");
+  }
+  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, hq, ah, H, I, o, s); }),
+         "down GEMM launch");
   if (shared) {
     FT_HIP(timed("gemm_shared_gateup", s,
                  [&] {
@@ -426,7 +436,9 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
                  }),
            "shared gate_up GEMM launch");
     FT_HIP(timed("gemm_shared_down", s,
-                 [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, H, L->shared_inter, sh, s); }),
+                 [&] {
+                   return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, nullptr, H, L->shared_inter, sh, s);
+                 }),
            "shared down GEMM launch");
   }
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),

@@ -8,21 +8,28 @@
 //            rows, so h = silu(gate) * up is formed in registers;
 //   down:    a wave's two column tiles are 64 consecutive output columns.
 //
-// K advances in stages of 64.  Activation rows (gathered through the sorted
-// row ids) are staged through LDS, double-buffered, with their 16-byte
-// vectors XOR-swizzled by row so that the 8 lanes of a ds_read_b128 phase hit
-// 8 different bank groups.  Weights never touch LDS: each wave loads its own
-// column tiles straight into registers one stage ahead and dequantises them
-// right before the MFMA (MXFP4 with the E8M0-scaled hardware convert, NVFP4
-// as E2M1 x E4M3, exact in bf16), feeding v_mfma_f32_32x32x16_bf16.  FP8
-// weights with FP8 activations feed v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-// scales and need no conversion at all; tensor and activation scales are
-// applied in the epilogue.
+// K advances in stages of 64.  Both operands of a stage -- the activation
+// rows, gathered through the sorted row ids, and the weight rows in their
+// packed format -- are copied HBM -> LDS by LDS DMA (global_load_lds_dwordx4)
+// into a ring of kRing stage buffers, kRing - 1 stages ahead of the MFMA work,
+// so the long latency of the gathered rows and of the weight stream is
+// covered by several stages of MFMA work.  The ring buffers are distinct LDS
+// objects, so the compiler's wait before a read covers only the DMA into that
+// buffer; each wave additionally waits for its own DMA of the stage before
+// the one barrier per stage.  16-byte vectors are XOR-swizzled by row so that
+// the 8 lanes of a ds_read_b128 phase hit 8 different bank groups.
+//
+// Weights are dequantised right before the MFMA: MXFP4 with the E8M0-scaled
+// hardware convert, NVFP4 as E2M1 x E4M3 (exact in bf16), into
+// v_mfma_f32_32x32x16_bf16.  FP8 weights with FP8 activations feed
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales; tensor and activation
+// scales are applied in the epilogue.  Block scales of FP4 weights travel
+// with their stage too (one dword per weight row and stage).
 //
 // Within a stage, lane group g (lane / 32) of the bf16 MFMA takes K elements
 // [32g + 8t, 32g + 8t + 8) at MFMA step t: both operands use this assignment,
 // so a lane's weight bytes for the stage are one contiguous 16-byte run (one
-// FP4 block scale per MXFP4 lane, two for NVFP4).
+// E8M0 scale per MXFP4 lane, two E4M3 scales for NVFP4).
 //
 // Workgroups are numbered so that each XCD (workgroup w runs on XCD w % 8)
 // receives a contiguous range of (block, tile) pairs: the column tiles of a
@@ -35,18 +42,41 @@ namespace ftmoe {
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kStageK = 64;
+constexpr int kRing = 4;
 
-template <int BM>
-struct TileShape {
-  static constexpr int kWM = BM / 64;              // waves along rows
-  static constexpr int kWN = kGemmWaves / kWM;     // waves along columns
-  static constexpr int kBN = 64 * kWN;             // weight rows per workgroup
-};
+using lds_void = __attribute__((address_space(3))) void;
 
-int gemm_block_m(int T, int k, int E) {
-  // Small experts (few rows each) waste less padding with 64-row blocks.
+int gemm_block_m(int T, int k, int E, int wfmt) {
+  // Small experts (few rows each) waste less padding with 64-row blocks; FP8
+  // weight stages are twice as wide and always use 128-row blocks.
+  if (wfmt == kFP8) return 128;
   return static_cast<long long>(T) * k >= 192LL * E ? 128 : 64;
 }
+
+template <int WFMT, bool FP8ACT, int BM>
+struct Cfg {
+  static constexpr int kWM = BM / 64;                  // waves along rows
+  static constexpr int kWN = kGemmWaves / kWM;         // waves along columns
+  static constexpr int kBN = 64 * kWN;                 // weight rows per workgroup
+  static constexpr int kAV = FP8ACT ? 4 : 8;           // 16-byte vectors per activation row and stage
+  static constexpr int kARowB = 16 * kAV;
+  static constexpr int kBRowB = WFMT == kFP8 ? 64 : 32;  // weight bytes per row and stage
+  static constexpr int kBV = kBRowB / 16;
+  static constexpr int kABytes = BM * kARowB;
+  static constexpr int kBBytes = kBN * kBRowB;
+  static constexpr bool kScales = WFMT != kFP8;        // FP4: one scale dword per weight row and stage
+  static constexpr int kSBytes = kScales ? 4 * kBN : 0;
+  static constexpr int kSlotBytes = kABytes + kBBytes + kSBytes;
+  static constexpr int kAChunks = kABytes / 1024;     // 1 KB = one wave's 16-byte DMA instruction
+  static constexpr int kChunks = (kABytes + kBBytes) / 1024;
+  static constexpr int kChunksPerWave = kChunks / kGemmWaves;
+  static_assert(kChunks % kGemmWaves == 0, "every wave issues the same number of DMA instructions");
+  static constexpr int kScaleRowsPerWave = kBN / kGemmWaves;   // one 4-byte DMA instruction per wave
+  static_assert(kScaleRowsPerWave <= 64, "scale rows per wave");
+  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0);
+  static_assert(kVmPerStage * (kRing - 2) < 64, "vmcnt range");
+  static_assert(kRing * kSlotBytes <= 150 * 1024, "LDS");
+};
 
 // ------------------------------------------------------------ helpers -----
 __device__ __forceinline__ int logical_tile(int w, int total) {
@@ -54,14 +84,35 @@ __device__ __forceinline__ int logical_tile(int w, int total) {
   return (w & 7) * per + (w >> 3);
 }
 
-// Position of vector q in an LDS row of V 16-byte vectors (V = 8 or 4).
+// Position of vector q in an LDS row of V 16-byte vectors (V = 8, 4 or 2).
 template <int V>
 __device__ __forceinline__ int swz(int r, int q) {
   if constexpr (V == 8)
     return q ^ (r & 7);
-  else
+  else if constexpr (V == 4)
     return q ^ ((r >> 1) & 3);
+  else
+    return q ^ ((r >> 2) & 1);
 }
+
+// Waits until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS DMA of 16 (4) bytes per lane: lane l's bytes land at dst + 16 l (4 l);
+// dst is the same for every lane of the wave.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses
+// across it (no fence: outstanding DMA is waited for explicitly).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Valid rows of block b: routed blocks end where their expert's segment does.
 __device__ __forceinline__ int block_rows(const Rows& rows, int b, int e, int BM) {
@@ -78,42 +129,67 @@ __device__ __forceinline__ float amax_scale(const uint32_t* bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
-// ------------------------------------------------------- weight slices ----
-// One lane's part of one 32-row column tile for one stage.
-template <int WFMT, bool FP8ACT>
-struct BSlice {
-  uint4 c0, c1;   // FP4: c0 only (32 nibbles); FP8: 32 bytes
-  uint32_t sc;    // MXFP4: E8M0 byte; NVFP4: two E4M3 bytes
-};
-
-template <int WFMT, bool FP8ACT>
-__device__ __forceinline__ void load_bslice(BSlice<WFMT, FP8ACT>& s, const QW& w, size_t row, int K, int k0, int g) {
-  if constexpr (WFMT == kFP8) {
-    const uint8_t* p = w.codes + row * K + k0;
-    if constexpr (FP8ACT) {
-      // hardware 8-bit operand layout: bytes [16g, 16g+16) and [32+16g, ...)
-      s.c0 = load_nt(p + 16 * g);
-      s.c1 = load_nt(p + 32 + 16 * g);
-    } else {
-      s.c0 = load_nt(p + 32 * g);
-      s.c1 = load_nt(p + 32 * g + 16);
-    }
-    s.sc = 0;
-  } else {
-    s.c0 = load_nt(w.codes + row * (K / 2) + k0 / 2 + 16 * g);
-    if constexpr (WFMT == kMXFP4)
-      s.sc = w.scales[row * (K / 32) + k0 / 32 + g];
-    else
-      s.sc = *reinterpret_cast<const uint16_t*>(w.scales + row * (K / 16) + k0 / 16 + 2 * g);
-  }
+__device__ __forceinline__ i32x8 u4x2(const uint4& p, const uint4& q) {
+  return i32x8{static_cast<int>(p.x), static_cast<int>(p.y), static_cast<int>(p.z), static_cast<int>(p.w),
+               static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w)};
 }
 
-// bf16 operand of MFMA step t (elements [32g + 8t, +8) of the stage).
-template <int WFMT, bool FP8ACT>
-__device__ __forceinline__ bf16x8 bslice_bf16(const BSlice<WFMT, FP8ACT>& s, int t) {
+
+// ---- LDS fragment reads --------------------------------------------------
+// The ring buffers are written by LDS DMA, which the compiler can only order
+// against LDS reads by waiting for every DMA in flight (all later stages
+// included).  Fragment reads therefore go through these asm blocks, which
+// wait for their own results before returning; the stage's DMA has been
+// waited for explicitly before the barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// FP4 weights: 2 weight vectors, 8 activation vectors, 2 scale dwords.
+__device__ __forceinline__ void lds_read_fp4(const uint32_t (&ad)[12], u32x4 (&v)[10], uint32_t (&sc)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n ds_read_b128 %1, %13\n ds_read_b128 %2, %14\n ds_read_b128 %3, %15\n"
+      "ds_read_b128 %4, %16\n ds_read_b128 %5, %17\n ds_read_b128 %6, %18\n ds_read_b128 %7, %19\n"
+      "ds_read_b128 %8, %20\n ds_read_b128 %9, %21\n ds_read_b32 %10, %22\n ds_read_b32 %11, %23\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(sc[0]), "=&v"(sc[1])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "v"(ad[8]),
+        "v"(ad[9]), "v"(ad[10]), "v"(ad[11]));
+}
+
+// FP8 weights and activations: 4 weight vectors, 4 activation vectors.
+__device__ __forceinline__ void lds_read8(const uint32_t (&ad)[8], u32x4 (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+}
+
+// FP8 weights with bf16 activations: 4 weight vectors, 8 activation vectors.
+__device__ __forceinline__ void lds_read12(const uint32_t (&ad)[12], u32x4 (&v)[12]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n ds_read_b128 %1, %13\n ds_read_b128 %2, %14\n ds_read_b128 %3, %15\n"
+      "ds_read_b128 %4, %16\n ds_read_b128 %5, %17\n ds_read_b128 %6, %18\n ds_read_b128 %7, %19\n"
+      "ds_read_b128 %8, %20\n ds_read_b128 %9, %21\n ds_read_b128 %10, %22\n ds_read_b128 %11, %23\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "v"(ad[8]),
+        "v"(ad[9]), "v"(ad[10]), "v"(ad[11]));
+}
+
+__device__ __forceinline__ uint4 to_u4(const u32x4& v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// bf16 operand of MFMA step t from a lane's weight bytes of the stage:
+// FP4 c0 = 32 nibbles ([32g, 32g+32)), FP8 c0|c1 = 32 bytes.
+template <int WFMT>
+__device__ __forceinline__ bf16x8 weight_bf16(const uint4& c0, const uint4& c1, uint32_t sc, int t) {
   uint32_t o[4];
   if constexpr (WFMT == kFP8) {
-    const uint4 c = t < 2 ? s.c0 : s.c1;
+    const uint4 c = t < 2 ? c0 : c1;
     const uint32_t w0 = (t & 1) ? c.z : c.x, w1 = (t & 1) ? c.w : c.y;
     const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
     const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
@@ -124,194 +200,42 @@ __device__ __forceinline__ bf16x8 bslice_bf16(const BSlice<WFMT, FP8ACT>& s, int
     o[2] = pack_bf16x2(c2[0], c2[1]);
     o[3] = pack_bf16x2(d[0], d[1]);
   } else {
-    const uint32_t word = t == 0 ? s.c0.x : t == 1 ? s.c0.y : t == 2 ? s.c0.z : s.c0.w;
+    const uint32_t word = t == 0 ? c0.x : t == 1 ? c0.y : t == 2 ? c0.z : c0.w;
     if constexpr (WFMT == kMXFP4)
-      fp4x8_to_bf16(word, e8m0_as_scale(s.sc), o);
+      fp4x8_to_bf16(word, e8m0_as_scale(sc & 0xFF), o);
     else
-      fp4x8_to_bf16_mul(word, e4m3_to_f32((s.sc >> (t < 2 ? 0 : 8)) & 0xFF), o);
+      fp4x8_to_bf16_mul(word, e4m3_to_f32((sc >> (t < 2 ? 0 : 8)) & 0xFF), o);
   }
   return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-__device__ __forceinline__ i32x8 u4x2(const uint4& p, const uint4& q) {
-  return i32x8{static_cast<int>(p.x), static_cast<int>(p.y), static_cast<int>(p.z), static_cast<int>(p.w),
-               static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w)};
-}
-
-// ---------------------------------------------------- activation staging --
-// LDS stage: BM rows of one K stage, V vectors of 16 bytes per row (bf16: 8,
-// FP8: 4).  Thread tid stages vectors tid, tid + 512, ... of the row-major
-// sequence; a thread's rows are fixed for the whole K loop.
-template <int BM, bool FP8ROWS>
-struct AStage {
-  static constexpr int V = FP8ROWS ? 4 : 8;
-  static constexpr int kVecs = BM * V;
-  static constexpr int kPer = (kVecs + kGemmThreads - 1) / kGemmThreads;
-  static constexpr int kBytes = BM * V * 16;
+// ------------------------------------------------------------- kernel ----
+struct GemmArgs {
+  QW w;
+  Rows rows;
+  const uint8_t* a;          // activation rows: bf16 (x or h) or E4M3 (x_q or h_q)
+  int K;                     // reduction length (H for gate_up, I for down)
+  int N;                     // gate_up: I (gate columns); down: H (output columns)
+  int a_pitch;               // elements per activation row (H for gate_up, I for down)
+  const uint32_t* amax_a;    // FP8 activations: amax bits of the activation tensor
+  uint16_t* out;             // gate_up: h [rows][I]; down: o [flat][H]
+  uint32_t* amax_slots;      // gate_up with FP8 activations: partial maxima of |h|
 };
 
-// bf16 source rows (gate_up from x, down from h) or FP8 rows (gate_up from x_q).
-template <int BM, bool FP8ROWS, bool QUANT>
-struct ALoader {
-  using S = AStage<BM, FP8ROWS>;
-  const uint8_t* src[S::kPer];   // row start + this thread's vector (advances per stage)
-  int dst[S::kPer];              // LDS byte offset within a stage buffer (-1: none)
-  uint4 v[S::kPer][QUANT ? 2 : 1];
-
-  __device__ __forceinline__ void issue() {
-#pragma unroll
-    for (int j = 0; j < S::kPer; ++j) {
-      if (dst[j] < 0) continue;
-      const uint4* p = reinterpret_cast<const uint4*>(src[j]);
-      v[j][0] = p[0];
-      if constexpr (QUANT) v[j][1] = p[1];
-      src[j] += QUANT ? 2 * kStageK : (FP8ROWS ? kStageK : 2 * kStageK);
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* buf, float sh) const {
-#pragma unroll
-    for (int j = 0; j < S::kPer; ++j) {
-      if (dst[j] < 0) continue;
-      uint4 o = v[j][0];
-      if constexpr (QUANT) {
-        const uint32_t w[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w,
-                               v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
-        uint32_t q[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = f32x2_to_e4m3x2(bf16_to_f32(w[2 * i] & 0xFFFF) / sh, bf16_to_f32(w[2 * i] >> 16) / sh);
-          const uint32_t hi =
-              f32x2_to_e4m3x2(bf16_to_f32(w[2 * i + 1] & 0xFFFF) / sh, bf16_to_f32(w[2 * i + 1] >> 16) / sh);
-          q[i] = lo | (hi << 16);
-        }
-        o = make_uint4(q[0], q[1], q[2], q[3]);
-      }
-      *reinterpret_cast<uint4*>(buf + dst[j]) = o;
-    }
-  }
-};
-
-// Sets up the loader for rows whose start addresses row_ptr(r) gives (bytes
-// per element: 2 for bf16 sources, 1 for FP8 sources).
-template <int BM, bool FP8ROWS, bool QUANT, class RowPtr>
-__device__ __forceinline__ void aloader_init(ALoader<BM, FP8ROWS, QUANT>& L, RowPtr row_ptr) {
-  using S = AStage<BM, FP8ROWS>;
-#pragma unroll
-  for (int j = 0; j < S::kPer; ++j) {
-    const int i = threadIdx.x + j * kGemmThreads;
-    if (i >= S::kVecs) {
-      L.dst[j] = -1;
-      L.src[j] = nullptr;
-      continue;
-    }
-    const int r = i / S::V, q = i % S::V;
-    L.dst[j] = r * (S::V * 16) + 16 * swz<S::V>(r, q);
-    // source bytes of vector q of the stage: FP8 rows 16 per vector; bf16
-    // rows 16 per vector, or 32 when two bf16 vectors quantise into one
-    L.src[j] = static_cast<const uint8_t*>(row_ptr(r)) + q * (QUANT ? 32 : 16);
-  }
-}
-
-// ------------------------------------------------------------- compute ----
-// One stage of a wave's 64 x 64 tile: acc[m][c] over rows 32m.. of the wave,
-// column tile c.  rows_ok[m]: M-tile m holds at least one valid row.
-template <int WFMT, bool FP8ACT, int V>
-__device__ __forceinline__ void mma_stage(const uint8_t* As, int arow0, const BSlice<WFMT, FP8ACT> (&bs)[2],
-                                          const bool (&rows_ok)[2], f32x16 (&acc)[2][2], int lane) {
-  const int i = lane & 31, g = lane >> 5;
-  if constexpr (FP8ACT) {
-    const i32x8 b0 = u4x2(bs[0].c0, bs[0].c1), b1 = u4x2(bs[1].c0, bs[1].c1);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (!rows_ok[m]) continue;
-      const int r = arow0 + 32 * m + i;
-      const uint8_t* row = As + r * (V * 16);
-      const i32x8 a = u4x2(*reinterpret_cast<const uint4*>(row + 16 * swz<V>(r, g)),
-                           *reinterpret_cast<const uint4*>(row + 16 * swz<V>(r, 2 + g)));
-      acc[m][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[m][0], 0, 0, 0, 127, 0, 127);
-      acc[m][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[m][1], 0, 0, 0, 127, 0, 127);
-    }
-  } else {
-    // all A fragments of the stage first, so the LDS reads overlap
-    bf16x8 a[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = arow0 + 32 * m + i;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        a[m][t] = __builtin_bit_cast(bf16x8,
-                                     *reinterpret_cast<const uint4*>(As + r * (V * 16) + 16 * swz<V>(r, 4 * g + t)));
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 b0 = bslice_bf16(bs[0], t), b1 = bslice_bf16(bs[1], t);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (!rows_ok[m]) continue;
-        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m][t], b0, acc[m][0], 0, 0, 0);
-        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m][t], b1, acc[m][1], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// The K loop shared by both GEMMs: activations staged double-buffered in LDS,
-// weights one stage ahead in registers.
-template <int WFMT, bool FP8ACT, int BM, bool FP8ROWS, bool QUANT>
-__device__ __forceinline__ void k_loop(ALoader<BM, FP8ROWS, QUANT>& L, uint8_t* As0, uint8_t* As1, const QW& w,
-                                       const size_t (&wrow)[2], int K, int arow0, const bool (&rows_ok)[2],
-                                       float sh, f32x16 (&acc)[2][2], int lane) {
-  constexpr int V = AStage<BM, FP8ROWS>::V;
-  const int g = lane >> 5;
-  const int ns = K / kStageK;
-  BSlice<WFMT, FP8ACT> b0[2], b1[2];
-  L.issue();
-#pragma unroll
-  for (int c = 0; c < 2; ++c) load_bslice(b0[c], w, wrow[c], K, 0, g);
-  L.store(As0, sh);
-  if (ns > 1) {
-    L.issue();
-#pragma unroll
-    for (int c = 0; c < 2; ++c) load_bslice(b1[c], w, wrow[c], K, kStageK, g);
-  }
-  __syncthreads();
-  for (int s = 0; s < ns; s += 2) {
-    // stage s from As0 / b0
-    mma_stage<WFMT, FP8ACT, V>(As0, arow0, b0, rows_ok, acc, lane);
-    if (s + 1 < ns) L.store(As1, sh);
-    if (s + 2 < ns) {
-      L.issue();
-#pragma unroll
-      for (int c = 0; c < 2; ++c) load_bslice(b0[c], w, wrow[c], K, (s + 2) * kStageK, g);
-    }
-    __syncthreads();
-    if (s + 1 >= ns) break;
-    // stage s + 1 from As1 / b1
-    mma_stage<WFMT, FP8ACT, V>(As1, arow0, b1, rows_ok, acc, lane);
-    if (s + 2 < ns) L.store(As0, sh);
-    if (s + 3 < ns) {
-      L.issue();
-#pragma unroll
-      for (int c = 0; c < 2; ++c) load_bslice(b1[c], w, wrow[c], K, (s + 3) * kStageK, g);
-    }
-    __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------- gate_up ----
-template <int WFMT, bool FP8ACT, int BM>
-__global__ __launch_bounds__(kGemmThreads) void gemm_gateup_kernel(QW w, Rows rows, const uint16_t* __restrict__ x,
-                                                                   const uint8_t* __restrict__ xq,
-                                                                   const uint32_t* __restrict__ amax_x, int H, int I,
-                                                                   uint16_t* __restrict__ h,
-                                                                   uint32_t* __restrict__ amax_h) {
-  using TS = TileShape<BM>;
-  constexpr int kStageBytes = AStage<BM, FP8ACT>::kBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kStageBytes];
+template <int WFMT, bool FP8ACT, int BM, bool GATEUP>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
+  using C = Cfg<WFMT, FP8ACT, BM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[C::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[C::kSlotBytes];
+  __shared__ int flat_of[BM];
   __shared__ float red[kGemmWaves];
 
-  const int ntile = (I + TS::kBN / 2 - 1) / (TS::kBN / 2);
+  const Rows& rows = ga.rows;
+  const QW& w = ga.w;
+  const int K = ga.K, N = ga.N;
+  const int ntile = GATEUP ? (N + C::kBN / 2 - 1) / (C::kBN / 2) : (N + C::kBN - 1) / C::kBN;
   const int t = logical_tile(blockIdx.x, rows.num_blocks * ntile);
   if (t >= rows.num_blocks * ntile) return;
   const int b = t / ntile, nt = t % ntile;
@@ -319,151 +243,262 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_gateup_kernel(QW w, Rows ro
   if (e < 0) return;
   const int nvalid = block_rows(rows, b, e, BM);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int wm = wave % TS::kWM, wn = wave / TS::kWM;
+  const int wm = wave % C::kWM, wn = wave / C::kWM;
   const int arow0 = wm * 64;
-  const int n0 = nt * (TS::kBN / 2) + wn * 32;   // this wave's first gate column
-  const bool wact = n0 < I;                      // a last tile may reach past I
-  const bool rows_ok[2] = {wact && arow0 < nvalid, wact && arow0 + 32 < nvalid};
   const int j = lane & 31, g = lane >> 5;
-  const int nw0 = wact ? n0 : 0;                 // idle waves stream a valid row, unused
-  const size_t wrow[2] = {static_cast<size_t>(e) * (2 * I) + nw0 + j, static_cast<size_t>(e) * (2 * I) + I + nw0 + j};
+  const int ns = K / kStageK;
 
-  ALoader<BM, FP8ACT, false> L;
-  aloader_init(L, [&](int r) -> const void* {
-    const int p = b * BM + r;
-    int tok = 0;
-    if (rows.sorted_ids) {
-      const int f = rows.sorted_ids[p];
-      tok = f < rows.n_flat ? f / rows.top_k : 0;
+  // weight row (within the expert's matrix) of tile row R, or -1 past N
+  auto tile_col = [&](int R) -> int {
+    if constexpr (GATEUP) {
+      const int half = C::kBN / 2;
+      const int c = nt * half + (R < half ? R : R - half);
+      if (c >= N) return -1;
+      return R < half ? c : N + c;
     } else {
-      tok = p < rows.n_flat ? p : 0;
+      const int c = nt * C::kBN + R;
+      return c < N ? c : -1;
     }
-    if constexpr (FP8ACT)
-      return xq + static_cast<size_t>(tok) * H;
-    else
-      return x + static_cast<size_t>(tok) * H;
-  });
+  };
+  // this wave's two column tiles: first tile row of each
+  const int R0 = GATEUP ? 32 * wn : 64 * wn;
+  const int R1 = GATEUP ? C::kBN / 2 + 32 * wn : 64 * wn + 32;
+  const bool wact = tile_col(R0) >= 0;
+  const bool rows_ok[2] = {wact && arow0 < nvalid, wact && arow0 + 32 < nvalid};
 
-  f32x16 acc[2][2] = {};
-  k_loop<WFMT, FP8ACT, BM, FP8ACT, false>(L, As, As + kStageBytes, w, wrow, H, arow0, rows_ok, 1.0f, acc, lane);
-
-  float f = 1.0f;
-  if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-  if constexpr (FP8ACT) f *= amax_scale(amax_x);
-  float mx = 0.f;
+  // ---- DMA sources: chunks wave, wave + 8, ... of every stage (A first) ----
+  const size_t wrows = static_cast<size_t>(GATEUP ? 2 * N : N);
+  const size_t wrow_bytes = WFMT == kFP8 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
+  const uint8_t* src[C::kChunksPerWave];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (!wact || i >= nvalid) continue;
-      const float v = swiglu(acc[m][0][r] * f, acc[m][1][r] * f);
-      mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
-      h[static_cast<size_t>(b * BM + i) * I + n0 + j] = f32_to_bf16(v);
+  for (int i = 0; i < C::kChunksPerWave; ++i) {
+    const int c = wave + kGemmWaves * i;
+    if (c < C::kAChunks) {
+      const int v = c * 64 + lane;
+      const int r = v / C::kAV, q = swz<C::kAV>(r, v % C::kAV);
+      int row;
+      if (GATEUP && rows.sorted_ids) {
+        const int f = rows.sorted_ids[b * BM + r];
+        row = f < rows.n_flat ? f / rows.top_k : 0;
+      } else if (GATEUP) {
+        const int p = b * BM + r;
+        row = p < rows.n_flat ? p : 0;
+      } else {
+        row = b * BM + r;   // h rows of the block (padding rows hold unused values)
+      }
+      src[i] = ga.a + static_cast<size_t>(row) * ga.a_pitch * (FP8ACT ? 1 : 2) + 16 * q;
+    } else {
+      const int v = (c - C::kAChunks) * 64 + lane;
+      const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
+      const int col = tile_col(R);
+      src[i] = w.codes + (static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col)) * wrow_bytes + 16 * q;
     }
   }
-  if constexpr (FP8ACT) wg_amax_to_slots(mx, amax_h, red);
-}
-
-// ---------------------------------------------------------------- down ----
-template <int WFMT, bool FP8ACT, int BM>
-__global__ __launch_bounds__(kGemmThreads) void gemm_down_kernel(QW w, Rows rows, const uint16_t* __restrict__ h,
-                                                                 const uint32_t* __restrict__ amax_h, int H, int I,
-                                                                 uint16_t* __restrict__ o) {
-  using TS = TileShape<BM>;
-  constexpr int kStageBytes = AStage<BM, FP8ACT>::kBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kStageBytes];
-  __shared__ int flat_of[BM];
-
-  const int ntile = (H + TS::kBN - 1) / TS::kBN;
-  const int t = logical_tile(blockIdx.x, rows.num_blocks * ntile);
-  if (t >= rows.num_blocks * ntile) return;
-  const int b = t / ntile, nt = t % ntile;
-  const int e = rows.sorted_ids ? rows.block_expert[b] : 0;
-  if (e < 0) return;
-  const int nvalid = block_rows(rows, b, e, BM);
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int wm = wave % TS::kWM, wn = wave / TS::kWM;
-  const int arow0 = wm * 64;
-  const int n0 = nt * TS::kBN + wn * 64;
-  const bool wact = n0 < H;   // a last tile may reach past H
-  const bool rows_ok[2] = {wact && arow0 < nvalid, wact && arow0 + 32 < nvalid};
-  const int j = lane & 31, g = lane >> 5;
-  const int nw0 = wact ? n0 : 0;
-  const size_t wrow[2] = {static_cast<size_t>(e) * H + nw0 + j, static_cast<size_t>(e) * H + nw0 + 32 + j};
-  if (threadIdx.x < BM) {
+  // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
+  // dword of tile row w * kScaleRowsPerWave + l per stage (for MXFP4 it holds
+  // the scales of two stages, for NVFP4 those of one; the byte is picked at
+  // use).
+  const uint8_t* ssrc = nullptr;
+  if constexpr (C::kScales) {
+    const int R = wave * C::kScaleRowsPerWave + (lane < C::kScaleRowsPerWave ? lane : 0);
+    const int col = tile_col(R);
+    const size_t row = static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col);
+    ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
+  }
+  if (!GATEUP && threadIdx.x < BM) {
     const int p = b * BM + threadIdx.x;
     flat_of[threadIdx.x] = rows.sorted_ids ? rows.sorted_ids[p] : p;
   }
-  float sh = 1.0f;
-  if constexpr (FP8ACT) sh = amax_scale(amax_h);
 
-  ALoader<BM, FP8ACT, FP8ACT> L;
-  aloader_init(L, [&](int r) -> const void* { return h + static_cast<size_t>(b * BM + r) * I; });
+  // Issues the next stage into `buf`: the wave's DMA chunks, then its scale
+  // rows.  Every step issues exactly one stage, so the number of memory
+  // operations in flight per stage is a constant; past the last stage the
+  // sources stop advancing and the last stage is fetched again into a buffer
+  // nobody reads.
+  int next = 0;
+  auto issue = [&](uint8_t* buf) {
+    const int cur_stage = next;
+    const bool adv = ++next < ns;
+#pragma unroll
+    for (int i = 0; i < C::kChunksPerWave; ++i) {
+      const int c = wave + kGemmWaves * i;
+      dma16(src[i], buf + c * 1024);
+      src[i] += adv ? (c < C::kAChunks ? C::kARowB : C::kBRowB) : 0;
+    }
+    if constexpr (C::kScales) {
+      if (lane < C::kScaleRowsPerWave)
+        dma4(ssrc, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
+      // MXFP4: stages 2m and 2m + 1 share the dword at 4m
+      ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
+    }
+  };
 
-  f32x16 acc[2][2] = {};
-  k_loop<WFMT, FP8ACT, BM, FP8ACT, FP8ACT>(L, As, As + kStageBytes, w, wrow, I, arow0, rows_ok, sh, acc, lane);
-
-  float f = 1.0f;
-  if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-  if constexpr (FP8ACT) f *= sh;
+  // Per-lane fragment offsets within a ring buffer: weight vectors of the
+  // two column tiles, activation vectors, then (FP4) the two scale dwords.
+  constexpr int kBRead = WFMT == kFP8 ? 4 : 2;
+  constexpr int kARead = FP8ACT ? 4 : 8;
+  constexpr int kReads = kBRead + kARead + (C::kScales ? 2 : 0);
+  uint32_t roff[kReads];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int R = (ct ? R1 : R0) + j;
+    const uint32_t row = C::kABytes + R * C::kBRowB;
+    if constexpr (WFMT != kFP8) {
+      roff[ct] = row + 16 * swz<C::kBV>(R, g);
+      roff[kBRead + kARead + ct] = C::kABytes + C::kBBytes + 4 * R;
+    } else if constexpr (FP8ACT) {
+      roff[2 * ct] = row + 16 * swz<C::kBV>(R, g);
+      roff[2 * ct + 1] = row + 16 * swz<C::kBV>(R, 2 + g);
+    } else {
+      roff[2 * ct] = row + 16 * swz<C::kBV>(R, 2 * g);
+      roff[2 * ct + 1] = row + 16 * swz<C::kBV>(R, 2 * g + 1);
+    }
+  }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
+    const int r = arow0 + 32 * m + j;
+    const uint32_t row = r * C::kARowB;
+    if constexpr (FP8ACT) {
+      roff[kBRead + 2 * m] = row + 16 * swz<C::kAV>(r, g);
+      roff[kBRead + 2 * m + 1] = row + 16 * swz<C::kAV>(r, 2 + g);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (!wact || i >= nvalid) continue;
-      const size_t fr = static_cast<size_t>(flat_of[i]);
+      for (int tt = 0; tt < 4; ++tt) roff[kBRead + 4 * m + tt] = row + 16 * swz<C::kAV>(r, 4 * g + tt);
+    }
+  }
+
+  f32x16 acc[2][2] = {};
+  // One stage from ring buffer `cur`: wait for its DMA, barrier, read the
+  // fragments, refill the buffer the previous stage used, then the MFMA work.
+  auto step = [&](int s, uint8_t* cur, uint8_t* refill) {
+    wait_vm<C::kVmPerStage * (kRing - 2)>();
+    stage_barrier();
+    const uint32_t base = lds_addr(cur);
+    uint32_t ad[kReads];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) o[fr * H + n0 + 32 * c + j] = f32_to_bf16(acc[m][c][r] * f);
+    for (int i = 0; i < kReads; ++i) ad[i] = base + roff[i];
+    u32x4 fr[kBRead + kARead];
+    uint32_t scw[2] = {0, 0};
+    if constexpr (C::kScales)
+      lds_read_fp4(ad, fr, scw);
+    else if constexpr (FP8ACT)
+      lds_read8(ad, fr);
+    else
+      lds_read12(ad, fr);
+    issue(refill);
+    if (s >= ns) return;   // a stage past the end of K: nothing to multiply
+    if constexpr (FP8ACT) {
+      const i32x8 b0 = u4x2(to_u4(fr[0]), to_u4(fr[1])), b1 = u4x2(to_u4(fr[2]), to_u4(fr[3]));
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (!rows_ok[m]) continue;
+        const i32x8 a = u4x2(to_u4(fr[kBRead + 2 * m]), to_u4(fr[kBRead + 2 * m + 1]));
+        acc[m][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[m][0], 0, 0, 0, 127, 0, 127);
+        acc[m][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[m][1], 0, 0, 0, 127, 0, 127);
+      }
+    } else {
+      // this lane's scale byte(s): MXFP4 byte 2 (s & 1) + g, NVFP4 bytes 2g, 2g + 1
+      const int sh = WFMT == kMXFP4 ? 16 * (s & 1) + 8 * g : 16 * g;
+      const uint32_t sc0 = scw[0] >> sh, sc1 = scw[1] >> sh;
+      uint4 bw[2][2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if constexpr (WFMT == kFP8) {
+          bw[ct][0] = to_u4(fr[2 * ct]);
+          bw[ct][1] = to_u4(fr[2 * ct + 1]);
+        } else {
+          bw[ct][0] = bw[ct][1] = to_u4(fr[ct]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const bf16x8 b0 = weight_bf16<WFMT>(bw[0][0], bw[0][1], sc0, tt);
+        const bf16x8 b1 = weight_bf16<WFMT>(bw[1][0], bw[1][1], sc1, tt);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (!rows_ok[m]) continue;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, to_u4(fr[kBRead + 4 * m + tt]));
+          acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[m][1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // prologue: stages 0 .. kRing - 2 into buffers 0 .. kRing - 2
+  issue(lds0);
+  issue(lds1);
+  issue(lds2);
+  static_assert(kRing == 4, "the ring is unrolled by hand");
+  for (int s = 0; s < ns; s += kRing) {
+    step(s, lds0, lds3);
+    step(s + 1, lds1, lds0);
+    step(s + 2, lds2, lds1);
+    step(s + 3, lds3, lds2);
+  }
+  wait_vm<0>();   // no DMA into LDS may outlive the workgroup
+
+  // ---- epilogue ----
+  float f = 1.0f;
+  if constexpr (WFMT != kMXFP4) f = w.tscale[e];
+  if constexpr (FP8ACT) f *= amax_scale(ga.amax_a);
+  if constexpr (GATEUP) {
+    const int c0 = tile_col(R0 + j);   // gate column of this lane
+    float mx = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (!wact || i >= nvalid) continue;
+        const float v = swiglu(acc[m][0][r] * f, acc[m][1][r] * f);
+        mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+        ga.out[static_cast<size_t>(b * BM + i) * N + c0] = f32_to_bf16(v);
+      }
+    }
+    if constexpr (FP8ACT) wg_amax_to_slots(mx, ga.amax_slots, red);
+  } else {
+    __syncthreads();   // flat_of
+    const int c0 = nt * C::kBN + R0 + j;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (!wact || i >= nvalid) continue;
+        const size_t fr = static_cast<size_t>(flat_of[i]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) ga.out[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------ launches ----
-template <int WFMT, bool FP8ACT, int BM>
-static hipError_t run_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
-                             const uint32_t* amax_x, int H, int I, uint16_t* h, uint32_t* amax_h, hipStream_t s) {
-  const int ntile = (I + TileShape<BM>::kBN / 2 - 1) / (TileShape<BM>::kBN / 2);
-  const int total = rows.num_blocks * ntile;
+template <int WFMT, bool FP8ACT, int BM, bool GATEUP>
+static hipError_t run(const GemmArgs& ga, hipStream_t s) {
+  using C = Cfg<WFMT, FP8ACT, BM>;
+  const int ntile = GATEUP ? (ga.N + C::kBN / 2 - 1) / (C::kBN / 2) : (ga.N + C::kBN - 1) / C::kBN;
+  const int total = ga.rows.num_blocks * ntile;
   if (total == 0) return hipSuccess;
-  gemm_gateup_kernel<WFMT, FP8ACT, BM>
-      <<<8 * ((total + 7) / 8), kGemmThreads, 0, s>>>(w, rows, x, xq, amax_x, H, I, h, amax_h);
+  if (ga.K % kStageK) return hipErrorInvalidValue;
+  gemm_kernel<WFMT, FP8ACT, BM, GATEUP><<<8 * ((total + 7) / 8), kGemmThreads, 0, s>>>(ga);
   return hipGetLastError();
 }
 
-template <int WFMT, bool FP8ACT, int BM>
-static hipError_t run_down(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h, int H, int I,
-                           uint16_t* o, hipStream_t s) {
-  const int ntile = (H + TileShape<BM>::kBN - 1) / TileShape<BM>::kBN;
-  const int total = rows.num_blocks * ntile;
-  if (total == 0) return hipSuccess;
-  gemm_down_kernel<WFMT, FP8ACT, BM><<<8 * ((total + 7) / 8), kGemmThreads, 0, s>>>(w, rows, h, amax_h, H, I, o);
-  return hipGetLastError();
-}
-
-template <int BM>
-static hipError_t gateup_bm(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
-                            const uint32_t* amax_x, int H, int inter, uint16_t* h, uint32_t* amax_h, hipStream_t s) {
-  switch (w.fmt) {
-    case kMXFP4: return run_gateup<kMXFP4, false, BM>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s);
-    case kNVFP4: return run_gateup<kNVFP4, false, BM>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s);
+template <bool GATEUP>
+static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
+  const int bm = ga.rows.block_m;
+  switch (ga.w.fmt) {
+    case kMXFP4:
+      if (fp8act) return hipErrorInvalidValue;
+      return bm == 128 ? run<kMXFP4, false, 128, GATEUP>(ga, s) : run<kMXFP4, false, 64, GATEUP>(ga, s);
+    case kNVFP4:
+      if (fp8act) return hipErrorInvalidValue;
+      return bm == 128 ? run<kNVFP4, false, 128, GATEUP>(ga, s) : run<kNVFP4, false, 64, GATEUP>(ga, s);
     case kFP8:
-      return xq ? run_gateup<kFP8, true, BM>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s)
-                : run_gateup<kFP8, false, BM>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int BM>
-static hipError_t down_bm(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h, int H, int inter,
-                          uint16_t* o, hipStream_t s) {
-  switch (w.fmt) {
-    case kMXFP4: return run_down<kMXFP4, false, BM>(w, rows, h, amax_h, H, inter, o, s);
-    case kNVFP4: return run_down<kNVFP4, false, BM>(w, rows, h, amax_h, H, inter, o, s);
-    case kFP8:
-      return amax_h ? run_down<kFP8, true, BM>(w, rows, h, amax_h, H, inter, o, s)
-                    : run_down<kFP8, false, BM>(w, rows, h, amax_h, H, inter, o, s);
+      if (bm != 128) return hipErrorInvalidValue;
+      return fp8act ? run<kFP8, true, 128, GATEUP>(ga, s) : run<kFP8, false, 128, GATEUP>(ga, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -471,16 +506,31 @@ static hipError_t down_bm(const QW& w, const Rows& rows, const uint16_t* h, cons
 hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
                               const uint32_t* amax_x, int H, int inter, uint16_t* h, uint32_t* amax_h,
                               hipStream_t s) {
-  if (rows.block_m == 128) return gateup_bm<128>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s);
-  if (rows.block_m == 64) return gateup_bm<64>(w, rows, x, xq, amax_x, H, inter, h, amax_h, s);
-  return hipErrorInvalidValue;
+  GemmArgs ga{};
+  ga.w = w;
+  ga.rows = rows;
+  ga.a = xq ? xq : reinterpret_cast<const uint8_t*>(x);
+  ga.K = H;
+  ga.N = inter;
+  ga.a_pitch = H;
+  ga.amax_a = amax_x;
+  ga.out = h;
+  ga.amax_slots = amax_h;
+  return dispatch<true>(ga, xq != nullptr, s);
 }
 
-hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h, int H,
-                            int inter, uint16_t* o, hipStream_t s) {
-  if (rows.block_m == 128) return down_bm<128>(w, rows, h, amax_h, H, inter, o, s);
-  if (rows.block_m == 64) return down_bm<64>(w, rows, h, amax_h, H, inter, o, s);
-  return hipErrorInvalidValue;
+hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint8_t* hq,
+                            const uint32_t* amax_h, int H, int inter, uint16_t* o, hipStream_t s) {
+  GemmArgs ga{};
+  ga.w = w;
+  ga.rows = rows;
+  ga.a = hq ? hq : reinterpret_cast<const uint8_t*>(h);
+  ga.K = inter;
+  ga.N = H;
+  ga.a_pitch = inter;
+  ga.amax_a = amax_h;
+  ga.out = o;
+  return dispatch<false>(ga, hq != nullptr, s);
 }
 
 }  // namespace ftmoe

@@ -112,13 +112,14 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill experts (grouped GEMMs on MFMA) ----
 // Rows per block of the prefill GEMMs for a layer routing T*k rows over E experts.
-int gemm_block_m(int T, int k, int E);
+int gemm_block_m(int T, int k, int E, int wfmt);
 // amax_slots: FP8 activations only, the kAmaxSlots partial maxima of |h|.
 hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
                               const uint32_t* amax_x, int H, int inter, uint16_t* h,
                               uint32_t* amax_slots, hipStream_t s);
-hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint32_t* amax_h,
-                            int H, int inter, uint16_t* o, hipStream_t s);
+// FP8 activations: hq is h quantised per tensor with the scale of amax_h.
+hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint8_t* hq,
+                            const uint32_t* amax_h, int H, int inter, uint16_t* o, hipStream_t s);
 
 // ---- combine ----
 // y[t] = sum_j w[t,j] o[t*k+j] (+ sg[t] * sh[t]) -> bf16.
