@@ -85,14 +85,18 @@ __device__ __forceinline__ int logical_tile(int w, int total) {
 }
 
 // Position of vector q in an LDS row of V 16-byte vectors (V = 8, 4 or 2).
+// A fragment read takes one vector from each of 32 consecutive rows; the XOR
+// pattern puts every 8 and every 16 consecutive rows of it on distinct
+// 16-byte bank groups, so the read is conflict-free whether the LDS serves 8
+// or 16 lanes of a 128-bit read per cycle.
 template <int V>
 __device__ __forceinline__ int swz(int r, int q) {
   if constexpr (V == 8)
-    return q ^ (r & 7);
+    return q ^ ((r & 7) ^ ((r >> 3) & 1));
   else if constexpr (V == 4)
-    return q ^ ((r >> 1) & 3);
+    return q ^ (((r >> 1) ^ (r >> 3)) & 3);
   else
-    return q ^ ((r >> 2) & 1);
+    return q ^ (((r >> 2) ^ (r >> 3)) & 1);
 }
 
 // Waits until at most N vector memory operations of this wave are in flight.
