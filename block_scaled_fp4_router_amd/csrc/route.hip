@@ -48,72 +48,97 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- GEMM ----
-// Many tokens: 64 tokens x 64 router rows per workgroup, fp32 FMA, operands
-// staged through LDS in K slices of 32.  Each thread owns a 4x4 micro-tile.
-constexpr int kRT = 64, kRE = 64, kRK = 32;
+// Many tokens: bf16 MFMA with the fp32 router weights split exactly into
+// three bf16 terms, w = w1 + w2 + w3 (w1 = bf16(w), w2 = bf16(w - w1),
+// w3 = w - w1 - w2, which fits bf16 because each rounding leaves at most 8
+// significant bits fewer).  Each product x * w_i of a bf16 x is exact in
+// fp32 and the MFMA accumulates in fp32, so the logits keep fp32 accuracy.
+// Workgroup: 64 tokens x 64 router rows, 4 waves of one 32 x 32 tile each;
+// K stages of 64 staged through LDS (rows of 128 bytes, XOR-swizzled).
+constexpr int kRT = 64, kRE = 64, kRK = 64;
+
+__device__ __forceinline__ int rswz(int r, int q) { return q ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+__device__ __forceinline__ void split3(float w, uint16_t& a, uint16_t& b, uint16_t& c) {
+  a = f32_to_bf16(w);
+  const float r1 = w - bf16_to_f32(a);
+  b = f32_to_bf16(r1);
+  c = f32_to_bf16(r1 - bf16_to_f32(b));
+}
 
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ router_w, int E,
                                                           const float* __restrict__ shared_gate_w,
                                                           float* __restrict__ logits) {
-  __shared__ float xs[kRK][kRT + 4];
-  __shared__ float wsh[kRK][kRE + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
   const int rows = E + (shared_gate_w ? 1 : 0);
   const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;  // tx -> experts, ty -> tokens
-  float acc[4][4] = {};
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
+  const int j = lane & 31, g = lane >> 5;
+
+  // staging: thread tid owns row tid / 4, vectors 2 (tid % 4) and + 1 of the
+  // 128-byte stage row (x: 16 bf16 per thread; W: 16 fp32 -> 3 x 16 bf16)
+  const int sr = tid >> 2, sq = (tid & 3) * 2;
+  const int t = t0 + sr, e = e0 + sr;
+  const uint16_t* xrow = t < T ? x + static_cast<size_t>(t) * H : nullptr;
+  const float* wrow = e < E ? router_w + static_cast<size_t>(e) * H : (e == E ? shared_gate_w : nullptr);
+
+  f32x16 acc = {};
   for (int k0 = 0; k0 < H; k0 += kRK) {
-    // x tile: 64 tokens x 32 k = 2048 bf16; each thread 8 consecutive k.
-    {
-      const int r = tid >> 2, c = (tid & 3) * 8;
-      const int t = t0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < T) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + k0 + c);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    uint4 xv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (xrow) {
+      xv[0] = *reinterpret_cast<const uint4*>(xrow + k0 + sq * 8);
+      xv[1] = *reinterpret_cast<const uint4*>(xrow + k0 + sq * 8 + 8);
+    }
+    float wv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (wrow) f = *reinterpret_cast<const float4*>(wrow + k0 + sq * 8 + 4 * i);
+      wv[4 * i] = f.x;
+      wv[4 * i + 1] = f.y;
+      wv[4 * i + 2] = f.z;
+      wv[4 * i + 3] = f.w;
+    }
+    __syncthreads();   // the previous stage's reads are done
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int off = sr * 128 + 16 * rswz(sr, sq + h);
+      *reinterpret_cast<uint4*>(xs + off) = xv[h];
+      uint32_t p[3][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xs[c + 2 * i][r] = bf16_to_f32(w4[i] & 0xFFFF);
-        xs[c + 2 * i + 1][r] = bf16_to_f32(w4[i] >> 16);
+        uint16_t a0, b0, c0, a1, b1, c1;
+        split3(wv[8 * h + 2 * i], a0, b0, c0);
+        split3(wv[8 * h + 2 * i + 1], a1, b1, c1);
+        p[0][i] = a0 | (static_cast<uint32_t>(a1) << 16);
+        p[1][i] = b0 | (static_cast<uint32_t>(b1) << 16);
+        p[2][i] = c0 | (static_cast<uint32_t>(c1) << 16);
       }
-    }
-    // W tile: 64 rows x 32 k fp32; each thread 8 consecutive k.
-    {
-      const int r = tid >> 2, c = (tid & 3) * 8;
-      const int e = e0 + r;
-      float4 a = make_float4(0, 0, 0, 0), b = a;
-      if (e < rows) {
-        const float* wrow = e < E ? router_w + static_cast<size_t>(e) * H : shared_gate_w;
-        a = *reinterpret_cast<const float4*>(wrow + k0 + c);
-        b = *reinterpret_cast<const float4*>(wrow + k0 + c + 4);
-      }
-      wsh[c + 0][r] = a.x; wsh[c + 1][r] = a.y; wsh[c + 2][r] = a.z; wsh[c + 3][r] = a.w;
-      wsh[c + 4][r] = b.x; wsh[c + 5][r] = b.y; wsh[c + 6][r] = b.z; wsh[c + 7][r] = b.w;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) *reinterpret_cast<uint4*>(ws[m] + off) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kRK; ++kk) {
-      float xa[4], wb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = xs[kk][ty * 4 + i];
+    for (int ks = 0; ks < 4; ++ks) {
+      const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
+      const int ra = wt + j, rb = we + j;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + ra * 128 + 16 * rswz(ra, q)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wb[j] = wsh[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wb[j], acc[i][j]);
+      for (int m = 0; m < 3; ++m) {
+        const bf16x8 b =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ws[m] + rb * 128 + 16 * rswz(rb, q)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < rows) logits[static_cast<size_t>(t) * (E + 1) + e] = acc[i][j];
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int tt = t0 + wt + 8 * (r >> 2) + 4 * g + (r & 3);
+    const int ee = e0 + we + j;
+    if (tt < T && ee < rows) logits[static_cast<size_t>(tt) * (E + 1) + ee] = acc[r];
   }
 }
 
