@@ -73,30 +73,79 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<size_t>(c) * E + e] = cnt[e];
 }
 
+// Exclusive prefix of the per-chunk histograms over chunks, per expert, plus
+// the layout.  The 1024 threads are split into parts = 1024 / E groups of E
+// (one thread per expert and part); each part owns a contiguous range of
+// chunks, so the histogram is read with many loads in flight.
 __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, int P, int nchunks,
                                                           int32_t* __restrict__ hist, int32_t* counts,
                                                           int32_t* offsets, int32_t* sorted_ids,
                                                           int32_t* block_expert, int32_t* num_padded) {
   __shared__ int tmp[32];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      int32_t* h = hist + static_cast<size_t>(c) * E + e;
-      const int v = *h;
-      *h = run;  // rows of expert e in earlier chunks
-      run += v;
+  __shared__ int part_base[1024];
+  __shared__ int exp_off[kAlignMaxE];
+  const int tid = threadIdx.x;
+  const int parts = E < 1024 ? 1024 / E : 1;
+  const int e = tid % E, p = tid / E;
+  const bool worker = p < parts;
+  const int per = (nchunks + parts - 1) / parts;
+  const int c0 = min(nchunks, p * per), c1 = min(nchunks, c0 + per);
+  // 1. each part's sum
+  int sum = 0;
+  if (worker) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[static_cast<size_t>(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; c < c1; ++c) sum += hist[static_cast<size_t>(c) * E + e];
+    part_base[tid] = sum;
+  }
+  __syncthreads();
+  // 2. per expert: exclusive prefix over its parts, total
+  int total_e = 0;
+  if (tid < E) {
+    for (int q = 0; q < parts; ++q) {
+      const int v = part_base[q * E + tid];
+      part_base[q * E + tid] = total_e;
+      total_e += v;
     }
   }
+  __syncthreads();
+  // 3. layout (thread e = expert e)
   int off, total;
-  finish_layout(e, E, run, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off, &total);
-  if (e < E)
-    for (int c = 0; c < nchunks; ++c) hist[static_cast<size_t>(c) * E + e] += off;
+  finish_layout(tid, E, tid < E ? total_e : 0, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded,
+                tmp, &off, &total);
+  if (tid < E) exp_off[tid] = off;
+  __syncthreads();
+  // 4. every (chunk, expert) entry becomes the expert's first slot for that chunk
+  if (worker) {
+    int base = exp_off[e] + part_base[tid];
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[static_cast<size_t>(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hist[static_cast<size_t>(c + u) * E + e] = base;
+        base += v[u];
+      }
+    }
+    for (; c < c1; ++c) {
+      const int v = hist[static_cast<size_t>(c) * E + e];
+      hist[static_cast<size_t>(c) * E + e] = base;
+      base += v;
+    }
+  }
 }
 
 // One wave per chunk: rows are taken 64 at a time in index order; a row's
 // slot is its expert's running position plus the number of earlier lanes in
-// the same group with the same expert.
+// the group with the same expert (found with one ballot per id bit).
 __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                            const int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ sorted_ids) {
@@ -104,6 +153,9 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
   const int c = blockIdx.x;
   const int lane = lane_id();
   for (int e = lane; e < E; e += kWave) run[e] = hist[static_cast<size_t>(c) * E + e];
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (uint64_t{1} << lane) - 1, gt = ~lt & ~(uint64_t{1} << lane);
   __syncthreads();
   const int i0 = c * kAlignChunk, i1 = min(n, i0 + kAlignChunk);
   for (int g = i0; g < i1; g += kWave) {
@@ -111,21 +163,20 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
     int id = i < i1 ? ids[i] : -1;
     if (static_cast<unsigned>(id) >= static_cast<unsigned>(E)) id = -1;  // ignored, as in the count
     const bool valid = id >= 0;
-    int rank = 0, after = 0;
-#pragma unroll 8
-    for (int j = 0; j < kWave; ++j) {
-      const int vj = __shfl(id, j, kWave);
-      if (vj == id) {
-        rank += j < lane ? 1 : 0;
-        after += j > lane ? 1 : 0;
-      }
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (id >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
     }
+    const int rank = __popcll(peers & lt);
+    const bool last = (peers & gt) == 0;
     int pos = 0;
     if (valid) pos = run[id] + rank;
     __syncthreads();
     if (valid) {
       sorted_ids[pos] = i;
-      if (after == 0) run[id] = pos + 1;
+      if (last) run[id] = pos + 1;
     }
     __syncthreads();
   }
