@@ -42,7 +42,6 @@ namespace ftmoe {
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kStageK = 64;
-constexpr int kRing = 4;
 
 using lds_void = __attribute__((address_space(3))) void;
 
@@ -57,7 +56,8 @@ template <int WFMT, bool FP8ACT, int BM>
 struct Cfg {
   static constexpr int kWM = BM / 64;                  // waves along rows
   static constexpr int kWN = kGemmWaves / kWM;         // waves along columns
-  static constexpr int kBN = 64 * kWN;                 // weight rows per workgroup
+  static constexpr int kNT = BM == 128 ? 4 : 2;        // 32-column MFMA tiles per wave
+  static constexpr int kBN = 32 * kNT * kWN;           // weight rows per workgroup
   static constexpr int kAV = FP8ACT ? 4 : 8;           // 16-byte vectors per activation row and stage
   static constexpr int kARowB = 16 * kAV;
   static constexpr int kBRowB = WFMT == kFP8 ? 64 : 32;  // weight bytes per row and stage
@@ -67,6 +67,8 @@ struct Cfg {
   static constexpr bool kScales = WFMT != kFP8;        // FP4: one scale dword per weight row and stage
   static constexpr int kSBytes = kScales ? 4 * kBN : 0;
   static constexpr int kSlotBytes = kABytes + kBBytes + kSBytes;
+  static constexpr int kRing = kSlotBytes * 4 <= 150 * 1024 ? 4 : 3;   // stage buffers in LDS
+  static_assert(kRing * kSlotBytes <= 150 * 1024, "LDS");
   static constexpr int kAChunks = kABytes / 1024;     // 1 KB = one wave's 16-byte DMA instruction
   static constexpr int kChunks = (kABytes + kBBytes) / 1024;
   static constexpr int kChunksPerWave = kChunks / kGemmWaves;
@@ -75,7 +77,6 @@ struct Cfg {
   static_assert(kScaleRowsPerWave <= 64, "scale rows per wave");
   static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0);
   static_assert(kVmPerStage * (kRing - 2) < 64, "vmcnt range");
-  static_assert(kRing * kSlotBytes <= 150 * 1024, "LDS");
 };
 
 // ------------------------------------------------------------ helpers -----
@@ -149,40 +150,100 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
-// FP4 weights: 2 weight vectors, 8 activation vectors, 2 scale dwords.
-__device__ __forceinline__ void lds_read_fp4(const uint32_t (&ad)[12], u32x4 (&v)[10], uint32_t (&sc)[2]) {
+// FP4 weights, 4 column tiles: weight vectors, scale dwords, activation vectors.
+template <int OB1, int OB2, int OB3, int OS1, int OS2, int OS3, int OAM>
+__device__ __forceinline__ void frag_read_fp4_4(uint32_t vB, uint32_t vS, const uint32_t (&vA)[4], u32x4 (&b)[4],
+                                                uint32_t (&s)[4], u32x4 (&a)[8]) {
   asm volatile(
-      "ds_read_b128 %0, %12\n ds_read_b128 %1, %13\n ds_read_b128 %2, %14\n ds_read_b128 %3, %15\n"
-      "ds_read_b128 %4, %16\n ds_read_b128 %5, %17\n ds_read_b128 %6, %18\n ds_read_b128 %7, %19\n"
-      "ds_read_b128 %8, %20\n ds_read_b128 %9, %21\n ds_read_b32 %10, %22\n ds_read_b32 %11, %23\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-        "=&v"(v[8]), "=&v"(v[9]), "=&v"(sc[0]), "=&v"(sc[1])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "v"(ad[8]),
-        "v"(ad[9]), "v"(ad[10]), "v"(ad[11]));
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:%22\n"
+      "ds_read_b128 %2, %16 offset:%23\n"
+      "ds_read_b128 %3, %16 offset:%24\n"
+      "ds_read_b32 %4, %17\n"
+      "ds_read_b32 %5, %17 offset:%25\n"
+      "ds_read_b32 %6, %17 offset:%26\n"
+      "ds_read_b32 %7, %17 offset:%27\n"
+      "ds_read_b128 %8, %18\n"
+      "ds_read_b128 %9, %19\n"
+      "ds_read_b128 %10, %20\n"
+      "ds_read_b128 %11, %21\n"
+      "ds_read_b128 %12, %18 offset:%28\n"
+      "ds_read_b128 %13, %19 offset:%28\n"
+      "ds_read_b128 %14, %20 offset:%28\n"
+      "ds_read_b128 %15, %21 offset:%28\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB), "v"(vS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OB2), "n"(OB3), "n"(OS1), "n"(OS2), "n"(OS3), "n"(OAM));
 }
 
-// FP8 weights and activations: 4 weight vectors, 4 activation vectors.
-__device__ __forceinline__ void lds_read8(const uint32_t (&ad)[8], u32x4 (&v)[8]) {
+// FP4 weights, 2 column tiles.
+template <int OB1, int OS1, int OAM>
+__device__ __forceinline__ void frag_read_fp4_2(uint32_t vB, uint32_t vS, const uint32_t (&vA)[4], u32x4 (&b)[2],
+                                                uint32_t (&s)[2], u32x4 (&a)[8]) {
   asm volatile(
-      "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"
-      "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %12 offset:%18\n"
+      "ds_read_b32 %2, %13\n"
+      "ds_read_b32 %3, %13 offset:%19\n"
+      "ds_read_b128 %4, %14\n"
+      "ds_read_b128 %5, %15\n"
+      "ds_read_b128 %6, %16\n"
+      "ds_read_b128 %7, %17\n"
+      "ds_read_b128 %8, %14 offset:%20\n"
+      "ds_read_b128 %9, %15 offset:%20\n"
+      "ds_read_b128 %10, %16 offset:%20\n"
+      "ds_read_b128 %11, %17 offset:%20\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB), "v"(vS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OS1), "n"(OAM));
 }
 
-// FP8 weights with bf16 activations: 4 weight vectors, 8 activation vectors.
-__device__ __forceinline__ void lds_read12(const uint32_t (&ad)[12], u32x4 (&v)[12]) {
+// FP8 weights and activations, 4 column tiles: two vectors per operand row.
+template <int OB1, int OB2, int OB3, int OAM>
+__device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
+                                                u32x4 (&a)[4]) {
   asm volatile(
-      "ds_read_b128 %0, %12\n ds_read_b128 %1, %13\n ds_read_b128 %2, %14\n ds_read_b128 %3, %15\n"
-      "ds_read_b128 %4, %16\n ds_read_b128 %5, %17\n ds_read_b128 %6, %18\n ds_read_b128 %7, %19\n"
-      "ds_read_b128 %8, %20\n ds_read_b128 %9, %21\n ds_read_b128 %10, %22\n ds_read_b128 %11, %23\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "v"(ad[8]),
-        "v"(ad[9]), "v"(ad[10]), "v"(ad[11]));
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %13\n"
+      "ds_read_b128 %2, %12 offset:%16\n"
+      "ds_read_b128 %3, %13 offset:%16\n"
+      "ds_read_b128 %4, %12 offset:%17\n"
+      "ds_read_b128 %5, %13 offset:%17\n"
+      "ds_read_b128 %6, %12 offset:%18\n"
+      "ds_read_b128 %7, %13 offset:%18\n"
+      "ds_read_b128 %8, %14\n"
+      "ds_read_b128 %9, %15\n"
+      "ds_read_b128 %10, %14 offset:%19\n"
+      "ds_read_b128 %11, %15 offset:%19\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(vB0), "v"(vB1), "v"(vA0), "v"(vA1), "n"(OB1), "n"(OB2), "n"(OB3), "n"(OAM));
+}
+
+// FP8 weights with bf16 activations, 4 column tiles.
+template <int OB1, int OB2, int OB3, int OAM>
+__device__ __forceinline__ void frag_read_fp8_bf16_4(uint32_t vB0, uint32_t vB1, const uint32_t (&vA)[4], u32x4 (&b)[8],
+                                                     u32x4 (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %17\n"
+      "ds_read_b128 %2, %16 offset:%22\n"
+      "ds_read_b128 %3, %17 offset:%22\n"
+      "ds_read_b128 %4, %16 offset:%23\n"
+      "ds_read_b128 %5, %17 offset:%23\n"
+      "ds_read_b128 %6, %16 offset:%24\n"
+      "ds_read_b128 %7, %17 offset:%24\n"
+      "ds_read_b128 %8, %18\n"
+      "ds_read_b128 %9, %19\n"
+      "ds_read_b128 %10, %20\n"
+      "ds_read_b128 %11, %21\n"
+      "ds_read_b128 %12, %18 offset:%25\n"
+      "ds_read_b128 %13, %19 offset:%25\n"
+      "ds_read_b128 %14, %20 offset:%25\n"
+      "ds_read_b128 %15, %21 offset:%25\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB0), "v"(vB1), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OB2), "n"(OB3), "n"(OAM));
 }
 
 __device__ __forceinline__ uint4 to_u4(const u32x4& v) { return make_uint4(v.x, v.y, v.z, v.w); }
@@ -229,10 +290,8 @@ struct GemmArgs {
 template <int WFMT, bool FP8ACT, int BM, bool GATEUP>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   using C = Cfg<WFMT, FP8ACT, BM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[C::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[C::kSlotBytes];
+  constexpr int NT = C::kNT;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[C::kRing * C::kSlotBytes];
   __shared__ int flat_of[BM];
   __shared__ float red[kGemmWaves];
 
@@ -264,16 +323,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       return c < N ? c : -1;
     }
   };
-  // this wave's two column tiles: first tile row of each
-  const int R0 = GATEUP ? 32 * wn : 64 * wn;
-  const int R1 = GATEUP ? C::kBN / 2 + 32 * wn : 64 * wn + 32;
-  const bool wact = tile_col(R0) >= 0;
+  // first tile row of each of this wave's column tiles: gate_up pairs gate
+  // tile u with up tile u + NT/2; down takes NT consecutive tiles
+  int Rt[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    if constexpr (GATEUP)
+      Rt[ct] = (ct < NT / 2 ? 0 : C::kBN / 2) + 32 * (wn * (NT / 2) + ct % (NT / 2));
+    else
+      Rt[ct] = 32 * (wn * NT + ct);
+  }
+  const bool wact = tile_col(Rt[0]) >= 0;
   const bool rows_ok[2] = {wact && arow0 < nvalid, wact && arow0 + 32 < nvalid};
 
   // ---- DMA sources: chunks wave, wave + 8, ... of every stage (A first) ----
+  // 32-bit per-lane offsets from uniform bases (one expert's matrix < 4 GiB)
   const size_t wrows = static_cast<size_t>(GATEUP ? 2 * N : N);
-  const size_t wrow_bytes = WFMT == kFP8 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
-  const uint8_t* src[C::kChunksPerWave];
+  const uint32_t wrow_bytes = WFMT == kFP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
+  const uint8_t* const wbase = w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
+  uint32_t src[C::kChunksPerWave];
 #pragma unroll
   for (int i = 0; i < C::kChunksPerWave; ++i) {
     const int c = wave + kGemmWaves * i;
@@ -290,12 +358,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       } else {
         row = b * BM + r;   // h rows of the block (padding rows hold unused values)
       }
-      src[i] = ga.a + static_cast<size_t>(row) * ga.a_pitch * (FP8ACT ? 1 : 2) + 16 * q;
+      src[i] = static_cast<uint32_t>(row) * ga.a_pitch * (FP8ACT ? 1 : 2) + 16 * q;
     } else {
       const int v = (c - C::kAChunks) * 64 + lane;
       const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
       const int col = tile_col(R);
-      src[i] = w.codes + (static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col)) * wrow_bytes + 16 * q;
+      src[i] = static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
     }
   }
   // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
@@ -326,119 +394,124 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
 #pragma unroll
     for (int i = 0; i < C::kChunksPerWave; ++i) {
       const int c = wave + kGemmWaves * i;
-      dma16(src[i], buf + c * 1024);
+      dma16((c < C::kAChunks ? ga.a : wbase) + src[i], buf + c * 1024);
       src[i] += adv ? (c < C::kAChunks ? C::kARowB : C::kBRowB) : 0;
     }
     if constexpr (C::kScales) {
-      if (lane < C::kScaleRowsPerWave)
-        dma4(ssrc, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
+      if (lane < C::kScaleRowsPerWave) dma4(ssrc, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
       // MXFP4: stages 2m and 2m + 1 share the dword at 4m
       ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
     }
   };
 
-  // Per-lane fragment offsets within a ring buffer: weight vectors of the
-  // two column tiles, activation vectors, then (FP4) the two scale dwords.
-  constexpr int kBRead = WFMT == kFP8 ? 4 : 2;
-  constexpr int kARead = FP8ACT ? 4 : 8;
-  constexpr int kReads = kBRead + kARead + (C::kScales ? 2 : 0);
-  uint32_t roff[kReads];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int R = (ct ? R1 : R0) + j;
-    const uint32_t row = C::kABytes + R * C::kBRowB;
-    if constexpr (WFMT != kFP8) {
-      roff[ct] = row + 16 * swz<C::kBV>(R, g);
-      roff[kBRead + kARead + ct] = C::kABytes + C::kBBytes + 4 * R;
-    } else if constexpr (FP8ACT) {
-      roff[2 * ct] = row + 16 * swz<C::kBV>(R, g);
-      roff[2 * ct + 1] = row + 16 * swz<C::kBV>(R, 2 + g);
-    } else {
-      roff[2 * ct] = row + 16 * swz<C::kBV>(R, 2 * g);
-      roff[2 * ct + 1] = row + 16 * swz<C::kBV>(R, 2 * g + 1);
-    }
+  // Per-lane fragment addresses within a ring buffer: the first weight row
+  // and the first activation row of the wave; the other column and row tiles
+  // are 32 rows further on, where the swizzle repeats, so they are reached
+  // through immediate offsets of the same read instructions.
+  const int RB = Rt[0] + j, RA = arow0 + j;
+  const uint32_t brow = C::kABytes + RB * C::kBRowB, arow = RA * C::kARowB;
+  uint32_t bo[2], ao[4];
+  const uint32_t so = C::kABytes + C::kBBytes + 4 * RB;
+  if constexpr (WFMT != kFP8) {
+    bo[0] = bo[1] = brow + 16 * swz<C::kBV>(RB, g);
+  } else if constexpr (FP8ACT) {
+    bo[0] = brow + 16 * swz<C::kBV>(RB, g);
+    bo[1] = brow + 16 * swz<C::kBV>(RB, 2 + g);
+  } else {
+    bo[0] = brow + 16 * swz<C::kBV>(RB, 2 * g);
+    bo[1] = brow + 16 * swz<C::kBV>(RB, 2 * g + 1);
   }
+  if constexpr (FP8ACT) {
+    ao[0] = arow + 16 * swz<C::kAV>(RA, g);
+    ao[1] = arow + 16 * swz<C::kAV>(RA, 2 + g);
+    ao[2] = ao[3] = ao[0];
+  } else {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int r = arow0 + 32 * m + j;
-    const uint32_t row = r * C::kARowB;
-    if constexpr (FP8ACT) {
-      roff[kBRead + 2 * m] = row + 16 * swz<C::kAV>(r, g);
-      roff[kBRead + 2 * m + 1] = row + 16 * swz<C::kAV>(r, 2 + g);
-    } else {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) roff[kBRead + 4 * m + tt] = row + 16 * swz<C::kAV>(r, 4 * g + tt);
-    }
+    for (int tt = 0; tt < 4; ++tt) ao[tt] = arow + 16 * swz<C::kAV>(RA, 4 * g + tt);
   }
+  // tile-row distances of this wave's column tiles from the first
+  constexpr int kHalf = C::kBN / 2;
+  constexpr int kD1 = GATEUP ? (NT == 4 ? 32 : kHalf) : 32;
+  constexpr int kD2 = GATEUP ? kHalf : 64;
+  constexpr int kD3 = GATEUP ? kHalf + 32 : 96;
+  constexpr int kOAM = 32 * C::kARowB;
+  constexpr int kBVec = WFMT == kFP8 ? 2 * NT : NT;
+  constexpr int kAVec = FP8ACT ? 4 : 8;
 
-  f32x16 acc[2][2] = {};
+  f32x16 acc[2][NT];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[m][ct] = f32x16{};
+
   // One stage from ring buffer `cur`: wait for its DMA, barrier, read the
   // fragments, refill the buffer the previous stage used, then the MFMA work.
   auto step = [&](int s, uint8_t* cur, uint8_t* refill) {
-    wait_vm<C::kVmPerStage * (kRing - 2)>();
+    wait_vm<C::kVmPerStage * (C::kRing - 2)>();
     stage_barrier();
     const uint32_t base = lds_addr(cur);
-    uint32_t ad[kReads];
-#pragma unroll
-    for (int i = 0; i < kReads; ++i) ad[i] = base + roff[i];
-    u32x4 fr[kBRead + kARead];
-    uint32_t scw[2] = {0, 0};
-    if constexpr (C::kScales)
-      lds_read_fp4(ad, fr, scw);
-    else if constexpr (FP8ACT)
-      lds_read8(ad, fr);
-    else
-      lds_read12(ad, fr);
+    u32x4 bv[kBVec], av[kAVec];
+    uint32_t scw[NT];
+    if constexpr (WFMT != kFP8) {
+      const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
+      if constexpr (NT == 4)
+        frag_read_fp4_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM>(
+            base + bo[0], base + so, vA, bv, scw, av);
+      else
+        frag_read_fp4_2<kD1 * C::kBRowB, kD1 * 4, kOAM>(base + bo[0], base + so, vA, bv, scw, av);
+    } else if constexpr (FP8ACT) {
+      frag_read_fp8_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kOAM>(base + bo[0], base + bo[1],
+                                                                               base + ao[0], base + ao[1], bv, av);
+    } else {
+      const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
+      frag_read_fp8_bf16_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kOAM>(base + bo[0], base + bo[1], vA,
+                                                                                    bv, av);
+    }
     issue(refill);
-    if (s >= ns) return;   // a stage past the end of K: nothing to multiply
     if constexpr (FP8ACT) {
-      const i32x8 b0 = u4x2(to_u4(fr[0]), to_u4(fr[1])), b1 = u4x2(to_u4(fr[2]), to_u4(fr[3]));
+      i32x8 bq[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) bq[ct] = u4x2(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]));
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (!rows_ok[m]) continue;
-        const i32x8 a = u4x2(to_u4(fr[kBRead + 2 * m]), to_u4(fr[kBRead + 2 * m + 1]));
-        acc[m][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[m][0], 0, 0, 0, 127, 0, 127);
-        acc[m][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[m][1], 0, 0, 0, 127, 0, 127);
+        const i32x8 a = u4x2(to_u4(av[2 * m]), to_u4(av[2 * m + 1]));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq[ct], acc[m][ct], 0, 0, 0, 127, 0, 127);
       }
     } else {
       // this lane's scale byte(s): MXFP4 byte 2 (s & 1) + g, NVFP4 bytes 2g, 2g + 1
       const int sh = WFMT == kMXFP4 ? 16 * (s & 1) + 8 * g : 16 * g;
-      const uint32_t sc0 = scw[0] >> sh, sc1 = scw[1] >> sh;
-      uint4 bw[2][2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if constexpr (WFMT == kFP8) {
-          bw[ct][0] = to_u4(fr[2 * ct]);
-          bw[ct][1] = to_u4(fr[2 * ct + 1]);
-        } else {
-          bw[ct][0] = bw[ct][1] = to_u4(fr[ct]);
-        }
-      }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const bf16x8 b0 = weight_bf16<WFMT>(bw[0][0], bw[0][1], sc0, tt);
-        const bf16x8 b1 = weight_bf16<WFMT>(bw[1][0], bw[1][1], sc1, tt);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (!rows_ok[m]) continue;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, to_u4(fr[kBRead + 4 * m + tt]));
-          acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[m][0], 0, 0, 0);
-          acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[m][1], 0, 0, 0);
+        for (int ct = 0; ct < NT; ++ct) {
+          bf16x8 bt;
+          if constexpr (WFMT == kFP8)
+            bt = weight_bf16<WFMT>(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]), 0, tt);
+          else
+            bt = weight_bf16<WFMT>(to_u4(bv[ct]), to_u4(bv[ct]), scw[ct] >> sh, tt);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            if (!rows_ok[m]) continue;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, to_u4(av[4 * m + tt]));
+            acc[m][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bt, acc[m][ct], 0, 0, 0);
+          }
         }
       }
     }
   };
 
   // prologue: stages 0 .. kRing - 2 into buffers 0 .. kRing - 2
-  issue(lds0);
-  issue(lds1);
-  issue(lds2);
-  static_assert(kRing == 4, "the ring is unrolled by hand");
-  for (int s = 0; s < ns; s += kRing) {
-    step(s, lds0, lds3);
-    step(s + 1, lds1, lds0);
-    step(s + 2, lds2, lds1);
-    step(s + 3, lds3, lds2);
+#pragma unroll
+  for (int i = 0; i < C::kRing - 1; ++i) issue(ring + i * C::kSlotBytes);
+  for (int s = 0; s < ns; s += C::kRing) {
+#pragma unroll
+    for (int r = 0; r < C::kRing; ++r) {
+      if (s + r >= ns) break;
+      step(s + r, ring + r * C::kSlotBytes, ring + ((r + C::kRing - 1) % C::kRing) * C::kSlotBytes);
+    }
   }
   wait_vm<0>();   // no DMA into LDS may outlive the workgroup
 
@@ -447,23 +520,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   if constexpr (WFMT != kMXFP4) f = w.tscale[e];
   if constexpr (FP8ACT) f *= amax_scale(ga.amax_a);
   if constexpr (GATEUP) {
-    const int c0 = tile_col(R0 + j);   // gate column of this lane
     float mx = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int u = 0; u < NT / 2; ++u) {
+      const int col = tile_col(Rt[u] + j);   // gate column of this lane
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (!wact || i >= nvalid) continue;
-        const float v = swiglu(acc[m][0][r] * f, acc[m][1][r] * f);
-        mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
-        ga.out[static_cast<size_t>(b * BM + i) * N + c0] = f32_to_bf16(v);
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!wact || i >= nvalid) continue;
+          const float v = swiglu(acc[m][u][r] * f, acc[m][u + NT / 2][r] * f);
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+          ga.out[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
+        }
       }
     }
     if constexpr (FP8ACT) wg_amax_to_slots(mx, ga.amax_slots, red);
   } else {
     __syncthreads();   // flat_of
-    const int c0 = nt * C::kBN + R0 + j;
+    const int c0 = nt * C::kBN + Rt[0] + j;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -472,7 +548,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
         if (!wact || i >= nvalid) continue;
         const size_t fr = static_cast<size_t>(flat_of[i]);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) ga.out[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
+        for (int ct = 0; ct < NT; ++ct) ga.out[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
       }
     }
   }
