@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
                                                            int32_t* block_expert, int32_t* num_padded,
                                                            uint32_t* zero_words, int n_zero) {
   __shared__ int cnt[kAlignMaxE];
-  __shared__ int ids_s[kAlignSmallN];
+  __shared__ __attribute__((aligned(16))) int ids_s[kAlignSmallN];
   __shared__ int tmp[32];
   const int e = threadIdx.x;
   for (int i = e; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
@@ -47,10 +47,21 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
   const int c = e < E ? cnt[e] : 0;
   int off, total;
   finish_layout(e, E, c, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off, &total);
-  if (e < E && c > 0) {
-    int pos = off;
-    for (int i = 0; i < n; ++i)
-      if (ids_s[i] == e) sorted_ids[pos++] = i;
+  if (e < E) cnt[e] = off;   // the counts are no longer needed: reuse as segment starts
+  __syncthreads();
+  // row i goes after the earlier rows of its expert (stable counting sort);
+  // ignored ids (outside [0, E)) are neither counted nor placed
+  if (threadIdx.x < n) {
+    const int i = threadIdx.x;
+    const int id = ids_s[i];
+    if (static_cast<unsigned>(id) < static_cast<unsigned>(E)) {
+      int rank = 0;
+      for (int j0 = 0; j0 < i; j0 += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(&ids_s[j0]);
+        rank += (v.x == id) + (j0 + 1 < i && v.y == id) + (j0 + 2 < i && v.z == id) + (j0 + 3 < i && v.w == id);
+      }
+      sorted_ids[cnt[id] + rank] = i;
+    }
   }
 }
 

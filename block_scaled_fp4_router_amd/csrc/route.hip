@@ -365,7 +365,7 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
     const float* __restrict__ part, int S, int T, int E, int k, const float* __restrict__ bias, int has_shared,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ sgate, int32_t* counts, int32_t* offsets,
     int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, int P, uint32_t* zero_words, int n_zero) {
-  __shared__ int ids_s[kDecodeMaxT * 16];
+  __shared__ __attribute__((aligned(16))) int ids_s[kDecodeMaxT * 16];
   __shared__ int cnt[kAlignMaxE];
   __shared__ int tmp[32];
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
@@ -407,10 +407,17 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
   int off, total;
   finish_layout(tid, E, c, kDecodeBM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off,
                 &total);
-  if (tid < E && c > 0) {
-    int pos = off;
-    for (int i = 0; i < n; ++i)
-      if (ids_s[i] == tid) sorted_ids[pos++] = i;
+  if (tid < E) cnt[tid] = off;   // the counts are no longer needed: reuse as segment starts
+  __syncthreads();
+  // row i goes after the earlier rows of its expert (stable counting sort)
+  if (tid < n) {
+    const int id = ids_s[tid];
+    int rank = 0;
+    for (int j0 = 0; j0 < tid; j0 += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(&ids_s[j0]);
+      rank += (v.x == id) + (j0 + 1 < tid && v.y == id) + (j0 + 2 < tid && v.z == id) + (j0 + 3 < tid && v.w == id);
+    }
+    sorted_ids[cnt[id] + rank] = tid;
   }
 }
 
