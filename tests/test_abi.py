@@ -81,6 +81,9 @@ def test_workspace_size_of_a_valid_layer():
 @needs_lib
 @pytest.mark.parametrize("field,value,status", [
     ("hidden", 100, ft.ERR_UNSUPPORTED),
+    ("hidden", 4096 + 128, ft.ERR_UNSUPPORTED),
+    ("inter", 192, ft.ERR_UNSUPPORTED),
+    ("inter", 4096 + 128, ft.ERR_UNSUPPORTED),
     ("inter", 0, ft.ERR_UNSUPPORTED),
     ("top_k", 0, ft.ERR_UNSUPPORTED),
     ("top_k", 9, ft.ERR_UNSUPPORTED),
