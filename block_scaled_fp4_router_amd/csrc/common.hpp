@@ -23,9 +23,10 @@ constexpr int kFP8 = 3;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte streaming load (non-temporal: weights are read once per use).
-__device__ __forceinline__ uint4 load_nt(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// 16-byte load with the default cache policy.  (Measured on MI355X for the
+// decode weight streams: the non-temporal hint made them about 13% slower.)
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

@@ -104,22 +104,20 @@ __device__ __forceinline__ void dma_split_rows(uint8_t* lds, int rows, int K, in
   const int hv = K / 16, sv = spitch / 16, nh = rows * hv;
   const float inv_h = 1.0f / static_cast<float>(hv), inv_s = 1.0f / static_cast<float>(sv);
   dma_stage(lds, 2 * nh + rows * sv, [&](int v) -> const void* {
+    const bool is_sc = v >= 2 * nh, is_lo = !is_sc && v >= nh;
     int r, s;
-    if (v < 2 * nh) {
-      const bool is_lo = v >= nh;
-      split_index(is_lo ? v - nh : v, hv, inv_h, r, s);
-      const uint8_t* base = is_lo ? lo : hi;
-      return base + static_cast<size_t>(src_row(r)) * K + 16 * swz(r, s);
-    }
-    split_index(v - 2 * nh, sv, inv_s, r, s);
-    return sc + static_cast<size_t>(src_row(r)) * spitch + 16 * s;
+    split_index(is_sc ? v - 2 * nh : is_lo ? v - nh : v, is_sc ? sv : hv, is_sc ? inv_s : inv_h, r, s);
+    // src_row may be a cross-lane shuffle: every lane evaluates it, outside
+    // any branch on the lane's region
+    const size_t row = static_cast<size_t>(src_row(r));
+    if (is_sc) return sc + row * spitch + 16 * s;
+    return (is_lo ? lo : hi) + row * K + 16 * swz(r, s);
   });
 }
 
 // ------------------------------------------------------------ blocks ------
-// A routed block's LDS holds every token of the batch when T <= kAllRowsT
-// (its DMA needs nothing from the slot table), else the block's 16 slot rows.
-constexpr int kAllRowsT = 8;
+// A block's LDS holds the rows of its valid slots (at most min(T, 16)): the
+// slot table is read first, and only those rows are fetched.
 
 // This lane's token slot (lane & 15) of block b: token row, flat row, valid.
 struct LaneSlot {
@@ -127,7 +125,14 @@ struct LaneSlot {
   bool valid;
 };
 
-__device__ __forceinline__ LaneSlot lane_slot(const DecodeArgs& a, int b, bool shared, int p0) {
+// The slot table entry is fetched first and decoded only after the weight
+// loads are issued, so that its latency overlaps theirs (a use before them
+// would make the wave wait for it alone).
+__device__ __forceinline__ int slot_fetch(const DecodeArgs& a, int b, bool shared) {
+  return shared ? 0 : a.sorted_ids[b * kDecodeBM + (lane_id() & 15)];
+}
+
+__device__ __forceinline__ LaneSlot slot_decode(const DecodeArgs& a, bool shared, int p0, int raw) {
   const int j = lane_id() & 15;
   LaneSlot s;
   if (shared) {
@@ -135,7 +140,7 @@ __device__ __forceinline__ LaneSlot lane_slot(const DecodeArgs& a, int b, bool s
     s.tok = s.flat;
     s.valid = s.flat < a.T;
   } else {
-    s.flat = a.sorted_ids[b * kDecodeBM + j];
+    s.flat = raw;
     s.valid = s.flat < a.T * a.k;
     s.tok = s.valid ? s.flat / a.k : 0;
   }
@@ -173,23 +178,22 @@ struct MxW {
 template <int NB, bool PACK>
 __device__ __forceinline__ void mx_wload(MxW<NB, PACK>& w, const uint8_t* codes, const uint8_t* scales, int u0,
                                          int nch, int g) {
+  // Chunks past the row end reload its last chunk (unused): every call issues
+  // the same loads, so the compiler's wait counts stay exact.
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
-    if (u0 + u < nch) w.c[u] = load_nt(codes + 64 * (u0 + u) + 16 * g);
+  for (int u = 0; u < NB; ++u) w.c[u] = load16(codes + 64 * min(u0 + u, nch - 1) + 16 * g);
   if constexpr (PACK) {
 #pragma unroll
-    for (int m = 0; m < NB / 4; ++m)
-      if (u0 + 4 * m < nch) {
-        const uint4 v = *reinterpret_cast<const uint4*>(scales + 4 * (u0 + 4 * m));
-        w.s[4 * m] = v.x;
-        w.s[4 * m + 1] = v.y;
-        w.s[4 * m + 2] = v.z;
-        w.s[4 * m + 3] = v.w;
-      }
+    for (int m = 0; m < NB / 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(scales + 4 * min(u0 + 4 * m, nch - 4));
+      w.s[4 * m] = v.x;
+      w.s[4 * m + 1] = v.y;
+      w.s[4 * m + 2] = v.z;
+      w.s[4 * m + 3] = v.w;
+    }
   } else {
 #pragma unroll
-    for (int u = 0; u < NB; ++u)
-      if (u0 + u < nch) w.s[u] = scales[4 * (u0 + u) + g];
+    for (int u = 0; u < NB; ++u) w.s[u] = scales[4 * min(u0 + u, nch - 1) + g];
   }
 }
 
@@ -256,7 +260,7 @@ __device__ __forceinline__ HSplit h_split_rows(const DecodeArgs& a, bool shared,
 
 // gate_up: 4 waves, each on 8 intermediate indices (8 gate + 8 up rows); the
 // token rows arrive already split (xhi / xlo / xsc).
-template <int NB, bool PACK, bool ALLROWS>
+template <int NB, bool PACK>
 __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float red[kGateWaves][kDecodeBM];
@@ -274,29 +278,23 @@ __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(Decod
   const int i0 = c0 + wave * 8;
   const int j = lane & 15, g = lane >> 4;
   const size_t wrow = static_cast<size_t>(e) * (2 * I) + (j < 8 ? i0 + j : I + i0 + (j - 8));
-  const int rows = ALLROWS ? a.T : kDecodeBM;
-  const MxRows m = mx_rows(smem, H, a.xsc_pitch, rows);
-  LaneSlot ls;
-  if constexpr (!ALLROWS) ls = lane_slot(a, b, shared, p0);
 
-  // 1. token rows -> LDS
-  dma_split_rows(smem, rows, H, a.xsc_pitch, a.xhi, a.xlo, a.xsc, [&](int r) {
-    if constexpr (ALLROWS)
-      return r;
-    else
-      return __shfl(ls.tok, r, kWave);
-  });
-  // 2. the weight stream
+  // 1. the block's slot entries, then the weight stream
+  const int raw = slot_fetch(a, b, shared);
   const uint8_t* codes = w.codes + wrow * (H / 2);
   const uint8_t* scales = w.scales + wrow * (H / 32);
   MxW<NB, PACK> wt;
   mx_wload(wt, codes, scales, 0, nch, g);
-  if constexpr (ALLROWS) ls = lane_slot(a, b, shared, p0);
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  const LaneSlot ls = slot_decode(a, shared, p0, raw);
+  // 2. the split token rows of the valid slots -> LDS rows 0 .. count - 1
   const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  const MxRows m = mx_rows(smem, H, a.xsc_pitch, count);
+  dma_split_rows(smem, count, H, a.xsc_pitch, a.xhi, a.xlo, a.xsc, [&](int r) { return __shfl(ls.tok, r, kWave); });
+  __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mx_row_dot(wt, codes, scales, m, ALLROWS ? ls.tok : j, j < count, nch, g, acc);
+  mx_row_dot(wt, codes, scales, m, j, j < count, nch, g, acc);
 
   // 3. h = SwiGLU(gate, up) rounded to bf16, then split per 32-block: lanes
   //    j < 8 hold column i0 + j of slots 4g + r; the 32-block of a slot spans
@@ -349,18 +347,20 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeA
   const int n0 = blockIdx.x * kDownTileN + wave * 16;
   const int j = lane & 15, g = lane >> 4;
   const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
-  const int rows = decode_rows(a.T);  // rows past the block's count are stale and unused
-  const MxRows m = mx_rows(smem, K, a.hsc_pitch, rows);
   const HSplit hs = h_split_rows(a, shared, p0);
 
-  dma_split_rows(smem, rows, K, a.hsc_pitch, hs.hi, hs.lo, hs.sc, [](int r) { return r; });
+  const int raw = slot_fetch(a, b, shared);
   const uint8_t* codes = w.codes + wrow * (K / 2);
   const uint8_t* scales = w.scales + wrow * (K / 32);
   MxW<NB, PACK> wt;
   mx_wload(wt, codes, scales, 0, nch, g);
-  const LaneSlot ls = lane_slot(a, b, shared, p0);
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  const LaneSlot ls = slot_decode(a, shared, p0, raw);
+  // the h rows of the valid slots -> LDS rows 0 .. count - 1
   const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  const MxRows m = mx_rows(smem, K, a.hsc_pitch, count);
+  dma_split_rows(smem, count, K, a.hsc_pitch, hs.hi, hs.lo, hs.sc, [](int r) { return r; });
+  __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   mx_row_dot(wt, codes, scales, m, j, j < count, nch, g, acc);
@@ -394,10 +394,10 @@ __device__ __forceinline__ typename WSliceT<WFMT>::type load_wslice(const QW& w,
   typename WSliceT<WFMT>::type s;
   if constexpr (WFMT == kFP8) {
     const uint8_t* p = w.codes + row * K + kb;
-    s.c0 = load_nt(p);
-    s.c1 = load_nt(p + 16);
+    s.c0 = load16(p);
+    s.c1 = load16(p + 16);
   } else {
-    s.c = load_nt(w.codes + row * (K / 2) + kb / 2);
+    s.c = load16(w.codes + row * (K / 2) + kb / 2);
     s.sc = *reinterpret_cast<const uint16_t*>(w.scales + row * (K / 16) + kb / 16);
   }
   return s;
@@ -479,7 +479,7 @@ __device__ __forceinline__ void mma_batch(const typename WSliceT<WFMT>::type* ws
   }
 }
 
-template <int WFMT, bool FP8ACT, int NB, int WPB, bool ALLROWS>
+template <int WFMT, bool FP8ACT, int NB, int WPB>
 __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ float red[16];
@@ -492,47 +492,37 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   const int I = shared ? a.Is : a.I;
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = lane_id();
+  // I is a multiple of 128, so a workgroup's waves are all inside or all past it
+  static_assert(16 % WPB == 0, "waves per workgroup");
+  if (blockIdx.x * WPB * 8 >= I) return;
   const int i0 = (blockIdx.x * WPB + wave) * 8;
-  const bool active = i0 < I;
   const int j = lane & 15, g = lane >> 4;
   const size_t wrow = static_cast<size_t>(e) * (2 * I) + (j < 8 ? i0 + j : I + i0 + (j - 8));
   const int row_bytes = FP8ACT ? H : 2 * H;
-  const int rows = ALLROWS ? a.T : kDecodeBM;
-  LaneSlot ls;
-  if constexpr (!ALLROWS) ls = lane_slot(a, b, shared, p0);
 
-  dma_rows(xs, rows, row_bytes / 16, [&](int r) -> const void* {
-    size_t t;
-    if constexpr (ALLROWS)
-      t = static_cast<size_t>(r);
-    else
-      t = static_cast<size_t>(__shfl(ls.tok, r, kWave));
+  // the block's slots, the weight stream, then the token rows of the valid
+  // slots -> LDS rows 0 .. count - 1
+  const int raw = slot_fetch(a, b, shared);
+  typename WSliceT<WFMT>::type ws[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) ws[u] = load_wslice<WFMT>(w, wrow, H, min(u * 128, H - 128) + g * 32);
+  __builtin_amdgcn_sched_barrier(0);
+  const LaneSlot ls = slot_decode(a, shared, p0, raw);
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  dma_rows(xs, count, row_bytes / 16, [&](int r) -> const void* {
+    const size_t t = static_cast<size_t>(__shfl(ls.tok, r, kWave));
     return FP8ACT ? a.xq + t * H : reinterpret_cast<const uint8_t*>(a.x + t * H);
   });
-  typename WSliceT<WFMT>::type ws[NB];
-  if (active) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-      if (u * 128 < H) ws[u] = load_wslice<WFMT>(w, wrow, H, u * 128 + g * 32);
-  }
-  if constexpr (ALLROWS) ls = lane_slot(a, b, shared, p0);
   __syncthreads();
-  if constexpr (!FP8ACT) {
-    if (!active) return;
-  }
-  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
 
-  const int arow = ALLROWS ? ls.tok : j;
+  const int arow = j;
   const bool aval = j < count;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    mma_batch<WFMT, FP8ACT, false, NB>(ws, 0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
-    for (int kc0 = NB * 128; kc0 < H; kc0 += NB * 128) {
+  mma_batch<WFMT, FP8ACT, false, NB>(ws, 0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
+  for (int kc0 = NB * 128; kc0 < H; kc0 += NB * 128) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (kc0 + u * 128 < H) ws[u] = load_wslice<WFMT>(w, wrow, H, kc0 + u * 128 + g * 32);
-      mma_batch<WFMT, FP8ACT, false, NB>(ws, kc0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
-    }
+    for (int u = 0; u < NB; ++u) ws[u] = load_wslice<WFMT>(w, wrow, H, min(kc0 + u * 128, H - 128) + g * 32);
+    mma_batch<WFMT, FP8ACT, false, NB>(ws, kc0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
   }
 
   float f = w.tscale[e];
@@ -543,7 +533,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   for (int r = 0; r < 4; ++r) {
     const float up = __shfl_xor(acc[r], 8, kWave);
     const int slot = 4 * g + r;
-    if (active && j < 8 && slot < count) {
+    if (j < 8 && slot < count) {
       const float v = swiglu(acc[r] * f, up * f);
       h[static_cast<size_t>(p0 + slot) * I + i0 + j] = f32_to_bf16(v);
       mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
@@ -568,25 +558,27 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
   const int j = lane & 15, g = lane >> 4;
   const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
   const uint16_t* hsrc = shared ? a.hs : a.h;
-  const int rows = decode_rows(a.T);  // rows past the block's count are stale and unused
 
-  dma_rows(hsm, rows, K / 8, [&](int r) -> const void* { return hsrc + static_cast<size_t>(p0 + r) * K; });
+  const int raw = slot_fetch(a, b, shared);
   typename WSliceT<WFMT>::type ws[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u)
-    if (u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, u * 128 + g * 32);
-  const LaneSlot ls = lane_slot(a, b, shared, p0);
+    ws[u] = load_wslice<WFMT>(w, wrow, K, min(u * 128, K - 128) + g * 32);
+  __builtin_amdgcn_sched_barrier(0);
+  const LaneSlot ls = slot_decode(a, shared, p0, raw);
+  // the h rows of the valid slots -> LDS
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  dma_rows(hsm, count, K / 8, [&](int r) -> const void* { return hsrc + static_cast<size_t>(p0 + r) * K; });
   float sh = 1.0f;
   if constexpr (FP8ACT) sh = scale_from_amax(a.amax_h);
   __syncthreads();
-  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
   const bool aval = j < count;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   mma_batch<WFMT, FP8ACT, true, NB>(ws, 0, K, g, hsm, 2 * K, j, aval, sh, acc);
   for (int kc0 = NB * 128; kc0 < K; kc0 += NB * 128) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (kc0 + u * 128 < K) ws[u] = load_wslice<WFMT>(w, wrow, K, kc0 + u * 128 + g * 32);
+      ws[u] = load_wslice<WFMT>(w, wrow, K, min(kc0 + u * 128, K - 128) + g * 32);
     mma_batch<WFMT, FP8ACT, true, NB>(ws, kc0, K, g, hsm, 2 * K, j, aval, sh, acc);
   }
   const float f = w.tscale[e] * sh;
@@ -667,40 +659,32 @@ static hipError_t allow_lds(Kern kernel, size_t bytes) {
                              static_cast<int>(bytes));
 }
 
-template <bool PACK, bool ALLROWS>
-static hipError_t run_gateup_mx_r(const DecodeArgs& a, hipStream_t s) {
+template <bool PACK>
+static hipError_t run_gateup_mx_p(const DecodeArgs& a, hipStream_t s) {
   constexpr int NB = 16;
   const int imax = a.Is > a.I ? a.Is : a.I;
-  const size_t lds = mx_rows_bytes(a.H, a.xsc_pitch, ALLROWS ? a.T : kDecodeBM);
+  const size_t lds = mx_rows_bytes(a.H, a.xsc_pitch, decode_rows(a.T));
   dim3 grid(imax / (8 * kGateWaves), a.nb_routed + a.nb_shared);
-  const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK, ALLROWS>, lds);
+  const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK>, lds);
   if (e != hipSuccess) return e;
-  decode_gateup_mx_kernel<NB, PACK, ALLROWS><<<grid, 64 * kGateWaves, lds, s>>>(a);
+  decode_gateup_mx_kernel<NB, PACK><<<grid, 64 * kGateWaves, lds, s>>>(a);
   return hipGetLastError();
 }
 
 static hipError_t run_gateup_mx(const DecodeArgs& a, hipStream_t s) {
-  const bool pack = (a.H / 128) % 4 == 0;
-  if (a.T <= kAllRowsT) return pack ? run_gateup_mx_r<true, true>(a, s) : run_gateup_mx_r<false, true>(a, s);
-  return pack ? run_gateup_mx_r<true, false>(a, s) : run_gateup_mx_r<false, false>(a, s);
-}
-
-template <int WFMT, bool FP8ACT, int WPB, bool ALLROWS>
-static hipError_t run_gateup_r(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NB = WFMT == kFP8 ? 8 : 16;
-  const int imax = a.Is > a.I ? a.Is : a.I;
-  const size_t lds = static_cast<size_t>(ALLROWS ? a.T : kDecodeBM) * (FP8ACT ? a.H : 2 * a.H);
-  dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
-  const hipError_t e = allow_lds(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB, ALLROWS>, lds);
-  if (e != hipSuccess) return e;
-  decode_gateup_kernel<WFMT, FP8ACT, NB, WPB, ALLROWS><<<grid, 64 * WPB, lds, s>>>(a);
-  return hipGetLastError();
+  return (a.H / 128) % 4 == 0 ? run_gateup_mx_p<true>(a, s) : run_gateup_mx_p<false>(a, s);
 }
 
 template <int WFMT, bool FP8ACT, int WPB>
 static hipError_t run_gateup(const DecodeArgs& a, hipStream_t s) {
-  return a.T <= kAllRowsT ? run_gateup_r<WFMT, FP8ACT, WPB, true>(a, s)
-                          : run_gateup_r<WFMT, FP8ACT, WPB, false>(a, s);
+  constexpr int NB = WFMT == kFP8 ? 8 : 16;
+  const int imax = a.Is > a.I ? a.Is : a.I;
+  const size_t lds = static_cast<size_t>(decode_rows(a.T)) * (FP8ACT ? a.H : 2 * a.H);
+  dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
+  const hipError_t e = allow_lds(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB>, lds);
+  if (e != hipSuccess) return e;
+  decode_gateup_kernel<WFMT, FP8ACT, NB, WPB><<<grid, 64 * WPB, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <bool PACK>
