@@ -105,11 +105,14 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
 // lo = E4M3(16 (x / 2^e - hi)).  e = floor(log2 amax) - 7 keeps |x / 2^e| below
 // 256 (no saturation), so the pair keeps about 8 significant bits -- the
 // precision of the bf16 input -- while the weights stay as 4-bit codes.
-// The scale is returned as its E8M0 code (e + 127, clamped to [0, 254]).
+// The scale is returned as its E8M0 code (e + 127, clamped to [4, 254]).
+// The code is at least 4, so that the lo codes' scale (code - 4) is a valid
+// E8M0 code and can be formed by a plain subtraction; this only matters for
+// blocks whose largest magnitude is below 2^-116.
 __device__ __forceinline__ uint32_t mx_split_scale_code(float amax) {
   const int ebits = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
   int code = ebits - 7;
-  code = code < 0 ? 0 : (code > 254 ? 254 : code);
+  code = code < 4 ? 4 : (code > 254 ? 254 : code);
   return static_cast<uint32_t>(code);
 }
 

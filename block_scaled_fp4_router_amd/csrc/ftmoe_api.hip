@@ -167,9 +167,11 @@ struct Plan {
   int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0;
   size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
          scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
-         hsc = 0, hq = 0, total = 0;
+         hsc = 0, hq = 0, xs = 0, xssc = 0, hgsc = 0, hssc = 0, total = 0;
   int hsc_pitch = 0;
-  bool mx_split = false;  // MXFP4: activations travel as split E4M3 pairs
+  bool mx_split = false;  // MXFP4 decode: activations travel as split E4M3 pairs
+  bool mx_gemm = false;   // MXFP4 prefill, routed experts: split x and h
+  bool mx_gemm_shared = false;  // MXFP4 prefill, shared expert
 };
 
 Plan make_plan(const ftmoe_layer* L, int T) {
@@ -224,8 +226,17 @@ Plan make_plan(const ftmoe_layer* L, int T) {
     p.hlo = take(hbytes);
     p.hsc = take(static_cast<size_t>(p.P + p.shared_rows) * p.hsc_pitch);
   } else {
+    // bf16 h, or for MXFP4 its split form (2 code bytes per element + scales)
+    p.mx_gemm = !p.decode && L->gate_up.fmt == FTMOE_W_MXFP4;
+    p.mx_gemm_shared = !p.decode && shared && L->shared_gate_up.fmt == FTMOE_W_MXFP4;
+    if (p.mx_gemm || p.mx_gemm_shared) {
+      p.xs = take(static_cast<size_t>(T) * H * 2);
+      p.xssc = take(static_cast<size_t>(T) * (H / 32));
+    }
     p.h = take(static_cast<size_t>(p.P) * I * 2);
+    if (p.mx_gemm) p.hgsc = take(static_cast<size_t>(p.P) * (I / 32));
     if (shared) p.hs = take(static_cast<size_t>(p.shared_rows) * L->shared_inter * 2);
+    if (p.mx_gemm_shared) p.hssc = take(static_cast<size_t>(p.shared_rows) * (L->shared_inter / 32));
     // FP8 activations, prefill: h quantised once for the down GEMM
     if (!p.decode && L->act == FTMOE_ACT_FP8_PER_TENSOR) p.hq = take(static_cast<size_t>(p.P) * I);
   }
@@ -416,29 +427,55 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   rs.block_m = p.BM;
   uint16_t* o = at<uint16_t>(ws, p.o);
   uint16_t* sh = shared ? at<uint16_t>(ws, p.s) : nullptr;
-  FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, x, xq, ax, H, I, h, ahs, s); }),
+  GemmAct xa{};
+  xa.bf16 = x;
+  xa.q = xq;
+  xa.amax = ax;
+  if (p.mx_gemm || p.mx_gemm_shared) {
+    xa.split = at<uint8_t>(ws, p.xs);
+    xa.split_sc = at<uint8_t>(ws, p.xssc);
+    FT_HIP(timed("x_split", s,
+                 [&] { return launch_x_split_gemm(x, T, H, at<uint8_t>(ws, p.xs), at<uint8_t>(ws, p.xssc), s); }),
+           "x split launch");
+  }
+  uint8_t* hgsc = p.mx_gemm ? at<uint8_t>(ws, p.hgsc) : nullptr;
+  FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, xa, H, I, h, hgsc, ahs, s); }),
          "gate_up GEMM launch");
   if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
-  uint8_t* hq = nullptr;
+  GemmAct ha{};
+  ha.bf16 = h;
+  ha.amax = ah;
+  if (p.mx_gemm) {
+    ha.split = reinterpret_cast<const uint8_t*>(h);
+    ha.split_sc = hgsc;
+  }
   if (fp8act) {
-    hq = at<uint8_t>(ws, p.hq);
+    uint8_t* hq = at<uint8_t>(ws, p.hq);
     FT_HIP(timed("quant_h", s,
                  [&] { return launch_quant_fp8(h, static_cast<int64_t>(p.P) * I, ah, hq, nullptr, s); }),
            "quantise launch");
+    ha.q = hq;
   }
-  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, h, hq, ah, H, I, o, s); }),
-         "down GEMM launch");
+  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, ha, H, I, o, s); }), "down GEMM launch");
   if (shared) {
+    GemmAct xs = xa;
+    xs.q = nullptr;
+    xs.amax = nullptr;
+    uint8_t* hssc = p.mx_gemm_shared ? at<uint8_t>(ws, p.hssc) : nullptr;
     FT_HIP(timed("gemm_shared_gateup", s,
                  [&] {
-                   return launch_gemm_gateup(to_qw(L->shared_gate_up), rs, x, nullptr, nullptr, H, L->shared_inter,
-                                             hs, nullptr, s);
+                   return launch_gemm_gateup(to_qw(L->shared_gate_up), rs, xs, H, L->shared_inter, hs, hssc, nullptr,
+                                             s);
                  }),
            "shared gate_up GEMM launch");
+    GemmAct hsa{};
+    hsa.bf16 = hs;
+    if (p.mx_gemm_shared) {
+      hsa.split = reinterpret_cast<const uint8_t*>(hs);
+      hsa.split_sc = hssc;
+    }
     FT_HIP(timed("gemm_shared_down", s,
-                 [&] {
-                   return launch_gemm_down(to_qw(L->shared_down), rs, hs, nullptr, nullptr, H, L->shared_inter, sh, s);
-                 }),
+                 [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hsa, H, L->shared_inter, sh, s); }),
            "shared down GEMM launch");
   }
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),

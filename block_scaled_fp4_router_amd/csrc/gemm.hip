@@ -19,17 +19,23 @@
 // the one barrier per stage.  16-byte vectors are XOR-swizzled by row so that
 // the 8 lanes of a ds_read_b128 phase hit 8 different bank groups.
 //
-// Weights are dequantised right before the MFMA: MXFP4 with the E8M0-scaled
-// hardware convert, NVFP4 as E2M1 x E4M3 (exact in bf16), into
-// v_mfma_f32_32x32x16_bf16.  FP8 weights with FP8 activations feed
-// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales; tensor and activation
-// scales are applied in the epilogue.  Block scales of FP4 weights travel
-// with their stage too (one dword per weight row and stage).
+// MXFP4 weights never leave their format: the activations arrive split into
+// two E4M3 codes per element with an E8M0 scale per 32 (x = s (hi + lo/16),
+// as exact as bf16), and v_mfma_scale_f32_32x32x64_f8f6f4 multiplies them
+// with the E2M1 codes, applying both E8M0 block scales in hardware -- two
+// MFMAs (hi, lo) per 64 K, no per-element conversion.  The gate_up epilogue
+// writes h in the same split form for the down GEMM.  NVFP4 weights (E4M3
+// block scales are not powers of two) are converted to bf16 (E2M1 x E4M3 is
+// exact in bf16) for v_mfma_f32_32x32x16_bf16.  FP8 weights with FP8
+// activations feed the scaled MFMA with unit scales; tensor and activation
+// scales are applied in the epilogue.  Block scales travel with their stage
+// (one dword per row per stage or per two stages).
 //
 // Within a stage, lane group g (lane / 32) of the bf16 MFMA takes K elements
 // [32g + 8t, 32g + 8t + 8) at MFMA step t: both operands use this assignment,
-// so a lane's weight bytes for the stage are one contiguous 16-byte run (one
-// E8M0 scale per MXFP4 lane, two E4M3 scales for NVFP4).
+// so a lane's weight bytes for the stage are one contiguous 16-byte run (two
+// E4M3 scales for NVFP4).  The scaled MFMA takes E2M1 K [32g, 32g + 32) and
+// 8-bit K [16g, 16g + 16) + [32 + 16g, 48 + 16g) in lane group g.
 //
 // Workgroups are numbered so that each XCD (workgroup w runs on XCD w % 8)
 // receives a contiguous range of (block, tile) pairs: the column tiles of a
@@ -66,7 +72,11 @@ struct Cfg {
   static constexpr int kBBytes = kBN * kBRowB;
   static constexpr bool kScales = WFMT != kFP8;        // FP4: one scale dword per weight row and stage
   static constexpr int kSBytes = kScales ? 4 * kBN : 0;
-  static constexpr int kSlotBytes = kABytes + kBBytes + kSBytes;
+  // MXFP4: split E4M3 activations (a row's stage = 64 hi + 64 lo bytes) and
+  // one E8M0 scale dword per activation row and two stages
+  static constexpr bool kSplitA = WFMT == kMXFP4;
+  static constexpr int kASBytes = kSplitA ? 4 * BM : 0;
+  static constexpr int kSlotBytes = kABytes + kBBytes + kSBytes + kASBytes;
   static constexpr int kRing = kSlotBytes * 4 <= 150 * 1024 ? 4 : 3;   // stage buffers in LDS
   static_assert(kRing * kSlotBytes <= 150 * 1024, "LDS");
   static constexpr int kAChunks = kABytes / 1024;     // 1 KB = one wave's 16-byte DMA instruction
@@ -75,7 +85,8 @@ struct Cfg {
   static_assert(kChunks % kGemmWaves == 0, "every wave issues the same number of DMA instructions");
   static constexpr int kScaleRowsPerWave = kBN / kGemmWaves;   // one 4-byte DMA instruction per wave
   static_assert(kScaleRowsPerWave <= 64, "scale rows per wave");
-  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0);
+  static constexpr int kARowsPerWave = BM / kGemmWaves;   // activation scale rows per wave
+  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0) + (kSplitA ? 1 : 0);
   static_assert(kVmPerStage * (kRing - 2) < 64, "vmcnt range");
 };
 
@@ -198,6 +209,64 @@ __device__ __forceinline__ void frag_read_fp4_2(uint32_t vB, uint32_t vS, const 
       : "v"(vB), "v"(vS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OS1), "n"(OAM));
 }
 
+// MXFP4 weights with split activations, 4 column tiles: as frag_read_fp4_4
+// plus the activation scale dwords of the wave's two row tiles.
+template <int OB1, int OB2, int OB3, int OS1, int OS2, int OS3, int OAM, int OAS>
+__device__ __forceinline__ void frag_read_mx_4(uint32_t vB, uint32_t vS, uint32_t vAS, const uint32_t (&vA)[4],
+                                               u32x4 (&b)[4], uint32_t (&s)[4], uint32_t (&as)[2], u32x4 (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %18\n"
+      "ds_read_b128 %1, %18 offset:%25\n"
+      "ds_read_b128 %2, %18 offset:%26\n"
+      "ds_read_b128 %3, %18 offset:%27\n"
+      "ds_read_b32 %4, %19\n"
+      "ds_read_b32 %5, %19 offset:%28\n"
+      "ds_read_b32 %6, %19 offset:%29\n"
+      "ds_read_b32 %7, %19 offset:%30\n"
+      "ds_read_b32 %8, %20\n"
+      "ds_read_b32 %9, %20 offset:%32\n"
+      "ds_read_b128 %10, %21\n"
+      "ds_read_b128 %11, %22\n"
+      "ds_read_b128 %12, %23\n"
+      "ds_read_b128 %13, %24\n"
+      "ds_read_b128 %14, %21 offset:%31\n"
+      "ds_read_b128 %15, %22 offset:%31\n"
+      "ds_read_b128 %16, %23 offset:%31\n"
+      "ds_read_b128 %17, %24 offset:%31\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]),
+        "=&v"(as[0]), "=&v"(as[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB), "v"(vS), "v"(vAS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OB2), "n"(OB3),
+        "n"(OS1), "n"(OS2), "n"(OS3), "n"(OAM), "n"(OAS));
+}
+
+// MXFP4 weights with split activations, 2 column tiles.
+template <int OB1, int OS1, int OAM, int OAS>
+__device__ __forceinline__ void frag_read_mx_2(uint32_t vB, uint32_t vS, uint32_t vAS, const uint32_t (&vA)[4],
+                                               u32x4 (&b)[2], uint32_t (&s)[2], uint32_t (&as)[2], u32x4 (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %14\n"
+      "ds_read_b128 %1, %14 offset:%21\n"
+      "ds_read_b32 %2, %15\n"
+      "ds_read_b32 %3, %15 offset:%22\n"
+      "ds_read_b32 %4, %16\n"
+      "ds_read_b32 %5, %16 offset:%24\n"
+      "ds_read_b128 %6, %17\n"
+      "ds_read_b128 %7, %18\n"
+      "ds_read_b128 %8, %19\n"
+      "ds_read_b128 %9, %20\n"
+      "ds_read_b128 %10, %17 offset:%23\n"
+      "ds_read_b128 %11, %18 offset:%23\n"
+      "ds_read_b128 %12, %19 offset:%23\n"
+      "ds_read_b128 %13, %20 offset:%23\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(as[0]), "=&v"(as[1]), "=&v"(a[0]), "=&v"(a[1]),
+        "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB), "v"(vS), "v"(vAS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OS1), "n"(OAM),
+        "n"(OAS));
+}
+
 // FP8 weights and activations, 4 column tiles: two vectors per operand row.
 template <int OB1, int OB2, int OB3, int OAM>
 __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
@@ -278,12 +347,16 @@ __device__ __forceinline__ bf16x8 weight_bf16(const uint4& c0, const uint4& c1, 
 struct GemmArgs {
   QW w;
   Rows rows;
-  const uint8_t* a;          // activation rows: bf16 (x or h) or E4M3 (x_q or h_q)
+  const uint8_t* a;          // activation rows: bf16 (x or h), E4M3 (x_q or h_q) or split E4M3 (MXFP4)
+  const uint8_t* a_sc;       // MXFP4: E8M0 scales of the split activations [rows][a_sc_pitch]
+  int a_sc_pitch;
   int K;                     // reduction length (H for gate_up, I for down)
   int N;                     // gate_up: I (gate columns); down: H (output columns)
-  int a_pitch;               // elements per activation row (H for gate_up, I for down)
+  int a_row_bytes;           // bytes per activation row
   const uint32_t* amax_a;    // FP8 activations: amax bits of the activation tensor
-  uint16_t* out;             // gate_up: h [rows][I]; down: o [flat][H]
+  void* out;                 // gate_up: h [rows][I] (bf16, or split E4M3 for MXFP4); down: o [flat][H] bf16
+  uint8_t* out_sc;           // gate_up, MXFP4: E8M0 scales of the split h [rows][out_sc_pitch]
+  int out_sc_pitch;
   uint32_t* amax_slots;      // gate_up with FP8 activations: partial maxima of |h|
 };
 
@@ -358,7 +431,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       } else {
         row = b * BM + r;   // h rows of the block (padding rows hold unused values)
       }
-      src[i] = static_cast<uint32_t>(row) * ga.a_pitch * (FP8ACT ? 1 : 2) + 16 * q;
+      src[i] = static_cast<uint32_t>(row) * ga.a_row_bytes + 16 * q;
     } else {
       const int v = (c - C::kAChunks) * 64 + lane;
       const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
@@ -376,6 +449,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     const int col = tile_col(R);
     const size_t row = static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col);
     ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
+  }
+  // Activation scales (split activations): lanes l < kARowsPerWave of wave
+  // w fetch the scale dword of tile row w * kARowsPerWave + l (two stages).
+  const uint8_t* asrc = nullptr;
+  if constexpr (C::kSplitA) {
+    const int r = wave * C::kARowsPerWave + (lane < C::kARowsPerWave ? lane : 0);
+    int row;
+    if (GATEUP && rows.sorted_ids) {
+      const int f = rows.sorted_ids[b * BM + r];
+      row = f < rows.n_flat ? f / rows.top_k : 0;
+    } else if (GATEUP) {
+      const int p = b * BM + r;
+      row = p < rows.n_flat ? p : 0;
+    } else {
+      row = b * BM + r;
+    }
+    asrc = ga.a_sc + static_cast<size_t>(row) * ga.a_sc_pitch;
   }
   if (!GATEUP && threadIdx.x < BM) {
     const int p = b * BM + threadIdx.x;
@@ -402,6 +492,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       // MXFP4: stages 2m and 2m + 1 share the dword at 4m
       ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
     }
+    if constexpr (C::kSplitA) {
+      if (lane < C::kARowsPerWave)
+        dma4(asrc, buf + C::kABytes + C::kBBytes + C::kSBytes + wave * 4 * C::kARowsPerWave);
+      asrc += adv && (cur_stage & 1) ? 4 : 0;
+    }
   };
 
   // Per-lane fragment addresses within a ring buffer: the first weight row
@@ -412,6 +507,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   const uint32_t brow = C::kABytes + RB * C::kBRowB, arow = RA * C::kARowB;
   uint32_t bo[2], ao[4];
   const uint32_t so = C::kABytes + C::kBBytes + 4 * RB;
+  const uint32_t sao = C::kABytes + C::kBBytes + C::kSBytes + 4 * RA;
   if constexpr (WFMT != kFP8) {
     bo[0] = bo[1] = brow + 16 * swz<C::kBV>(RB, g);
   } else if constexpr (FP8ACT) {
@@ -425,6 +521,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     ao[0] = arow + 16 * swz<C::kAV>(RA, g);
     ao[1] = arow + 16 * swz<C::kAV>(RA, 2 + g);
     ao[2] = ao[3] = ao[0];
+  } else if constexpr (C::kSplitA) {
+    // The 8-bit operand of the scaled 32x32x64 MFMA holds K [16g, 16g + 16)
+    // and [32 + 16g, 48 + 16g) in lane group g (hi vectors g, 2 + g; lo
+    // vectors 4 + g, 6 + g), while the 4-bit operand holds K [32g, 32g + 32);
+    // the scale of K block b (32 wide) is the one lane group b supplies.
+    ao[0] = arow + 16 * swz<C::kAV>(RA, g);
+    ao[1] = arow + 16 * swz<C::kAV>(RA, 2 + g);
+    ao[2] = arow + 16 * swz<C::kAV>(RA, 4 + g);
+    ao[3] = arow + 16 * swz<C::kAV>(RA, 6 + g);
   } else {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) ao[tt] = arow + 16 * swz<C::kAV>(RA, 4 * g + tt);
@@ -451,8 +556,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     stage_barrier();
     const uint32_t base = lds_addr(cur);
     u32x4 bv[kBVec], av[kAVec];
-    uint32_t scw[NT];
-    if constexpr (WFMT != kFP8) {
+    uint32_t scw[NT], asw[2];
+    if constexpr (C::kSplitA) {
+      const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
+      if constexpr (NT == 4)
+        frag_read_mx_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM, 32 * 4>(
+            base + bo[0], base + so, base + sao, vA, bv, scw, asw, av);
+      else
+        frag_read_mx_2<kD1 * C::kBRowB, kD1 * 4, kOAM, 32 * 4>(base + bo[0], base + so, base + sao, vA, bv, scw, asw,
+                                                               av);
+    } else if constexpr (WFMT != kFP8) {
       const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
       if constexpr (NT == 4)
         frag_read_fp4_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM>(
@@ -468,7 +581,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
                                                                                     bv, av);
     }
     issue(refill);
-    if constexpr (FP8ACT) {
+    if constexpr (C::kSplitA) {
+      // the E8M0 bytes of this lane's K block: byte 2 (s & 1) + g of the dwords
+      const int sh = 16 * (s & 1) + 8 * g;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (!rows_ok[m]) continue;
+        const int sa = static_cast<int>(asw[m] >> sh);
+        const i32x8 ah = u4x2(to_u4(av[4 * m]), to_u4(av[4 * m + 1]));
+        const i32x8 al = u4x2(to_u4(av[4 * m + 2]), to_u4(av[4 * m + 3]));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const uint4 c = to_u4(bv[ct]);
+          const i32x8 bq = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w),
+                            0, 0, 0, 0};
+          const int sb = static_cast<int>(scw[ct] >> sh);
+          // lo codes carry 2^4 times the residual: scale exponent lowered by 4
+          // (split scales are at least 4, so the low byte does not borrow)
+          acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, bq, acc[m][ct], 0, 4, 0, sa, 0, sb);
+          acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bq, acc[m][ct], 0, 4, 0, sa - 4, 0, sb);
+        }
+      }
+    } else if constexpr (FP8ACT) {
       i32x8 bq[NT];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) bq[ct] = u4x2(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]));
@@ -519,7 +653,38 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   float f = 1.0f;
   if constexpr (WFMT != kMXFP4) f = w.tscale[e];
   if constexpr (FP8ACT) f *= amax_scale(ga.amax_a);
-  if constexpr (GATEUP) {
+  if constexpr (GATEUP && C::kSplitA) {
+    // h rounded to bf16 goes through LDS (the ring is free now) so that each
+    // thread then splits one 32-column block of a row: tile [BM][kHalf].
+    __syncthreads();
+    uint16_t* tile = reinterpret_cast<uint16_t*>(ring);
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+      const int cl = Rt[u] + j;   // column within the workgroup's half tile
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+          tile[i * kHalf + cl] = f32_to_bf16(swiglu(acc[m][u][r], acc[m][u + NT / 2][r]));
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kBlocks = kHalf / 32;   // 32-column blocks per tile row
+    uint8_t* hsp = static_cast<uint8_t*>(ga.out);
+    for (int q = threadIdx.x; q < BM * kBlocks; q += kGemmThreads) {
+      const int i = q / kBlocks, cb = q % kBlocks;
+      const int col = nt * kHalf + 32 * cb;   // first intermediate index of the block
+      if (i >= nvalid || col >= N) continue;
+      const uint4* src = reinterpret_cast<const uint4*>(tile + i * kHalf + 32 * cb);
+      const uint4 v[4] = {src[0], src[1], src[2], src[3]};
+      const size_t row = static_cast<size_t>(b * BM + i);
+      // a row of split h: per 64 columns, 64 hi codes then 64 lo codes
+      uint8_t* hi = hsp + row * (2 * static_cast<size_t>(N)) + (col / 64) * 128 + (col % 64);
+      mx_split_block(v, hi, hi + 64, ga.out_sc + row * ga.out_sc_pitch + col / 32);
+    }
+  } else if constexpr (GATEUP) {
     float mx = 0.f;
 #pragma unroll
     for (int u = 0; u < NT / 2; ++u) {
@@ -532,7 +697,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
           if (!wact || i >= nvalid) continue;
           const float v = swiglu(acc[m][u][r] * f, acc[m][u + NT / 2][r] * f);
           mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
-          ga.out[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
+          static_cast<uint16_t*>(ga.out)[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
         }
       }
     }
@@ -548,7 +713,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
         if (!wact || i >= nvalid) continue;
         const size_t fr = static_cast<size_t>(flat_of[i]);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) ga.out[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
+        for (int ct = 0; ct < NT; ++ct)
+          static_cast<uint16_t*>(ga.out)[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
       }
     }
   }
@@ -571,7 +737,7 @@ static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
   const int bm = ga.rows.block_m;
   switch (ga.w.fmt) {
     case kMXFP4:
-      if (fp8act) return hipErrorInvalidValue;
+      if (fp8act || !ga.a_sc || (GATEUP && !ga.out_sc)) return hipErrorInvalidValue;
       return bm == 128 ? run<kMXFP4, false, 128, GATEUP>(ga, s) : run<kMXFP4, false, 64, GATEUP>(ga, s);
     case kNVFP4:
       if (fp8act) return hipErrorInvalidValue;
@@ -583,34 +749,76 @@ static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
   }
 }
 
-hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
-                              const uint32_t* amax_x, int H, int inter, uint16_t* h, uint32_t* amax_h,
-                              hipStream_t s) {
+hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, int H, int inter, void* h,
+                              uint8_t* h_sc, uint32_t* amax_h, hipStream_t s) {
   GemmArgs ga{};
   ga.w = w;
   ga.rows = rows;
-  ga.a = xq ? xq : reinterpret_cast<const uint8_t*>(x);
   ga.K = H;
   ga.N = inter;
-  ga.a_pitch = H;
-  ga.amax_a = amax_x;
+  if (w.fmt == kMXFP4) {
+    ga.a = x.split;
+    ga.a_sc = x.split_sc;
+    ga.a_sc_pitch = H / 32;
+    ga.a_row_bytes = 2 * H;
+    ga.out_sc = h_sc;
+    ga.out_sc_pitch = inter / 32;
+  } else if (x.q) {
+    ga.a = x.q;
+    ga.a_row_bytes = H;
+  } else {
+    ga.a = reinterpret_cast<const uint8_t*>(x.bf16);
+    ga.a_row_bytes = 2 * H;
+  }
+  ga.amax_a = x.amax;
   ga.out = h;
   ga.amax_slots = amax_h;
-  return dispatch<true>(ga, xq != nullptr, s);
+  return dispatch<true>(ga, x.q != nullptr, s);
 }
 
-hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint8_t* hq,
-                            const uint32_t* amax_h, int H, int inter, uint16_t* o, hipStream_t s) {
+hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int H, int inter, uint16_t* o,
+                            hipStream_t s) {
   GemmArgs ga{};
   ga.w = w;
   ga.rows = rows;
-  ga.a = hq ? hq : reinterpret_cast<const uint8_t*>(h);
   ga.K = inter;
   ga.N = H;
-  ga.a_pitch = inter;
-  ga.amax_a = amax_h;
+  if (w.fmt == kMXFP4) {
+    ga.a = h.split;
+    ga.a_sc = h.split_sc;
+    ga.a_sc_pitch = inter / 32;
+    ga.a_row_bytes = 2 * inter;
+  } else if (h.q) {
+    ga.a = h.q;
+    ga.a_row_bytes = inter;
+  } else {
+    ga.a = reinterpret_cast<const uint8_t*>(h.bf16);
+    ga.a_row_bytes = 2 * inter;
+  }
+  ga.amax_a = h.amax;
   ga.out = o;
-  return dispatch<false>(ga, hq != nullptr, s);
+  return dispatch<false>(ga, h.q != nullptr, s);
+}
+
+// ------------------------------------------------- split activations ------
+// Split E4M3 form of x for the MXFP4 GEMMs (one thread per 32-block).
+__global__ __launch_bounds__(256) void x_split_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                           uint8_t* __restrict__ xs, uint8_t* __restrict__ xsc) {
+  const int nb = H / 32;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * nb) return;
+  const int t = i / nb, blk = i % nb;
+  const uint4* p = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + blk * 32);
+  const uint4 v[4] = {p[0], p[1], p[2], p[3]};
+  uint8_t* hi = xs + static_cast<size_t>(t) * (2 * H) + (blk / 2) * 128 + (blk & 1) * 32;
+  mx_split_block(v, hi, hi + 64, xsc + static_cast<size_t>(t) * nb + blk);
+}
+
+hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s) {
+  const int n = T * (H / 32);
+  if (n == 0) return hipSuccess;
+  x_split_gemm_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, T, H, xs, xsc);
+  return hipGetLastError();
 }
 
 }  // namespace ftmoe

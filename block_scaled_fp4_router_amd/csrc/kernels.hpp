@@ -113,13 +113,26 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 // ---- prefill experts (grouped GEMMs on MFMA) ----
 // Rows per block of the prefill GEMMs for a layer routing T*k rows over E experts.
 int gemm_block_m(int T, int k, int E, int wfmt);
-// amax_slots: FP8 activations only, the kAmaxSlots partial maxima of |h|.
-hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const uint16_t* x, const uint8_t* xq,
-                              const uint32_t* amax_x, int H, int inter, uint16_t* h,
-                              uint32_t* amax_slots, hipStream_t s);
-// FP8 activations: hq is h quantised per tensor with the scale of amax_h.
-hipError_t launch_gemm_down(const QW& w, const Rows& rows, const uint16_t* h, const uint8_t* hq,
-                            const uint32_t* amax_h, int H, int inter, uint16_t* o, hipStream_t s);
+// Activation operand of a prefill GEMM, by weight format: MXFP4 takes the
+// split E4M3 form (per 64 columns of a row: 64 hi codes then 64 lo codes,
+// 2 bytes per element; E8M0 scales [rows][K/32]); FP8 weights with FP8
+// activations take q (E4M3, per-tensor scale from amax); otherwise bf16.
+struct GemmAct {
+  const uint16_t* bf16;
+  const uint8_t* q;
+  const uint32_t* amax;
+  const uint8_t* split;
+  const uint8_t* split_sc;
+};
+// gate_up writes h [rows][I]: bf16, or for MXFP4 split (h [rows][2I] codes,
+// h_sc [rows][I/32] scales).  amax_h: FP8 activations only, the kAmaxSlots
+// partial maxima of |h|.
+hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, int H, int inter, void* h,
+                              uint8_t* h_sc, uint32_t* amax_h, hipStream_t s);
+hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int H, int inter, uint16_t* o,
+                            hipStream_t s);
+// Split E4M3 form of x for the MXFP4 GEMMs: xs [T][2H], xsc [T][H/32].
+hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s);
 
 // ---- combine ----
 // y[t] = sum_j w[t,j] o[t*k+j] (+ sg[t] * sh[t]) -> bf16.
