@@ -28,6 +28,12 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 METRIC = "MoE-layer tokens/s (prefill) + decode expert-weight GB/s, % of MI355X roofline"
+# Arithmetic of the expert GEMMs by weight format: MXFP4 codes meet the
+# activations as a pair of E4M3 codes per element (as exact as bf16) on the
+# E8M0-scaled MFMA (two MFMAs per product, so its roofline is the bf16 one);
+# NVFP4 dequantises exactly to bf16; FP8 W8A8 runs E4M3 x E4M3.
+DTYPE = {"mxfp4": "e2m1 x e4m3-pair mfma/fp32-acc", "nvfp4": "bf16-mfma/fp32-acc",
+         "fp8": "bf16-mfma/fp32-acc", "fp8act": "fp8-e4m3-mfma/fp32-acc"}
 
 WORKLOADS = {
     # name: (config, T, kind)
@@ -123,7 +129,8 @@ def main() -> int:
     ms = (t1 - t0) * 1e3 / args.steps
     mean_bytes = float(np.mean([sel_bytes[i % nb] for i in range(args.steps)]))
 
-    # Same steps again with every kernel bracketed by HIP events on its stream.
+    # Same steps again with per-kernel timing: events attached to each kernel's
+    # launch (recorded at its start and end), or bracketing a multi-kernel step.
     ft.timing_enable(True)
     for i in range(args.steps):
         step(i)
@@ -171,7 +178,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": ("fp8-e4m3" if cfg.act == "fp8" else "bf16") + "-mfma/fp32-acc",
+        "vs_baseline": None, "dtype": DTYPE[cfg.fmt if cfg.act != "fp8" else "fp8act"],
         "data": "synthetic (seeded generator; random-init weights quantised to the named format)",
         "config": {"workload": describe(cfg, T), "kind": kind, "tokens": T, "layer_copies_cycled": ring,
                    "token_batches_cycled": nb, "path": args.path,

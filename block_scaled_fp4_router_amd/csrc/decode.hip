@@ -645,8 +645,7 @@ __global__ __launch_bounds__(256) void x_split_kernel(const uint16_t* __restrict
 hipError_t launch_x_split(const uint16_t* x, int T, int H, int xsc_pitch, uint8_t* xhi, uint8_t* xlo,
                           uint8_t* xsc, hipStream_t s) {
   const int n = T * (H / 32);
-  x_split_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, T, H, xsc_pitch, xhi, xlo, xsc);
-  return hipGetLastError();
+  return launch(x_split_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, T, H, xsc_pitch, xhi, xlo, xsc);
 }
 
 // ============================================================ launches ====
@@ -667,8 +666,7 @@ static hipError_t run_gateup_mx_p(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(imax / (8 * kGateWaves), a.nb_routed + a.nb_shared);
   const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK>, lds);
   if (e != hipSuccess) return e;
-  decode_gateup_mx_kernel<NB, PACK><<<grid, 64 * kGateWaves, lds, s>>>(a);
-  return hipGetLastError();
+  return launch(decode_gateup_mx_kernel<NB, PACK>, grid, dim3(64 * kGateWaves), lds, s, a);
 }
 
 static hipError_t run_gateup_mx(const DecodeArgs& a, hipStream_t s) {
@@ -683,8 +681,7 @@ static hipError_t run_gateup(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
   const hipError_t e = allow_lds(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB>, lds);
   if (e != hipSuccess) return e;
-  decode_gateup_kernel<WFMT, FP8ACT, NB, WPB><<<grid, 64 * WPB, lds, s>>>(a);
-  return hipGetLastError();
+  return launch(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB>, grid, dim3(64 * WPB), lds, s, a);
 }
 
 template <bool PACK>
@@ -695,8 +692,7 @@ static hipError_t run_down_mx_p(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
   const hipError_t e = allow_lds(decode_down_mx_kernel<NB, PACK>, lds);
   if (e != hipSuccess) return e;
-  decode_down_mx_kernel<NB, PACK><<<grid, 64 * kDownWaves, lds, s>>>(a);
-  return hipGetLastError();
+  return launch(decode_down_mx_kernel<NB, PACK>, grid, dim3(64 * kDownWaves), lds, s, a);
 }
 
 static hipError_t run_down_mx(const DecodeArgs& a, hipStream_t s) {
@@ -713,8 +709,7 @@ static hipError_t run_down(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
   const hipError_t e = allow_lds(decode_down_kernel<WFMT, FP8ACT, NB>, lds);
   if (e != hipSuccess) return e;
-  decode_down_kernel<WFMT, FP8ACT, NB><<<grid, 64 * kDownWaves, lds, s>>>(a);
-  return hipGetLastError();
+  return launch(decode_down_kernel<WFMT, FP8ACT, NB>, grid, dim3(64 * kDownWaves), lds, s, a);
 }
 
 // bf16 / FP8 gate_up: one-token batches touch few experts, so single-wave
@@ -745,8 +740,7 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   const int n = a.T * (a.H / 4);
-  decode_combine_kernel<<<(n + 255) / 256, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch(decode_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a);
 }
 
 }  // namespace ftmoe

@@ -47,12 +47,15 @@ ftmoe_status hip_status(hipError_t e, const char* what) {
   } while (0)
 
 // ---- optional per-kernel timing (diagnostics) ----
-// When enabled on this thread, each launch is bracketed by two HIP events on
-// its stream; ftmoe_timing_collect() waits for them and sums durations per
-// kernel name.  Events come from a pool that is reused after each collect.
+// When enabled on this thread, a step that is one kernel launched through
+// launch() carries a pair of events recorded at the kernel's own start and
+// end; any other step is bracketed by two events on its stream.
+// ftmoe_timing_collect() waits for them and sums durations per step name.
+// Events come from a pool that is reused after each collect.
 struct TimedLaunch {
   const char* name;
-  hipEvent_t a, b;
+  hipEvent_t a, b;   // the pair that timed the step
+  hipEvent_t c, d;   // the other pair (unused), returned to the pool
 };
 thread_local bool g_timing = false;
 thread_local std::vector<TimedLaunch> g_pending;
@@ -69,14 +72,30 @@ hipEvent_t pool_event() {
   return e;
 }
 
+}  // namespace
+
+ftmoe::KernelEvents& ftmoe::kernel_events() {
+  thread_local KernelEvents ev{nullptr, nullptr};
+  return ev;
+}
+
+namespace {
+
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   if (!g_timing) return launch();
-  TimedLaunch t{name, pool_event(), pool_event()};
-  if (t.a) hipEventRecord(t.a, s);
+  TimedLaunch t{name, pool_event(), pool_event(), pool_event(), pool_event()};
+  if (!t.a || !t.b || !t.c || !t.d) return launch();
+  kernel_events() = KernelEvents{t.a, t.b};
+  hipEventRecord(t.c, s);
   const hipError_t e = launch();
-  if (t.b) hipEventRecord(t.b, s);
-  if (t.a && t.b) g_pending.push_back(t);
+  hipEventRecord(t.d, s);
+  if (kernel_events().start) {   // not a single launch() kernel: time the stream span
+    kernel_events() = KernelEvents{nullptr, nullptr};
+    std::swap(t.a, t.c);
+    std::swap(t.b, t.d);
+  }
+  g_pending.push_back(t);
   return e;
 }
 
@@ -614,8 +633,11 @@ int32_t ftmoe_timing_collect(int32_t max_entries, char* names, double* total_ms,
     }
     ms[i] += m;
     cnt[i] += 1;
+    hipEventSynchronize(t.d);
     g_event_pool.push_back(t.a);
     g_event_pool.push_back(t.b);
+    g_event_pool.push_back(t.c);
+    g_event_pool.push_back(t.d);
   }
   g_pending.clear();
   const int32_t n = static_cast<int32_t>(keys.size());

@@ -728,8 +728,7 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
   const int total = ga.rows.num_blocks * ntile;
   if (total == 0) return hipSuccess;
   if (ga.K % kStageK) return hipErrorInvalidValue;
-  gemm_kernel<WFMT, FP8ACT, BM, GATEUP><<<8 * ((total + 7) / 8), kGemmThreads, 0, s>>>(ga);
-  return hipGetLastError();
+  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP>, dim3(8 * ((total + 7) / 8)), dim3(kGemmThreads), 0, s, ga);
 }
 
 template <bool GATEUP>
@@ -817,8 +816,7 @@ __global__ __launch_bounds__(256) void x_split_gemm_kernel(const uint16_t* __res
 hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s) {
   const int n = T * (H / 32);
   if (n == 0) return hipSuccess;
-  x_split_gemm_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, T, H, xs, xsc);
-  return hipGetLastError();
+  return launch(x_split_gemm_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, T, H, xs, xsc);
 }
 
 }  // namespace ftmoe

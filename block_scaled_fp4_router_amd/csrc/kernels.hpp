@@ -2,10 +2,36 @@
 // launcher enqueues on `stream` and returns the launch status.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ftmoe {
+
+// ---- launches ----
+// Kernel timing (diagnostics): while a pair of events is parked in this
+// thread's slot, the next kernel launched through launch() carries them, and
+// the runtime records them at that kernel's own start and end (no extra
+// stream operations, so the elapsed time is the kernel's execution alone).
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+KernelEvents& kernel_events();
+
+template <class... P, class... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+  KernelEvents& ev = kernel_events();
+  if (ev.start) {
+    const KernelEvents e = ev;
+    ev = KernelEvents{nullptr, nullptr};
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, e.start, e.stop, 0u,
+                          static_cast<P>(args)...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<P>(args)...);
+  }
+  return hipGetLastError();
+}
+
 
 // Device view of one stacked packed matrix set [E][N][K].
 struct QW {

@@ -53,8 +53,7 @@ __global__ void amax_fold_kernel(const uint32_t* __restrict__ slots, uint32_t* _
 }
 
 hipError_t launch_amax_fold(const uint32_t* slots, uint32_t* out, hipStream_t s) {
-  amax_fold_kernel<<<1, 64, 0, s>>>(slots, out);
-  return hipGetLastError();
+  return launch(amax_fold_kernel, dim3(1), dim3(64), 0, s, slots, out);
 }
 
 // s = amax / 448 (1 when amax is 0), the dequantisation scale.
@@ -95,14 +94,12 @@ static int elementwise_grid(int64_t n8, int64_t cap = 4096) {
 }
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* amax_bits, hipStream_t s) {
-  amax_bf16_kernel<<<elementwise_grid(n / 8, 512), 256, 0, s>>>(x, n, amax_bits);
-  return hipGetLastError();
+  return launch(amax_bf16_kernel, dim3(elementwise_grid(n / 8, 512)), dim3(256), 0, s, x, n, amax_bits);
 }
 
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, const uint32_t* amax_bits, uint8_t* q,
                             float* scale_out, hipStream_t s) {
-  quant_fp8_kernel<<<elementwise_grid(n / 8), 256, 0, s>>>(x, n, amax_bits, q, scale_out);
-  return hipGetLastError();
+  return launch(quant_fp8_kernel, dim3(elementwise_grid(n / 8)), dim3(256), 0, s, x, n, amax_bits, q, scale_out);
 }
 
 // -------------------------------------------------------------- combine ---
@@ -150,8 +147,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H, const float* sg,
                           const uint16_t* sh, uint16_t* y, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
-  combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(o, w, T, k, H, sg, sh, y);
-  return hipGetLastError();
+  return launch(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, o, w, T, k, H, sg, sh,
+                y);
 }
 
 }  // namespace ftmoe

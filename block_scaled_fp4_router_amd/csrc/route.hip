@@ -148,16 +148,15 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
   if (T <= kGemvMaxT) {
     dim3 grid((rows + 3) / 4);
     if (T <= 1)
-      router_gemv_kernel<1><<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, logits);
+      return launch(router_gemv_kernel<1>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
     else if (T <= 4)
-      router_gemv_kernel<4><<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, logits);
+      return launch(router_gemv_kernel<4>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
     else
-      router_gemv_kernel<kGemvMaxT><<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, logits);
+      return launch(router_gemv_kernel<kGemvMaxT>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   } else {
     dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE);
-    router_gemm_kernel<<<grid, 256, 0, s>>>(x, T, H, router_w, E, shared_gate_w, logits);
+    return launch(router_gemm_kernel, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- top-k ---
@@ -264,8 +263,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bi
                        int32_t* ids, float* w, float* sgate, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   return with_slots(E, [&]<int SL>() {
-    topk_kernel<SL><<<grid, 256, 0, s>>>(logits, T, E, k, bias, has_shared ? 1 : 0, ids, w, sgate);
-    return hipGetLastError();
+    return launch(topk_kernel<SL>, grid, dim3(256), 0, s, logits, T, E, k, bias, has_shared ? 1 : 0, ids, w, sgate);
   });
 }
 
@@ -338,9 +336,8 @@ hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* r
   const int rows = E + (shared_gate_w ? 1 : 0);
   const int S = router_splits(H);
   dim3 grid((rows + 3) / 4, S);
-  router_partial_kernel<<<grid, 256, 0, s>>>(x, T, H, S, router_w, E, shared_gate_w, part, xhi, xlo, xsc,
-                                             xsc_pitch);
-  return hipGetLastError();
+  return launch(router_partial_kernel, grid, dim3(256), 0, s, x, T, H, S, router_w, E, shared_gate_w, part, xhi, xlo,
+                xsc, xsc_pitch);
 }
 
 // Logit of (token t, row e): the S partials, added in slice order.
@@ -428,10 +425,9 @@ hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int 
                                     hipStream_t s) {
   return with_slots(E, [&]<int SL>() {
     auto go = [&]<int SQ>() {
-      topk_align_decode_kernel<SL, SQ><<<1, 1024, 0, s>>>(part, S, T, E, k, bias, has_shared ? 1 : 0, ids, w, sg,
-                                                          counts, offsets, sorted_ids, block_expert, num_padded, P,
-                                                          zero_words, n_zero);
-      return hipGetLastError();
+      return launch(topk_align_decode_kernel<SL, SQ>, dim3(1), dim3(1024), 0, s, part, S, T, E, k, bias,
+                    has_shared ? 1 : 0, ids, w, sg, counts, offsets, sorted_ids, block_expert, num_padded, P,
+                    zero_words, n_zero);
     };
     switch (S / 4) {
       case 1: return go.template operator()<1>();

@@ -202,9 +202,11 @@ ftmoe_status ftmoe_quantize_fp8_per_tensor(const uint16_t* x, int64_t n, uint8_t
                                            void* ws, size_t ws_bytes, void* stream);
 
 /* Diagnostics: per-kernel timing.  While enabled on the calling thread,
- * every kernel the entry points enqueue is bracketed by two HIP events on its
- * stream (not for use under graph capture; the events are host objects the
- * library creates and reuses).  ftmoe_timing_collect waits for the recorded
+ * every step the entry points enqueue is timed by a pair of HIP events: for
+ * a step that is a single kernel the events are attached to its launch and
+ * recorded at the kernel's own start and end; other steps are bracketed by
+ * events on the stream (not for use under graph capture; the events are
+ * host objects the library creates and reuses).  ftmoe_timing_collect waits for the recorded
  * events, writes up to max_entries rows -- kernel name (32-byte slots in
  * `names`), summed milliseconds and launch count -- clears the record and
  * returns the number of distinct kernels seen.  Any output may be NULL.    */
