@@ -7,9 +7,10 @@
 // whose 16 columns are its weight rows and whose 16 rows are token slots
 // (absent slots are zero).
 //
-// Prologue: the token rows a workgroup multiplies are copied HBM/L2 -> LDS
-// by LDS DMA (global_load_lds_dwordx4: no registers, so nothing to spill),
-// then every wave issues its whole weight stream into registers, and one
+// Prologue: every wave reads its lanes' slot-table entries, issues its whole
+// weight stream into registers, and then copies the token rows of the
+// block's valid slots HBM/L2 -> LDS by LDS DMA (global_load_lds_dwordx4: no
+// registers, so nothing to spill) while the weights are in flight; one
 // barrier later the MFMA work runs out of registers and LDS.  Rows in LDS are
 // stored with their 16-byte vectors XOR-swizzled by (row & 7), so the eight
 // lanes of a ds_read_b128 phase that read one K offset of eight different
