@@ -90,6 +90,12 @@ def main() -> int:
     ring = args.ring or (4 if kind == "decode" else 1)
     dev = "cuda"
     dlays = [ft.DeviceLayer.from_host(lay, dev, path=args.path) for _ in range(ring)]
+    if kind == "prefill" or args.path == "prefill":
+        # load-time step: the prefill GEMMs read their weight stages from the
+        # packed tile layout (outside the timed region, like loading a model)
+        for d in dlays:
+            d.pack()
+        torch.cuda.synchronize()
     descs = [d.desc() for d in dlays]
     nb = args.batches if kind == "decode" else 2
     xs_host = [synth.make_tokens(lay, T, stream=100 + b) for b in range(nb)]

@@ -36,7 +36,9 @@ EXPORTS = (
     "ftmoe_workspace_size", "ftmoe_align_max_padded", "ftmoe_align_workspace_size", "ftmoe_route",
     "ftmoe_align", "ftmoe_experts_forward", "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor",
     "ftmoe_timing_enable", "ftmoe_timing_collect", "ftmoe_status_string", "ftmoe_last_error", "ftmoe_version",
+    "ftmoe_packed_size", "ftmoe_pack_qweight",
 )
+ROLE_GATE_UP, ROLE_DOWN = 0, 1
 
 
 class FtmoeError(RuntimeError):
@@ -49,6 +51,7 @@ class QWeightDesc(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p), ("tensor_scales", ctypes.c_void_p),
+        ("packed", ctypes.c_void_p),
     ]
 
 
@@ -89,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_experts_forward.argtypes = [P(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp, vp]
     lib.ftmoe_forward.argtypes = [P(LayerDesc), vp, i32, vp, sz, vp, vp, vp, vp]
     lib.ftmoe_quantize_fp8_per_tensor.argtypes = [vp, i64, vp, vp, vp, sz, vp]
+    lib.ftmoe_packed_size.argtypes = [P(QWeightDesc), i32, P(sz)]
+    lib.ftmoe_pack_qweight.argtypes = [P(QWeightDesc), i32, vp, sz, vp]
     lib.ftmoe_status_string.argtypes = [i32]
     lib.ftmoe_status_string.restype = ctypes.c_char_p
     lib.ftmoe_last_error.argtypes = []
@@ -99,7 +104,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_timing_collect.argtypes = [i32, ctypes.c_char_p, P(ctypes.c_double), P(i64)]
     lib.ftmoe_timing_collect.restype = i32
     for name in ("ftmoe_workspace_size", "ftmoe_route", "ftmoe_align", "ftmoe_experts_forward",
-                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor"):
+                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -140,10 +145,22 @@ class DeviceQWeight:
     codes: object
     block_scales: object = None
     tensor_scales: object = None
+    packed: object = None   # the prefill tile layout (pack()), or None
 
     def desc(self) -> QWeightDesc:
         return QWeightDesc(FMT_CODES[self.fmt], self.num_experts, self.n, self.k, _ptr(self.codes),
-                           _ptr(self.block_scales), _ptr(self.tensor_scales))
+                           _ptr(self.block_scales), _ptr(self.tensor_scales), _ptr(self.packed))
+
+    def pack(self, role: int, stream=None) -> None:
+        """Adds the prefill tile layout of these matrices (ftmoe_pack_qweight)."""
+        import torch
+        d = self.desc()
+        d.packed = None
+        n = ctypes.c_size_t(0)
+        _check(load().ftmoe_packed_size(ctypes.byref(d), role, ctypes.byref(n)))
+        buf = torch.empty(max(256, n.value), dtype=torch.uint8, device=self.codes.device)
+        _check(load().ftmoe_pack_qweight(ctypes.byref(d), role, _ptr(buf), buf.numel(), _stream(stream)))
+        self.packed = buf
 
 
 class DeviceLayer:
@@ -163,6 +180,16 @@ class DeviceLayer:
         self.act, self.path = act, path
         self.shared_inter = shared_inter
         self.shared_gate_up, self.shared_down, self.shared_gate_w = shared_gate_up, shared_down, shared_gate_w
+
+    def pack(self) -> "DeviceLayer":
+        """Adds the prefill tile layout of every matrix set (a load-time step;
+        doubles the weights' footprint).  Returns self."""
+        self.gate_up.pack(ROLE_GATE_UP)
+        self.down.pack(ROLE_DOWN)
+        if self.shared_inter:
+            self.shared_gate_up.pack(ROLE_GATE_UP)
+            self.shared_down.pack(ROLE_DOWN)
+        return self
 
     @classmethod
     def from_host(cls, lay, device="cuda", path="auto") -> "DeviceLayer":

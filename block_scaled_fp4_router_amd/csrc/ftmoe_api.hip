@@ -123,6 +123,8 @@ ftmoe_status check_qweight(const ftmoe_qweight& q, const char* name, int fmt, in
   if (fmt == FTMOE_W_NVFP4 || fmt == FTMOE_W_FP8_E4M3) {
     if (!q.tensor_scales) return fail(FTMOE_ERR_INVALID_ARG, "%s.tensor_scales is NULL", name);
   }
+  if (q.packed && (reinterpret_cast<uintptr_t>(q.packed) & 255u))
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.packed is not 256-byte aligned", name);
   return FTMOE_OK;
 }
 
@@ -273,6 +275,7 @@ QW to_qw(const ftmoe_qweight& q) {
   w.codes = static_cast<const uint8_t*>(q.codes);
   w.scales = static_cast<const uint8_t*>(q.block_scales);
   w.tscale = q.tensor_scales;
+  w.packed = static_cast<const uint8_t*>(q.packed);
   return w;
 }
 
@@ -595,6 +598,37 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
   const bool fused_align = p.decode && p.small_route;
   FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, s));
   return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, s);
+}
+
+ftmoe_status ftmoe_packed_size(const ftmoe_qweight* w, int32_t role, size_t* bytes) {
+  g_last_error.clear();
+  if (!w || !bytes) return fail(FTMOE_ERR_INVALID_ARG, "w and bytes must be non-NULL");
+  if (role != FTMOE_ROLE_GATE_UP && role != FTMOE_ROLE_DOWN)
+    return fail(FTMOE_ERR_INVALID_ARG, "role=%d is not an ftmoe_role", role);
+  if (w->fmt != FTMOE_W_MXFP4 && w->fmt != FTMOE_W_NVFP4 && w->fmt != FTMOE_W_FP8_E4M3)
+    return fail(FTMOE_ERR_INVALID_ARG, "fmt=%d is not an ftmoe_wfmt", w->fmt);
+  if (w->num_experts < 1 || w->num_experts > kMaxExperts || w->n < 1 || w->k < 128 || w->k % 128 ||
+      w->k > kMaxDim || w->n > 2 * kMaxDim || (role == FTMOE_ROLE_GATE_UP && w->n % 256))
+    return fail(FTMOE_ERR_UNSUPPORTED, "matrix set [%d][%d][%d] has no packed layout", w->num_experts, w->n, w->k);
+  *bytes = packed_bytes(w->fmt, w->num_experts, w->n, w->k, role == FTMOE_ROLE_GATE_UP);
+  return FTMOE_OK;
+}
+
+ftmoe_status ftmoe_pack_qweight(const ftmoe_qweight* w, int32_t role, void* packed, size_t packed_bytes_,
+                                void* stream) {
+  size_t need = 0;
+  FT_TRY(ftmoe_packed_size(w, role, &need));
+  ftmoe_qweight src = *w;
+  src.packed = nullptr;   // the source is the row-major matrices
+  FT_TRY(check_qweight(src, "w", src.fmt, src.num_experts, src.n, src.k));
+  if (!packed || (reinterpret_cast<uintptr_t>(packed) & 255u))
+    return fail(FTMOE_ERR_INVALID_ARG, "packed must be non-NULL and 256-byte aligned");
+  if (packed_bytes_ < need)
+    return fail(FTMOE_ERR_INVALID_ARG, "packed holds %zu bytes, %zu needed", packed_bytes_, need);
+  FT_HIP(launch_pack_weights(to_qw(src), src.num_experts, role == FTMOE_ROLE_GATE_UP, static_cast<uint8_t*>(packed),
+                             static_cast<hipStream_t>(stream)),
+         "pack launch");
+  return FTMOE_OK;
 }
 
 ftmoe_status ftmoe_quantize_fp8_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale, void* ws,

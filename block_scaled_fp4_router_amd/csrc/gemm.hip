@@ -413,7 +413,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // 32-bit per-lane offsets from uniform bases (one expert's matrix < 4 GiB)
   const size_t wrows = static_cast<size_t>(GATEUP ? 2 * N : N);
   const uint32_t wrow_bytes = WFMT == kFP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
-  const uint8_t* const wbase = w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
+  // Weight stages come from the row-major matrices, or from the packed tile
+  // layout, where a stage of this tile is one contiguous run: codes in LDS
+  // order, then (FP4) one scale dword per tile row.
+  const bool packed = w.packed != nullptr;
+  constexpr uint32_t kPackStage = packed_stage_bytes(WFMT);
+  const uint8_t* const wbase =
+      packed ? w.packed + (static_cast<size_t>(e) * ntile + nt) * ns * kPackStage
+             : w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
+  const uint32_t badv = packed ? kPackStage : C::kBRowB;   // weight source advance per stage
   uint32_t src[C::kChunksPerWave];
 #pragma unroll
   for (int i = 0; i < C::kChunksPerWave; ++i) {
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       const int v = (c - C::kAChunks) * 64 + lane;
       const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
       const int col = tile_col(R);
-      src[i] = static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
+      src[i] = packed ? 16u * static_cast<uint32_t>(v) : static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
     }
   }
   // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
@@ -446,9 +454,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   const uint8_t* ssrc = nullptr;
   if constexpr (C::kScales) {
     const int R = wave * C::kScaleRowsPerWave + (lane < C::kScaleRowsPerWave ? lane : 0);
-    const int col = tile_col(R);
-    const size_t row = static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col);
-    ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
+    if (packed) {
+      ssrc = wbase + C::kBBytes + 4 * R;
+    } else {
+      const int col = tile_col(R);
+      const size_t row = static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col);
+      ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
+    }
   }
   // Activation scales (split activations): lanes l < kARowsPerWave of wave
   // w fetch the scale dword of tile row w * kARowsPerWave + l (two stages).
@@ -485,12 +497,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     for (int i = 0; i < C::kChunksPerWave; ++i) {
       const int c = wave + kGemmWaves * i;
       dma16((c < C::kAChunks ? ga.a : wbase) + src[i], buf + c * 1024);
-      src[i] += adv ? (c < C::kAChunks ? C::kARowB : C::kBRowB) : 0;
+      src[i] += adv ? (c < C::kAChunks ? static_cast<uint32_t>(C::kARowB) : badv) : 0;
     }
     if constexpr (C::kScales) {
       if (lane < C::kScaleRowsPerWave) dma4(ssrc, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
-      // MXFP4: stages 2m and 2m + 1 share the dword at 4m
-      ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
+      // row-major MXFP4: stages 2m and 2m + 1 share the dword at 4m
+      if (packed)
+        ssrc += adv ? kPackStage : 0;
+      else
+        ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
     }
     if constexpr (C::kSplitA) {
       if (lane < C::kARowsPerWave)
@@ -797,6 +812,82 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
   ga.amax_a = h.amax;
   ga.out = o;
   return dispatch<false>(ga, h.q != nullptr, s);
+}
+
+// ---------------------------------------------------- packed weights -----
+// The weight operand of a workgroup is a tile of kTileRows matrix rows (the
+// same for every configuration: 512), gate_up tiles pairing gate rows
+// [256 nt, 256 nt + 256) with the matching up rows.  The packed layout holds,
+// for each expert, tile and 64-wide K stage, the stage's codes in the order
+// the kernel keeps them in LDS (16-byte vector v = R * V + p of tile row R is
+// row R's vector swz(R, p)), then for FP4 one scale dword per tile row (MXFP4:
+// the dword of the stage pair; NVFP4: the stage's).  Rows past N are zero.
+constexpr int kTileRows = 512;
+static_assert(Cfg<kMXFP4, false, 128>::kBN == kTileRows && Cfg<kMXFP4, false, 64>::kBN == kTileRows &&
+                  Cfg<kNVFP4, false, 64>::kBN == kTileRows && Cfg<kFP8, true, 128>::kBN == kTileRows,
+              "one packed layout serves every tile configuration");
+
+int packed_tiles(int n, bool gate_up) {
+  return gate_up ? (n / 2 + kTileRows / 2 - 1) / (kTileRows / 2) : (n + kTileRows - 1) / kTileRows;
+}
+
+size_t packed_bytes(int fmt, int E, int n, int k, bool gate_up) {
+  return static_cast<size_t>(E) * packed_tiles(n, gate_up) * (k / kStageK) * packed_stage_bytes(fmt);
+}
+
+template <int WFMT>
+__global__ __launch_bounds__(256) void pack_weights_kernel(QW w, int E, int ntile, int gate_up, uint8_t* out) {
+  constexpr int kRowB = WFMT == kFP8 ? 64 : 32;   // bytes of a row per stage
+  constexpr int kV = kRowB / 16;
+  const int N = w.n, K = w.k, ns = K / kStageK;
+  const int st = blockIdx.x;   // (expert, tile, stage)
+  const int s = st % ns, nt = (st / ns) % ntile, e = st / (ns * ntile);
+  const int half = kTileRows / 2, I = N / 2;
+  const uint32_t row_bytes = WFMT == kFP8 ? K : K / 2;
+  uint8_t* dst = out + static_cast<size_t>(st) * packed_stage_bytes(WFMT);
+  auto row_of = [&](int R) -> int {   // matrix row of tile row R, or -1
+    if (gate_up) {
+      const int c = nt * half + (R < half ? R : R - half);
+      return c < I ? (R < half ? c : I + c) : -1;
+    }
+    const int c = nt * kTileRows + R;
+    return c < N ? c : -1;
+  };
+  for (int v = threadIdx.x; v < kTileRows * kV; v += blockDim.x) {
+    const int R = v / kV, p = v % kV;
+    const int row = row_of(R);
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (row >= 0)
+      val = *reinterpret_cast<const uint4*>(w.codes + (static_cast<size_t>(e) * N + row) * row_bytes +
+                                            static_cast<size_t>(s) * kRowB + 16 * swz<kV>(R, p));
+    reinterpret_cast<uint4*>(dst)[v] = val;
+  }
+  if constexpr (WFMT != kFP8) {
+    uint32_t* sd = reinterpret_cast<uint32_t*>(dst + kTileRows * kRowB);
+    for (int R = threadIdx.x; R < kTileRows; R += blockDim.x) {
+      const int row = row_of(R);
+      uint32_t val = 0u;
+      if (row >= 0) {
+        const size_t base = static_cast<size_t>(e) * N + row;
+        val = WFMT == kMXFP4 ? *reinterpret_cast<const uint32_t*>(w.scales + base * (K / 32) + 4 * (s / 2))
+                             : *reinterpret_cast<const uint32_t*>(w.scales + base * (K / 16) + 4 * s);
+      }
+      sd[R] = val;
+    }
+  }
+}
+
+hipError_t launch_pack_weights(const QW& w, int E, bool gate_up, uint8_t* out, hipStream_t s) {
+  if (w.k % kStageK || (gate_up && w.n % 2)) return hipErrorInvalidValue;
+  const int ntile = packed_tiles(w.n, gate_up);
+  const int blocks = E * ntile * (w.k / kStageK);
+  if (blocks == 0) return hipSuccess;
+  switch (w.fmt) {
+    case kMXFP4: return launch(pack_weights_kernel<kMXFP4>, dim3(blocks), dim3(256), 0, s, w, E, ntile, gate_up ? 1 : 0, out);
+    case kNVFP4: return launch(pack_weights_kernel<kNVFP4>, dim3(blocks), dim3(256), 0, s, w, E, ntile, gate_up ? 1 : 0, out);
+    case kFP8: return launch(pack_weights_kernel<kFP8>, dim3(blocks), dim3(256), 0, s, w, E, ntile, gate_up ? 1 : 0, out);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ------------------------------------------------- split activations ------

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace ftmoe {
 
 // ---- launches ----
@@ -40,7 +42,14 @@ struct QW {
   const uint8_t* codes;        // fp4: [E][N][K/2]; fp8: [E][N][K]
   const uint8_t* scales;       // mxfp4 [E][N][K/32]; nvfp4 [E][N][K/16]; fp8 unused
   const float* tscale;         // nvfp4 / fp8: [E]; mxfp4 unused
+  const uint8_t* packed;       // optional: the same matrices in the prefill tile layout, or NULL
 };
+
+// Bytes of one packed stage (512 tile rows x 64 K): codes, then for FP4 one
+// block-scale dword per row.
+__host__ __device__ constexpr uint32_t packed_stage_bytes(int fmt) {
+  return fmt == kFP8 ? 512u * 64u : 512u * 32u + 512u * 4u;
+}
 
 // Row source of an expert GEMM: either an expert-sorted block list (routed
 // experts) or the identity over T tokens (the shared expert).
@@ -157,6 +166,9 @@ hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, i
                               uint8_t* h_sc, uint32_t* amax_h, hipStream_t s);
 hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int H, int inter, uint16_t* o,
                             hipStream_t s);
+// Packed tile layout of a matrix set for the prefill GEMMs (see gemm.hip).
+size_t packed_bytes(int fmt, int E, int n, int k, bool gate_up);
+hipError_t launch_pack_weights(const QW& w, int E, bool gate_up, uint8_t* out, hipStream_t s);
 // Split E4M3 form of x for the MXFP4 GEMMs: xs [T][2H], xsc [T][H/32].
 hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s);
 

@@ -99,6 +99,9 @@ typedef struct {
   const void* codes;
   const void* block_scales;
   const float* tensor_scales;
+  const void* packed;   /* optional (NULL = none): the same matrices in the
+                           prefill tile layout written by ftmoe_pack_qweight,
+                           256-byte aligned; read by the prefill GEMMs only */
 } ftmoe_qweight;
 
 /* One MoE layer.
@@ -132,6 +135,27 @@ typedef struct {
   ftmoe_qweight shared_down;
   const float* shared_gate_w;
 } ftmoe_layer;
+
+/* Role of a matrix set in a layer: the prefill tile layout pairs the gate
+ * and up rows of gate_up.                                                 */
+typedef enum { FTMOE_ROLE_GATE_UP = 0, FTMOE_ROLE_DOWN = 1 } ftmoe_role;
+
+/* Prefill tile layout of one matrix set (a load-time step, for callers that
+ * run prefill).  The prefill GEMMs read the weight operand in stages of 64
+ * K for a tile of 512 matrix rows (gate_up: 256 gate rows and the 256
+ * matching up rows); in the packed layout every such stage is one
+ * contiguous run -- the codes in the order the kernel keeps them in LDS,
+ * then for FP4 one block-scale dword per row -- so it streams as whole cache
+ * lines instead of 32-byte pieces of 512 rows.  The row-major matrices stay
+ * in use (decode reads them), so a packed copy doubles the weights'
+ * footprint.  The layout is private to this library version.
+ *  ftmoe_packed_size: bytes of the packed copy of `w` in `role`.
+ *  ftmoe_pack_qweight: enqueues the repack on `stream`; `packed` is device
+ *  memory of ftmoe_packed_size bytes, 256-byte aligned; `w` is validated as
+ *  in a layer (fmt, shape, pointers; w->packed is ignored).               */
+ftmoe_status ftmoe_packed_size(const ftmoe_qweight* w, int32_t role, size_t* bytes);
+ftmoe_status ftmoe_pack_qweight(const ftmoe_qweight* w, int32_t role, void* packed, size_t packed_bytes,
+                                void* stream);
 
 /* Bytes of workspace that ftmoe_forward / ftmoe_experts_forward /
  * ftmoe_route need for T tokens of this layer (T >= 0).  The workspace must

@@ -18,10 +18,12 @@ def say(msg: str) -> None:
 
 
 @functools.lru_cache(maxsize=4)
-def layer_pair(name: str):
-    """(host layer, device layer) for a named configuration, cached."""
+def layer_pair(name: str, packed: bool = False):
+    """(host layer, device layer) for a named configuration, cached; with
+    ``packed`` the device layer also holds the prefill tile layout."""
     lay = synth.make_layer(name)
-    return lay, ft.DeviceLayer.from_host(lay, DEV)
+    dlay = ft.DeviceLayer.from_host(lay, DEV)
+    return lay, dlay.pack() if packed else dlay
 
 
 def to_dev_bf16(x_bits: np.ndarray):

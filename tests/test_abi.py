@@ -172,3 +172,44 @@ def test_status_strings():
     assert lib.ftmoe_status_string(ft.ERR_WORKSPACE) == b"FTMOE_ERR_WORKSPACE"
     assert lib.ftmoe_status_string(99) == b"FTMOE_UNKNOWN_STATUS"
     assert ft.version() >= 100
+
+
+@needs_lib
+@pytest.mark.parametrize("fmt,E,n,k,role,stage", [
+    (ft.W_MXFP4, 8, 256, 256, ft.ROLE_GATE_UP, 512 * 32 + 512 * 4),
+    (ft.W_MXFP4, 128, 1536, 2048, ft.ROLE_GATE_UP, 512 * 32 + 512 * 4),
+    (ft.W_MXFP4, 128, 2048, 768, ft.ROLE_DOWN, 512 * 32 + 512 * 4),
+    (ft.W_NVFP4, 512, 1024, 2048, ft.ROLE_GATE_UP, 512 * 32 + 512 * 4),
+    (ft.W_FP8_E4M3, 128, 3072, 4096, ft.ROLE_GATE_UP, 512 * 64),
+    (ft.W_FP8_E4M3, 128, 4096, 1536, ft.ROLE_DOWN, 512 * 64),
+])
+def test_packed_size(fmt, E, n, k, role, stage):
+    """E experts x tiles of 512 rows (gate_up: 256 gate + 256 up) x K/64 stages."""
+    tiles = -(-(n // 2) // 256) if role == ft.ROLE_GATE_UP else -(-n // 512)
+    q = ft.QWeightDesc(fmt, E, n, k, FAKE, FAKE, FAKE, None)
+    got = ctypes.c_size_t(0)
+    assert ft.load().ftmoe_packed_size(ctypes.byref(q), role, ctypes.byref(got)) == ft.OK
+    assert got.value == E * tiles * (k // 64) * stage
+
+
+@needs_lib
+def test_packed_size_rejects_bad_arguments():
+    lib = ft.load()
+    got = ctypes.c_size_t(0)
+    q = ft.QWeightDesc(ft.W_MXFP4, 8, 256, 256, FAKE, FAKE, FAKE, None)
+    assert lib.ftmoe_packed_size(ctypes.byref(q), 7, ctypes.byref(got)) == ft.ERR_INVALID_ARG
+    q.k = 100
+    assert lib.ftmoe_packed_size(ctypes.byref(q), ft.ROLE_DOWN, ctypes.byref(got)) == ft.ERR_UNSUPPORTED
+    q.k, q.fmt = 256, 9
+    assert lib.ftmoe_packed_size(ctypes.byref(q), ft.ROLE_DOWN, ctypes.byref(got)) == ft.ERR_INVALID_ARG
+    q.fmt = ft.W_MXFP4
+    # misaligned destination, and too small a destination, are refused before any launch
+    assert lib.ftmoe_pack_qweight(ctypes.byref(q), ft.ROLE_DOWN, FAKE + 16, 1 << 30, None) == ft.ERR_INVALID_ARG
+    assert lib.ftmoe_pack_qweight(ctypes.byref(q), ft.ROLE_DOWN, FAKE, 16, None) == ft.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_layer_rejects_misaligned_packed_weights():
+    d = good_layer()
+    d.gate_up.packed = FAKE + 16
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG

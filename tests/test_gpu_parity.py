@@ -117,8 +117,8 @@ def test_forward_parity_full(name, T, path):
 @pytest.mark.parametrize("name,T,nsample", [("c2", 4096, 48), ("c3", 8192, 40), ("c4", 16384, 24)])
 @pytest.mark.timeout(900)
 def test_forward_parity_full_size_sampled(name, T, nsample):
-    say(f"forward parity full size {name} T={T} (sample {nsample})")
-    lay, dlay = layer_pair(name)
+    say(f"forward parity full size {name} T={T} (sample {nsample}), packed weights as the benchmark runs")
+    lay, dlay = layer_pair(name, packed=True)
     x = synth.make_tokens(lay, T)
     y, ids, w = run_forward(dlay, x, "auto")
     tok = sample_tokens(T, nsample, seed=T)
