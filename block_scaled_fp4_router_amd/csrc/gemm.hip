@@ -38,7 +38,7 @@
 // 8-bit K [16g, 16g + 16) + [32 + 16g, 48 + 16g) in lane group g.
 //
 // Workgroups are numbered so that each XCD (workgroup w runs on XCD w % 8)
-// receives a contiguous range of (block, tile) pairs: the column tiles of a
+// receives runs of consecutive (block, tile) pairs: the column tiles of a
 // row block, and the row blocks of one expert, then share that XCD's L2.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -91,9 +91,14 @@ struct Cfg {
 };
 
 // ------------------------------------------------------------ helpers -----
-__device__ __forceinline__ int logical_tile(int w, int total) {
-  const int per = (total + 7) >> 3;
-  return (w & 7) * per + (w >> 3);
+// Workgroup w runs on XCD w % 8.  Tiles are dealt to the XCDs in chunks of
+// kXcdChunk consecutive tiles (chunk c to XCD c % 8), so each XCD's L2 sees
+// runs of tiles of the same expert, while the empty tail of the padded block
+// list (the grid covers the largest possible one) is spread over all XCDs.
+constexpr int kXcdChunk = 8;
+__device__ __forceinline__ int logical_tile(int w) {
+  const int x = w & 7, li = w >> 3;
+  return ((li / kXcdChunk) * 8 + x) * kXcdChunk + li % kXcdChunk;
 }
 
 // Position of vector q in an LDS row of V 16-byte vectors (V = 8, 4 or 2).
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   const QW& w = ga.w;
   const int K = ga.K, N = ga.N;
   const int ntile = GATEUP ? (N + C::kBN / 2 - 1) / (C::kBN / 2) : (N + C::kBN - 1) / C::kBN;
-  const int t = logical_tile(blockIdx.x, rows.num_blocks * ntile);
+  const int t = logical_tile(blockIdx.x);
   if (t >= rows.num_blocks * ntile) return;
   const int b = t / ntile, nt = t % ntile;
   const int e = rows.sorted_ids ? rows.block_expert[b] : 0;
@@ -743,7 +748,10 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
   const int total = ga.rows.num_blocks * ntile;
   if (total == 0) return hipSuccess;
   if (ga.K % kStageK) return hipErrorInvalidValue;
-  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP>, dim3(8 * ((total + 7) / 8)), dim3(kGemmThreads), 0, s, ga);
+  // whole chunks for every XCD, so that every tile index is reached
+  const int per_round = 8 * kXcdChunk;
+  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP>, dim3(per_round * ((total + per_round - 1) / per_round)),
+                dim3(kGemmThreads), 0, s, ga);
 }
 
 template <bool GATEUP>
