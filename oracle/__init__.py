@@ -13,7 +13,8 @@ weight formats MXFP4, NVFP4, FP8 and BF16 and describes a Mixture-of-Experts
 serving engine, but never writes the layer's arithmetic down.  The readings
 used here (router GEMM, softmax over the k selected logits, SwiGLU experts,
 weighted combine, sigmoid-gated shared expert, per-tensor E4M3 activations)
-are the standard routed-MoE layer; each is listed with its justification in
+are the standard routed-MoE layer, and the MXFP8 activation mode follows
+the OCP Microscaling v1.0 conversion rule; each is listed with its justification in
 the design notes.  Code tables follow the public OCP Microscaling v1.0 (E2M1,
 E8M0), OCP OFP8 (E4M3FN) and NVIDIA NVFP4 definitions.
 
@@ -44,6 +45,7 @@ from .moe import (  # noqa: F401
     align,
     align_max_padded,
     quant_act_per_tensor,
+    quant_act_mxfp8,
     swiglu_expert,
     forward,
     forward_grouped,

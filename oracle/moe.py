@@ -5,7 +5,7 @@ Inputs are duck-typed (no import of the generator): a layer object with
 ``router_w [E,H] fp32``, ``router_b [E] or None``, ``gate_up`` and ``down``
 stacked packed matrices (fields fmt, codes, block_scales, tensor_scales, n, k),
 optional ``shared_gate_up``/``shared_down``/``shared_gate_w``, and ``cfg``
-with ``top_k``, ``act`` ("bf16" | "fp8").  Hidden states are bf16 bit
+with ``top_k``, ``act`` ("bf16" | "fp8" | "mxfp8").  Hidden states are bf16 bit
 patterns (uint16).
 
 Arithmetic is float64 throughout, except where a floating-point value decides
@@ -20,11 +20,14 @@ routed SwiGLU MoE):
   2. ids_t   = the k largest logits, descending, ties to the lower index
   3. w_t     = softmax over the k selected logits
   4. sg_t    = sigmoid(x_t . w_sg)                          (shared expert)
-  5. x^      = x, or E4M3 per-tensor quantise-dequantise of x  (FP8 layers)
+  5. x^      = x, or E4M3 per-tensor quantise-dequantise of x  (FP8 layers),
+               or MXFP8 of each row of x                      (MXFP8 layers)
   6. a       = W_gu[e] x^_t ; h = silu(a[:I]) * a[I:]
-  7. h^      = h, or E4M3 per-tensor over all T*k rows of h     (FP8 layers)
+  7. h^      = h, or E4M3 per-tensor over all T*k rows of h     (FP8 layers),
+               or MXFP8 of each row of h                      (MXFP8 layers)
   8. y_t     = sum_j w_tj W_d[e_j] h^_tj   (ascending j)
-  9. y_t    += sg_t * W_ds (silu(W_gs x^_t)[:Is] * ...[Is:])    (shared expert)
+  9. y_t    += sg_t * W_ds hs^_t,  hs_t = silu(W_gs x^_t)[:Is] * ...[Is:]
+               (shared expert; hs^ = hs, or its MXFP8 form in MXFP8 layers)
 """
 from __future__ import annotations
 
@@ -132,6 +135,35 @@ def quant_act_per_tensor(v: np.ndarray):
     return e4m3_decode(codes) * np.float64(s), float(s), codes
 
 
+def quant_act_mxfp8(v: np.ndarray):
+    """MXFP8 quantise-dequantise along the last axis (OCP Microscaling v1.0:
+    E4M3 elements, one E8M0 scale per block of 32 consecutive elements).
+
+    The conversion rule of the MX specification: a block's shared exponent is
+    X = floor(log2(amax)) - 8, 8 being the largest exponent of E4M3, so the
+    block maximum lands in [256, 512) and saturates to 448 above 448.  X is
+    kept inside E8M0's range (at least -127, which is also taken for an
+    all-zero block).  Each element becomes the nearest E4M3 (ties to even,
+    saturating) of v / 2^X.  The block maximum and the quotient are fp32, the
+    precision the GPU kernels decide in; v / 2^X is exact.
+
+    Returns (dequantised float64 values, element codes uint8 of v's shape,
+    scale codes uint8 of shape [..., n / 32] holding X + 127)."""
+    v32 = np.asarray(v, np.float64).astype(np.float32)
+    n = v32.shape[-1]
+    assert n % 32 == 0, "MXFP8 blocks need a multiple of 32 elements"
+    blk = v32.reshape(*v32.shape[:-1], n // 32, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex with m in [0.5, 1)
+    X = np.where(amax > 0, ex - 1 - 8, -127)
+    X = np.maximum(X, -127)
+    q = blk * np.ldexp(1.0, -X)[..., None]       # exact power-of-two scaling
+    codes = e4m3_encode_nearest(q.astype(np.float32))
+    deq = e4m3_decode(codes) * np.ldexp(1.0, X)[..., None]
+    return (deq.reshape(v32.shape), codes.reshape(v32.shape),
+            (X + 127).astype(np.uint8))
+
+
 # ---------------------------------------------------------------- experts --
 
 
@@ -161,6 +193,30 @@ def _is_fp8_act(lay) -> bool:
     return getattr(lay.cfg, "act", "bf16") == "fp8"
 
 
+def _is_mxfp8_act(lay) -> bool:
+    return getattr(lay.cfg, "act", "bf16") == "mxfp8"
+
+
+def _quant_x(lay, xf):
+    """x^ of step 5."""
+    if _is_fp8_act(lay):
+        return quant_act_per_tensor(xf)[0]
+    if _is_mxfp8_act(lay):
+        return quant_act_mxfp8(xf)[0]
+    return xf
+
+
+def _quant_rows_mx(lay, h):
+    """h^ of MXFP8 layers: every row of h (last axis) on its own."""
+    return quant_act_mxfp8(h)[0] if _is_mxfp8_act(lay) else h
+
+
+def _shared_out(lay, wgs, wds, xr):
+    """Shared expert output W_ds hs^ for rows xr (step 9)."""
+    hs = swiglu_expert(wgs, wds, xr)[0]
+    return _quant_rows_mx(lay, hs) @ wds.T
+
+
 def forward(lay, x_bits: np.ndarray) -> dict:
     """Per-token mode: the literal loop over tokens and their k experts.
     FP8-activation layers need the amax of h over every token, so this mode
@@ -168,7 +224,7 @@ def forward(lay, x_bits: np.ndarray) -> dict:
     xf, lg, ids, w, sg = _routing(lay, x_bits)
     T, H = xf.shape
     k = lay.cfg.top_k
-    xq = quant_act_per_tensor(xf)[0] if _is_fp8_act(lay) else xf
+    xq = _quant_x(lay, xf)
     cache = {}
 
     def W(qw, e):
@@ -185,6 +241,7 @@ def forward(lay, x_bits: np.ndarray) -> dict:
             h[t, j] = swiglu_expert(W(lay.gate_up, e), W(lay.down, e), xq[t])[0]
     if _is_fp8_act(lay):
         h = quant_act_per_tensor(h)[0].reshape(h.shape)
+    h = _quant_rows_mx(lay, h)
     y = np.zeros((T, H))
     for t in range(T):
         acc = np.zeros(H)
@@ -195,7 +252,7 @@ def forward(lay, x_bits: np.ndarray) -> dict:
     if sg is not None:
         wgs, wds = dequant(lay.shared_gate_up, 0), dequant(lay.shared_down, 0)
         for t in range(T):
-            y[t] = y[t] + sg[t] * swiglu_expert(wgs, wds, xq[t])[1]
+            y[t] = y[t] + sg[t] * _shared_out(lay, wgs, wds, xq[t])
     return dict(y=y, ids=ids, w=w, logits=lg, sgate=sg)
 
 
@@ -210,7 +267,7 @@ def forward_grouped(lay, x_bits: np.ndarray, tokens=None, dtype=np.float64) -> d
     k = lay.cfg.top_k
     E = lay.router_w.shape[0]
     fp8 = _is_fp8_act(lay)
-    xq = quant_act_per_tensor(xf)[0] if fp8 else xf
+    xq = _quant_x(lay, xf)
     sel = np.arange(T) if tokens is None else np.asarray(tokens)
     flat = ids.reshape(-1)
     I = lay.gate_up.n // 2
@@ -230,7 +287,7 @@ def forward_grouped(lay, x_bits: np.ndarray, tokens=None, dtype=np.float64) -> d
         wgu = dequant(lay.gate_up, e).astype(dtype)
         a = xq[rows // k].astype(dtype) @ wgu.T
         g, u = a[:, :I].astype(np.float64), a[:, I:].astype(np.float64)
-        h = _silu(g) * u
+        h = _quant_rows_mx(lay, _silu(g) * u)
         if fp8:
             h_amax = max(h_amax, float(np.abs(h.astype(np.float32)).max()))
             keep = need[rows // k]
@@ -254,7 +311,7 @@ def forward_grouped(lay, x_bits: np.ndarray, tokens=None, dtype=np.float64) -> d
         wds = dequant(lay.shared_down, 0).astype(dtype)
         Is = wgs.shape[0] // 2
         a = (xq[sel].astype(dtype) @ wgs.T).astype(np.float64)
-        hs = _silu(a[:, :Is]) * a[:, Is:]
+        hs = _quant_rows_mx(lay, _silu(a[:, :Is]) * a[:, Is:])
         y[sel] += sg[sel, None] * (hs.astype(dtype) @ wds.T).astype(np.float64)
     out = dict(y=y[sel], ids=ids, w=w, logits=lg, sgate=sg)
     if fp8:
@@ -268,7 +325,7 @@ def forward_tokens(lay, x_bits: np.ndarray, tokens, s_h=None) -> np.ndarray:
     from ``forward_grouped`` over the full batch."""
     xf, lg, ids, w, sg = _routing(lay, x_bits)
     fp8 = _is_fp8_act(lay)
-    xq = quant_act_per_tensor(xf)[0] if fp8 else xf
+    xq = _quant_x(lay, xf)
     k = lay.cfg.top_k
     out = np.zeros((len(tokens), xf.shape[1]))
     cache = {}
@@ -288,9 +345,10 @@ def forward_tokens(lay, x_bits: np.ndarray, tokens, s_h=None) -> np.ndarray:
             if fp8:
                 s = np.float32(s_h)
                 h = e4m3_decode(e4m3_encode_nearest(h.astype(np.float32) / s)) * np.float64(s)
+            h = _quant_rows_mx(lay, h)
             acc = acc + w[t, j] * (wd @ h)
         if sg is not None:
-            acc = acc + sg[t] * swiglu_expert(W(lay.shared_gate_up, 0), W(lay.shared_down, 0), xq[t])[1]
+            acc = acc + sg[t] * _shared_out(lay, W(lay.shared_gate_up, 0), W(lay.shared_down, 0), xq[t])
         out[r] = acc
     return out
 
@@ -298,20 +356,26 @@ def forward_tokens(lay, x_bits: np.ndarray, tokens, s_h=None) -> np.ndarray:
 # ----------------------------------------------- independent formulations --
 
 
-def dense_swiglu(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, x: np.ndarray):
+def dense_swiglu(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, x: np.ndarray, qh=None):
     """A dense SwiGLU MLP with separate gate/up matrices:
-    W_down (silu(W_gate x) * (W_up x)), row-wise over x."""
+    W_down q(silu(W_gate x) * (W_up x)), row-wise over x; q is the identity
+    unless given."""
     g = x @ w_gate.T
     u = x @ w_up.T
-    return (g / (1.0 + np.exp(-g)) * u) @ w_down.T
+    h = g / (1.0 + np.exp(-g)) * u
+    return (h if qh is None else qh(h)) @ w_down.T
 
 
 def forward_all_experts_masked(lay, x_bits: np.ndarray) -> np.ndarray:
     """Brute force for tiny layers: every expert runs on every token and the
     results are mixed by a dense [T, E] matrix that is zero except on the
     k selected experts, where it holds the renormalised weights.
-    Only for bf16-activation layers (no per-tensor h scale)."""
+    For bf16 and MXFP8 activations (whose quantisation acts on each row
+    alone); not for per-tensor FP8, whose h scale spans the routed rows."""
+    assert not _is_fp8_act(lay)
     xf = bf16_to_f64(x_bits)
+    mx = _is_mxfp8_act(lay)
+    qh = (lambda h: quant_act_mxfp8(h)[0]) if mx else None
     lg = router_logits(lay, xf)
     T, E = lg.shape
     k = lay.cfg.top_k
@@ -323,12 +387,13 @@ def forward_all_experts_masked(lay, x_bits: np.ndarray) -> np.ndarray:
         M[t, top] = p / p.sum()
     y = np.zeros((T, xf.shape[1]))
     I = lay.gate_up.n // 2
+    xin = quant_act_mxfp8(xf)[0] if mx else xf
     for e in range(E):
         wgu = dequant(lay.gate_up, e)
-        y += M[:, e:e + 1] * dense_swiglu(wgu[:I], wgu[I:], dequant(lay.down, e), xf)
+        y += M[:, e:e + 1] * dense_swiglu(wgu[:I], wgu[I:], dequant(lay.down, e), xin, qh)
     if getattr(lay, "shared_gate_w", None) is not None:
         wgs = dequant(lay.shared_gate_up, 0)
         Is = wgs.shape[0] // 2
         sg = 1.0 / (1.0 + np.exp(-(xf @ np.asarray(lay.shared_gate_w, np.float64))))
-        y += sg[:, None] * dense_swiglu(wgs[:Is], wgs[Is:], dequant(lay.shared_down, 0), xf)
+        y += sg[:, None] * dense_swiglu(wgs[:Is], wgs[Is:], dequant(lay.shared_down, 0), xin, qh)
     return y

@@ -184,7 +184,7 @@ class LayerConfig:
     top_k: int
     inter: int
     fmt: str
-    act: str = "bf16"             # "bf16" | "fp8"  (per-tensor E4M3 activations)
+    act: str = "bf16"             # "bf16" | "fp8" (per-tensor E4M3) | "mxfp8" (E4M3 + E8M0 per 32)
     shared_inter: int = 0
     router_std: Optional[float] = None   # None -> 1/sqrt(hidden)
     zipf_s: Optional[float] = None

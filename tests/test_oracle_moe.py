@@ -71,6 +71,89 @@ def test_single_expert_fp8_activations_match_torch_quantiser():
     assert np.abs(r["y"] - ref).max() <= 1e-12 * np.abs(ref).max()
 
 
+def _torch_mxfp8(v64):
+    """MXFP8 quantise-dequantise by torch ops: block exponent from
+    torch.frexp, elements through torch's float8_e4m3fn conversion."""
+    v = v64.to(torch.float32)
+    b = v.reshape(*v.shape[:-1], -1, 32)
+    amax = b.abs().amax(-1)
+    _, ex = torch.frexp(amax)
+    X = torch.where(amax > 0, ex.to(torch.int64) - 9, torch.full_like(ex, -127, dtype=torch.int64)).clamp(min=-127)
+    p2 = torch.pow(torch.tensor(2.0, dtype=torch.float64), X.to(torch.float64))[..., None]
+    q = (b.double() / p2).to(torch.float32).clamp(-448, 448).to(torch.float8_e4m3fn)
+    return (q.to(torch.float64) * p2).reshape(v.shape), q.view(torch.uint8).reshape(v.shape), X
+
+
+def test_single_expert_mxfp8_activations_match_torch_quantiser():
+    """E=1, k=1 with MXFP8 activations (and a shared expert): x, h and the
+    shared expert's h go through the torch MXFP8 quantiser above."""
+    lay = tiny("mxfp4", E=1, k=1, H=64, I=64, act="mxfp8", shared=32)
+    x = make_tokens(lay, 12)
+    r = oracle.forward(lay, x)
+    xf = _t(oracle.bf16_to_f64(x))
+    xt = _torch_mxfp8(xf)[0]
+    h, wd = _torch_dense(lay, 0, xt)
+    ref = F.linear(_torch_mxfp8(h)[0], wd)
+    wgs = _t(oracle.dequant(lay.shared_gate_up, 0))
+    wds = _t(oracle.dequant(lay.shared_down, 0))
+    a = F.linear(xt, wgs)
+    hs = F.silu(a[:, :32]) * a[:, 32:]
+    sg = torch.sigmoid(xf @ _t(lay.shared_gate_w))
+    ref = ref + sg[:, None] * F.linear(_torch_mxfp8(hs)[0], wds)
+    assert np.abs(r["y"] - ref.numpy()).max() <= 1e-12 * np.abs(ref.numpy()).max()
+
+
+def test_mxfp8_quantiser_definition():
+    """Block exponent by its defining inequality 2^(X+8) <= amax < 2^(X+9)
+    (X = -127 for a zero block and below E8M0's range), element codes and
+    values against torch's E4M3 conversion."""
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((6, 8, 32)) * np.exp2(rng.integers(-20, 20, (6, 8, 1)))
+    v[0, 0] = 0.0                       # zero block
+    v[0, 1] = 0.0
+    v[0, 1, 5] = 2.0 ** -130            # fp32 subnormal maximum
+    v[0, 2, :] = 1e-3
+    v[0, 2, 7] = 2.0 ** -118            # exponent clamped at -127
+    v[0, 3, :] = 0.1
+    v[0, 3, 3] = 8.0                    # amax an exact power of two: X = 3 - 8
+    v[0, 4, :] = 0.1
+    v[0, 4, 9] = -15.5                  # X = -5 and 15.5 * 32 = 496 saturates to 448
+    v = v.reshape(6, 256)
+    deq, codes, sc = oracle.quant_act_mxfp8(v)
+    assert sc.shape == (6, 8) and codes.shape == v.shape
+    v32 = v.astype(np.float32).astype(np.float64)
+    for r in range(6):
+        for b in range(8):
+            amax = np.abs(v32[r, 32 * b:32 * b + 32]).max()
+            X = int(sc[r, b]) - 127
+            if amax == 0 or amax < 2.0 ** -119:
+                assert X == -127
+            else:
+                assert 2.0 ** (X + 8) <= amax < 2.0 ** (X + 9)
+    assert int(sc[0, 3]) - 127 == 3 - 8
+    tq, tc, tX = _torch_mxfp8(torch.from_numpy(v))
+    assert np.array_equal(tX.numpy() + 127, sc.astype(np.int64))
+    assert np.array_equal(tc.numpy(), codes)
+    assert np.array_equal(tq.numpy(), deq)
+    assert deq[0, 3 * 32 + 3] == 8.0 and codes[0, 3 * 32 + 3] == 0x78
+    assert int(sc[0, 4]) - 127 == -5 and deq[0, 4 * 32 + 9] == -448 * 2.0 ** -5
+
+
+def test_mxfp8_hand_example():
+    """One block worked by hand: amax 1.9 gives X = -8 (floor(log2 1.9) = 0);
+    1.9 * 256 = 486.4 saturates to 448 (value 1.75); 1.0 -> 256 = 2^8 (code
+    0x78: exponent field 15, mantissa 0); 0.5 -> 128 (0x70); 0.001 * 256 =
+    0.256 -> 0.25 = 2^-2 (0x28); -0.3 * 256 = -76.8 -> -80 (sign 1, exponent
+    field 13, mantissa 2: 0xEA, since 72 < 76.8 and 80 - 76.8 < 76.8 - 72)."""
+    v = np.zeros(32)
+    v[:5] = [1.9, 1.0, 0.5, 0.001, -0.3]
+    deq, codes, sc = oracle.quant_act_mxfp8(v)
+    assert sc.tolist() == [127 - 8]
+    assert codes[:5].tolist() == [0x7E, 0x78, 0x70, 0x28, 0xEA]
+    assert np.array_equal(deq[:5], [1.75, 1.0, 0.5, 2.0 ** -10, -80 / 256])
+    assert np.all(codes[5:] == 0) and np.all(deq[5:] == 0)
+
+
 def test_k_equal_E_gives_full_softmax():
     lay = tiny(E=4, k=4)
     x = make_tokens(lay, 8)
@@ -90,16 +173,17 @@ def test_router_logits_match_torch_linear_with_bias():
     assert np.abs(oracle.router_logits(lay, xf) - ref).max() <= 1e-13
 
 
-@pytest.mark.parametrize("fmt,shared", [("mxfp4", 0), ("nvfp4", 32), ("fp8", 0)])
-def test_brute_force_all_experts_masked(fmt, shared):
-    lay = tiny(fmt, E=8, k=3, H=64, I=32, shared=shared)
+@pytest.mark.parametrize("fmt,act,shared", [("mxfp4", "bf16", 0), ("nvfp4", "bf16", 32), ("fp8", "bf16", 0),
+                                            ("mxfp4", "mxfp8", 32)])
+def test_brute_force_all_experts_masked(fmt, act, shared):
+    lay = tiny(fmt, E=8, k=3, H=64, I=32, shared=shared, act=act)
     x = make_tokens(lay, 16)
     r = oracle.forward(lay, x)
     b = oracle.forward_all_experts_masked(lay, x)
     assert np.abs(r["y"] - b).max() <= 1e-12 * np.abs(b).max()
 
 
-@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("act", ["bf16", "fp8", "mxfp8"])
 def test_token_permutation_is_bitwise(act):
     lay = tiny("fp8" if act == "fp8" else "mxfp4", E=8, k=2, act=act)
     x = make_tokens(lay, 16)
@@ -134,7 +218,8 @@ def test_topk_matches_full_sort_and_breaks_ties_low_index():
     assert ids[0, :3].tolist() == [3, 9, 12]
 
 
-@pytest.mark.parametrize("fmt,act,shared", [("mxfp4", "bf16", 0), ("nvfp4", "bf16", 32), ("fp8", "fp8", 0)])
+@pytest.mark.parametrize("fmt,act,shared", [("mxfp4", "bf16", 0), ("nvfp4", "bf16", 32), ("fp8", "fp8", 0),
+                                            ("mxfp4", "mxfp8", 32)])
 def test_grouped_mode_matches_per_token_mode(fmt, act, shared):
     lay = tiny(fmt, E=8, k=2, act=act, shared=shared)
     x = make_tokens(lay, 24)
