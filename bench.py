@@ -32,8 +32,11 @@ METRIC = "MoE-layer tokens/s (prefill) + decode expert-weight GB/s, % of MI355X 
 # activations as a pair of E4M3 codes per element (as exact as bf16) on the
 # E8M0-scaled MFMA (two MFMAs per product, so its roofline is the bf16 one);
 # NVFP4 dequantises exactly to bf16; FP8 W8A8 runs E4M3 x E4M3.
+# MXFP8 activations (W4A8) meet MXFP4 codes on one scaled MFMA per product,
+# at the 8-bit operand rate (FP8 roofline).
 DTYPE = {"mxfp4": "e2m1 x e4m3-pair mfma/fp32-acc", "nvfp4": "bf16-mfma/fp32-acc",
-         "fp8": "bf16-mfma/fp32-acc", "fp8act": "fp8-e4m3-mfma/fp32-acc"}
+         "fp8": "bf16-mfma/fp32-acc", "fp8act": "fp8-e4m3-mfma/fp32-acc",
+         "mxfp8act": "e2m1 x mxfp8-e4m3 mfma/fp32-acc"}
 
 WORKLOADS = {
     # name: (config, T, kind)
@@ -43,6 +46,8 @@ WORKLOADS = {
     "c2": ("c2", 4096, "prefill"),
     "c3": ("c3", 8192, "prefill"),
     "c4": ("c4", 16384, "prefill"),
+    "c1-w4a8": ("c1-w4a8", 8, "decode"),
+    "c2-w4a8": ("c2-w4a8", 4096, "prefill"),
 }
 
 
@@ -53,6 +58,8 @@ def describe(cfg, T):
         s += f", shared expert (intermediate {cfg.shared_inter})"
     if cfg.act == "fp8":
         s += ", per-tensor E4M3 activations"
+    if cfg.act == "mxfp8":
+        s += ", MXFP8 activations (W4A8)"
     if cfg.zipf_s:
         s += f", Zipf({cfg.zipf_s}) router bias"
     return s
@@ -176,7 +183,7 @@ def main() -> int:
         dom = "gemm_gateup"
         flops = 2.0 * T * k * H * 2 * I
         achieved = flops / (kernel_us[dom] * 1e-6) / 1e12
-        peak = MFMA_PEAK_TFLOPS["fp8" if cfg.act == "fp8" else "bf16"]
+        peak = MFMA_PEAK_TFLOPS["fp8" if cfg.act in ("fp8", "mxfp8") else "bf16"]
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
                 "algorithmic_flops_per_launch": flops, "avg_launch_us": round(kernel_us[dom], 3)}
@@ -184,7 +191,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": DTYPE[cfg.fmt if cfg.act != "fp8" else "fp8act"],
+        "vs_baseline": None, "dtype": DTYPE[cfg.fmt if cfg.act == "bf16" else cfg.act + "act"],
         "data": "synthetic (seeded generator; random-init weights quantised to the named format)",
         "config": {"workload": describe(cfg, T), "kind": kind, "tokens": T, "layer_copies_cycled": ring,
                    "token_batches_cycled": nb, "path": args.path,
@@ -203,7 +210,7 @@ def main() -> int:
     return 0
 
 
-PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64}
+PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64, "c2-w4a8": 128}
 
 
 def cpu_baseline(lay, xs, kind, T, sample_tokens, sel_bytes, seconds):

@@ -23,12 +23,12 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 # ftmoe_wfmt
 W_MXFP4, W_NVFP4, W_FP8_E4M3 = 1, 2, 3
 # ftmoe_afmt
-ACT_BF16, ACT_FP8_PER_TENSOR = 0, 1
+ACT_BF16, ACT_FP8_PER_TENSOR, ACT_MXFP8 = 0, 1, 2
 # ftmoe_path
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 FMT_CODES = {"mxfp4": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8_E4M3}
-ACT_CODES = {"bf16": ACT_BF16, "fp8": ACT_FP8_PER_TENSOR}
+ACT_CODES = {"bf16": ACT_BF16, "fp8": ACT_FP8_PER_TENSOR, "mxfp8": ACT_MXFP8}
 PATH_CODES = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL}
 
 # Every symbol include/ftmoe.h declares.

@@ -164,6 +164,58 @@ __device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi,
   *sc = static_cast<uint8_t>(code);
 }
 
+// ------------------------------------------------ MXFP8 activation blocks --
+// OCP Microscaling v1.0 conversion of a block of 32 values to E4M3 elements
+// under one E8M0 scale 2^X: X = floor(log2 amax) - 8 (8 being E4M3's largest
+// exponent), at least -127; each element is the nearest E4M3 of v / 2^X,
+// saturating at 448.  The scale is returned as its E8M0 code X + 127 (the
+// biased exponent field of amax minus 8, clamped at 0).
+__device__ __forceinline__ uint32_t mxfp8_scale_code(float amax) {
+  const int ebits = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
+  return static_cast<uint32_t>(ebits > 8 ? ebits - 8 : 0);
+}
+
+// Converts one 32-block of bf16 values (4 vectors of 8) to 32 E4M3 codes
+// (16-byte aligned destination, global or LDS) and the scale code.
+__device__ __forceinline__ void mxfp8_block(const uint4 (&v)[4], uint8_t* q, uint8_t* sc) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[c] & 0xFFFF)));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[c] >> 16)));
+    }
+  }
+  const uint32_t code = mxfp8_scale_code(amax);
+  const float inv = mx_inv_scale(code);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const uint32_t p0 = f32x2_to_e4m3x2(bf16_to_f32(w[0] & 0xFFFF) * inv, bf16_to_f32(w[0] >> 16) * inv);
+    const uint32_t p1 = f32x2_to_e4m3x2(bf16_to_f32(w[1] & 0xFFFF) * inv, bf16_to_f32(w[1] >> 16) * inv);
+    const uint32_t p2 = f32x2_to_e4m3x2(bf16_to_f32(w[2] & 0xFFFF) * inv, bf16_to_f32(w[2] >> 16) * inv);
+    const uint32_t p3 = f32x2_to_e4m3x2(bf16_to_f32(w[3] & 0xFFFF) * inv, bf16_to_f32(w[3] >> 16) * inv);
+    o[2 * i] = p0 | (p1 << 16);
+    o[2 * i + 1] = p2 | (p3 << 16);
+  }
+  reinterpret_cast<uint4*>(q)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4*>(q)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  *sc = static_cast<uint8_t>(code);
+}
+
+// Largest value over the 32 lanes of each half-wave (ds_swizzle butterfly).
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return v;
+}
+
 // ------------------------------------------------------------ wave ops ----
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -18,8 +18,10 @@
 //
 // MXFP4 weights go to v_mfma_scale_f32_16x16x128_f8f6f4 as raw E2M1 codes
 // with their E8M0 block scales, against activations carried as split E4M3
-// pairs (common.hpp); no weight is dequantised.  The gate_up workgroup covers one 32-block of h per token slot, so it writes
-// h directly in the split form the down kernel consumes.
+// pairs (common.hpp), or in the MXFP8 activation mode as single E4M3 codes
+// under E8M0 block scales (one MFMA per chunk instead of two); no weight is
+// dequantised.  The gate_up workgroup covers one 32-block of h per token
+// slot, so it writes h directly in the form the down kernel consumes.
 //
 // NVFP4 (E4M3 block scales, not expressible as E8M0) and FP8 weights with
 // bf16 activations are dequantised to bf16 in registers for
@@ -96,18 +98,18 @@ __device__ __forceinline__ void dma_rows(uint8_t* lds, int rows, int rowvec, Row
   });
 }
 
-// DMA of split rows: hi [rows][K], lo [rows][K] (swizzled) and the scale rows
-// [rows][spitch] (plain), consecutive in LDS.  Row r of the source is row
-// src_row(r) of hi / lo ([.][K]) and of sc ([.][spitch]).
+// DMA of split rows: hi [rows][K], lo [rows][K] (swizzled; absent when lo is
+// NULL) and the scale rows [rows][spitch] (plain), consecutive in LDS.  Row r
+// of the source is row src_row(r) of hi / lo ([.][K]) and of sc ([.][spitch]).
 template <class SrcRow>
 __device__ __forceinline__ void dma_split_rows(uint8_t* lds, int rows, int K, int spitch, const uint8_t* hi,
                                                const uint8_t* lo, const uint8_t* sc, SrcRow src_row) {
-  const int hv = K / 16, sv = spitch / 16, nh = rows * hv;
+  const int hv = K / 16, sv = spitch / 16, nh = rows * hv, ncode = lo ? 2 * nh : nh;
   const float inv_h = 1.0f / static_cast<float>(hv), inv_s = 1.0f / static_cast<float>(sv);
-  dma_stage(lds, 2 * nh + rows * sv, [&](int v) -> const void* {
-    const bool is_sc = v >= 2 * nh, is_lo = !is_sc && v >= nh;
+  dma_stage(lds, ncode + rows * sv, [&](int v) -> const void* {
+    const bool is_sc = v >= ncode, is_lo = !is_sc && v >= nh;
     int r, s;
-    split_index(is_sc ? v - 2 * nh : is_lo ? v - nh : v, is_sc ? sv : hv, is_sc ? inv_s : inv_h, r, s);
+    split_index(is_sc ? v - ncode : is_lo ? v - nh : v, is_sc ? sv : hv, is_sc ? inv_s : inv_h, r, s);
     // src_row may be a cross-lane shuffle: every lane evaluates it, outside
     // any branch on the lane's region
     const size_t row = static_cast<size_t>(src_row(r));
@@ -149,7 +151,8 @@ __device__ __forceinline__ LaneSlot slot_decode(const DecodeArgs& a, bool shared
 }
 
 // ======================================================== MXFP4 kernels ====
-// Split rows in LDS: hi / lo codes [rows][K] (swizzled), scales [rows][spitch].
+// Activation rows in LDS: hi / lo codes [rows][K] (swizzled), scales
+// [rows][spitch]; with MXFP8 activations (A8) only one code plane.
 struct MxRows {
   const uint8_t* hi;
   const uint8_t* lo;
@@ -157,12 +160,15 @@ struct MxRows {
   int K, spitch;
 };
 
+template <bool A8>
 __device__ __forceinline__ MxRows mx_rows(const uint8_t* base, int K, int spitch, int rows) {
-  return MxRows{base, base + rows * K, base + 2 * rows * K, K, spitch};
+  constexpr int kPlanes = A8 ? 1 : 2;
+  return MxRows{base, base + rows * K, base + kPlanes * rows * K, K, spitch};
 }
 
+template <bool A8>
 __host__ __device__ constexpr size_t mx_rows_bytes(int K, int spitch, int rows) {
-  return static_cast<size_t>(rows) * (2 * K + spitch);
+  return static_cast<size_t>(rows) * ((A8 ? 1 : 2) * K + spitch);
 }
 
 // Weight stream of NB chunks of one row: lane group g holds K block 4u + g
@@ -207,7 +213,9 @@ __device__ __forceinline__ int mx_wscale(const MxW<NB, PACK>& w, int u, int g) {
 }
 
 // MFMA chunk u (K [128u, 128u + 128)): A from LDS row r (zero unless
-// `valid`), hi then lo with the scale lowered by 2^4.
+// `valid`), hi then lo with the scale lowered by 2^4; with A8 the single
+// MXFP8 codes.
+template <bool A8>
 __device__ __forceinline__ void mx_mma(const MxRows& m, int r, bool valid, int u, int g, const uint4& wc, int sb,
                                        f32x4& acc) {
   i32x8 ah = {}, al = {};
@@ -215,31 +223,35 @@ __device__ __forceinline__ void mx_mma(const MxRows& m, int r, bool valid, int u
   if (valid) {
     const int q0 = 8 * u + g, q1 = q0 + 4;
     const uint8_t* rh = m.hi + r * m.K;
-    const uint8_t* rl = m.lo + r * m.K;
     ah = u4x2(lds16(rh, r, q0), lds16(rh, r, q1));
-    al = u4x2(lds16(rl, r, q0), lds16(rl, r, q1));
+    if constexpr (!A8) {
+      const uint8_t* rl = m.lo + r * m.K;
+      al = u4x2(lds16(rl, r, q0), lds16(rl, r, q1));
+    }
     sa = m.sc[r * m.spitch + 4 * u + g];
   }
-  const int sa_lo = sa >= 4 ? sa - 4 : 0;
   const i32x8 b = {static_cast<int>(wc.x), static_cast<int>(wc.y), static_cast<int>(wc.z), static_cast<int>(wc.w),
                    0, 0, 0, 0};
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, acc, 0, 4, 0, sa, 0, sb);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc, 0, 4, 0, sa_lo, 0, sb);
+  if constexpr (!A8) {
+    const int sa_lo = sa >= 4 ? sa - 4 : 0;
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, b, acc, 0, 4, 0, sa_lo, 0, sb);
+  }
 }
 
 // Streams one weight row (nch chunks) against LDS rows; the first NB chunks
 // are already loaded.
-template <int NB, bool PACK>
+template <int NB, bool PACK, bool A8>
 __device__ __forceinline__ void mx_row_dot(MxW<NB, PACK>& wt, const uint8_t* codes, const uint8_t* scales,
                                            const MxRows& m, int r, bool valid, int nch, int g, f32x4& acc) {
 #pragma unroll
   for (int u = 0; u < NB; ++u)
-    if (u < nch) mx_mma(m, r, valid, u, g, wt.c[u], mx_wscale(wt, u, g), acc);
+    if (u < nch) mx_mma<A8>(m, r, valid, u, g, wt.c[u], mx_wscale(wt, u, g), acc);
   for (int u0 = NB; u0 < nch; u0 += NB) {
     mx_wload(wt, codes, scales, u0, nch, g);
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (u0 + u < nch) mx_mma(m, r, valid, u0 + u, g, wt.c[u], mx_wscale(wt, u, g), acc);
+      if (u0 + u < nch) mx_mma<A8>(m, r, valid, u0 + u, g, wt.c[u], mx_wscale(wt, u, g), acc);
   }
 }
 
@@ -256,12 +268,12 @@ __device__ __forceinline__ HSplit h_split_rows(const DecodeArgs& a, bool shared,
   const size_t routed = static_cast<size_t>(a.nb_routed) * kDecodeBM;
   const size_t off = shared ? routed * a.I + static_cast<size_t>(row0) * a.Is : static_cast<size_t>(row0) * a.I;
   const size_t srow = shared ? routed + row0 : row0;
-  return HSplit{a.hhi + off, a.hlo + off, a.hsc + srow * a.hsc_pitch, shared ? a.Is : a.I};
+  return HSplit{a.hhi + off, a.hlo ? a.hlo + off : nullptr, a.hsc + srow * a.hsc_pitch, shared ? a.Is : a.I};
 }
 
 // gate_up: 4 waves, each on 8 intermediate indices (8 gate + 8 up rows); the
-// token rows arrive already split (xhi / xlo / xsc).
-template <int NB, bool PACK>
+// token rows arrive already split (xhi / xlo / xsc), or as MXFP8 (A8).
+template <int NB, bool PACK, bool A8>
 __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float red[kGateWaves][kDecodeBM];
@@ -290,21 +302,23 @@ __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(Decod
   const LaneSlot ls = slot_decode(a, shared, p0, raw);
   // 2. the split token rows of the valid slots -> LDS rows 0 .. count - 1
   const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
-  const MxRows m = mx_rows(smem, H, a.xsc_pitch, count);
-  dma_split_rows(smem, count, H, a.xsc_pitch, a.xhi, a.xlo, a.xsc, [&](int r) { return __shfl(ls.tok, r, kWave); });
+  const MxRows m = mx_rows<A8>(smem, H, a.xsc_pitch, count);
+  dma_split_rows(smem, count, H, a.xsc_pitch, a.xhi, A8 ? nullptr : a.xlo, a.xsc,
+                 [&](int r) { return __shfl(ls.tok, r, kWave); });
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mx_row_dot(wt, codes, scales, m, j, j < count, nch, g, acc);
+  mx_row_dot<NB, PACK, A8>(wt, codes, scales, m, j, j < count, nch, g, acc);
 
-  // 3. h = SwiGLU(gate, up) rounded to bf16, then split per 32-block: lanes
-  //    j < 8 hold column i0 + j of slots 4g + r; the 32-block of a slot spans
-  //    the 4 waves.
+  // 3. h = SwiGLU(gate, up) (rounded to bf16 for the split form), then
+  //    quantised per 32-block: lanes j < 8 hold column i0 + j of slots
+  //    4g + r; the 32-block of a slot spans the 4 waves.
   float hv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float up = __shfl_xor(acc[r], 8, kWave);
-    const float v = bf16_to_f32(f32_to_bf16(swiglu(acc[r], up)));
+    const float sw = swiglu(acc[r], up);
+    const float v = A8 ? sw : bf16_to_f32(f32_to_bf16(sw));
     hv[r] = j < 8 ? v : 0.f;
     float mx = __builtin_fabsf(hv[r]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, kWave));
@@ -321,19 +335,25 @@ __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(Decod
       float amax = red[0][slot];
 #pragma unroll
       for (int q = 1; q < kGateWaves; ++q) amax = __builtin_fmaxf(amax, red[q][slot]);
-      const uint32_t code = mx_split_scale_code(amax);
-      uint32_t h2, l2;
-      mx_split_pair(hv[r] * mx_inv_scale(code), 0.f, &h2, &l2);
       const size_t o = static_cast<size_t>(slot) * hs.K + i0 + j;
-      hs.hi[o] = static_cast<uint8_t>(h2 & 0xFF);
-      hs.lo[o] = static_cast<uint8_t>(l2 & 0xFF);
+      uint32_t code;
+      if constexpr (A8) {
+        code = mxfp8_scale_code(amax);
+        hs.hi[o] = static_cast<uint8_t>(f32x2_to_e4m3x2(hv[r] * mx_inv_scale(code), 0.f) & 0xFF);
+      } else {
+        code = mx_split_scale_code(amax);
+        uint32_t h2, l2;
+        mx_split_pair(hv[r] * mx_inv_scale(code), 0.f, &h2, &l2);
+        hs.hi[o] = static_cast<uint8_t>(h2 & 0xFF);
+        hs.lo[o] = static_cast<uint8_t>(l2 & 0xFF);
+      }
       if (wave == 0 && j == 0) hs.sc[static_cast<size_t>(slot) * a.hsc_pitch + c0 / 32] = static_cast<uint8_t>(code);
     }
   }
 }
 
-// down: 16 output rows per wave against the block's split h rows.
-template <int NB, bool PACK>
+// down: 16 output rows per wave against the block's split (or MXFP8) h rows.
+template <int NB, bool PACK, bool A8>
 __global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int b = blockIdx.y;
@@ -359,12 +379,12 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeA
   const LaneSlot ls = slot_decode(a, shared, p0, raw);
   // the h rows of the valid slots -> LDS rows 0 .. count - 1
   const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
-  const MxRows m = mx_rows(smem, K, a.hsc_pitch, count);
-  dma_split_rows(smem, count, K, a.hsc_pitch, hs.hi, hs.lo, hs.sc, [](int r) { return r; });
+  const MxRows m = mx_rows<A8>(smem, K, a.hsc_pitch, count);
+  dma_split_rows(smem, count, K, a.hsc_pitch, hs.hi, A8 ? nullptr : hs.lo, hs.sc, [](int r) { return r; });
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mx_row_dot(wt, codes, scales, m, j, j < count, nch, g, acc);
+  mx_row_dot<NB, PACK, A8>(wt, codes, scales, m, j, j < count, nch, g, acc);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int slot = 4 * g + r;
@@ -627,7 +647,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // ========================================================= x split prep ===
-// xhi / xlo [T][H] and xsc [T][xsc_pitch] of bf16 x: one thread per 32-block.
+// xhi / xlo [T][H] and xsc [T][xsc_pitch] of bf16 x: one thread per 32-block
+// (xlo NULL: MXFP8 codes in xhi).
 __global__ __launch_bounds__(256) void x_split_kernel(const uint16_t* __restrict__ x, int T, int H, int xsc_pitch,
                                                       uint8_t* __restrict__ xhi, uint8_t* __restrict__ xlo,
                                                       uint8_t* __restrict__ xsc) {
@@ -639,8 +660,11 @@ __global__ __launch_bounds__(256) void x_split_kernel(const uint16_t* __restrict
   uint4 v[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) v[q] = p[q];
-  mx_split_block(v, xhi + static_cast<size_t>(t) * H + blk * 32, xlo + static_cast<size_t>(t) * H + blk * 32,
-                 xsc + static_cast<size_t>(t) * xsc_pitch + blk);
+  uint8_t* sc = xsc + static_cast<size_t>(t) * xsc_pitch + blk;
+  if (xlo)
+    mx_split_block(v, xhi + static_cast<size_t>(t) * H + blk * 32, xlo + static_cast<size_t>(t) * H + blk * 32, sc);
+  else
+    mxfp8_block(v, xhi + static_cast<size_t>(t) * H + blk * 32, sc);
 }
 
 hipError_t launch_x_split(const uint16_t* x, int T, int H, int xsc_pitch, uint8_t* xhi, uint8_t* xlo,
@@ -659,19 +683,21 @@ static hipError_t allow_lds(Kern kernel, size_t bytes) {
                              static_cast<int>(bytes));
 }
 
-template <bool PACK>
+template <bool PACK, bool A8>
 static hipError_t run_gateup_mx_p(const DecodeArgs& a, hipStream_t s) {
   constexpr int NB = 16;
   const int imax = a.Is > a.I ? a.Is : a.I;
-  const size_t lds = mx_rows_bytes(a.H, a.xsc_pitch, decode_rows(a.T));
+  const size_t lds = mx_rows_bytes<A8>(a.H, a.xsc_pitch, decode_rows(a.T));
   dim3 grid(imax / (8 * kGateWaves), a.nb_routed + a.nb_shared);
-  const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK>, lds);
+  const hipError_t e = allow_lds(decode_gateup_mx_kernel<NB, PACK, A8>, lds);
   if (e != hipSuccess) return e;
-  return launch(decode_gateup_mx_kernel<NB, PACK>, grid, dim3(64 * kGateWaves), lds, s, a);
+  return launch(decode_gateup_mx_kernel<NB, PACK, A8>, grid, dim3(64 * kGateWaves), lds, s, a);
 }
 
 static hipError_t run_gateup_mx(const DecodeArgs& a, hipStream_t s) {
-  return (a.H / 128) % 4 == 0 ? run_gateup_mx_p<true>(a, s) : run_gateup_mx_p<false>(a, s);
+  const bool pack = (a.H / 128) % 4 == 0;
+  if (a.a8) return pack ? run_gateup_mx_p<true, true>(a, s) : run_gateup_mx_p<false, true>(a, s);
+  return pack ? run_gateup_mx_p<true, false>(a, s) : run_gateup_mx_p<false, false>(a, s);
 }
 
 template <int WFMT, bool FP8ACT, int WPB>
@@ -685,21 +711,22 @@ static hipError_t run_gateup(const DecodeArgs& a, hipStream_t s) {
   return launch(decode_gateup_kernel<WFMT, FP8ACT, NB, WPB>, grid, dim3(64 * WPB), lds, s, a);
 }
 
-template <bool PACK>
+template <bool PACK, bool A8>
 static hipError_t run_down_mx_p(const DecodeArgs& a, hipStream_t s) {
   constexpr int NB = 8;
   const int kmax = a.Is > a.I ? a.Is : a.I;
-  const size_t lds = mx_rows_bytes(kmax, a.hsc_pitch, decode_rows(a.T));
+  const size_t lds = mx_rows_bytes<A8>(kmax, a.hsc_pitch, decode_rows(a.T));
   dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
-  const hipError_t e = allow_lds(decode_down_mx_kernel<NB, PACK>, lds);
+  const hipError_t e = allow_lds(decode_down_mx_kernel<NB, PACK, A8>, lds);
   if (e != hipSuccess) return e;
-  return launch(decode_down_mx_kernel<NB, PACK>, grid, dim3(64 * kDownWaves), lds, s, a);
+  return launch(decode_down_mx_kernel<NB, PACK, A8>, grid, dim3(64 * kDownWaves), lds, s, a);
 }
 
 static hipError_t run_down_mx(const DecodeArgs& a, hipStream_t s) {
   // PACK needs every K of the launch (routed and shared) to hold whole dwords of scales
   const bool pack = (a.I / 128) % 4 == 0 && (a.Is / 128) % 4 == 0;
-  return pack ? run_down_mx_p<true>(a, s) : run_down_mx_p<false>(a, s);
+  if (a.a8) return pack ? run_down_mx_p<true, true>(a, s) : run_down_mx_p<false, true>(a, s);
+  return pack ? run_down_mx_p<true, false>(a, s) : run_down_mx_p<false, false>(a, s);
 }
 
 template <int WFMT, bool FP8ACT>

@@ -140,7 +140,7 @@ ftmoe_status check_layer(const ftmoe_layer* L) {
   if (L->num_experts < L->top_k || L->num_experts > kMaxExperts)
     return fail(FTMOE_ERR_UNSUPPORTED, "num_experts=%d outside [top_k=%d, %d]", L->num_experts, L->top_k,
                 kMaxExperts);
-  if (L->act != FTMOE_ACT_BF16 && L->act != FTMOE_ACT_FP8_PER_TENSOR)
+  if (L->act != FTMOE_ACT_BF16 && L->act != FTMOE_ACT_FP8_PER_TENSOR && L->act != FTMOE_ACT_MXFP8)
     return fail(FTMOE_ERR_INVALID_ARG, "act=%d is not an ftmoe_afmt", L->act);
   if (L->path != FTMOE_PATH_AUTO && L->path != FTMOE_PATH_DECODE && L->path != FTMOE_PATH_PREFILL)
     return fail(FTMOE_ERR_INVALID_ARG, "path=%d is not an ftmoe_path", L->path);
@@ -151,6 +151,8 @@ ftmoe_status check_layer(const ftmoe_layer* L) {
     return fail(FTMOE_ERR_INVALID_ARG, "gate_up.fmt=%d is not an ftmoe_wfmt", fmt);
   if (L->act == FTMOE_ACT_FP8_PER_TENSOR && fmt != FTMOE_W_FP8_E4M3)
     return fail(FTMOE_ERR_UNSUPPORTED, "FP8 per-tensor activations need FP8 weights");
+  if (L->act == FTMOE_ACT_MXFP8 && fmt != FTMOE_W_MXFP4)
+    return fail(FTMOE_ERR_UNSUPPORTED, "MXFP8 activations need MXFP4 weights");
   FT_TRY(check_qweight(L->gate_up, "gate_up", fmt, L->num_experts, 2 * L->inter, L->hidden));
   FT_TRY(check_qweight(L->down, "down", fmt, L->num_experts, L->hidden, L->inter));
   if (L->shared_inter < 0) return fail(FTMOE_ERR_INVALID_ARG, "shared_inter=%d is negative", L->shared_inter);
@@ -190,7 +192,8 @@ struct Plan {
          scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
          hsc = 0, hq = 0, xs = 0, xssc = 0, hgsc = 0, hssc = 0, total = 0;
   int hsc_pitch = 0;
-  bool mx_split = false;  // MXFP4 decode: activations travel as split E4M3 pairs
+  bool a8 = false;        // MXFP8 activations: single codes where MXFP4 otherwise splits
+  bool mx_split = false;  // MXFP4 decode: activations travel as split E4M3 pairs (or MXFP8)
   bool mx_gemm = false;   // MXFP4 prefill, routed experts: split x and h
   bool mx_gemm_shared = false;  // MXFP4 prefill, shared expert
 };
@@ -201,7 +204,8 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   const bool shared = L->shared_inter > 0;
   p.decode = L->path == FTMOE_PATH_DECODE || (L->path == FTMOE_PATH_AUTO && T <= kDecodeAutoMaxT);
   p.small_route = T <= kDecodeMaxT;
-  p.BM = p.decode ? kDecodeBM : gemm_block_m(T, k, E, L->gate_up.fmt);
+  p.a8 = L->act == FTMOE_ACT_MXFP8;
+  p.BM = p.decode ? kDecodeBM : gemm_block_m(T, k, E, L->gate_up.fmt, p.a8);
   p.P = max_padded(T, k, E, p.BM);
   p.nblocks = p.P / p.BM;
   p.nb_shared = shared ? (T + p.BM - 1) / p.BM : 0;
@@ -233,9 +237,10 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   p.ascratch = take(align_scratch_bytes(T, k, E, p.BM));
   p.xq = take(L->act == FTMOE_ACT_FP8_PER_TENSOR ? static_cast<size_t>(T) * H : 0);
   p.mx_split = p.decode && L->gate_up.fmt == FTMOE_W_MXFP4;
+  const size_t lo_planes = p.a8 ? 0 : 1;   // MXFP8 activations have no lo codes
   if (p.mx_split) {
     p.xhi = take(static_cast<size_t>(T) * H);
-    p.xlo = take(static_cast<size_t>(T) * H);
+    p.xlo = take(lo_planes * T * H);
     p.xsc = take(static_cast<size_t>(T) * xsc_pitch_of(H));
   }
   if (p.mx_split) {
@@ -244,14 +249,14 @@ Plan make_plan(const ftmoe_layer* L, int T) {
     const size_t hbytes = static_cast<size_t>(p.P) * I + static_cast<size_t>(p.shared_rows) * L->shared_inter;
     p.hsc_pitch = xsc_pitch_of(imax);
     p.hhi = take(hbytes);
-    p.hlo = take(hbytes);
+    p.hlo = take(lo_planes * hbytes);
     p.hsc = take(static_cast<size_t>(p.P + p.shared_rows) * p.hsc_pitch);
   } else {
     // bf16 h, or for MXFP4 its split form (2 code bytes per element + scales)
     p.mx_gemm = !p.decode && L->gate_up.fmt == FTMOE_W_MXFP4;
     p.mx_gemm_shared = !p.decode && shared && L->shared_gate_up.fmt == FTMOE_W_MXFP4;
     if (p.mx_gemm || p.mx_gemm_shared) {
-      p.xs = take(static_cast<size_t>(T) * H * 2);
+      p.xs = take(static_cast<size_t>(T) * H * (1 + lo_planes));
       p.xssc = take(static_cast<size_t>(T) * (H / 32));
     }
     p.h = take(static_cast<size_t>(p.P) * I * 2);
@@ -302,12 +307,12 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
   const int E = L->num_experts, k = L->top_k;
   if (p.small_route) {
     float* part = at<float>(ws, p.part);
-    const bool split = align && p.mx_split;  // the experts stage of this call reads the split x
+    const bool split = align && p.mx_split;  // the experts stage of this call reads the split (MXFP8) x
     FT_HIP(timed("router_partial", s,
                  [&] {
                    return launch_router_partial(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
                                                 part, split ? at<uint8_t>(ws, p.xhi) : nullptr,
-                                                split ? at<uint8_t>(ws, p.xlo) : nullptr,
+                                                split && !p.a8 ? at<uint8_t>(ws, p.xlo) : nullptr,
                                                 split ? at<uint8_t>(ws, p.xsc) : nullptr, xsc_pitch_of(L->hidden), s);
                  }),
            "router launch");
@@ -377,7 +382,8 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
       // the router of this call did not produce the split x
       FT_HIP(timed("x_split", s,
                    [&] {
-                     return launch_x_split(x, T, H, xsc_pitch_of(H), at<uint8_t>(ws, p.xhi), at<uint8_t>(ws, p.xlo),
+                     return launch_x_split(x, T, H, xsc_pitch_of(H), at<uint8_t>(ws, p.xhi),
+                                           p.a8 ? nullptr : at<uint8_t>(ws, p.xlo),
                                            at<uint8_t>(ws, p.xsc), s);
                    }),
              "x split launch");
@@ -399,9 +405,10 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     a.nb_routed = p.nblocks;
     a.nb_shared = p.nb_shared;
     a.x = x;
+    a.a8 = p.a8 ? 1 : 0;
     if (p.mx_split) {
       a.xhi = at<uint8_t>(ws, p.xhi);
-      a.xlo = at<uint8_t>(ws, p.xlo);
+      a.xlo = p.a8 ? nullptr : at<uint8_t>(ws, p.xlo);
       a.xsc = at<uint8_t>(ws, p.xsc);
       a.xsc_pitch = xsc_pitch_of(H);
     }
@@ -411,7 +418,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     a.hs = hs;
     if (p.mx_split) {
       a.hhi = at<uint8_t>(ws, p.hhi);
-      a.hlo = at<uint8_t>(ws, p.hlo);
+      a.hlo = p.a8 ? nullptr : at<uint8_t>(ws, p.hlo);
       a.hsc = at<uint8_t>(ws, p.hsc);
       a.hsc_pitch = p.hsc_pitch;
     }
@@ -456,8 +463,11 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   if (p.mx_gemm || p.mx_gemm_shared) {
     xa.split = at<uint8_t>(ws, p.xs);
     xa.split_sc = at<uint8_t>(ws, p.xssc);
+    xa.mx8 = p.a8;
     FT_HIP(timed("x_split", s,
-                 [&] { return launch_x_split_gemm(x, T, H, at<uint8_t>(ws, p.xs), at<uint8_t>(ws, p.xssc), s); }),
+                 [&] {
+                   return launch_x_split_gemm(x, T, H, at<uint8_t>(ws, p.xs), at<uint8_t>(ws, p.xssc), p.a8, s);
+                 }),
            "x split launch");
   }
   uint8_t* hgsc = p.mx_gemm ? at<uint8_t>(ws, p.hgsc) : nullptr;
@@ -470,6 +480,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   if (p.mx_gemm) {
     ha.split = reinterpret_cast<const uint8_t*>(h);
     ha.split_sc = hgsc;
+    ha.mx8 = p.a8;
   }
   if (fp8act) {
     uint8_t* hq = at<uint8_t>(ws, p.hq);
@@ -495,6 +506,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     if (p.mx_gemm_shared) {
       hsa.split = reinterpret_cast<const uint8_t*>(hs);
       hsa.split_sc = hssc;
+      hsa.mx8 = p.a8;
     }
     FT_HIP(timed("gemm_shared_down", s,
                  [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hsa, H, L->shared_inter, sh, s); }),

@@ -24,7 +24,9 @@
 // as exact as bf16), and v_mfma_scale_f32_32x32x64_f8f6f4 multiplies them
 // with the E2M1 codes, applying both E8M0 block scales in hardware -- two
 // MFMAs (hi, lo) per 64 K, no per-element conversion.  The gate_up epilogue
-// writes h in the same split form for the down GEMM.  NVFP4 weights (E4M3
+// writes h in the same split form for the down GEMM.  In the MXFP8
+// activation mode (W4A8) x and h are single E4M3 codes under E8M0 block
+// scales: one scaled MFMA per 64 K, and half the activation bytes.  NVFP4 weights (E4M3
 // block scales are not powers of two) are converted to bf16 (E2M1 x E4M3 is
 // exact in bf16) for v_mfma_f32_32x32x16_bf16.  FP8 weights with FP8
 // activations feed the scaled MFMA with unit scales; tensor and activation
@@ -51,10 +53,11 @@ constexpr int kStageK = 64;
 
 using lds_void = __attribute__((address_space(3))) void;
 
-int gemm_block_m(int T, int k, int E, int wfmt) {
+int gemm_block_m(int T, int k, int E, int wfmt, bool a8) {
   // Small experts (few rows each) waste less padding with 64-row blocks; FP8
-  // weight stages are twice as wide and always use 128-row blocks.
-  if (wfmt == kFP8) return 128;
+  // weight stages are twice as wide, and MXFP8 activation stages half as
+  // wide, so both always use 128-row blocks (whole DMA chunks per wave).
+  if (wfmt == kFP8 || a8) return 128;
   return static_cast<long long>(T) * k >= 192LL * E ? 128 : 64;
 }
 
@@ -72,10 +75,12 @@ struct Cfg {
   static constexpr int kBBytes = kBN * kBRowB;
   static constexpr bool kScales = WFMT != kFP8;        // FP4: one scale dword per weight row and stage
   static constexpr int kSBytes = kScales ? 4 * kBN : 0;
-  // MXFP4: split E4M3 activations (a row's stage = 64 hi + 64 lo bytes) and
-  // one E8M0 scale dword per activation row and two stages
-  static constexpr bool kSplitA = WFMT == kMXFP4;
-  static constexpr int kASBytes = kSplitA ? 4 * BM : 0;
+  // MXFP4: split E4M3 activations (a row's stage = 64 hi + 64 lo bytes), or
+  // with FP8ACT the MXFP8 form (64 bytes), and one E8M0 scale dword per
+  // activation row and two stages
+  static constexpr bool kAScales = WFMT == kMXFP4;
+  static constexpr bool kSplitA = kAScales && !FP8ACT;
+  static constexpr int kASBytes = kAScales ? 4 * BM : 0;
   static constexpr int kSlotBytes = kABytes + kBBytes + kSBytes + kASBytes;
   static constexpr int kRing = kSlotBytes * 4 <= 150 * 1024 ? 4 : 3;   // stage buffers in LDS
   static_assert(kRing * kSlotBytes <= 150 * 1024, "LDS");
@@ -86,7 +91,7 @@ struct Cfg {
   static constexpr int kScaleRowsPerWave = kBN / kGemmWaves;   // one 4-byte DMA instruction per wave
   static_assert(kScaleRowsPerWave <= 64, "scale rows per wave");
   static constexpr int kARowsPerWave = BM / kGemmWaves;   // activation scale rows per wave
-  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0) + (kSplitA ? 1 : 0);
+  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0) + (kAScales ? 1 : 0);
   static_assert(kVmPerStage * (kRing - 2) < 64, "vmcnt range");
 };
 
@@ -272,6 +277,34 @@ __device__ __forceinline__ void frag_read_mx_2(uint32_t vB, uint32_t vS, uint32_
         "n"(OAS));
 }
 
+// MXFP4 weights with MXFP8 activations, 4 column tiles: FP4 weight vectors
+// and scale dwords, the activation scale dwords of the two row tiles, and two
+// activation vectors per row tile.
+template <int OB1, int OB2, int OB3, int OS1, int OS2, int OS3, int OAM, int OAS>
+__device__ __forceinline__ void frag_read_mx8_4(uint32_t vB, uint32_t vS, uint32_t vAS, uint32_t vA0, uint32_t vA1,
+                                                u32x4 (&b)[4], uint32_t (&s)[4], uint32_t (&as)[2], u32x4 (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %14\n"
+      "ds_read_b128 %1, %14 offset:%19\n"
+      "ds_read_b128 %2, %14 offset:%20\n"
+      "ds_read_b128 %3, %14 offset:%21\n"
+      "ds_read_b32 %4, %15\n"
+      "ds_read_b32 %5, %15 offset:%22\n"
+      "ds_read_b32 %6, %15 offset:%23\n"
+      "ds_read_b32 %7, %15 offset:%24\n"
+      "ds_read_b32 %8, %16\n"
+      "ds_read_b32 %9, %16 offset:%26\n"
+      "ds_read_b128 %10, %17\n"
+      "ds_read_b128 %11, %18\n"
+      "ds_read_b128 %12, %17 offset:%25\n"
+      "ds_read_b128 %13, %18 offset:%25\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]),
+        "=&v"(as[0]), "=&v"(as[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(vB), "v"(vS), "v"(vAS), "v"(vA0), "v"(vA1), "n"(OB1), "n"(OB2), "n"(OB3), "n"(OS1), "n"(OS2), "n"(OS3),
+        "n"(OAM), "n"(OAS));
+}
+
 // FP8 weights and activations, 4 column tiles: two vectors per operand row.
 template <int OB1, int OB2, int OB3, int OAM>
 __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
@@ -353,14 +386,14 @@ struct GemmArgs {
   QW w;
   Rows rows;
   const uint8_t* a;          // activation rows: bf16 (x or h), E4M3 (x_q or h_q) or split E4M3 (MXFP4)
-  const uint8_t* a_sc;       // MXFP4: E8M0 scales of the split activations [rows][a_sc_pitch]
+  const uint8_t* a_sc;       // MXFP4: E8M0 scales of the split / MXFP8 activations [rows][a_sc_pitch]
   int a_sc_pitch;
   int K;                     // reduction length (H for gate_up, I for down)
   int N;                     // gate_up: I (gate columns); down: H (output columns)
   int a_row_bytes;           // bytes per activation row
   const uint32_t* amax_a;    // FP8 activations: amax bits of the activation tensor
-  void* out;                 // gate_up: h [rows][I] (bf16, or split E4M3 for MXFP4); down: o [flat][H] bf16
-  uint8_t* out_sc;           // gate_up, MXFP4: E8M0 scales of the split h [rows][out_sc_pitch]
+  void* out;                 // gate_up: h [rows][I] (bf16, or split E4M3 / MXFP8 for MXFP4); down: o [flat][H] bf16
+  uint8_t* out_sc;           // gate_up, MXFP4: E8M0 scales of h [rows][out_sc_pitch]
   int out_sc_pitch;
   uint32_t* amax_slots;      // gate_up with FP8 activations: partial maxima of |h|
 };
@@ -467,10 +500,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
     }
   }
-  // Activation scales (split activations): lanes l < kARowsPerWave of wave
-  // w fetch the scale dword of tile row w * kARowsPerWave + l (two stages).
+  // Activation scales (MXFP4): lanes l < kARowsPerWave of wave w fetch the
+  // scale dword of tile row w * kARowsPerWave + l (two stages).
   const uint8_t* asrc = nullptr;
-  if constexpr (C::kSplitA) {
+  if constexpr (C::kAScales) {
     const int r = wave * C::kARowsPerWave + (lane < C::kARowsPerWave ? lane : 0);
     int row;
     if (GATEUP && rows.sorted_ids) {
@@ -512,7 +545,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       else
         ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
     }
-    if constexpr (C::kSplitA) {
+    if constexpr (C::kAScales) {
       if (lane < C::kARowsPerWave)
         dma4(asrc, buf + C::kABytes + C::kBBytes + C::kSBytes + wave * 4 * C::kARowsPerWave);
       asrc += adv && (cur_stage & 1) ? 4 : 0;
@@ -577,7 +610,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     const uint32_t base = lds_addr(cur);
     u32x4 bv[kBVec], av[kAVec];
     uint32_t scw[NT], asw[2];
-    if constexpr (C::kSplitA) {
+    if constexpr (C::kAScales && FP8ACT) {
+      static_assert(NT == 4, "MXFP8 activations use 128-row blocks");
+      frag_read_mx8_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM, 32 * 4>(
+          base + bo[0], base + so, base + sao, base + ao[0], base + ao[1], bv, scw, asw, av);
+    } else if constexpr (C::kSplitA) {
       const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
       if constexpr (NT == 4)
         frag_read_mx_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM, 32 * 4>(
@@ -601,7 +638,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
                                                                                     bv, av);
     }
     issue(refill);
-    if constexpr (C::kSplitA) {
+    if constexpr (C::kAScales && FP8ACT) {
+      // one scaled MFMA: E4M3 activations (format 0) x E2M1 weights (format 4)
+      const int sh = 16 * (s & 1) + 8 * g;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (!rows_ok[m]) continue;
+        const int sa = static_cast<int>(asw[m] >> sh);
+        const i32x8 a = u4x2(to_u4(av[2 * m]), to_u4(av[2 * m + 1]));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const uint4 c = to_u4(bv[ct]);
+          const i32x8 bq = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w),
+                            0, 0, 0, 0};
+          acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, acc[m][ct], 0, 4, 0, sa,
+                                                                       0, static_cast<int>(scw[ct] >> sh));
+        }
+      }
+    } else if constexpr (C::kSplitA) {
       // the E8M0 bytes of this lane's K block: byte 2 (s & 1) + g of the dwords
       const int sh = 16 * (s & 1) + 8 * g;
 #pragma unroll
@@ -672,8 +726,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // ---- epilogue ----
   float f = 1.0f;
   if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-  if constexpr (FP8ACT) f *= amax_scale(ga.amax_a);
-  if constexpr (GATEUP && C::kSplitA) {
+  if constexpr (FP8ACT && WFMT == kFP8) f *= amax_scale(ga.amax_a);
+  if constexpr (GATEUP && C::kAScales && FP8ACT) {
+    // MXFP8 h straight from the accumulators: the 32 columns of a block are
+    // the 32 lanes of a half-wave (one row per register), so the block
+    // maximum is a half-wave reduction and each lane writes its own code.
+    uint8_t* hq = static_cast<uint8_t*>(ga.out);
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+      const int col = tile_col(Rt[u] + j);   // gate column of this lane
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float v = swiglu(acc[m][u][r], acc[m][u + NT / 2][r]);
+          const uint32_t code = mxfp8_scale_code(half_wave_max(__builtin_fabsf(v)));
+          if (!wact || i >= nvalid) continue;
+          const size_t row = static_cast<size_t>(b * BM + i);
+          hq[row * N + col] = static_cast<uint8_t>(f32x2_to_e4m3x2(v * mx_inv_scale(code), 0.f) & 0xFF);
+          if (j == 0) ga.out_sc[row * ga.out_sc_pitch + col / 32] = static_cast<uint8_t>(code);
+        }
+      }
+    }
+  } else if constexpr (GATEUP && C::kSplitA) {
     // h rounded to bf16 goes through LDS (the ring is free now) so that each
     // thread then splits one 32-column block of a row: tile [BM][kHalf].
     __syncthreads();
@@ -758,8 +834,9 @@ template <bool GATEUP>
 static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
   const int bm = ga.rows.block_m;
   switch (ga.w.fmt) {
-    case kMXFP4:
-      if (fp8act || !ga.a_sc || (GATEUP && !ga.out_sc)) return hipErrorInvalidValue;
+    case kMXFP4:   // fp8act: MXFP8 activations
+      if (!ga.a_sc || (GATEUP && !ga.out_sc)) return hipErrorInvalidValue;
+      if (fp8act) return bm == 128 ? run<kMXFP4, true, 128, GATEUP>(ga, s) : hipErrorInvalidValue;
       return bm == 128 ? run<kMXFP4, false, 128, GATEUP>(ga, s) : run<kMXFP4, false, 64, GATEUP>(ga, s);
     case kNVFP4:
       if (fp8act) return hipErrorInvalidValue;
@@ -782,7 +859,7 @@ hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, i
     ga.a = x.split;
     ga.a_sc = x.split_sc;
     ga.a_sc_pitch = H / 32;
-    ga.a_row_bytes = 2 * H;
+    ga.a_row_bytes = x.mx8 ? H : 2 * H;
     ga.out_sc = h_sc;
     ga.out_sc_pitch = inter / 32;
   } else if (x.q) {
@@ -795,7 +872,7 @@ hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, i
   ga.amax_a = x.amax;
   ga.out = h;
   ga.amax_slots = amax_h;
-  return dispatch<true>(ga, x.q != nullptr, s);
+  return dispatch<true>(ga, w.fmt == kMXFP4 ? x.mx8 : x.q != nullptr, s);
 }
 
 hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int H, int inter, uint16_t* o,
@@ -809,7 +886,7 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
     ga.a = h.split;
     ga.a_sc = h.split_sc;
     ga.a_sc_pitch = inter / 32;
-    ga.a_row_bytes = 2 * inter;
+    ga.a_row_bytes = h.mx8 ? inter : 2 * inter;
   } else if (h.q) {
     ga.a = h.q;
     ga.a_row_bytes = inter;
@@ -819,7 +896,7 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
   }
   ga.amax_a = h.amax;
   ga.out = o;
-  return dispatch<false>(ga, h.q != nullptr, s);
+  return dispatch<false>(ga, w.fmt == kMXFP4 ? h.mx8 : h.q != nullptr, s);
 }
 
 // ---------------------------------------------------- packed weights -----
@@ -832,6 +909,7 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
 // the dword of the stage pair; NVFP4: the stage's).  Rows past N are zero.
 constexpr int kTileRows = 512;
 static_assert(Cfg<kMXFP4, false, 128>::kBN == kTileRows && Cfg<kMXFP4, false, 64>::kBN == kTileRows &&
+                  Cfg<kMXFP4, true, 128>::kBN == kTileRows &&
                   Cfg<kNVFP4, false, 64>::kBN == kTileRows && Cfg<kFP8, true, 128>::kBN == kTileRows,
               "one packed layout serves every tile configuration");
 
@@ -899,23 +977,30 @@ hipError_t launch_pack_weights(const QW& w, int E, bool gate_up, uint8_t* out, h
 }
 
 // ------------------------------------------------- split activations ------
-// Split E4M3 form of x for the MXFP4 GEMMs (one thread per 32-block).
+// Split E4M3 form of x for the MXFP4 GEMMs, or with a8 the MXFP8 form (one
+// thread per 32-block).
 __global__ __launch_bounds__(256) void x_split_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                           uint8_t* __restrict__ xs, uint8_t* __restrict__ xsc) {
+                                                           uint8_t* __restrict__ xs, uint8_t* __restrict__ xsc,
+                                                           int a8) {
   const int nb = H / 32;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * nb) return;
   const int t = i / nb, blk = i % nb;
   const uint4* p = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + blk * 32);
   const uint4 v[4] = {p[0], p[1], p[2], p[3]};
-  uint8_t* hi = xs + static_cast<size_t>(t) * (2 * H) + (blk / 2) * 128 + (blk & 1) * 32;
-  mx_split_block(v, hi, hi + 64, xsc + static_cast<size_t>(t) * nb + blk);
+  uint8_t* sc = xsc + static_cast<size_t>(t) * nb + blk;
+  if (a8) {
+    mxfp8_block(v, xs + static_cast<size_t>(t) * H + blk * 32, sc);
+  } else {
+    uint8_t* hi = xs + static_cast<size_t>(t) * (2 * H) + (blk / 2) * 128 + (blk & 1) * 32;
+    mx_split_block(v, hi, hi + 64, sc);
+  }
 }
 
-hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s) {
+hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, bool a8, hipStream_t s) {
   const int n = T * (H / 32);
   if (n == 0) return hipSuccess;
-  return launch(x_split_gemm_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, T, H, xs, xsc);
+  return launch(x_split_gemm_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, T, H, xs, xsc, a8 ? 1 : 0);
 }
 
 }  // namespace ftmoe

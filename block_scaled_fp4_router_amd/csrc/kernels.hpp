@@ -93,12 +93,14 @@ constexpr int kDecodeBM = 16;
 constexpr int kDecodeMaxT = 16;
 // Router partial logits part[t][row][s], s over S = router_splits(H) slices
 // of H (a multiple of 4).  With xhi non-NULL the kernel also writes the split
-// E4M3 form of x (xhi / xlo [T][H], xsc [T][xsc_pitch]) for the MXFP4 MFMA.
+// E4M3 form of x (xhi / xlo [T][H], xsc [T][xsc_pitch]) for the MXFP4 MFMA,
+// or with xlo NULL the MXFP8 form (codes in xhi, scales in xsc).
 int router_splits(int H);
 hipError_t launch_router_partial(const uint16_t* x, int T, int H, const float* router_w, int E,
                                  const float* shared_gate_w, float* part, uint8_t* xhi, uint8_t* xlo,
                                  uint8_t* xsc, int xsc_pitch, hipStream_t s);
-// Split E4M3 form of x without the router (one thread per 32-block).
+// Split E4M3 form of x without the router (one thread per 32-block); with
+// xlo NULL the MXFP8 form.
 hipError_t launch_x_split(const uint16_t* x, int T, int H, int xsc_pitch, uint8_t* xhi, uint8_t* xlo,
                           uint8_t* xsc, hipStream_t s);
 inline int xsc_pitch_of(int H) { return (H / 32 + 15) / 16 * 16; }
@@ -118,8 +120,9 @@ struct DecodeArgs {
   int T, k, H, I, Is;
   int nb_routed, nb_shared;   // grid blocks: routed blocks, then shared blocks
   const uint16_t* x;
-  const uint8_t* xhi;         // MXFP4: split activations [T][H] (hi codes)
-  const uint8_t* xlo;         //        [T][H] (lo codes)
+  int a8;                     // MXFP4 with MXFP8 activations: single E4M3 codes in xhi / hhi, no lo
+  const uint8_t* xhi;         // MXFP4: split activations [T][H] (hi codes, or the MXFP8 codes)
+  const uint8_t* xlo;         //        [T][H] (lo codes; NULL with a8)
   const uint8_t* xsc;         //        [T][xsc_pitch] E8M0 scale per 32-block
   int xsc_pitch;
   const uint8_t* xq;          // FP8 activations or NULL
@@ -127,7 +130,7 @@ struct DecodeArgs {
   uint16_t* h;                // [nb_routed * 16][I] bf16 (NVFP4 / FP8)
   uint16_t* hs;               // [nb_shared * 16][Is] bf16 (NVFP4 / FP8)
   uint8_t* hhi;               // MXFP4: split h, routed rows [nb_routed * 16][I] then shared [nb_shared * 16][Is]
-  uint8_t* hlo;               //        (lo codes, same layout)
+  uint8_t* hlo;               //        (lo codes, same layout; NULL with a8)
   uint8_t* hsc;               //        [(nb_routed + nb_shared) * 16][hsc_pitch] E8M0 scales
   int hsc_pitch;
   uint32_t* amax_slots;       // FP8 activations: gate_up partial maxima of |h| (or NULL)
@@ -147,21 +150,26 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill experts (grouped GEMMs on MFMA) ----
 // Rows per block of the prefill GEMMs for a layer routing T*k rows over E experts.
-int gemm_block_m(int T, int k, int E, int wfmt);
+// MXFP8 activations (a8) always take 128-row blocks.
+int gemm_block_m(int T, int k, int E, int wfmt, bool a8);
 // Activation operand of a prefill GEMM, by weight format: MXFP4 takes the
 // split E4M3 form (per 64 columns of a row: 64 hi codes then 64 lo codes,
-// 2 bytes per element; E8M0 scales [rows][K/32]); FP8 weights with FP8
-// activations take q (E4M3, per-tensor scale from amax); otherwise bf16.
+// 2 bytes per element; E8M0 scales [rows][K/32]), or with mx8 the MXFP8
+// form (one E4M3 code per element, [rows][K], same scales); FP8 weights
+// with FP8 activations take q (E4M3, per-tensor scale from amax); otherwise
+// bf16.
 struct GemmAct {
   const uint16_t* bf16;
   const uint8_t* q;
   const uint32_t* amax;
   const uint8_t* split;
   const uint8_t* split_sc;
+  bool mx8;
 };
 // gate_up writes h [rows][I]: bf16, or for MXFP4 split (h [rows][2I] codes,
-// h_sc [rows][I/32] scales).  amax_h: FP8 activations only, the kAmaxSlots
-// partial maxima of |h|.
+// h_sc [rows][I/32] scales) or, with x.mx8, MXFP8 (h [rows][I] codes, same
+// scales).  amax_h: FP8 activations only, the kAmaxSlots partial maxima of
+// |h|.
 hipError_t launch_gemm_gateup(const QW& w, const Rows& rows, const GemmAct& x, int H, int inter, void* h,
                               uint8_t* h_sc, uint32_t* amax_h, hipStream_t s);
 hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int H, int inter, uint16_t* o,
@@ -169,8 +177,9 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
 // Packed tile layout of a matrix set for the prefill GEMMs (see gemm.hip).
 size_t packed_bytes(int fmt, int E, int n, int k, bool gate_up);
 hipError_t launch_pack_weights(const QW& w, int E, bool gate_up, uint8_t* out, hipStream_t s);
-// Split E4M3 form of x for the MXFP4 GEMMs: xs [T][2H], xsc [T][H/32].
-hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, hipStream_t s);
+// Split E4M3 form of x for the MXFP4 GEMMs: xs [T][2H], xsc [T][H/32]; with
+// a8 the MXFP8 form xs [T][H] and the same scales.
+hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, bool a8, hipStream_t s);
 
 // ---- combine ----
 // y[t] = sum_j w[t,j] o[t*k+j] (+ sg[t] * sh[t]) -> bf16.

@@ -312,7 +312,11 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __r
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4*>(&xs[t][blk * 32 + q * 8]);
       const size_t o = static_cast<size_t>(t) * H + h0 + blk * 32;
-      mx_split_block(v, xhi + o, xlo + o, xsc + static_cast<size_t>(t) * xsc_pitch + (h0 / 32) + blk);
+      uint8_t* sc = xsc + static_cast<size_t>(t) * xsc_pitch + (h0 / 32) + blk;
+      if (xlo)
+        mx_split_block(v, xhi + o, xlo + o, sc);
+      else
+        mxfp8_block(v, xhi + o, sc);
     }
   }
   if (!have_row) return;

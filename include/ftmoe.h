@@ -16,7 +16,9 @@
  *
  * With per-tensor FP8 activations, x and h are each quantised to E4M3 with
  * one scale amax/448 over the whole GEMM input (all T rows of x; all T*k rows
- * of h) before their GEMM.
+ * of h) before their GEMM.  With MXFP8 activations, every row of x, of h and
+ * of the shared expert's h is quantised per block of 32 (OCP Microscaling
+ * v1.0 conversion, see ftmoe_afmt) before its GEMM.
  *
  * Conventions for every entry point:
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  Structs
@@ -71,10 +73,17 @@ typedef enum {
 
 /* Activation format fed to the expert GEMMs.  FP8_PER_TENSOR is the W8A8
  * scheme of the FreeToken commit message on per-tensor FP8 projections: one
- * dynamic E4M3 scale per GEMM input.  It requires FP8 weights.            */
+ * dynamic E4M3 scale per GEMM input.  It requires FP8 weights.
+ * MXFP8 is a W4A8 scheme for MXFP4 weights (the FreeToken README lists MXFP4
+ * among the formats; the MX specification defines the 8-bit element type):
+ * each block of 32 consecutive activations along K becomes E4M3 codes under
+ * one E8M0 scale 2^X, X = floor(log2 max|v|) - 8 (at least -127), codes the
+ * nearest E4M3 of v / 2^X saturating at 448.  Both operands then feed the
+ * scaled MFMA with their own block scales.  It requires MXFP4 weights.    */
 typedef enum {
   FTMOE_ACT_BF16 = 0,
-  FTMOE_ACT_FP8_PER_TENSOR = 1
+  FTMOE_ACT_FP8_PER_TENSOR = 1,
+  FTMOE_ACT_MXFP8 = 2
 } ftmoe_afmt;
 
 /* Expert-kernel family.  AUTO picks the bandwidth-bound decode kernels for

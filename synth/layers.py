@@ -199,6 +199,9 @@ CONFIGS = {
     "c2": LayerConfig("c2", (4096,), 2048, 128, 8, 768, "mxfp4", seed=1),
     "c3": LayerConfig("c3", (1, 8192), 2048, 512, 10, 512, "nvfp4", shared_inter=512, seed=3),
     "c4": LayerConfig("c4", (16384,), 4096, 128, 8, 1536, "fp8", act="fp8", zipf_s=1.1, seed=4),
+    # the c1 / c2 layers (same weights) with MXFP8 activations (W4A8)
+    "c1-w4a8": LayerConfig("c1-w4a8", (1, 8), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),
+    "c2-w4a8": LayerConfig("c2-w4a8", (4096,), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),
 }
 
 
@@ -283,7 +286,8 @@ def make_layer(cfg, cache: bool = True) -> Layer:
     """Build (or fetch from the in-process cache) the layer for a config."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
-    key = (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.fmt, cfg.act,
+    # the arrays do not depend on the activation mode or the name
+    key = (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.fmt,
            cfg.shared_inter, cfg.router_std, cfg.zipf_s, cfg.zipf_ratio, cfg.seed)
     if cache and key in _LAYER_CACHE:
         lay = _LAYER_CACHE[key]

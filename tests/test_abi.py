@@ -102,6 +102,26 @@ def test_layer_validation(field, value, status):
 
 
 @needs_lib
+def test_mxfp8_activations_need_mxfp4_weights_and_shrink_the_workspace():
+    d = good_layer()
+    _, n_split = _ws_status(d, T=8)
+    _, n_split_pf = _ws_status(d, T=4096)
+    d.act = ft.ACT_MXFP8
+    st, n8 = _ws_status(d, T=8)
+    st_pf, n8_pf = _ws_status(d, T=4096)
+    assert st == ft.OK and st_pf == ft.OK
+    # no lo code plane: decode drops T*H (x) and the h rows' bytes, prefill T*H
+    assert n8 < n_split and n8_pf < n_split_pf
+    for fmt in (ft.W_NVFP4, ft.W_FP8_E4M3):
+        d2 = good_layer()
+        d2.act = ft.ACT_MXFP8
+        d2.gate_up = _qw(fmt, 8, 256, 256)
+        d2.down = _qw(fmt, 8, 256, 128)
+        assert _ws_status(d2)[0] == ft.ERR_UNSUPPORTED
+        assert "MXFP8" in ft.load().ftmoe_last_error().decode()
+
+
+@needs_lib
 def test_weight_shape_and_format_validation():
     d = good_layer()
     d.down = _qw(ft.W_MXFP4, 8, 256, 256)          # K must equal inter

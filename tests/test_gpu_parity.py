@@ -4,7 +4,7 @@ same seeded inputs.
 Bars: routing ids, per-expert counts and the align outputs are bit-exact;
 routing weights and the shared gate within 1e-5; the layer output within a
 relative Frobenius error of 2e-2 (bf16 activations) or 3e-2 (FP8 per-tensor
-activations), max-abs error reported.  Full-size layers are compared on a
+or MXFP8 activations), max-abs error reported.  Full-size layers are compared on a
 sample of tokens the oracle evaluates one by one (the FP8 layer's h scale is a
 whole-batch quantity, so the oracle's own grouped pass over every token
 supplies it)."""
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def tol_for(name):
-    return 3e-2 if synth.CONFIGS[name].act == "fp8" else 2e-2
+    return 3e-2 if synth.CONFIGS[name].act in ("fp8", "mxfp8") else 2e-2
 
 
 # ------------------------------------------------------------------ route --
@@ -95,7 +95,8 @@ SMALL_CASES = [("c0", 16, "auto"), ("c0", 16, "decode"), ("c0", 16, "prefill"),
                ("c0", 5, "decode"), ("c0", 5, "prefill"), ("c0", 70, "prefill"), ("c0", 70, "decode"),
                ("c1", 1, "decode"), ("c1", 1, "prefill"), ("c1", 8, "decode"), ("c1", 8, "prefill"),
                ("c1", 17, "auto"), ("c3", 1, "decode"), ("c3", 1, "prefill"), ("c3", 8, "decode"),
-               ("c3", 20, "prefill")]
+               ("c3", 20, "prefill"), ("c1-w4a8", 1, "decode"), ("c1-w4a8", 8, "decode"),
+               ("c1-w4a8", 8, "prefill"), ("c1-w4a8", 40, "prefill")]
 
 
 @pytest.mark.parametrize("name,T,path", SMALL_CASES)
@@ -114,7 +115,8 @@ def test_forward_parity_full(name, T, path):
     assert err <= tol_for(name)
 
 
-@pytest.mark.parametrize("name,T,nsample", [("c2", 4096, 48), ("c3", 8192, 40), ("c4", 16384, 24)])
+@pytest.mark.parametrize("name,T,nsample", [("c2", 4096, 48), ("c3", 8192, 40), ("c4", 16384, 24),
+                                            ("c2-w4a8", 4096, 48)])
 @pytest.mark.timeout(900)
 def test_forward_parity_full_size_sampled(name, T, nsample):
     say(f"forward parity full size {name} T={T} (sample {nsample}), packed weights as the benchmark runs")
