@@ -206,16 +206,6 @@ __device__ __forceinline__ void mxfp8_block(const uint4 (&v)[4], uint8_t* q, uin
   *sc = static_cast<uint8_t>(code);
 }
 
-// Largest value over the 32 lanes of each half-wave (ds_swizzle butterfly).
-__device__ __forceinline__ float half_wave_max(float v) {
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-  return v;
-}
-
 // ------------------------------------------------------------ wave ops ----
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -245,6 +235,16 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16 lanes
+
+// Largest value over the 32 lanes of each half-wave: DPP within each 16-lane
+// row, then one swizzle exchanging rows 0 <-> 1 and 2 <-> 3 (lane ^ 16).
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f<kDppXor1>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppXor2>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = __builtin_fmaxf(v, dpp_f<kDppMirror>(v));
+  return __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+}
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
@@ -313,8 +313,10 @@ __device__ __forceinline__ void wg_amax_to_slots(float m, uint32_t* slots, float
 }
 
 // silu(g) * u in fp32.
+// silu(g) * u with the hardware exponential and reciprocal (about 1 ulp
+// each), instead of an IEEE division.
 __device__ __forceinline__ float swiglu(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 }  // namespace ftmoe

@@ -305,6 +305,46 @@ __device__ __forceinline__ void frag_read_mx8_4(uint32_t vB, uint32_t vS, uint32
         "n"(OAM), "n"(OAS));
 }
 
+// Fragment groups of the software-pipelined MXFP8-activation stage (read
+// while the previous stage's MFMAs run): the four weight vectors; the
+// weight and activation scale dwords; the two activation vectors of one row
+// tile.
+template <int OB1, int OB2, int OB3>
+__device__ __forceinline__ void frag_read_b4(uint32_t vB, u32x4 (&b)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:%5\n"
+      "ds_read_b128 %2, %4 offset:%6\n"
+      "ds_read_b128 %3, %4 offset:%7\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+      : "v"(vB), "n"(OB1), "n"(OB2), "n"(OB3));
+}
+
+template <int OS1, int OS2, int OS3, int OAS>
+__device__ __forceinline__ void frag_read_sc(uint32_t vS, uint32_t vAS, uint32_t (&s)[4], uint32_t (&as)[2]) {
+  asm volatile(
+      "ds_read_b32 %0, %6\n"
+      "ds_read_b32 %1, %6 offset:%8\n"
+      "ds_read_b32 %2, %6 offset:%9\n"
+      "ds_read_b32 %3, %6 offset:%10\n"
+      "ds_read_b32 %4, %7\n"
+      "ds_read_b32 %5, %7 offset:%11\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]), "=&v"(as[0]), "=&v"(as[1])
+      : "v"(vS), "v"(vAS), "n"(OS1), "n"(OS2), "n"(OS3), "n"(OAS));
+}
+
+template <int OFF>
+__device__ __forceinline__ void frag_read_a2(uint32_t vA0, uint32_t vA1, u32x4& a0, u32x4& a1) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n"
+      "ds_read_b128 %1, %3 offset:%4\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(a0), "=&v"(a1)
+      : "v"(vA0), "v"(vA1), "n"(OFF));
+}
+
 // FP8 weights and activations, 4 column tiles: two vectors per operand row.
 template <int OB1, int OB2, int OB3, int OAM>
 __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
@@ -711,14 +751,80 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     }
   };
 
-  // prologue: stages 0 .. kRing - 2 into buffers 0 .. kRing - 2
+  if constexpr (C::kAScales && FP8ACT) {
+    // MXFP8 activations: software-pipelined stages.  The fragments of stage
+    // s are in registers when step s starts; its MFMAs are issued in four
+    // groups, and between them the fragments of stage s + 1 are read into
+    // the other register set, so the LDS reads of one wave overlap the MFMA
+    // work of its SIMD.  Buffer s is refilled (stage s + kRing) at step s,
+    // after the barrier that follows every wave's reads of it in step s - 1.
+    static_assert(C::kRing % 2 == 0 && NT == 4, "pipelined stages");
+    struct Frag {
+      u32x4 b[4];
+      uint32_t s[4], as[2];
+      u32x4 a[4];
+    };
+    Frag fr[2];
+    auto read_frags = [&](uint32_t base, Frag& f, int part) {
+      if (part == 0) frag_read_b4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB>(base + bo[0], f.b);
+      if (part == 1) frag_read_sc<kD1 * 4, kD2 * 4, kD3 * 4, 32 * 4>(base + so, base + sao, f.s, f.as);
+      if (part == 2) frag_read_a2<0>(base + ao[0], base + ao[1], f.a[0], f.a[1]);
+      if (part == 3) frag_read_a2<kOAM>(base + ao[0], base + ao[1], f.a[2], f.a[3]);
+    };
+    auto pipe_step = [&](int s, Frag& cur, Frag& nxt, uint8_t* refill, uint8_t* nextbuf) {
+      wait_vm<C::kVmPerStage * (C::kRing - 2)>();
+      stage_barrier();
+      issue(refill);
+      const int sh = 16 * (s & 1) + 8 * g;
+      int sa[2], sb[4];
 #pragma unroll
-  for (int i = 0; i < C::kRing - 1; ++i) issue(ring + i * C::kSlotBytes);
-  for (int s = 0; s < ns; s += C::kRing) {
+      for (int m = 0; m < 2; ++m) sa[m] = static_cast<int>(cur.as[m] >> sh);
 #pragma unroll
-    for (int r = 0; r < C::kRing; ++r) {
-      if (s + r >= ns) break;
-      step(s + r, ring + r * C::kSlotBytes, ring + ((r + C::kRing - 1) % C::kRing) * C::kSlotBytes);
+      for (int ct = 0; ct < NT; ++ct) sb[ct] = static_cast<int>(cur.s[ct] >> sh);
+      const i32x8 a[2] = {u4x2(to_u4(cur.a[0]), to_u4(cur.a[1])), u4x2(to_u4(cur.a[2]), to_u4(cur.a[3]))};
+      const uint32_t base = lds_addr(nextbuf);
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int m = grp >> 1;
+        if (rows_ok[m]) {
+#pragma unroll
+          for (int ct = 2 * (grp & 1); ct < 2 * (grp & 1) + 2; ++ct) {
+            const uint4 c = to_u4(cur.b[ct]);
+            const i32x8 bq = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z),
+                              static_cast<int>(c.w), 0, 0, 0, 0};
+            acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[m], bq, acc[m][ct], 0, 4, 0, sa[m], 0, sb[ct]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(base, nxt, grp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // prologue: stages 0 .. kRing - 1 into every buffer, then stage 0's fragments
+#pragma unroll
+    for (int i = 0; i < C::kRing; ++i) issue(ring + i * C::kSlotBytes);
+    wait_vm<C::kVmPerStage * (C::kRing - 1)>();
+    stage_barrier();
+#pragma unroll
+    for (int part = 0; part < 4; ++part) read_frags(lds_addr(ring), fr[0], part);
+    for (int s = 0; s < ns; s += C::kRing) {
+#pragma unroll
+      for (int r = 0; r < C::kRing; ++r) {
+        if (s + r >= ns) break;
+        pipe_step(s + r, fr[r & 1], fr[(r + 1) & 1], ring + r * C::kSlotBytes,
+                  ring + ((r + 1) % C::kRing) * C::kSlotBytes);
+      }
+    }
+  } else {
+    // prologue: stages 0 .. kRing - 2 into buffers 0 .. kRing - 2
+#pragma unroll
+    for (int i = 0; i < C::kRing - 1; ++i) issue(ring + i * C::kSlotBytes);
+    for (int s = 0; s < ns; s += C::kRing) {
+#pragma unroll
+      for (int r = 0; r < C::kRing; ++r) {
+        if (s + r >= ns) break;
+        step(s + r, ring + r * C::kSlotBytes, ring + ((r + C::kRing - 1) % C::kRing) * C::kSlotBytes);
+      }
     }
   }
   wait_vm<0>();   // no DMA into LDS may outlive the workgroup
@@ -728,26 +834,62 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   if constexpr (WFMT != kMXFP4) f = w.tscale[e];
   if constexpr (FP8ACT && WFMT == kFP8) f *= amax_scale(ga.amax_a);
   if constexpr (GATEUP && C::kAScales && FP8ACT) {
-    // MXFP8 h straight from the accumulators: the 32 columns of a block are
-    // the 32 lanes of a half-wave (one row per register), so the block
-    // maximum is a half-wave reduction and each lane writes its own code.
-    uint8_t* hq = static_cast<uint8_t*>(ga.out);
+    // MXFP8 h from the fp32 accumulators: the 32 columns of a block are the
+    // 32 lanes of a half-wave (one row per register), so the block maximum
+    // is a half-wave reduction.  Codes and scales are collected in LDS (the
+    // ring is free now) and leave as 16-byte pieces of rows.
+    constexpr int kSBlk = kHalf / 32;   // scale bytes per tile row
+    __syncthreads();
+    uint8_t* qt = ring;                  // [BM][kHalf] codes
+    uint8_t* st = ring + BM * kHalf;     // [BM][kSBlk] scale codes
 #pragma unroll
     for (int u = 0; u < NT / 2; ++u) {
-      const int col = tile_col(Rt[u] + j);   // gate column of this lane
+      const int cl = Rt[u] + j;   // column within the workgroup's half tile
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        // the 16 rows of this register set at once: independent reduction
+        // chains (|v| compared as integers, exact for non-negative floats)
+        float v[16];
+        int am[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v[r] = swiglu(acc[m][u][r], acc[m][u + NT / 2][r]);
+          am[r] = static_cast<int>(__float_as_uint(v[r]) & 0x7FFFFFFFu);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor1>(am[r]));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor2>(am[r]));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppHalfMirror>(am[r]));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppMirror>(am[r]));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = max(am[r], __builtin_amdgcn_ds_swizzle(am[r], 0x401F));   // lane ^ 16
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float v = swiglu(acc[m][u][r], acc[m][u + NT / 2][r]);
-          const uint32_t code = mxfp8_scale_code(half_wave_max(__builtin_fabsf(v)));
-          if (!wact || i >= nvalid) continue;
-          const size_t row = static_cast<size_t>(b * BM + i);
-          hq[row * N + col] = static_cast<uint8_t>(f32x2_to_e4m3x2(v * mx_inv_scale(code), 0.f) & 0xFF);
-          if (j == 0) ga.out_sc[row * ga.out_sc_pitch + col / 32] = static_cast<uint8_t>(code);
+          const uint32_t code = mxfp8_scale_code(__int_as_float(am[r]));
+          qt[i * kHalf + cl] = static_cast<uint8_t>(f32x2_to_e4m3x2(v[r] * mx_inv_scale(code), 0.f) & 0xFF);
+          if (j == 0) st[i * kSBlk + cl / 32] = static_cast<uint8_t>(code);
         }
       }
+    }
+    __syncthreads();
+    uint8_t* hq = static_cast<uint8_t*>(ga.out);
+    constexpr int kRowVec = kHalf / 16;
+    for (int q = threadIdx.x; q < BM * kRowVec; q += kGemmThreads) {
+      const int i = q / kRowVec, c = 16 * (q % kRowVec);
+      const int col = nt * kHalf + c;
+      if (i >= nvalid || col >= N) continue;
+      *reinterpret_cast<uint4*>(hq + static_cast<size_t>(b * BM + i) * N + col) =
+          *reinterpret_cast<const uint4*>(qt + i * kHalf + c);
+    }
+    for (int q = threadIdx.x; q < BM * kSBlk; q += kGemmThreads) {
+      const int i = q / kSBlk, cb = q % kSBlk;
+      const int col = nt * kHalf + 32 * cb;
+      if (i >= nvalid || col >= N) continue;
+      ga.out_sc[static_cast<size_t>(b * BM + i) * ga.out_sc_pitch + col / 32] = st[i * kSBlk + cb];
     }
   } else if constexpr (GATEUP && C::kSplitA) {
     // h rounded to bf16 goes through LDS (the ring is free now) so that each
