@@ -54,8 +54,11 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 // significant bits fewer).  Each product x * w_i of a bf16 x is exact in
 // fp32 and the MFMA accumulates in fp32, so the logits keep fp32 accuracy.
 // Workgroup: 64 tokens x 64 router rows, 4 waves of one 32 x 32 tile each;
-// K stages of 64 staged through LDS (rows of 128 bytes, XOR-swizzled).
-constexpr int kRT = 64, kRE = 64, kRK = 64;
+// K stages of 64 staged through LDS (rows of 128 bytes, XOR-swizzled).  The
+// global loads of stage k + 1 are issued before the MFMA work of stage k.
+// (Every workgroup re-reads its 64 fp32 router rows, so larger token tiles
+// would save L2 traffic, but T = 4096 then leaves CUs idle.)
+constexpr int kRT = 64, kRE = 64, kRK = 64, kRThreads = 256;
 
 __device__ __forceinline__ int rswz(int r, int q) { return q ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
@@ -66,10 +69,10 @@ __device__ __forceinline__ void split3(float w, uint16_t& a, uint16_t& b, uint16
   c = f32_to_bf16(r1 - bf16_to_f32(b));
 }
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                          const float* __restrict__ router_w, int E,
-                                                          const float* __restrict__ shared_gate_w,
-                                                          float* __restrict__ logits) {
+__global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                                const float* __restrict__ router_w, int E,
+                                                                const float* __restrict__ shared_gate_w,
+                                                                float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
   const int rows = E + (shared_gate_w ? 1 : 0);
@@ -78,49 +81,56 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
   const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
   const int j = lane & 31, g = lane >> 5;
 
-  // staging: thread tid owns row tid / 4, vectors 2 (tid % 4) and + 1 of the
-  // 128-byte stage row (x: 16 bf16 per thread; W: 16 fp32 -> 3 x 16 bf16)
-  const int sr = tid >> 2, sq = (tid & 3) * 2;
-  const int t = t0 + sr, e = e0 + sr;
+  // staging: x row tid / 4, vectors 2 (tid % 4) and + 1 of its 128-byte stage
+  // row; W row tid / 4, 16 fp32 (vectors 2 (tid % 4) and + 1 of each bf16 plane)
+  const int xr = tid >> 2, xq = (tid & 3) * 2;
+  const int wr = tid >> 2, wq = (tid & 3) * 2;
+  const int t = t0 + xr, e = e0 + wr;
   const uint16_t* xrow = t < T ? x + static_cast<size_t>(t) * H : nullptr;
   const float* wrow = e < E ? router_w + static_cast<size_t>(e) * H : (e == E ? shared_gate_w : nullptr);
 
-  f32x16 acc = {};
-  for (int k0 = 0; k0 < H; k0 += kRK) {
-    uint4 xv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  uint4 xv[2];
+  float4 wv[4];
+  auto load = [&](int k0) {
+    xv[0] = xv[1] = make_uint4(0, 0, 0, 0);
     if (xrow) {
-      xv[0] = *reinterpret_cast<const uint4*>(xrow + k0 + sq * 8);
-      xv[1] = *reinterpret_cast<const uint4*>(xrow + k0 + sq * 8 + 8);
+      xv[0] = *reinterpret_cast<const uint4*>(xrow + k0 + xq * 8);
+      xv[1] = *reinterpret_cast<const uint4*>(xrow + k0 + xq * 8 + 8);
     }
-    float wv[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (wrow) f = *reinterpret_cast<const float4*>(wrow + k0 + sq * 8 + 4 * i);
-      wv[4 * i] = f.x;
-      wv[4 * i + 1] = f.y;
-      wv[4 * i + 2] = f.z;
-      wv[4 * i + 3] = f.w;
-    }
-    __syncthreads();   // the previous stage's reads are done
+    for (int i = 0; i < 4; ++i)
+      wv[i] = wrow ? *reinterpret_cast<const float4*>(wrow + k0 + wq * 8 + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto store = [&]() {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int off = sr * 128 + 16 * rswz(sr, sq + h);
-      *reinterpret_cast<uint4*>(xs + off) = xv[h];
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(xs + xr * 128 + 16 * rswz(xr, xq + h)) = xv[h];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {   // bf16 vector wq + v: fp32 elements 8v .. 8v + 7 of the thread's 16
+      const float f[8] = {wv[2 * v].x, wv[2 * v].y, wv[2 * v].z, wv[2 * v].w,
+                          wv[2 * v + 1].x, wv[2 * v + 1].y, wv[2 * v + 1].z, wv[2 * v + 1].w};
       uint32_t p[3][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint16_t a0, b0, c0, a1, b1, c1;
-        split3(wv[8 * h + 2 * i], a0, b0, c0);
-        split3(wv[8 * h + 2 * i + 1], a1, b1, c1);
+        split3(f[2 * i], a0, b0, c0);
+        split3(f[2 * i + 1], a1, b1, c1);
         p[0][i] = a0 | (static_cast<uint32_t>(a1) << 16);
         p[1][i] = b0 | (static_cast<uint32_t>(b1) << 16);
         p[2][i] = c0 | (static_cast<uint32_t>(c1) << 16);
       }
+      const int off = wr * 128 + 16 * rswz(wr, wq + v);
 #pragma unroll
       for (int m = 0; m < 3; ++m) *reinterpret_cast<uint4*>(ws[m] + off) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
     }
+  };
+
+  f32x16 acc = {};
+  load(0);
+  for (int k0 = 0; k0 < H; k0 += kRK) {
+    __syncthreads();   // the previous stage's reads are done
+    store();
     __syncthreads();
+    if (k0 + kRK < H) load(k0 + kRK);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
@@ -155,7 +165,7 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
       return launch(router_gemv_kernel<kGemvMaxT>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   } else {
     dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE);
-    return launch(router_gemm_kernel, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
+    return launch(router_gemm_kernel, grid, dim3(kRThreads), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   }
 }
 
