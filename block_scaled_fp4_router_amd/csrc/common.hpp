@@ -312,7 +312,16 @@ __device__ __forceinline__ void wg_amax_to_slots(float m, uint32_t* slots, float
   }
 }
 
-// silu(g) * u in fp32.
+// The same from one wave, without LDS: its lane 0 updates the slot of
+// (workgroup, wave).
+__device__ __forceinline__ void wave_amax_to_slots(float m, uint32_t* slots) {
+  m = wave_max_fast(m);
+  if (lane_id() == 0) {
+    const unsigned slot = (blockIdx.x * 8u + (threadIdx.x >> 6)) % kAmaxSlots;
+    atomicMax(slots + slot * kAmaxStride, __float_as_uint(m));
+  }
+}
+
 // silu(g) * u with the hardware exponential and reciprocal (about 1 ulp
 // each), instead of an IEEE division.
 __device__ __forceinline__ float swiglu(float g, float u) {

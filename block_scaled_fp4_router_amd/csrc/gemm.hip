@@ -42,6 +42,8 @@
 // Workgroups are numbered so that each XCD (workgroup w runs on XCD w % 8)
 // receives runs of consecutive (block, tile) pairs: the column tiles of a
 // row block, and the row blocks of one expert, then share that XCD's L2.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -169,6 +171,13 @@ __device__ __forceinline__ i32x8 u4x2(const uint4& p, const uint4& q) {
 // waited for explicitly before the barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// One LDS dword, waited for.
+__device__ __forceinline__ int lds_i32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n s_waitcnt lgkmcnt(0)\n" : "=v"(v) : "v"(addr));
+  return v;
 }
 
 // FP4 weights, 4 column tiles: weight vectors, scale dwords, activation vectors.
@@ -438,32 +447,29 @@ struct GemmArgs {
   uint32_t* amax_slots;      // gate_up with FP8 activations: partial maxima of |h|
 };
 
-template <int WFMT, bool FP8ACT, int BM, bool GATEUP>
+template <int WFMT, bool FP8ACT, int BM, bool GATEUP, bool PERSIST>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   using C = Cfg<WFMT, FP8ACT, BM>;
   constexpr int NT = C::kNT;
+  // MXFP8 activations: fragments of the next stage are read while the
+  // current stage's MFMAs run (two register sets)
+  constexpr bool kPipe = C::kAScales && FP8ACT;
+  constexpr int kAhead = kPipe ? C::kRing : C::kRing - 1;   // stages in flight ahead of the MFMA work
   __shared__ __attribute__((aligned(16))) uint8_t ring[C::kRing * C::kSlotBytes];
-  __shared__ int flat_of[BM];
-  __shared__ float red[kGemmWaves];
 
   const Rows& rows = ga.rows;
   const QW& w = ga.w;
   const int K = ga.K, N = ga.N;
   const int ntile = GATEUP ? (N + C::kBN / 2 - 1) / (C::kBN / 2) : (N + C::kBN - 1) / C::kBN;
-  const int t = logical_tile(blockIdx.x);
-  if (t >= rows.num_blocks * ntile) return;
-  const int b = t / ntile, nt = t % ntile;
-  const int e = rows.sorted_ids ? rows.block_expert[b] : 0;
-  if (e < 0) return;
-  const int nvalid = block_rows(rows, b, e, BM);
+  const int total = rows.num_blocks * ntile;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int wm = wave % C::kWM, wn = wave / C::kWM;
   const int arow0 = wm * 64;
   const int j = lane & 31, g = lane >> 5;
   const int ns = K / kStageK;
 
-  // weight row (within the expert's matrix) of tile row R, or -1 past N
-  auto tile_col = [&](int R) -> int {
+  // weight row (within the expert's matrix) of tile row R of column tile nt, or -1 past N
+  auto tile_col = [&](int nt, int R) -> int {
     if constexpr (GATEUP) {
       const int half = C::kBN / 2;
       const int c = nt * half + (R < half ? R : R - half);
@@ -484,10 +490,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     else
       Rt[ct] = 32 * (wn * NT + ct);
   }
-  const bool wact = tile_col(Rt[0]) >= 0;
-  const bool rows_ok[2] = {wact && arow0 < nvalid, wact && arow0 + 32 < nvalid};
 
-  // ---- DMA sources: chunks wave, wave + 8, ... of every stage (A first) ----
+  // ---- the workgroup's tiles ----
+  // Tile k of this workgroup is logical_tile(blockIdx.x + k * gridDim.x):
+  // ascending in k, and the grid is a multiple of 8 workgroups, so every
+  // tile of a workgroup comes from its own XCD's chunks.  The sequence ends
+  // at `total` or at the first block without an expert (the padding blocks
+  // are at the end of the list).
+  auto tile_bnt = [&](int k, int& b, int& nt) -> bool {
+    const int t = logical_tile(static_cast<int>(blockIdx.x) + k * static_cast<int>(gridDim.x));
+    b = t / ntile;
+    nt = t % ntile;
+    return t < total;
+  };
+  // The sorted row ids of a tile's block are copied into LDS (meta[k & 1]) by
+  // wave 0 while the tile before it is fetched, so that no register holds
+  // them across the stages.
+  __shared__ __attribute__((aligned(16))) int meta[2][BM];
+  const int* const sid = rows.sorted_ids;
+  auto meta_fetch = [&](int k, int b) {
+    if (sid && wave == 0 && lane < BM / 4) dma16(sid + b * BM + 4 * lane, reinterpret_cast<uint8_t*>(meta[k & 1]));
+  };
+  // sorted id of tile row r of tile k (from LDS), or of block b directly
+  auto meta_row = [&](int k, int r) -> int { return lds_i32(lds_addr(&meta[k & 1][r])); };
+  // activation row of a sorted id, or of tile row r of block b without sorted ids
+  auto act_row = [&](int f, int b, int r) -> int {
+    if (GATEUP && sid) return f < rows.n_flat ? f / rows.top_k : 0;
+    if (GATEUP) {
+      const int p = b * BM + r;
+      return p < rows.n_flat ? p : 0;
+    }
+    return b * BM + r;   // h rows of the block (padding rows hold unused values)
+  };
+
+  // ---- DMA side: the tile whose stages are being fetched ----
   // 32-bit per-lane offsets from uniform bases (one expert's matrix < 4 GiB)
   const size_t wrows = static_cast<size_t>(GATEUP ? 2 * N : N);
   const uint32_t wrow_bytes = WFMT == kFP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
@@ -496,81 +532,125 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // order, then (FP4) one scale dword per tile row.
   const bool packed = w.packed != nullptr;
   constexpr uint32_t kPackStage = packed_stage_bytes(WFMT);
-  const uint8_t* const wbase =
-      packed ? w.packed + (static_cast<size_t>(e) * ntile + nt) * ns * kPackStage
-             : w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
   const uint32_t badv = packed ? kPackStage : C::kBRowB;   // weight source advance per stage
+  const uint32_t spitch = WFMT == kMXFP4 ? K / 32 : K / 16;  // row-major block-scale bytes per row
+  const uint8_t* wbase = nullptr;   // the tile's weight stages
+  const uint8_t* sbase = nullptr;   // its block scales
   uint32_t src[C::kChunksPerWave];
+  uint32_t soff = 0, aoff = 0;      // this lane's block-scale and activation-scale offsets
+  int dnext = 0;        // next stage of the DMA tile
+  bool dlive = false;   // the DMA tile exists (else stages are refetched into buffers nobody reads)
+  // sources of tile k (block b, column tile nt, expert e); f(r) gives the
+  // sorted id of tile row r
+  auto set_sources = [&](int b, int nt, int e, auto f) {
+    wbase = packed ? w.packed + (static_cast<size_t>(e) * ntile + nt) * ns * kPackStage
+                   : w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
 #pragma unroll
-  for (int i = 0; i < C::kChunksPerWave; ++i) {
-    const int c = wave + kGemmWaves * i;
-    if (c < C::kAChunks) {
-      const int v = c * 64 + lane;
-      const int r = v / C::kAV, q = swz<C::kAV>(r, v % C::kAV);
-      int row;
-      if (GATEUP && rows.sorted_ids) {
-        const int f = rows.sorted_ids[b * BM + r];
-        row = f < rows.n_flat ? f / rows.top_k : 0;
-      } else if (GATEUP) {
-        const int p = b * BM + r;
-        row = p < rows.n_flat ? p : 0;
+    for (int i = 0; i < C::kChunksPerWave; ++i) {
+      const int c = wave + kGemmWaves * i;
+      if (c < C::kAChunks) {
+        const int v = c * 64 + lane;
+        const int r = v / C::kAV;
+        src[i] = static_cast<uint32_t>(act_row(f(r), b, r)) * ga.a_row_bytes + 16 * swz<C::kAV>(r, v % C::kAV);
       } else {
-        row = b * BM + r;   // h rows of the block (padding rows hold unused values)
+        const int v = (c - C::kAChunks) * 64 + lane;
+        const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
+        const int col = tile_col(nt, R);
+        src[i] = packed ? 16u * static_cast<uint32_t>(v) : static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
       }
-      src[i] = static_cast<uint32_t>(row) * ga.a_row_bytes + 16 * q;
-    } else {
-      const int v = (c - C::kAChunks) * 64 + lane;
-      const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
-      const int col = tile_col(R);
-      src[i] = packed ? 16u * static_cast<uint32_t>(v) : static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
     }
-  }
-  // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
-  // dword of tile row w * kScaleRowsPerWave + l per stage (for MXFP4 it holds
-  // the scales of two stages, for NVFP4 those of one; the byte is picked at
-  // use).
-  const uint8_t* ssrc = nullptr;
-  if constexpr (C::kScales) {
-    const int R = wave * C::kScaleRowsPerWave + (lane < C::kScaleRowsPerWave ? lane : 0);
-    if (packed) {
-      ssrc = wbase + C::kBBytes + 4 * R;
-    } else {
-      const int col = tile_col(R);
-      const size_t row = static_cast<size_t>(e) * wrows + (col < 0 ? 0 : col);
-      ssrc = WFMT == kMXFP4 ? w.scales + row * (K / 32) : w.scales + row * (K / 16);
+    // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
+    // dword of tile row w * kScaleRowsPerWave + l per stage (for MXFP4 it
+    // holds the scales of two stages, for NVFP4 those of one; the byte is
+    // picked at use).
+    if constexpr (C::kScales) {
+      const int R = wave * C::kScaleRowsPerWave + (lane < C::kScaleRowsPerWave ? lane : 0);
+      if (packed) {
+        sbase = wbase;
+        soff = C::kBBytes + 4 * R;
+      } else {
+        const int col = tile_col(nt, R);
+        sbase = w.scales + static_cast<size_t>(e) * wrows * spitch;
+        soff = static_cast<uint32_t>(col < 0 ? 0 : col) * spitch;
+      }
     }
-  }
-  // Activation scales (MXFP4): lanes l < kARowsPerWave of wave w fetch the
-  // scale dword of tile row w * kARowsPerWave + l (two stages).
-  const uint8_t* asrc = nullptr;
-  if constexpr (C::kAScales) {
-    const int r = wave * C::kARowsPerWave + (lane < C::kARowsPerWave ? lane : 0);
-    int row;
-    if (GATEUP && rows.sorted_ids) {
-      const int f = rows.sorted_ids[b * BM + r];
-      row = f < rows.n_flat ? f / rows.top_k : 0;
-    } else if (GATEUP) {
-      const int p = b * BM + r;
-      row = p < rows.n_flat ? p : 0;
-    } else {
-      row = b * BM + r;
+    // Activation scales (MXFP4): lanes l < kARowsPerWave of wave w fetch the
+    // scale dword of tile row w * kARowsPerWave + l (two stages).
+    if constexpr (C::kAScales) {
+      const int r = wave * C::kARowsPerWave + (lane < C::kARowsPerWave ? lane : 0);
+      aoff = static_cast<uint32_t>(act_row(f(r), b, r)) * ga.a_sc_pitch;
     }
-    asrc = ga.a_sc + static_cast<size_t>(row) * ga.a_sc_pitch;
+    dnext = 0;
+  };
+
+  // ---- compute side: the tile whose MFMA work runs ----
+  int cb = 0, cnt = 0, ce = 0, cflat = 0, nvalid = 0;
+  bool wact = false, rows_ok[2] = {false, false};
+  auto enter = [&](int b, int nt, int e, int nv, int flat) {
+    cb = b;
+    cnt = nt;
+    ce = e;
+    cflat = flat;
+    nvalid = nv;
+    wact = tile_col(cnt, Rt[0]) >= 0;
+    rows_ok[0] = wact && arow0 < nvalid;
+    rows_ok[1] = wact && arow0 + 32 < nvalid;
+  };
+
+  // first tile: metadata straight from global memory
+  int dk = 0;   // sequence number of the DMA tile
+  {
+    int b, nt;
+    if (!tile_bnt(0, b, nt)) return;
+    const int e = sid ? rows.block_expert[b] : 0;
+    if (e < 0) return;
+    auto fsid = [&](int r) -> int { return sid ? sid[b * BM + r] : 0; };
+    set_sources(b, nt, e, fsid);
+    dlive = true;
+    int flat = 0;
+    if constexpr (!GATEUP) flat = sid ? sid[b * BM + arow0 + lane] : b * BM + arow0 + lane;
+    enter(b, nt, e, block_rows(rows, b, e, BM), flat);
   }
-  if (!GATEUP && threadIdx.x < BM) {
-    const int p = b * BM + threadIdx.x;
-    flat_of[threadIdx.x] = rows.sorted_ids ? rows.sorted_ids[p] : p;
+  // the tile after the DMA tile: block, column tile, expert (uniform)
+  int nb = 0, nnt = 0, ne = -1;
+  if constexpr (PERSIST) {
+    const bool nok0 = tile_bnt(1, nb, nnt);
+    ne = nok0 ? (sid ? rows.block_expert[nb] : 0) : -1;
+    if (nok0) meta_fetch(1, nb);
   }
+  // the compute side's next tile, once the DMA side reached it
+  int qb = 0, qnt = 0, qe = 0, qnv = 0;
+  bool have_next = false;
+
+  // After the DMA tile's last stage has been issued, the fetching continues
+  // with the workgroup's next tile (called at the step whose issue would be
+  // its first stage); past the last tile the sources stop advancing and the
+  // last stage is fetched again into buffers nobody reads.
+  auto next_dma_tile = [&]() {
+    if (PERSIST && ne >= 0) {
+      ++dk;
+      const int k = dk;
+      set_sources(nb, nnt, ne, [&](int r) -> int { return sid ? meta_row(k, r) : 0; });
+      qb = nb;
+      qnt = nnt;
+      qe = ne;
+      qnv = block_rows(rows, nb, ne, BM);
+      have_next = true;
+      const bool ok = tile_bnt(dk + 1, nb, nnt);
+      ne = ok ? (sid ? rows.block_expert[nb] : 0) : -1;
+      if (ok) meta_fetch(dk + 1, nb);
+    } else {
+      dlive = false;
+    }
+  };
 
   // Issues the next stage into `buf`: the wave's DMA chunks, then its scale
   // rows.  Every step issues exactly one stage, so the number of memory
-  // operations in flight per stage is a constant; past the last stage the
-  // sources stop advancing and the last stage is fetched again into a buffer
-  // nobody reads.
-  int next = 0;
+  // operations in flight per stage is a constant.
   auto issue = [&](uint8_t* buf) {
-    const int cur_stage = next;
-    const bool adv = ++next < ns;
+    const int cur_stage = dnext;
+    const bool adv = dlive && dnext + 1 < ns;
+    dnext += dnext < ns ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < C::kChunksPerWave; ++i) {
       const int c = wave + kGemmWaves * i;
@@ -578,17 +658,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       src[i] += adv ? (c < C::kAChunks ? static_cast<uint32_t>(C::kARowB) : badv) : 0;
     }
     if constexpr (C::kScales) {
-      if (lane < C::kScaleRowsPerWave) dma4(ssrc, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
+      if (lane < C::kScaleRowsPerWave) dma4(sbase + soff, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
       // row-major MXFP4: stages 2m and 2m + 1 share the dword at 4m
       if (packed)
-        ssrc += adv ? kPackStage : 0;
+        soff += adv ? kPackStage : 0;
       else
-        ssrc += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
+        soff += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
     }
     if constexpr (C::kAScales) {
       if (lane < C::kARowsPerWave)
-        dma4(asrc, buf + C::kABytes + C::kBBytes + C::kSBytes + wave * 4 * C::kARowsPerWave);
-      asrc += adv && (cur_stage & 1) ? 4 : 0;
+        dma4(ga.a_sc + aoff, buf + C::kABytes + C::kBBytes + C::kSBytes + wave * 4 * C::kARowsPerWave);
+      aoff += adv && (cur_stage & 1) ? 4 : 0;
     }
   };
 
@@ -637,24 +717,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   constexpr int kAVec = FP8ACT ? 4 : 8;
 
   f32x16 acc[2][NT];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[m][ct] = f32x16{};
 
-  // One stage from ring buffer `cur`: wait for its DMA, barrier, read the
-  // fragments, refill the buffer the previous stage used, then the MFMA work.
+  // One stage of the compute tile from ring buffer `cur`: wait for its DMA,
+  // barrier, read the fragments, refill the buffer the previous stage used,
+  // then the MFMA work.
   auto step = [&](int s, uint8_t* cur, uint8_t* refill) {
+    if constexpr (!kPipe) {
     wait_vm<C::kVmPerStage * (C::kRing - 2)>();
     stage_barrier();
     const uint32_t base = lds_addr(cur);
     u32x4 bv[kBVec], av[kAVec];
     uint32_t scw[NT], asw[2];
-    if constexpr (C::kAScales && FP8ACT) {
-      static_assert(NT == 4, "MXFP8 activations use 128-row blocks");
-      frag_read_mx8_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM, 32 * 4>(
-          base + bo[0], base + so, base + sao, base + ao[0], base + ao[1], bv, scw, asw, av);
-    } else if constexpr (C::kSplitA) {
+    if constexpr (C::kSplitA) {
       const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
       if constexpr (NT == 4)
         frag_read_mx_4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB, kD1 * 4, kD2 * 4, kD3 * 4, kOAM, 32 * 4>(
@@ -678,24 +752,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
                                                                                     bv, av);
     }
     issue(refill);
-    if constexpr (C::kAScales && FP8ACT) {
-      // one scaled MFMA: E4M3 activations (format 0) x E2M1 weights (format 4)
-      const int sh = 16 * (s & 1) + 8 * g;
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (!rows_ok[m]) continue;
-        const int sa = static_cast<int>(asw[m] >> sh);
-        const i32x8 a = u4x2(to_u4(av[2 * m]), to_u4(av[2 * m + 1]));
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const uint4 c = to_u4(bv[ct]);
-          const i32x8 bq = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w),
-                            0, 0, 0, 0};
-          acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, acc[m][ct], 0, 4, 0, sa,
-                                                                       0, static_cast<int>(scw[ct] >> sh));
-        }
-      }
-    } else if constexpr (C::kSplitA) {
+    if constexpr (C::kSplitA) {
       // the E8M0 bytes of this lane's K block: byte 2 (s & 1) + g of the dwords
       const int sh = 16 * (s & 1) + 8 * g;
 #pragma unroll
@@ -716,7 +773,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
           acc[m][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, bq, acc[m][ct], 0, 4, 0, sa - 4, 0, sb);
         }
       }
-    } else if constexpr (FP8ACT) {
+    } else if constexpr (FP8ACT && WFMT == kFP8) {
       i32x8 bq[NT];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) bq[ct] = u4x2(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]));
@@ -749,29 +806,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
         }
       }
     }
+    }
   };
 
-  if constexpr (C::kAScales && FP8ACT) {
-    // MXFP8 activations: software-pipelined stages.  The fragments of stage
-    // s are in registers when step s starts; its MFMAs are issued in four
-    // groups, and between them the fragments of stage s + 1 are read into
-    // the other register set, so the LDS reads of one wave overlap the MFMA
-    // work of its SIMD.  Buffer s is refilled (stage s + kRing) at step s,
-    // after the barrier that follows every wave's reads of it in step s - 1.
-    static_assert(C::kRing % 2 == 0 && NT == 4, "pipelined stages");
-    struct Frag {
-      u32x4 b[4];
-      uint32_t s[4], as[2];
-      u32x4 a[4];
-    };
-    Frag fr[2];
-    auto read_frags = [&](uint32_t base, Frag& f, int part) {
+  // MXFP8 activations: the fragments of stage s are in registers when step s
+  // starts; its MFMAs are issued in four groups, and between them the
+  // fragments of the next stage are read into the other register set.  The
+  // buffer of stage s is refilled at step s, after the barrier that follows
+  // every wave's reads of it in step s - 1.
+  struct Frag {
+    u32x4 b[4];
+    uint32_t s[4], as[2];
+    u32x4 a[4];
+  };
+  Frag fr[2];
+  auto read_frags = [&](uint32_t base, Frag& f, int part) {
+    if constexpr (kPipe) {
       if (part == 0) frag_read_b4<kD1 * C::kBRowB, kD2 * C::kBRowB, kD3 * C::kBRowB>(base + bo[0], f.b);
       if (part == 1) frag_read_sc<kD1 * 4, kD2 * 4, kD3 * 4, 32 * 4>(base + so, base + sao, f.s, f.as);
       if (part == 2) frag_read_a2<0>(base + ao[0], base + ao[1], f.a[0], f.a[1]);
       if (part == 3) frag_read_a2<kOAM>(base + ao[0], base + ao[1], f.a[2], f.a[3]);
-    };
-    auto pipe_step = [&](int s, Frag& cur, Frag& nxt, uint8_t* refill, uint8_t* nextbuf) {
+    }
+  };
+  auto pipe_step = [&](int s, Frag& cur, Frag& nxt, uint8_t* refill, uint8_t* nextbuf) {
+    if constexpr (kPipe) {
       wait_vm<C::kVmPerStage * (C::kRing - 2)>();
       stage_barrier();
       issue(refill);
@@ -799,163 +857,199 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
         read_frags(base, nxt, grp);
         __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    // prologue: stages 0 .. kRing - 1 into every buffer, then stage 0's fragments
+    }
+  };
+
+  // ---- prologue: the first kAhead stages, then (pipelined) stage 0's fragments ----
+  uint32_t G = 0;   // global stage number of the compute side (ring position)
+  auto buf_of = [&](uint32_t stage) -> uint8_t* { return ring + (stage % C::kRing) * C::kSlotBytes; };
 #pragma unroll
-    for (int i = 0; i < C::kRing; ++i) issue(ring + i * C::kSlotBytes);
+  for (int i = 0; i < kAhead; ++i) issue(buf_of(i));
+  if constexpr (kPipe) {
+    static_assert(C::kRing % 2 == 0 && NT == 4, "pipelined stages");
     wait_vm<C::kVmPerStage * (C::kRing - 1)>();
     stage_barrier();
 #pragma unroll
     for (int part = 0; part < 4; ++part) read_frags(lds_addr(ring), fr[0], part);
-    for (int s = 0; s < ns; s += C::kRing) {
+  }
+
+  for (;;) {   // compute tiles
 #pragma unroll
-      for (int r = 0; r < C::kRing; ++r) {
-        if (s + r >= ns) break;
-        pipe_step(s + r, fr[r & 1], fr[(r + 1) & 1], ring + r * C::kSlotBytes,
-                  ring + ((r + 1) % C::kRing) * C::kSlotBytes);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) acc[m][ct] = f32x16{};
+    // the step at which the DMA side moves on to the next tile
+    const int s_next = PERSIST && dlive ? ns - kAhead : -1;
+    if constexpr (!PERSIST) {
+      // one tile: ring positions known at compile time (G = 0 here)
+      for (int s = 0; s < ns; s += C::kRing) {
+#pragma unroll
+        for (int r = 0; r < C::kRing; ++r) {
+          if (s + r >= ns) break;
+          if constexpr (kPipe)
+            pipe_step(s + r, fr[r & 1], fr[(r + 1) & 1], ring + r * C::kSlotBytes,
+                      ring + ((r + 1) % C::kRing) * C::kSlotBytes);
+          else
+            step(s + r, ring + r * C::kSlotBytes, ring + ((r + C::kRing - 1) % C::kRing) * C::kSlotBytes);
+        }
+      }
+      G += ns;
+    } else if constexpr (kPipe) {
+      // ns is even (K is a multiple of 128) and so is G here
+      for (int s = 0; s < ns; s += 2, G += 2) {
+        if (s == s_next) next_dma_tile();
+        pipe_step(s, fr[0], fr[1], buf_of(G), buf_of(G + 1));
+        if (s + 1 == s_next) next_dma_tile();
+        pipe_step(s + 1, fr[1], fr[0], buf_of(G + 1), buf_of(G + 2));
+      }
+    } else {
+      for (int s = 0; s < ns; ++s, ++G) {
+        if (s == s_next) next_dma_tile();
+        step(s, buf_of(G), buf_of(G + C::kRing - 1));
       }
     }
-  } else {
-    // prologue: stages 0 .. kRing - 2 into buffers 0 .. kRing - 2
+
+    // ---- epilogue (registers to global memory; the ring keeps filling) ----
+    const int b = cb, e = ce, nt = cnt;
+    float f = 1.0f;
+    if constexpr (WFMT != kMXFP4) f = w.tscale[e];
+    if constexpr (FP8ACT && WFMT == kFP8) f *= amax_scale(ga.amax_a);
+    // (gate_up runs one tile per workgroup: once the refetches are done the
+    // whole ring is free for the epilogue)
+    if constexpr (GATEUP && C::kAScales) {
+      static_assert(!PERSIST, "the MXFP4 gate_up epilogue uses the ring");
+      wait_vm<0>();
+    }
+    if constexpr (GATEUP && C::kAScales && FP8ACT) {
+      // MXFP8 h from the fp32 accumulators: the 32 columns of a block are the
+      // 32 lanes of a half-wave (one row per register), so the block maximum
+      // is a half-wave reduction.  Codes and scales are collected in LDS (the
+      // ring is free now) and leave as 16-byte pieces of rows.
+      constexpr int kSBlk = kHalf / 32;   // scale bytes per tile row
+      __syncthreads();
+      uint8_t* qt = ring;                  // [BM][kHalf] codes
+      uint8_t* st = ring + BM * kHalf;     // [BM][kSBlk] scale codes
 #pragma unroll
-    for (int i = 0; i < C::kRing - 1; ++i) issue(ring + i * C::kSlotBytes);
-    for (int s = 0; s < ns; s += C::kRing) {
+      for (int u = 0; u < NT / 2; ++u) {
+        const int cl = Rt[u] + j;   // column within the workgroup's half tile
 #pragma unroll
-      for (int r = 0; r < C::kRing; ++r) {
-        if (s + r >= ns) break;
-        step(s + r, ring + r * C::kSlotBytes, ring + ((r + C::kRing - 1) % C::kRing) * C::kSlotBytes);
+        for (int m = 0; m < 2; ++m) {
+          // the 16 rows of this register set at once: independent reduction
+          // chains (|v| compared as integers, exact for non-negative floats)
+          float v[16];
+          int am[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            v[r] = swiglu(acc[m][u][r], acc[m][u + NT / 2][r]);
+            am[r] = static_cast<int>(__float_as_uint(v[r]) & 0x7FFFFFFFu);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor1>(am[r]));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor2>(am[r]));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppHalfMirror>(am[r]));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppMirror>(am[r]));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am[r] = max(am[r], __builtin_amdgcn_ds_swizzle(am[r], 0x401F));   // lane ^ 16
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+            const uint32_t code = mxfp8_scale_code(__int_as_float(am[r]));
+            qt[i * kHalf + cl] = static_cast<uint8_t>(f32x2_to_e4m3x2(v[r] * mx_inv_scale(code), 0.f) & 0xFF);
+            if (j == 0) st[i * kSBlk + cl / 32] = static_cast<uint8_t>(code);
+          }
+        }
+      }
+      __syncthreads();
+      uint8_t* hq = static_cast<uint8_t*>(ga.out);
+      constexpr int kRowVec = kHalf / 16;
+      for (int q = threadIdx.x; q < BM * kRowVec; q += kGemmThreads) {
+        const int i = q / kRowVec, c = 16 * (q % kRowVec);
+        const int col = nt * kHalf + c;
+        if (i >= nvalid || col >= N) continue;
+        *reinterpret_cast<uint4*>(hq + static_cast<size_t>(b * BM + i) * N + col) =
+            *reinterpret_cast<const uint4*>(qt + i * kHalf + c);
+      }
+      for (int q = threadIdx.x; q < BM * kSBlk; q += kGemmThreads) {
+        const int i = q / kSBlk, cb = q % kSBlk;
+        const int col = nt * kHalf + 32 * cb;
+        if (i >= nvalid || col >= N) continue;
+        ga.out_sc[static_cast<size_t>(b * BM + i) * ga.out_sc_pitch + col / 32] = st[i * kSBlk + cb];
+      }
+    } else if constexpr (GATEUP && C::kSplitA) {
+      // h rounded to bf16 goes through LDS (the ring is free now) so that each
+      // thread then splits one 32-column block of a row: tile [BM][kHalf].
+      __syncthreads();
+      uint16_t* tile = reinterpret_cast<uint16_t*>(ring);
+#pragma unroll
+      for (int u = 0; u < NT / 2; ++u) {
+        const int cl = Rt[u] + j;   // column within the workgroup's half tile
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+            tile[i * kHalf + cl] = f32_to_bf16(swiglu(acc[m][u][r], acc[m][u + NT / 2][r]));
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int kBlocks = kHalf / 32;   // 32-column blocks per tile row
+      uint8_t* hsp = static_cast<uint8_t*>(ga.out);
+      for (int q = threadIdx.x; q < BM * kBlocks; q += kGemmThreads) {
+        const int i = q / kBlocks, cb = q % kBlocks;
+        const int col = nt * kHalf + 32 * cb;   // first intermediate index of the block
+        if (i >= nvalid || col >= N) continue;
+        const uint4* src = reinterpret_cast<const uint4*>(tile + i * kHalf + 32 * cb);
+        const uint4 v[4] = {src[0], src[1], src[2], src[3]};
+        const size_t row = static_cast<size_t>(b * BM + i);
+        // a row of split h: per 64 columns, 64 hi codes then 64 lo codes
+        uint8_t* hi = hsp + row * (2 * static_cast<size_t>(N)) + (col / 64) * 128 + (col % 64);
+        mx_split_block(v, hi, hi + 64, ga.out_sc + row * ga.out_sc_pitch + col / 32);
+      }
+    } else if constexpr (GATEUP) {
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < NT / 2; ++u) {
+        const int col = tile_col(nt, Rt[u] + j);   // gate column of this lane
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (!wact || i >= nvalid) continue;
+            const float v = swiglu(acc[m][u][r] * f, acc[m][u + NT / 2][r] * f);
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+            static_cast<uint16_t*>(ga.out)[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
+          }
+        }
+      }
+      if constexpr (FP8ACT) wave_amax_to_slots(mx, ga.amax_slots);
+    } else {
+      const int c0 = nt * C::kBN + Rt[0] + j;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);   // row within the wave's 64
+          const size_t fr_row = static_cast<size_t>(__shfl(cflat, il, kWave));
+          if (!wact || arow0 + il >= nvalid) continue;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct)
+            static_cast<uint16_t*>(ga.out)[fr_row * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
+        }
       }
     }
+
+    if (!PERSIST || !have_next) break;
+    have_next = false;
+    int flat = 0;
+    if constexpr (!GATEUP) flat = sid ? meta_row(dk, arow0 + lane) : qb * BM + arow0 + lane;
+    enter(qb, qnt, qe, qnv, flat);
   }
   wait_vm<0>();   // no DMA into LDS may outlive the workgroup
-
-  // ---- epilogue ----
-  float f = 1.0f;
-  if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-  if constexpr (FP8ACT && WFMT == kFP8) f *= amax_scale(ga.amax_a);
-  if constexpr (GATEUP && C::kAScales && FP8ACT) {
-    // MXFP8 h from the fp32 accumulators: the 32 columns of a block are the
-    // 32 lanes of a half-wave (one row per register), so the block maximum
-    // is a half-wave reduction.  Codes and scales are collected in LDS (the
-    // ring is free now) and leave as 16-byte pieces of rows.
-    constexpr int kSBlk = kHalf / 32;   // scale bytes per tile row
-    __syncthreads();
-    uint8_t* qt = ring;                  // [BM][kHalf] codes
-    uint8_t* st = ring + BM * kHalf;     // [BM][kSBlk] scale codes
-#pragma unroll
-    for (int u = 0; u < NT / 2; ++u) {
-      const int cl = Rt[u] + j;   // column within the workgroup's half tile
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        // the 16 rows of this register set at once: independent reduction
-        // chains (|v| compared as integers, exact for non-negative floats)
-        float v[16];
-        int am[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v[r] = swiglu(acc[m][u][r], acc[m][u + NT / 2][r]);
-          am[r] = static_cast<int>(__float_as_uint(v[r]) & 0x7FFFFFFFu);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor1>(am[r]));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppXor2>(am[r]));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppHalfMirror>(am[r]));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = max(am[r], dpp_i<kDppMirror>(am[r]));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = max(am[r], __builtin_amdgcn_ds_swizzle(am[r], 0x401F));   // lane ^ 16
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-          const uint32_t code = mxfp8_scale_code(__int_as_float(am[r]));
-          qt[i * kHalf + cl] = static_cast<uint8_t>(f32x2_to_e4m3x2(v[r] * mx_inv_scale(code), 0.f) & 0xFF);
-          if (j == 0) st[i * kSBlk + cl / 32] = static_cast<uint8_t>(code);
-        }
-      }
-    }
-    __syncthreads();
-    uint8_t* hq = static_cast<uint8_t*>(ga.out);
-    constexpr int kRowVec = kHalf / 16;
-    for (int q = threadIdx.x; q < BM * kRowVec; q += kGemmThreads) {
-      const int i = q / kRowVec, c = 16 * (q % kRowVec);
-      const int col = nt * kHalf + c;
-      if (i >= nvalid || col >= N) continue;
-      *reinterpret_cast<uint4*>(hq + static_cast<size_t>(b * BM + i) * N + col) =
-          *reinterpret_cast<const uint4*>(qt + i * kHalf + c);
-    }
-    for (int q = threadIdx.x; q < BM * kSBlk; q += kGemmThreads) {
-      const int i = q / kSBlk, cb = q % kSBlk;
-      const int col = nt * kHalf + 32 * cb;
-      if (i >= nvalid || col >= N) continue;
-      ga.out_sc[static_cast<size_t>(b * BM + i) * ga.out_sc_pitch + col / 32] = st[i * kSBlk + cb];
-    }
-  } else if constexpr (GATEUP && C::kSplitA) {
-    // h rounded to bf16 goes through LDS (the ring is free now) so that each
-    // thread then splits one 32-column block of a row: tile [BM][kHalf].
-    __syncthreads();
-    uint16_t* tile = reinterpret_cast<uint16_t*>(ring);
-#pragma unroll
-    for (int u = 0; u < NT / 2; ++u) {
-      const int cl = Rt[u] + j;   // column within the workgroup's half tile
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-          tile[i * kHalf + cl] = f32_to_bf16(swiglu(acc[m][u][r], acc[m][u + NT / 2][r]));
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int kBlocks = kHalf / 32;   // 32-column blocks per tile row
-    uint8_t* hsp = static_cast<uint8_t*>(ga.out);
-    for (int q = threadIdx.x; q < BM * kBlocks; q += kGemmThreads) {
-      const int i = q / kBlocks, cb = q % kBlocks;
-      const int col = nt * kHalf + 32 * cb;   // first intermediate index of the block
-      if (i >= nvalid || col >= N) continue;
-      const uint4* src = reinterpret_cast<const uint4*>(tile + i * kHalf + 32 * cb);
-      const uint4 v[4] = {src[0], src[1], src[2], src[3]};
-      const size_t row = static_cast<size_t>(b * BM + i);
-      // a row of split h: per 64 columns, 64 hi codes then 64 lo codes
-      uint8_t* hi = hsp + row * (2 * static_cast<size_t>(N)) + (col / 64) * 128 + (col % 64);
-      mx_split_block(v, hi, hi + 64, ga.out_sc + row * ga.out_sc_pitch + col / 32);
-    }
-  } else if constexpr (GATEUP) {
-    float mx = 0.f;
-#pragma unroll
-    for (int u = 0; u < NT / 2; ++u) {
-      const int col = tile_col(Rt[u] + j);   // gate column of this lane
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (!wact || i >= nvalid) continue;
-          const float v = swiglu(acc[m][u][r] * f, acc[m][u + NT / 2][r] * f);
-          mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
-          static_cast<uint16_t*>(ga.out)[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
-        }
-      }
-    }
-    if constexpr (FP8ACT) wg_amax_to_slots(mx, ga.amax_slots, red);
-  } else {
-    __syncthreads();   // flat_of
-    const int c0 = nt * C::kBN + Rt[0] + j;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (!wact || i >= nvalid) continue;
-        const size_t fr = static_cast<size_t>(flat_of[i]);
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-          static_cast<uint16_t*>(ga.out)[fr * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------ launches ----
@@ -965,11 +1059,28 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
   const int ntile = GATEUP ? (ga.N + C::kBN / 2 - 1) / (C::kBN / 2) : (ga.N + C::kBN - 1) / C::kBN;
   const int total = ga.rows.num_blocks * ntile;
   if (total == 0) return hipSuccess;
-  if (ga.K % kStageK) return hipErrorInvalidValue;
+  if (ga.K % (2 * kStageK)) return hipErrorInvalidValue;
   // whole chunks for every XCD, so that every tile index is reached
   const int per_round = 8 * kXcdChunk;
-  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP>, dim3(per_round * ((total + per_round - 1) / per_round)),
-                dim3(kGemmThreads), 0, s, ga);
+  int grid = per_round * ((total + per_round - 1) / per_round);
+  // One workgroup fits a CU (LDS), so a grid of about one workgroup per CU
+  // runs every tile with the next tile's first stages fetched during the
+  // current one's last; that needs at least as many stages per tile as are
+  // fetched ahead (else one workgroup per tile).
+  // (The down GEMMs run this way; the gate_up GEMMs, whose epilogue is
+  // longer and whose registers are all in use, run one tile per workgroup.)
+  constexpr int kAhead = C::kAScales && FP8ACT ? C::kRing : C::kRing - 1;
+  if constexpr (!GATEUP) {
+    if (ga.K / kStageK >= kAhead) {
+      int dev = 0, ncu = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        return hipErrorInvalidValue;
+      grid = std::min(grid, per_round * ((ncu + per_round - 1) / per_round));
+      return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP, true>, dim3(grid), dim3(kGemmThreads), 0, s, ga);
+    }
+  }
+  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP, false>, dim3(grid), dim3(kGemmThreads), 0, s, ga);
 }
 
 template <bool GATEUP>
