@@ -39,6 +39,8 @@ from .codecs import (  # noqa: F401
 from .moe import (  # noqa: F401
     bf16_to_f64,
     router_logits,
+    selection_scores,
+    route,
     select_topk,
     topk_softmax,
     shared_gate,

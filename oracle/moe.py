@@ -5,7 +5,8 @@ Inputs are duck-typed (no import of the generator): a layer object with
 ``router_w [E,H] fp32``, ``router_b [E] or None``, ``gate_up`` and ``down``
 stacked packed matrices (fields fmt, codes, block_scales, tensor_scales, n, k),
 optional ``shared_gate_up``/``shared_down``/``shared_gate_w``, and ``cfg``
-with ``top_k``, ``act`` ("bf16" | "fp8" | "mxfp8").  Hidden states are bf16 bit
+with ``top_k``, ``act`` ("bf16" | "fp8" | "mxfp8") and optionally
+``bias_mode`` ("logits", the default, or "select").  Hidden states are bf16 bit
 patterns (uint16).
 
 Arithmetic is float64 throughout, except where a floating-point value decides
@@ -19,6 +20,8 @@ routed SwiGLU MoE):
   1. l[t,e]  = x_t . W_r[e] + b[e]
   2. ids_t   = the k largest logits, descending, ties to the lower index
   3. w_t     = softmax over the k selected logits
+     (selection-only bias, bias_mode "select": l = x_t . W_r[e] in 1 and 3,
+      and step 2 ranks l + b instead)
   4. sg_t    = sigmoid(x_t . w_sg)                          (shared expert)
   5. x^      = x, or E4M3 per-tensor quantise-dequantise of x  (FP8 layers),
                or MXFP8 of each row of x                      (MXFP8 layers)
@@ -45,12 +48,32 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------- routing --
 
 
+def _bias_select_only(lay) -> bool:
+    return getattr(lay.cfg, "bias_mode", "logits") == "select"
+
+
 def router_logits(lay, xf: np.ndarray) -> np.ndarray:
-    """Step 1: l = x W_r^T + b  (float64)."""
+    """Step 1: l = x W_r^T + b  (float64); a selection-only bias is left to
+    ``selection_scores``."""
     lg = xf @ np.asarray(lay.router_w, np.float64).T
-    if getattr(lay, "router_b", None) is not None:
+    if getattr(lay, "router_b", None) is not None and not _bias_select_only(lay):
         lg = lg + np.asarray(lay.router_b, np.float64)
     return lg
+
+
+def selection_scores(lay, lg: np.ndarray) -> np.ndarray:
+    """The values step 2 ranks: the logits, or logits + b when the bias takes
+    part in the selection only."""
+    if getattr(lay, "router_b", None) is not None and _bias_select_only(lay):
+        return lg + np.asarray(lay.router_b, np.float64)
+    return lg
+
+
+def route(lay, xf: np.ndarray):
+    """Steps 1-3: (logits, selected ids, weights)."""
+    lg = router_logits(lay, xf)
+    ids = select_topk(selection_scores(lay, lg), lay.cfg.top_k)
+    return lg, ids, topk_softmax(lg, ids)
 
 
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
@@ -182,9 +205,7 @@ def swiglu_expert(w_gu: np.ndarray, w_d: np.ndarray, xr: np.ndarray):
 
 def _routing(lay, x_bits):
     xf = bf16_to_f64(x_bits)
-    lg = router_logits(lay, xf)
-    ids = select_topk(lg, lay.cfg.top_k)
-    w = topk_softmax(lg, ids)
+    lg, ids, w = route(lay, xf)
     sg = shared_gate(lay, xf) if getattr(lay, "shared_gate_w", None) is not None else None
     return xf, lg, ids, w, sg
 
@@ -379,7 +400,7 @@ def forward_all_experts_masked(lay, x_bits: np.ndarray) -> np.ndarray:
     lg = router_logits(lay, xf)
     T, E = lg.shape
     k = lay.cfg.top_k
-    order = np.argsort(-lg, axis=1, kind="stable")
+    order = np.argsort(-selection_scores(lay, lg), axis=1, kind="stable")
     M = np.zeros((T, E))
     for t in range(T):
         top = order[t, :k]

@@ -191,6 +191,7 @@ class LayerConfig:
     zipf_ratio: float = 10.0
     seed: int = 0
     gap: float = 1e-3
+    bias_mode: str = "logits"     # router bias in "logits" (selection and weights) or "select" (selection only)
 
 
 CONFIGS = {
@@ -199,6 +200,9 @@ CONFIGS = {
     "c2": LayerConfig("c2", (4096,), 2048, 128, 8, 768, "mxfp4", seed=1),
     "c3": LayerConfig("c3", (1, 8192), 2048, 512, 10, 512, "nvfp4", shared_inter=512, seed=3),
     "c4": LayerConfig("c4", (16384,), 4096, 128, 8, 1536, "fp8", act="fp8", zipf_s=1.1, seed=4),
+    # the c4 layer with its Zipf router bias taking part in the selection only
+    "c4-selbias": LayerConfig("c4-selbias", (16384,), 4096, 128, 8, 1536, "fp8", act="fp8", zipf_s=1.1,
+                              bias_mode="select", seed=4),
     # the c1 / c2 layers (same weights) with MXFP8 activations (W4A8)
     "c1-w4a8": LayerConfig("c1-w4a8", (1, 8), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),
     "c2-w4a8": LayerConfig("c2-w4a8", (4096,), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),

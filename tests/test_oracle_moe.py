@@ -154,6 +154,31 @@ def test_mxfp8_hand_example():
     assert np.all(codes[5:] == 0) and np.all(deq[5:] == 0)
 
 
+def test_selection_only_bias_ranks_biased_and_weights_unbiased():
+    """bias_mode "select": torch.topk of x W^T + b picks the experts (the
+    generator keeps a gap at the k-th place, so the order is unique) and the
+    weights are torch.softmax of the selected x W^T, without b."""
+    lay = tiny("mxfp4", E=16, k=3, zipf=1.1)
+    lay.cfg = synth.LayerConfig(**{**lay.cfg.__dict__, "bias_mode": "select"})
+    x = make_tokens(lay, 20)
+    lg, ids, w = oracle.route(lay, oracle.bf16_to_f64(x))
+    xt = _t(oracle.bf16_to_f64(x))
+    raw = F.linear(xt, _t(lay.router_w))
+    top = torch.topk(raw + _t(lay.router_b), 3, dim=1)
+    assert np.array_equal(ids, top.indices.numpy())
+    assert np.abs(lg - raw.numpy()).max() <= 1e-12
+    ref_w = torch.softmax(torch.gather(raw, 1, top.indices), dim=1).numpy()
+    assert np.abs(w - ref_w).max() <= 1e-12
+    r = oracle.forward(lay, x)
+    assert np.array_equal(r["ids"], ids) and np.abs(r["w"] - ref_w).max() <= 1e-12
+    b = oracle.forward_all_experts_masked(lay, x)
+    assert np.abs(r["y"] - b).max() <= 1e-12 * np.abs(b).max()
+    # the default mode puts the bias into the weights as well
+    lay.cfg = synth.LayerConfig(**{**lay.cfg.__dict__, "bias_mode": "logits"})
+    _, ids0, w0 = oracle.route(lay, oracle.bf16_to_f64(x))
+    assert np.array_equal(ids0, ids) and np.abs(w0 - w).max() > 1e-3
+
+
 def test_k_equal_E_gives_full_softmax():
     lay = tiny(E=4, k=4)
     x = make_tokens(lay, 8)
