@@ -30,6 +30,8 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 FMT_CODES = {"mxfp4": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8_E4M3}
 ACT_CODES = {"bf16": ACT_BF16, "fp8": ACT_FP8_PER_TENSOR, "mxfp8": ACT_MXFP8}
 PATH_CODES = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL}
+BIAS_LOGITS, BIAS_SELECT = 0, 1
+BIAS_CODES = {"logits": BIAS_LOGITS, "select": BIAS_SELECT}
 
 # Every symbol include/ftmoe.h declares.
 EXPORTS = (
@@ -61,7 +63,7 @@ class LayerDesc(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("act", ctypes.c_int32), ("path", ctypes.c_int32),
         ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
         ("gate_up", QWeightDesc), ("down", QWeightDesc),
-        ("shared_inter", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("shared_inter", ctypes.c_int32), ("router_bias_mode", ctypes.c_int32),
         ("shared_gate_up", QWeightDesc), ("shared_down", QWeightDesc),
         ("shared_gate_w", ctypes.c_void_p),
     ]
@@ -173,9 +175,9 @@ class DeviceLayer:
     def __init__(self, hidden, inter, num_experts, top_k, router_w, gate_up: DeviceQWeight,
                  down: DeviceQWeight, router_bias=None, act="bf16", path="auto", shared_inter=0,
                  shared_gate_up: Optional[DeviceQWeight] = None, shared_down: Optional[DeviceQWeight] = None,
-                 shared_gate_w=None):
+                 shared_gate_w=None, bias_mode="logits"):
         self.hidden, self.inter, self.num_experts, self.top_k = hidden, inter, num_experts, top_k
-        self.router_w, self.router_bias = router_w, router_bias
+        self.router_w, self.router_bias, self.bias_mode = router_w, router_bias, bias_mode
         self.gate_up, self.down = gate_up, down
         self.act, self.path = act, path
         self.shared_inter = shared_inter
@@ -207,13 +209,15 @@ class DeviceLayer:
         return cls(cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, t(lay.router_w), qw(lay.gate_up),
                    qw(lay.down), router_bias=t(lay.router_b), act=cfg.act, path=path,
                    shared_inter=cfg.shared_inter, shared_gate_up=qw(lay.shared_gate_up),
-                   shared_down=qw(lay.shared_down), shared_gate_w=t(lay.shared_gate_w))
+                   shared_down=qw(lay.shared_down), shared_gate_w=t(lay.shared_gate_w),
+                   bias_mode=getattr(cfg, "bias_mode", "logits"))
 
     def desc(self) -> LayerDesc:
         d = LayerDesc()
         d.hidden, d.inter, d.num_experts, d.top_k = self.hidden, self.inter, self.num_experts, self.top_k
         d.act, d.path = ACT_CODES[self.act], PATH_CODES[self.path]
         d.router_w, d.router_bias = _ptr(self.router_w), _ptr(self.router_bias)
+        d.router_bias_mode = BIAS_CODES[self.bias_mode]
         d.gate_up, d.down = self.gate_up.desc(), self.down.desc()
         d.shared_inter = self.shared_inter
         if self.shared_inter:

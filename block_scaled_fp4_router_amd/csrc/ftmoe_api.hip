@@ -142,6 +142,8 @@ ftmoe_status check_layer(const ftmoe_layer* L) {
                 kMaxExperts);
   if (L->act != FTMOE_ACT_BF16 && L->act != FTMOE_ACT_FP8_PER_TENSOR && L->act != FTMOE_ACT_MXFP8)
     return fail(FTMOE_ERR_INVALID_ARG, "act=%d is not an ftmoe_afmt", L->act);
+  if (L->router_bias_mode != FTMOE_BIAS_LOGITS && L->router_bias_mode != FTMOE_BIAS_SELECT)
+    return fail(FTMOE_ERR_INVALID_ARG, "router_bias_mode=%d is not an ftmoe_bias_mode", L->router_bias_mode);
   if (L->path != FTMOE_PATH_AUTO && L->path != FTMOE_PATH_DECODE && L->path != FTMOE_PATH_PREFILL)
     return fail(FTMOE_ERR_INVALID_ARG, "path=%d is not an ftmoe_path", L->path);
   if (!L->router_w) return fail(FTMOE_ERR_INVALID_ARG, "router_w is NULL");
@@ -318,7 +320,8 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
            "router launch");
     FT_HIP(timed("topk_align", s,
                  [&] {
-                   return launch_topk_align_decode(part, p.S, T, E, k, L->router_bias, shared, ids, w, sg,
+                   return launch_topk_align_decode(part, p.S, T, E, k, L->router_bias,
+                                                   L->router_bias_mode == FTMOE_BIAS_SELECT, shared, ids, w, sg,
                                                    at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
                                                    at<int32_t>(ws, p.sorted), at<int32_t>(ws, p.bexp),
                                                    at<int32_t>(ws, p.npad), align ? p.P : 0,
@@ -334,7 +337,11 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
                                              logits, s);
                }),
          "router logits launch");
-  FT_HIP(timed("topk", s, [&] { return launch_topk(logits, T, E, k, L->router_bias, shared, ids, w, sg, s); }),
+  FT_HIP(timed("topk", s,
+               [&] {
+                 return launch_topk(logits, T, E, k, L->router_bias, L->router_bias_mode == FTMOE_BIAS_SELECT,
+                                    shared, ids, w, sg, s);
+               }),
          "top-k launch");
   return FTMOE_OK;
 }

@@ -67,8 +67,10 @@ struct Rows {
 // ---- router ----
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
                                 const float* shared_gate_w, float* logits, hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool has_shared,
-                       int32_t* ids, float* w, float* sgate, hipStream_t s);
+// bias_select: the bias ranks the experts only; the weights are the softmax
+// of the selected logits without it.
+hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool bias_select,
+                       bool has_shared, int32_t* ids, float* w, float* sgate, hipStream_t s);
 
 // ---- align ----
 size_t align_scratch_bytes(int T, int k, int E, int BM);
@@ -107,7 +109,7 @@ inline int xsc_pitch_of(int H) { return (H / 32 + 15) / 16 * 16; }
 // Sums the partial logits, top-k + softmax (+ sigmoid gate), aligns the T*k
 // rows into blocks of kDecodeBM and zeroes `zero_words`.  One workgroup.
 hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int k, const float* bias,
-                                    bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
+                                    bool bias_select, bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
                                     int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert,
                                     int32_t* num_padded, int P, uint32_t* zero_words, int n_zero,
                                     hipStream_t s);

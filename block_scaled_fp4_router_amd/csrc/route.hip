@@ -230,9 +230,17 @@ __device__ __forceinline__ void wave_topk_softmax(float (&v)[SLOTS], int k, int*
   *sel_w = ex / sum;
 }
 
+// Softmax over lanes < k of `l` (a selection-only bias: the selected
+// experts' logits without the bias), in a wave.
+__device__ __forceinline__ float lanes_softmax(float l, int k) {
+  const float m = wave_max_fast(lane_id() < k ? l : -__builtin_inff());
+  const float ex = lane_id() < k ? expf(l - m) : 0.f;
+  return ex / wave_sum_fixed(ex);
+}
+
 template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                   const float* __restrict__ bias, int has_shared,
+                                                   const float* __restrict__ bias, int bias_select, int has_shared,
                                                    int32_t* __restrict__ ids, float* __restrict__ w,
                                                    float* __restrict__ sgate) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -249,6 +257,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   int sel_i;
   float sel_w;
   wave_topk_softmax<SLOTS>(v, k, &sel_i, &sel_w);
+  if (bias && bias_select) sel_w = lanes_softmax(lane < k ? row[sel_i] : 0.f, k);
   if (lane < k) {
     ids[static_cast<size_t>(t) * k + lane] = sel_i;
     w[static_cast<size_t>(t) * k + lane] = sel_w;
@@ -269,11 +278,12 @@ static hipError_t with_slots(int E, F&& f) {
   return f.template operator()<16>();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool has_shared,
-                       int32_t* ids, float* w, float* sgate, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool bias_select,
+                       bool has_shared, int32_t* ids, float* w, float* sgate, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   return with_slots(E, [&]<int SL>() {
-    return launch(topk_kernel<SL>, grid, dim3(256), 0, s, logits, T, E, k, bias, has_shared ? 1 : 0, ids, w, sgate);
+    return launch(topk_kernel<SL>, grid, dim3(256), 0, s, logits, T, E, k, bias, bias_select ? 1 : 0,
+                  has_shared ? 1 : 0, ids, w, sgate);
   });
 }
 
@@ -373,7 +383,8 @@ __device__ __forceinline__ float sum_partials(const float* part, size_t base) {
 // routed rows into blocks of kDecodeBM (stable counting sort in LDS).
 template <int SLOTS, int SQ>
 __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
-    const float* __restrict__ part, int S, int T, int E, int k, const float* __restrict__ bias, int has_shared,
+    const float* __restrict__ part, int S, int T, int E, int k, const float* __restrict__ bias, int bias_select,
+    int has_shared,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ sgate, int32_t* counts, int32_t* offsets,
     int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, int P, uint32_t* zero_words, int n_zero) {
   __shared__ __attribute__((aligned(16))) int ids_s[kDecodeMaxT * 16];
@@ -399,6 +410,8 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
     int sel_i;
     float sel_w;
     wave_topk_softmax<SLOTS>(v, k, &sel_i, &sel_w);
+    if (bias && bias_select)   // weights from the selected logits without the bias
+      sel_w = lanes_softmax(lane < k ? sum_partials<SQ>(part, (static_cast<size_t>(t) * rows + sel_i) * S) : 0.f, k);
     if (lane < k) {
       ids[t * k + lane] = sel_i;
       w[t * k + lane] = sel_w;
@@ -433,15 +446,15 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
 }
 
 hipError_t launch_topk_align_decode(const float* part, int S, int T, int E, int k, const float* bias,
-                                    bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
+                                    bool bias_select, bool has_shared, int32_t* ids, float* w, float* sg, int32_t* counts,
                                     int32_t* offsets, int32_t* sorted_ids, int32_t* block_expert,
                                     int32_t* num_padded, int P, uint32_t* zero_words, int n_zero,
                                     hipStream_t s) {
   return with_slots(E, [&]<int SL>() {
     auto go = [&]<int SQ>() {
       return launch(topk_align_decode_kernel<SL, SQ>, dim3(1), dim3(1024), 0, s, part, S, T, E, k, bias,
-                    has_shared ? 1 : 0, ids, w, sg, counts, offsets, sorted_ids, block_expert, num_padded, P,
-                    zero_words, n_zero);
+                    bias_select ? 1 : 0, has_shared ? 1 : 0, ids, w, sg, counts, offsets, sorted_ids, block_expert,
+                    num_padded, P, zero_words, n_zero);
     };
     switch (S / 4) {
       case 1: return go.template operator()<1>();

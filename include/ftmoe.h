@@ -10,6 +10,8 @@
  *   l[t,e]   = x_t . W_r[e] + b[e]                       router GEMM
  *   ids_t    = k largest l[t,:], descending, ties -> lower expert index
  *   w_t      = softmax of the k selected logits          renormalised weights
+ * (with a selection-only bias, FTMOE_BIAS_SELECT, l = x_t . W_r[e] and the
+ *  k largest l[t,e] + b[e] are selected)
  *   h_tj     = silu(Wg[e] x_t) * (Wu[e] x_t),  e = ids_t[j]     gate_up + SwiGLU
  *   y_t      = sum_j w_tj Wd[e] h_tj   (j ascending)    down + weighted combine
  *   y_t     += sigmoid(x_t . w_sg) * shared_mlp(x_t)    optional shared expert
@@ -86,6 +88,15 @@ typedef enum {
   FTMOE_ACT_MXFP8 = 2
 } ftmoe_afmt;
 
+/* Role of the router bias.  LOGITS adds it to the logits, so it shapes both
+ * the selection and the weights.  SELECT adds it for the ranking only and
+ * weights the selected experts by the softmax of their logits without it
+ * (a load-balancing bias that must not change the mixture).              */
+typedef enum {
+  FTMOE_BIAS_LOGITS = 0,
+  FTMOE_BIAS_SELECT = 1
+} ftmoe_bias_mode;
+
 /* Expert-kernel family.  AUTO picks the bandwidth-bound decode kernels for
  * small token counts and the MFMA grouped GEMMs otherwise; the other values
  * force one for A/B comparisons (both compute the same function).        */
@@ -114,8 +125,8 @@ typedef struct {
 } ftmoe_qweight;
 
 /* One MoE layer.
- *  router_w     [E][H] fp32.   router_bias [E] fp32 or NULL (added to the
- *               logits before both selection and weighting).
+ *  router_w     [E][H] fp32.   router_bias [E] fp32 or NULL, used as
+ *               router_bias_mode says (ftmoe_bias_mode).
  *  gate_up      N = 2*inter, K = hidden: rows [0, inter) are the gate
  *               projection, rows [inter, 2*inter) the up projection.
  *  down         N = hidden, K = inter.
@@ -139,7 +150,7 @@ typedef struct {
   ftmoe_qweight gate_up;
   ftmoe_qweight down;
   int32_t shared_inter;
-  int32_t reserved0;
+  int32_t router_bias_mode;   /* ftmoe_bias_mode */
   ftmoe_qweight shared_gate_up;
   ftmoe_qweight shared_down;
   const float* shared_gate_w;

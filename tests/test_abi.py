@@ -89,6 +89,7 @@ def test_workspace_size_of_a_valid_layer():
     ("top_k", 9, ft.ERR_UNSUPPORTED),
     ("num_experts", 2000, ft.ERR_UNSUPPORTED),
     ("act", 7, ft.ERR_INVALID_ARG),
+    ("router_bias_mode", 2, ft.ERR_INVALID_ARG),
     ("path", 9, ft.ERR_INVALID_ARG),
     ("router_w", None, ft.ERR_INVALID_ARG),
     ("router_w", FAKE + 4, ft.ERR_INVALID_ARG),

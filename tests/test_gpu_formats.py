@@ -20,6 +20,8 @@ LAYERS = {
     "f8a8": (256, 8, 2, 256, "fp8", "fp8", 0),
     "f8bf": (256, 8, 2, 128, "fp8", "bf16", 0),
     "mx8a": (512, 8, 2, 384, "mxfp4", "mxfp8", 128),
+    # Zipf router bias used for the selection only
+    "mxsel": (384, 16, 4, 256, "mxfp4", "bf16", 0, {"zipf_s": 1.1, "zipf_ratio": 2.5, "bias_mode": "select"}),
 }
 TOKENS = [(5, "auto"), (16, "decode"), (70, "prefill"), (1024, "prefill")]
 
@@ -29,11 +31,12 @@ _cache = {}
 def layer(name, packed=False):
     key = (name, packed)
     if key not in _cache:
-        H, E, k, I, fmt, act, Is = LAYERS[name]
+        H, E, k, I, fmt, act, Is = LAYERS[name][:7]
+        extra = LAYERS[name][7] if len(LAYERS[name]) > 7 else {}
         if (name, False) in _cache:
             lay = _cache[(name, False)][0]
         else:
-            cfg = synth.LayerConfig(name, (16,), H, E, k, I, fmt, act=act, shared_inter=Is, seed=7)
+            cfg = synth.LayerConfig(name, (16,), H, E, k, I, fmt, act=act, shared_inter=Is, seed=7, **extra)
             lay = synth.make_layer(cfg, cache=False)
         dlay = ft.DeviceLayer.from_host(lay, DEV)
         _cache[key] = (lay, dlay.pack() if packed else dlay)

@@ -26,7 +26,8 @@ def tol_for(name):
 
 # ------------------------------------------------------------------ route --
 @pytest.mark.parametrize("name,T", [("c0", 16), ("c1", 1), ("c1", 8), ("c2", 4096), ("c3", 1), ("c3", 8192),
-                                    ("c4", 16384), ("c1", 17), ("c3", 33)])
+                                    ("c4", 16384), ("c1", 17), ("c3", 33), ("c4-selbias", 1), ("c4-selbias", 8),
+                                    ("c4-selbias", 16384)])
 @pytest.mark.timeout(600)
 def test_route_parity(name, T):
     say(f"route parity {name} T={T}")
@@ -41,9 +42,7 @@ def test_route_parity(name, T):
     ft.route(dlay, xd, T, ws, ids, w, sg)
     torch.cuda.synchronize()
     xf = oracle.bf16_to_f64(x)
-    lg = oracle.router_logits(lay, xf)
-    ref_ids = oracle.select_topk(lg, k)
-    ref_w = oracle.topk_softmax(lg, ref_ids)
+    _, ref_ids, ref_w = oracle.route(lay, xf)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     assert np.abs(w.cpu().numpy() - ref_w).max() <= 1e-5
     if sg is not None:
@@ -125,7 +124,7 @@ def test_forward_parity_full_size_sampled(name, T, nsample):
     y, ids, w = run_forward(dlay, x, "auto")
     tok = sample_tokens(T, nsample, seed=T)
     xf = oracle.bf16_to_f64(x)
-    ref_ids = oracle.select_topk(oracle.router_logits(lay, xf), dlay.top_k)
+    ref_ids = oracle.route(lay, xf)[1]
     assert np.array_equal(ids, ref_ids)
     s_h = None
     if synth.CONFIGS[name].act == "fp8":
