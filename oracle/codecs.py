@@ -93,25 +93,30 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (el.reshape(*el.shape[:-1], -1, 32) * sc[..., None]).reshape(el.shape)
 
 
-def dequant_nvfp4(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
-    """W[n,k] = E2M1(code[n,k]) * E4M3(S[n, k//16]) * g, float64."""
+def dequant_nvfp4(codes: np.ndarray, scales: np.ndarray, g) -> np.ndarray:
+    """W[n,k] = E2M1(code[n,k]) * E4M3(S[n, k//16]) * g (g a scalar, or [N, 1]
+    per row), float64."""
     el = _E2M1_TABLE[_unpack_nibbles(codes)]
-    sc = _E4M3_TABLE[np.asarray(scales, np.uint8)] * np.float64(g)
+    sc = _E4M3_TABLE[np.asarray(scales, np.uint8)] * np.asarray(g, np.float64)
     return (el.reshape(*el.shape[:-1], -1, 16) * sc[..., None]).reshape(el.shape)
 
 
-def dequant_fp8(codes: np.ndarray, s: float) -> np.ndarray:
-    """W[n,k] = E4M3(code[n,k]) * s, float64."""
-    return _E4M3_TABLE[np.asarray(codes, np.uint8)] * np.float64(s)
+def dequant_fp8(codes: np.ndarray, s) -> np.ndarray:
+    """W[n,k] = E4M3(code[n,k]) * s (s a scalar, or [N, 1] per row), float64."""
+    return _E4M3_TABLE[np.asarray(codes, np.uint8)] * np.asarray(s, np.float64)
 
 
 def dequant(qw, e: int) -> np.ndarray:
     """Dequantise expert e of a stacked packed matrix (duck-typed: needs
-    fmt, codes, block_scales, tensor_scales)."""
+    fmt, codes, block_scales, tensor_scales).  NVFP4 and FP8 multipliers are
+    one per matrix ([E]) or one per matrix row ([E, N]: row-wise scaling,
+    and per-part scaling of a fused projection as runs of equal rows)."""
     if qw.fmt == "mxfp4":
         return dequant_mxfp4(qw.codes[e], qw.block_scales[e])
+    ts = np.asarray(qw.tensor_scales[e], np.float64)
+    g = ts[:, None] if ts.ndim == 1 else ts   # a row's multiplier broadcasts along K
     if qw.fmt == "nvfp4":
-        return dequant_nvfp4(qw.codes[e], qw.block_scales[e], qw.tensor_scales[e])
+        return dequant_nvfp4(qw.codes[e], qw.block_scales[e], g)
     if qw.fmt == "fp8":
-        return dequant_fp8(qw.codes[e], qw.tensor_scales[e])
+        return dequant_fp8(qw.codes[e], g)
     raise ValueError(f"unknown weight format {qw.fmt!r}")

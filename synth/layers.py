@@ -150,6 +150,36 @@ def quantize_fp8(w: np.ndarray) -> Tuple[np.ndarray, float]:
     return e4m3_encode(w / s), float(s)
 
 
+def _row_parts(n: int, mode: str, gate_up: bool):
+    """Row ranges that share one fp32 scale: the whole matrix ("tensor"), each
+    row ("row"), or the gate and up halves of a fused gate_up ("part"; a down
+    matrix is one part)."""
+    if mode == "tensor":
+        return [(0, n)]
+    if mode == "row":
+        return [(r, r + 1) for r in range(n)]
+    if mode == "part":
+        return [(0, n // 2), (n // 2, n)] if gate_up else [(0, n)]
+    raise ValueError(f"unknown scale mode {mode!r}")
+
+
+def quantize_scaled_rows(fmt: str, w: np.ndarray, parts):
+    """NVFP4 or FP8 with one fp32 scale per row range of ``parts`` (each range
+    quantised as its own matrix).  Returns (codes, block scales or None,
+    per-row scales [N] fp32)."""
+    n, k = w.shape
+    rs = np.empty((n,), np.float32)
+    codes = np.empty((n, k // 2 if fmt == "nvfp4" else k), np.uint8)
+    bs = np.empty((n, k // 16), np.uint8) if fmt == "nvfp4" else None
+    for a, b in parts:
+        if fmt == "nvfp4":
+            codes[a:b], bs[a:b], g = quantize_nvfp4(w[a:b])
+        else:
+            codes[a:b], g = quantize_fp8(w[a:b])
+        rs[a:b] = g
+    return codes, bs, rs
+
+
 # --------------------------------------------------------------------------
 # Layer description
 # --------------------------------------------------------------------------
@@ -164,14 +194,14 @@ class QWeight:
     k: int
     codes: np.ndarray             # fp4: [E, N, K/2] uint8; fp8: [E, N, K] uint8
     block_scales: Optional[np.ndarray]   # mxfp4 [E,N,K/32] | nvfp4 [E,N,K/16] | None
-    tensor_scales: Optional[np.ndarray]  # nvfp4/fp8 [E] fp32 | None
+    tensor_scales: Optional[np.ndarray]  # nvfp4/fp8 [E] fp32, or [E, N] (one per row) | None
 
     def nbytes_per_expert(self) -> int:
         b = self.codes[0].nbytes
         if self.block_scales is not None:
             b += self.block_scales[0].nbytes
         if self.tensor_scales is not None:
-            b += 4
+            b += self.tensor_scales[0].nbytes
         return b
 
 
@@ -192,6 +222,7 @@ class LayerConfig:
     seed: int = 0
     gap: float = 1e-3
     bias_mode: str = "logits"     # router bias in "logits" (selection and weights) or "select" (selection only)
+    scale_mode: str = "tensor"    # NVFP4/FP8 fp32 scale per matrix, "row", or "part" (gate and up halves)
 
 
 CONFIGS = {
@@ -249,8 +280,27 @@ def _normal(ss: np.random.SeedSequence, shape, std: float) -> np.ndarray:
     return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
 
 
-def _make_qweight(fmt: str, ss_list, n: int, k: int, std: float) -> QWeight:
+def _make_qweight(fmt: str, ss_list, n: int, k: int, std: float, scale_mode: str = "tensor",
+                  gate_up: bool = False) -> QWeight:
     e = len(ss_list)
+    if scale_mode != "tensor":
+        if fmt == "mxfp4":
+            raise ValueError("MXFP4 has no fp32 scale to split by rows")
+        parts = _row_parts(n, scale_mode, gate_up)
+        codes = np.empty((e, n, k // 2 if fmt == "nvfp4" else k), np.uint8)
+        bs = np.empty((e, n, k // 16), np.uint8) if fmt == "nvfp4" else None
+        ts = np.empty((e, n), np.float32)
+
+        def one_rows(i):
+            w = _normal(ss_list[i], (n, k), std)
+            c, b, r = quantize_scaled_rows(fmt, w, parts)
+            codes[i], ts[i] = c, r
+            if bs is not None:
+                bs[i] = b
+
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one_rows, range(e)))
+        return QWeight(fmt, e, n, k, codes, bs, ts)
     if fmt in ("mxfp4", "nvfp4"):
         codes = np.empty((e, n, k // 2), np.uint8)
         bs = np.empty((e, n, k // (32 if fmt == "mxfp4" else 16)), np.uint8)
@@ -290,8 +340,8 @@ def make_layer(cfg, cache: bool = True) -> Layer:
     """Build (or fetch from the in-process cache) the layer for a config."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
-    # the arrays do not depend on the activation mode or the name
-    key = (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.fmt,
+    # the arrays do not depend on the activation mode, the bias mode or the name
+    key = (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.fmt, cfg.scale_mode,
            cfg.shared_inter, cfg.router_std, cfg.zipf_s, cfg.zipf_ratio, cfg.seed)
     if cache and key in _LAYER_CACHE:
         lay = _LAYER_CACHE[key]
@@ -303,13 +353,14 @@ def make_layer(cfg, cache: bool = True) -> Layer:
     (s_router, s_bias, s_sg, s_gu, s_d, s_sgu, s_sd, s_cal) = root.spawn(8)
     std_r = cfg.router_std if cfg.router_std is not None else 1.0 / math.sqrt(H)
     router_w = _normal(s_router, (E, H), std_r)
-    gate_up = _make_qweight(cfg.fmt, s_gu.spawn(E), 2 * I, H, 1.0 / math.sqrt(H))
-    down = _make_qweight(cfg.fmt, s_d.spawn(E), H, I, 1.0 / math.sqrt(I))
+    gate_up = _make_qweight(cfg.fmt, s_gu.spawn(E), 2 * I, H, 1.0 / math.sqrt(H), cfg.scale_mode, gate_up=True)
+    down = _make_qweight(cfg.fmt, s_d.spawn(E), H, I, 1.0 / math.sqrt(I), cfg.scale_mode)
     lay = Layer(cfg, router_w, None, gate_up, down)
     if cfg.shared_inter:
         Is = cfg.shared_inter
-        lay.shared_gate_up = _make_qweight(cfg.fmt, s_sgu.spawn(1), 2 * Is, H, 1.0 / math.sqrt(H))
-        lay.shared_down = _make_qweight(cfg.fmt, s_sd.spawn(1), H, Is, 1.0 / math.sqrt(Is))
+        lay.shared_gate_up = _make_qweight(cfg.fmt, s_sgu.spawn(1), 2 * Is, H, 1.0 / math.sqrt(H), cfg.scale_mode,
+                                           gate_up=True)
+        lay.shared_down = _make_qweight(cfg.fmt, s_sd.spawn(1), H, Is, 1.0 / math.sqrt(Is), cfg.scale_mode)
         lay.shared_gate_w = _normal(s_sg, (H,), 1.0 / math.sqrt(H))
     if cfg.zipf_s is not None:
         # Router bias alpha * log(Zipf(s) probability) over a seeded rank

@@ -171,3 +171,71 @@ def test_nibble_order_low_is_even_element():
     scales = np.array([[127]], np.uint8)
     w = oracle.dequant_mxfp4(codes, scales)
     assert w[0, 0] == -1.0 and w[0, 1] == 2.0
+
+
+class _QW:
+    def __init__(self, fmt, codes, bs, ts):
+        self.fmt, self.codes, self.block_scales, self.tensor_scales = fmt, codes, bs, ts
+
+
+def test_row_scaled_fp8_dequant_matches_torch():
+    """Row-wise FP8 multipliers: W[n,k] = E4M3(code) * g[n], decoded by torch's
+    float8_e4m3fn."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, (2, 12, 64), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11   # no NaN codes
+    ts = (rng.random((2, 12)) * 0.01 + 1e-4).astype(np.float32)
+    qw = _QW("fp8", codes, None, ts)
+    for e in range(2):
+        ref = torch.from_numpy(codes[e]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        ref = ref * ts[e].astype(np.float64)[:, None]
+        assert np.array_equal(oracle.dequant(qw, e), ref)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_row_scales_reduce_to_tensor_scale_and_act_per_row(fmt):
+    """Equal row multipliers give exactly the per-matrix result; changing one
+    row's multiplier rescales that row alone (by the same factor)."""
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((3, 10, 64)) * 0.05).astype(np.float32)
+    if fmt == "fp8":
+        parts = [synth.quantize_fp8(w[e]) for e in range(3)]
+        codes = np.stack([c for c, _ in parts])
+        bs = None
+        g = np.array([s for _, s in parts], np.float32)
+    else:
+        parts = [synth.quantize_nvfp4(w[e]) for e in range(3)]
+        codes = np.stack([c for c, _, _ in parts])
+        bs = np.stack([b for _, b, _ in parts])
+        g = np.array([s for _, _, s in parts], np.float32)
+    tensor = _QW(fmt, codes, bs, g)
+    rows = np.repeat(g[:, None], 10, axis=1)
+    for e in range(3):
+        assert np.array_equal(oracle.dequant(_QW(fmt, codes, bs, rows), e), oracle.dequant(tensor, e))
+    rows2 = rows.copy()
+    rows2[1, 4] *= 4.0
+    a, b = oracle.dequant(_QW(fmt, codes, bs, rows), 1), oracle.dequant(_QW(fmt, codes, bs, rows2), 1)
+    assert np.array_equal(b[4], 4.0 * a[4])
+    assert np.array_equal(np.delete(b, 4, axis=0), np.delete(a, 4, axis=0))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_generator_scale_modes(fmt):
+    """Per-row and per-part scales: each row range is quantised as a matrix of
+    its own, so its multiplier is its own amax rule and the round trip keeps
+    the per-format bound within every range."""
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((8, 64)) * 0.05).astype(np.float32)
+    w[4:] *= 10.0   # the up half is ten times larger: per-part scales differ
+    for mode, parts in (("row", [(r, r + 1) for r in range(8)]), ("part", [(0, 4), (4, 8)])):
+        assert synth.layers._row_parts(8, mode, gate_up=True) == parts
+        codes, bs, rs = synth.layers.quantize_scaled_rows(fmt, w, parts)
+        for a, b in parts:
+            amax = np.float32(np.abs(w[a:b]).max())
+            expect = amax / np.float32(448.0) if fmt == "fp8" else amax / np.float32(6 * 448)
+            assert np.all(rs[a:b] == np.float32(expect))
+        wq = oracle.dequant(_QW(fmt, codes[None], None if bs is None else bs[None], rs[None]), 0)
+        for a, b in parts:
+            rel = np.abs(wq[a:b] - w[a:b]).max() / np.abs(w[a:b]).max()
+            assert rel <= (2 ** -4 if fmt == "fp8" else 1 / 6 + 1e-3)
+    assert synth.layers._row_parts(8, "part", gate_up=False) == [(0, 8)]

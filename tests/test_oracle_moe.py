@@ -22,9 +22,9 @@ from synth import LayerConfig, make_layer, make_tokens
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def tiny(fmt="mxfp4", H=64, E=4, k=2, I=64, act="bf16", shared=0, seed=11, std=None, zipf=None):
+def tiny(fmt="mxfp4", H=64, E=4, k=2, I=64, act="bf16", shared=0, seed=11, std=None, zipf=None, scale="tensor"):
     cfg = LayerConfig("tiny", (8,), H, E, k, I, fmt, act=act, shared_inter=shared,
-                      router_std=std, zipf_s=zipf, seed=seed)
+                      router_std=std, zipf_s=zipf, seed=seed, scale_mode=scale)
     return make_layer(cfg, cache=False)
 
 
@@ -198,10 +198,11 @@ def test_router_logits_match_torch_linear_with_bias():
     assert np.abs(oracle.router_logits(lay, xf) - ref).max() <= 1e-13
 
 
-@pytest.mark.parametrize("fmt,act,shared", [("mxfp4", "bf16", 0), ("nvfp4", "bf16", 32), ("fp8", "bf16", 0),
-                                            ("mxfp4", "mxfp8", 32)])
-def test_brute_force_all_experts_masked(fmt, act, shared):
-    lay = tiny(fmt, E=8, k=3, H=64, I=32, shared=shared, act=act)
+@pytest.mark.parametrize("fmt,act,shared,scale", [("mxfp4", "bf16", 0, "tensor"), ("nvfp4", "bf16", 32, "tensor"),
+                                                  ("fp8", "bf16", 0, "tensor"), ("mxfp4", "mxfp8", 32, "tensor"),
+                                                  ("fp8", "bf16", 0, "row"), ("nvfp4", "bf16", 32, "part")])
+def test_brute_force_all_experts_masked(fmt, act, shared, scale):
+    lay = tiny(fmt, E=8, k=3, H=64, I=32, shared=shared, act=act, scale=scale)
     x = make_tokens(lay, 16)
     r = oracle.forward(lay, x)
     b = oracle.forward_all_experts_masked(lay, x)
