@@ -164,7 +164,7 @@ def main() -> int:
             if q.block_scales is not None:
                 b += q.block_scales[0].nbytes
             if q.tensor_scales is not None:
-                b += 4
+                b += q.tensor_scales[0].nbytes
             return b
         gu_b, dn_b = per_expert(lay.gate_up), per_expert(lay.down)
         shared_b = per_expert(lay.shared_gate_up) + per_expert(lay.shared_down) if cfg.shared_inter else 0

@@ -53,7 +53,7 @@ class QWeightDesc(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p), ("tensor_scales", ctypes.c_void_p),
-        ("packed", ctypes.c_void_p),
+        ("packed", ctypes.c_void_p), ("row_scales", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -150,8 +150,9 @@ class DeviceQWeight:
     packed: object = None   # the prefill tile layout (pack()), or None
 
     def desc(self) -> QWeightDesc:
+        row_scales = 1 if self.tensor_scales is not None and self.tensor_scales.dim() == 2 else 0
         return QWeightDesc(FMT_CODES[self.fmt], self.num_experts, self.n, self.k, _ptr(self.codes),
-                           _ptr(self.block_scales), _ptr(self.tensor_scales), _ptr(self.packed))
+                           _ptr(self.block_scales), _ptr(self.tensor_scales), _ptr(self.packed), row_scales, 0)
 
     def pack(self, role: int, stream=None) -> None:
         """Adds the prefill tile layout of these matrices (ftmoe_pack_qweight)."""
@@ -242,7 +243,7 @@ class DeviceLayer:
             if q.block_scales is not None:
                 b += q.block_scales[0].numel()
             if q.tensor_scales is not None:
-                b += 4
+                b += q.tensor_scales[0].numel() * 4
             return b
 
         total = u * (per_expert(self.gate_up) + per_expert(self.down))

@@ -546,16 +546,18 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
     mma_batch<WFMT, FP8ACT, false, NB>(ws, kc0, H, g, xs, row_bytes, arow, aval, 1.0f, acc);
   }
 
-  float f = w.tscale[e];
+  // this lane's weight row's multiplier (and the activation scale)
+  float f = row_scale(w, e, j < 8 ? i0 + j : I + i0 + (j - 8));
   if constexpr (FP8ACT) f *= scale_from_amax(a.amax_x);
   uint16_t* h = shared ? a.hs : a.h;
   float mx = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float up = __shfl_xor(acc[r], 8, kWave);
+    const float val = acc[r] * f;
+    const float up = __shfl_xor(val, 8, kWave);
     const int slot = 4 * g + r;
     if (j < 8 && slot < count) {
-      const float v = swiglu(acc[r] * f, up * f);
+      const float v = swiglu(val, up);
       h[static_cast<size_t>(p0 + slot) * I + i0 + j] = f32_to_bf16(v);
       mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
     }
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
       ws[u] = load_wslice<WFMT>(w, wrow, K, min(kc0 + u * 128, K - 128) + g * 32);
     mma_batch<WFMT, FP8ACT, true, NB>(ws, kc0, K, g, hsm, 2 * K, j, aval, sh, acc);
   }
-  const float f = w.tscale[e] * sh;
+  const float f = row_scale(w, e, n0 + j) * sh;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int slot = 4 * g + r;

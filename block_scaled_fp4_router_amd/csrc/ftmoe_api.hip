@@ -122,7 +122,14 @@ ftmoe_status check_qweight(const ftmoe_qweight& q, const char* name, int fmt, in
   }
   if (fmt == FTMOE_W_NVFP4 || fmt == FTMOE_W_FP8_E4M3) {
     if (!q.tensor_scales) return fail(FTMOE_ERR_INVALID_ARG, "%s.tensor_scales is NULL", name);
+    if (reinterpret_cast<uintptr_t>(q.tensor_scales) & 3u)
+      return fail(FTMOE_ERR_INVALID_ARG, "%s.tensor_scales is not 4-byte aligned", name);
   }
+  if (q.row_scales != 0 && q.row_scales != 1)
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.row_scales=%d is neither 0 nor 1", name, q.row_scales);
+  if (q.row_scales && fmt == FTMOE_W_MXFP4)
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.row_scales: MXFP4 has no fp32 multipliers", name);
+  if (q.reserved != 0) return fail(FTMOE_ERR_INVALID_ARG, "%s.reserved=%d is not 0", name, q.reserved);
   if (q.packed && (reinterpret_cast<uintptr_t>(q.packed) & 255u))
     return fail(FTMOE_ERR_INVALID_ARG, "%s.packed is not 256-byte aligned", name);
   return FTMOE_OK;
@@ -283,6 +290,7 @@ QW to_qw(const ftmoe_qweight& q) {
   w.scales = static_cast<const uint8_t*>(q.block_scales);
   w.tscale = q.tensor_scales;
   w.packed = static_cast<const uint8_t*>(q.packed);
+  w.rowsc = q.row_scales;
   return w;
 }
 

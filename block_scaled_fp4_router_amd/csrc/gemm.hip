@@ -911,9 +911,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
 
     // ---- epilogue (registers to global memory; the ring keeps filling) ----
     const int b = cb, e = ce, nt = cnt;
-    float f = 1.0f;
-    if constexpr (WFMT != kMXFP4) f = w.tscale[e];
-    if constexpr (FP8ACT && WFMT == kFP8) f *= amax_scale(ga.amax_a);
+    // NVFP4 / FP8: the matrix's fp32 multiplier (one, or one per row), and
+    // for FP8 activations the activation scale
+    float fa = 1.0f;
+    if constexpr (FP8ACT && WFMT == kFP8) fa = amax_scale(ga.amax_a);
     // (gate_up runs one tile per workgroup: once the refetches are done the
     // whole ring is free for the epilogue)
     if constexpr (GATEUP && C::kAScales) {
@@ -1014,13 +1015,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
 #pragma unroll
       for (int u = 0; u < NT / 2; ++u) {
         const int col = tile_col(nt, Rt[u] + j);   // gate column of this lane
+        // multipliers of its gate row and of the matching up row
+        const float fg = wact ? row_scale(w, e, col) * fa : 0.f;
+        const float fu = wact ? row_scale(w, e, N + col) * fa : 0.f;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = arow0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
             if (!wact || i >= nvalid) continue;
-            const float v = swiglu(acc[m][u][r] * f, acc[m][u + NT / 2][r] * f);
+            const float v = swiglu(acc[m][u][r] * fg, acc[m][u + NT / 2][r] * fu);
             mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
             static_cast<uint16_t*>(ga.out)[static_cast<size_t>(b * BM + i) * N + col] = f32_to_bf16(v);
           }
@@ -1029,6 +1033,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       if constexpr (FP8ACT) wave_amax_to_slots(mx, ga.amax_slots);
     } else {
       const int c0 = nt * C::kBN + Rt[0] + j;
+      float fc[NT];   // multiplier of each of this lane's output columns
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) fc[ct] = 1.0f;
+      if constexpr (WFMT != kMXFP4) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) fc[ct] = wact ? row_scale(w, e, c0 + 32 * ct) * fa : 0.f;
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -1038,7 +1049,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
           if (!wact || arow0 + il >= nvalid) continue;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct)
-            static_cast<uint16_t*>(ga.out)[fr_row * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * f);
+            static_cast<uint16_t*>(ga.out)[fr_row * N + c0 + 32 * ct] = f32_to_bf16(acc[m][ct][r] * fc[ct]);
         }
       }
     }

@@ -41,9 +41,15 @@ struct QW {
   int n, k;
   const uint8_t* codes;        // fp4: [E][N][K/2]; fp8: [E][N][K]
   const uint8_t* scales;       // mxfp4 [E][N][K/32]; nvfp4 [E][N][K/16]; fp8 unused
-  const float* tscale;         // nvfp4 / fp8: [E]; mxfp4 unused
+  const float* tscale;         // nvfp4 / fp8: [E], or [E][N] with rowsc; mxfp4 unused
   const uint8_t* packed;       // optional: the same matrices in the prefill tile layout, or NULL
+  int rowsc;                   // tscale holds one multiplier per matrix row
 };
+
+// fp32 multiplier of row `row` of expert e's matrix (NVFP4 / FP8).
+__device__ __forceinline__ float row_scale(const QW& w, int e, int row) {
+  return w.rowsc ? w.tscale[static_cast<size_t>(e) * w.n + row] : w.tscale[e];
+}
 
 // Bytes of one packed stage (512 tile rows x 64 K): codes, then for FP4 one
 // block-scale dword per row.

@@ -109,8 +109,14 @@ typedef enum {
 /* One stacked set of expert matrices, [E][N][K], K contiguous.
  *  codes:         FP4: [E][N][K/2] bytes.  FP8: [E][N][K] bytes.
  *  block_scales:  MXFP4: [E][N][K/32] E8M0.  NVFP4: [E][N][K/16] E4M3.  FP8: NULL.
- *  tensor_scales: NVFP4, FP8: [E] fp32 dequantisation multipliers.  MXFP4: NULL.
- * All three must be 16-byte aligned.                                       */
+ *  tensor_scales: NVFP4, FP8: fp32 dequantisation multipliers, [E] (one per
+ *                 matrix) or, with row_scales = 1, [E][N] (one per matrix
+ *                 row: row-wise scaling).  MXFP4: NULL.
+ * A fused projection whose parts were quantised with separate per-tensor
+ * scales (the FreeToken commit message on FP8 projections: gate and up of a
+ * gate_up matrix, each with its own scale) is passed with row_scales = 1 and
+ * each part's scale repeated over its rows.
+ * codes and block_scales must be 16-byte aligned, tensor_scales 4-byte.   */
 typedef struct {
   int32_t fmt;          /* ftmoe_wfmt */
   int32_t num_experts;
@@ -122,6 +128,8 @@ typedef struct {
   const void* packed;   /* optional (NULL = none): the same matrices in the
                            prefill tile layout written by ftmoe_pack_qweight,
                            256-byte aligned; read by the prefill GEMMs only */
+  int32_t row_scales;   /* 0: tensor_scales [E]; 1: [E][N] (NVFP4, FP8)   */
+  int32_t reserved;     /* must be 0                                       */
 } ftmoe_qweight;
 
 /* One MoE layer.

@@ -143,6 +143,24 @@ def test_weight_shape_and_format_validation():
 
 
 @needs_lib
+def test_row_scale_flag_validation():
+    d = good_layer()
+    d.gate_up.row_scales = 1                       # MXFP4 has no fp32 multipliers
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    for fmt in (ft.W_NVFP4, ft.W_FP8_E4M3):
+        d = good_layer()
+        d.gate_up = _qw(fmt, 8, 256, 256)
+        d.down = _qw(fmt, 8, 256, 128)
+        d.gate_up.row_scales = 1
+        assert _ws_status(d)[0] == ft.OK
+        d.down.row_scales = 2
+        assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+        d.down.row_scales = 0
+        d.down.reserved = 1
+        assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+
+
+@needs_lib
 def test_tokens_and_workspace_validation():
     d = good_layer()
     lib = ft.load()

@@ -20,6 +20,10 @@ LAYERS = {
     "f8a8": (256, 8, 2, 256, "fp8", "fp8", 0),
     "f8bf": (256, 8, 2, 128, "fp8", "bf16", 0),
     "mx8a": (512, 8, 2, 384, "mxfp4", "mxfp8", 128),
+    # fp32 multipliers per matrix row, or per part of the fused gate_up
+    "f8row": (256, 8, 2, 256, "fp8", "fp8", 0, {"scale_mode": "row"}),
+    "f8part": (256, 8, 2, 128, "fp8", "bf16", 0, {"scale_mode": "part"}),
+    "nvrow": (256, 8, 2, 128, "nvfp4", "bf16", 128, {"scale_mode": "row"}),
     # Zipf router bias used for the selection only
     "mxsel": (384, 16, 4, 256, "mxfp4", "bf16", 0, {"zipf_s": 1.1, "zipf_ratio": 2.5, "bias_mode": "select"}),
 }
