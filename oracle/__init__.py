@@ -34,6 +34,7 @@ from .codecs import (  # noqa: F401
     dequant_mxfp4,
     dequant_nvfp4,
     dequant_fp8,
+    dequant_bf16,
     dequant,
 )
 from .moe import (  # noqa: F401

@@ -10,6 +10,7 @@ applies to activations.  TEST INFRASTRUCTURE ONLY (see package docstring).
 - NVFP4: blocks of 16 elements along K share one E4M3 scale, and the whole
   matrix has one fp32 multiplier.
 - Packing: element k of a row sits in byte k/2, low nibble for even k.
+- BF16 experts: one bf16 (the top 16 bits of an fp32) per element, no scale.
 """
 from __future__ import annotations
 
@@ -106,6 +107,13 @@ def dequant_fp8(codes: np.ndarray, s) -> np.ndarray:
     return _E4M3_TABLE[np.asarray(codes, np.uint8)] * np.asarray(s, np.float64)
 
 
+def dequant_bf16(bits: np.ndarray) -> np.ndarray:
+    """W[n,k] = the bf16 value of bits[n,k], float64 (exact: a bf16 is the
+    upper half of an fp32)."""
+    u = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
 def dequant(qw, e: int) -> np.ndarray:
     """Dequantise expert e of a stacked packed matrix (duck-typed: needs
     fmt, codes, block_scales, tensor_scales).  NVFP4 and FP8 multipliers are
@@ -113,6 +121,8 @@ def dequant(qw, e: int) -> np.ndarray:
     and per-part scaling of a fused projection as runs of equal rows)."""
     if qw.fmt == "mxfp4":
         return dequant_mxfp4(qw.codes[e], qw.block_scales[e])
+    if qw.fmt == "bf16":
+        return dequant_bf16(qw.codes[e])
     ts = np.asarray(qw.tensor_scales[e], np.float64)
     g = ts[:, None] if ts.ndim == 1 else ts   # a row's multiplier broadcasts along K
     if qw.fmt == "nvfp4":

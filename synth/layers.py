@@ -188,11 +188,11 @@ def quantize_scaled_rows(fmt: str, w: np.ndarray, parts):
 @dataclass
 class QWeight:
     """Stacked packed matrices, row-major [E][N][K] with K contiguous."""
-    fmt: str                      # "mxfp4" | "nvfp4" | "fp8"
+    fmt: str                      # "mxfp4" | "nvfp4" | "fp8" | "bf16"
     num_experts: int
     n: int
     k: int
-    codes: np.ndarray             # fp4: [E, N, K/2] uint8; fp8: [E, N, K] uint8
+    codes: np.ndarray             # fp4: [E, N, K/2] uint8; fp8: [E, N, K] uint8; bf16: [E, N, K] uint16
     block_scales: Optional[np.ndarray]   # mxfp4 [E,N,K/32] | nvfp4 [E,N,K/16] | None
     tensor_scales: Optional[np.ndarray]  # nvfp4/fp8 [E] fp32, or [E, N] (one per row) | None
 
@@ -284,8 +284,8 @@ def _make_qweight(fmt: str, ss_list, n: int, k: int, std: float, scale_mode: str
                   gate_up: bool = False) -> QWeight:
     e = len(ss_list)
     if scale_mode != "tensor":
-        if fmt == "mxfp4":
-            raise ValueError("MXFP4 has no fp32 scale to split by rows")
+        if fmt in ("mxfp4", "bf16"):
+            raise ValueError(f"{fmt} has no fp32 scale to split by rows")
         parts = _row_parts(n, scale_mode, gate_up)
         codes = np.empty((e, n, k // 2 if fmt == "nvfp4" else k), np.uint8)
         bs = np.empty((e, n, k // 16), np.uint8) if fmt == "nvfp4" else None
@@ -307,13 +307,18 @@ def _make_qweight(fmt: str, ss_list, n: int, k: int, std: float, scale_mode: str
     elif fmt == "fp8":
         codes = np.empty((e, n, k), np.uint8)
         bs = None
+    elif fmt == "bf16":
+        codes = np.empty((e, n, k), np.uint16)
+        bs = None
     else:
         raise ValueError(f"unknown weight format {fmt!r}")
-    ts = None if fmt == "mxfp4" else np.empty((e,), np.float32)
+    ts = None if fmt in ("mxfp4", "bf16") else np.empty((e,), np.float32)
 
     def one(i):
         w = _normal(ss_list[i], (n, k), std)
-        if fmt == "mxfp4":
+        if fmt == "bf16":
+            codes[i] = f32_to_bf16_bits(w)
+        elif fmt == "mxfp4":
             codes[i], bs[i] = quantize_mxfp4(w)
         elif fmt == "nvfp4":
             codes[i], bs[i], ts[i] = quantize_nvfp4(w)

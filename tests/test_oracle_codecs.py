@@ -239,3 +239,13 @@ def test_generator_scale_modes(fmt):
             rel = np.abs(wq[a:b] - w[a:b]).max() / np.abs(w[a:b]).max()
             assert rel <= (2 ** -4 if fmt == "fp8" else 1 / 6 + 1e-3)
     assert synth.layers._row_parts(8, "part", gate_up=False) == [(0, 8)]
+
+
+def test_bf16_weight_decode_matches_torch_on_all_finite_patterns():
+    """BF16 experts: every finite bf16 bit pattern against torch's bfloat16."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    bits = bits[exp != 0xFF]
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.dequant(_QW("bf16", bits.reshape(1, 1, -1), None, None), 0)[0]
+    assert np.array_equal(got, ref)

@@ -41,7 +41,7 @@ def _torch_dense(lay, e, x, qact=False):
     return F.silu(a[:, :I]) * a[:, I:], wd
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "fp8", "bf16"])
 def test_single_expert_is_dense_swiglu(fmt):
     lay = tiny(fmt, E=1, k=1, H=64, I=32)
     x = make_tokens(lay, 6)
@@ -200,7 +200,8 @@ def test_router_logits_match_torch_linear_with_bias():
 
 @pytest.mark.parametrize("fmt,act,shared,scale", [("mxfp4", "bf16", 0, "tensor"), ("nvfp4", "bf16", 32, "tensor"),
                                                   ("fp8", "bf16", 0, "tensor"), ("mxfp4", "mxfp8", 32, "tensor"),
-                                                  ("fp8", "bf16", 0, "row"), ("nvfp4", "bf16", 32, "part")])
+                                                  ("fp8", "bf16", 0, "row"), ("nvfp4", "bf16", 32, "part"),
+                                                  ("bf16", "bf16", 32, "tensor")])
 def test_brute_force_all_experts_masked(fmt, act, shared, scale):
     lay = tiny(fmt, E=8, k=3, H=64, I=32, shared=shared, act=act, scale=scale)
     x = make_tokens(lay, 16)
