@@ -36,7 +36,7 @@ METRIC = "MoE-layer tokens/s (prefill) + decode expert-weight GB/s, % of MI355X 
 # at the 8-bit operand rate (FP8 roofline).
 DTYPE = {"mxfp4": "e2m1 x e4m3-pair mfma/fp32-acc", "nvfp4": "bf16-mfma/fp32-acc",
          "fp8": "bf16-mfma/fp32-acc", "fp8act": "fp8-e4m3-mfma/fp32-acc",
-         "mxfp8act": "e2m1 x mxfp8-e4m3 mfma/fp32-acc"}
+         "mxfp8act": "e2m1 x mxfp8-e4m3 mfma/fp32-acc", "bf16": "bf16-mfma/fp32-acc"}
 
 WORKLOADS = {
     # name: (config, T, kind)
@@ -48,6 +48,7 @@ WORKLOADS = {
     "c4": ("c4", 16384, "prefill"),
     "c1-w4a8": ("c1-w4a8", 8, "decode"),
     "c2-w4a8": ("c2-w4a8", 4096, "prefill"),
+    "c2-bf16": ("c2-bf16", 4096, "prefill"),
 }
 
 
@@ -210,7 +211,7 @@ def main() -> int:
     return 0
 
 
-PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64, "c2-w4a8": 128}
+PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64, "c2-w4a8": 128, "c2-bf16": 128}
 
 
 def cpu_baseline(lay, xs, kind, T, sample_tokens, sel_bytes, seconds):

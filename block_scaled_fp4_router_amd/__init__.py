@@ -21,13 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libftmoe.so")
 # ftmoe_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 # ftmoe_wfmt
-W_MXFP4, W_NVFP4, W_FP8_E4M3 = 1, 2, 3
+W_MXFP4, W_NVFP4, W_FP8_E4M3, W_BF16 = 1, 2, 3, 4
 # ftmoe_afmt
 ACT_BF16, ACT_FP8_PER_TENSOR, ACT_MXFP8 = 0, 1, 2
 # ftmoe_path
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
-FMT_CODES = {"mxfp4": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8_E4M3}
+FMT_CODES = {"mxfp4": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8_E4M3, "bf16": W_BF16}
 ACT_CODES = {"bf16": ACT_BF16, "fp8": ACT_FP8_PER_TENSOR, "mxfp8": ACT_MXFP8}
 PATH_CODES = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL}
 BIAS_LOGITS, BIAS_SELECT = 0, 1
@@ -186,7 +186,10 @@ class DeviceLayer:
 
     def pack(self) -> "DeviceLayer":
         """Adds the prefill tile layout of every matrix set (a load-time step;
-        doubles the weights' footprint).  Returns self."""
+        doubles the weights' footprint).  Returns self.  BF16 experts have
+        no packed layout and are left as they are."""
+        if self.gate_up.fmt == "bf16":
+            return self
         self.gate_up.pack(ROLE_GATE_UP)
         self.down.pack(ROLE_DOWN)
         if self.shared_inter:
@@ -196,10 +199,15 @@ class DeviceLayer:
 
     @classmethod
     def from_host(cls, lay, device="cuda", path="auto") -> "DeviceLayer":
+        import numpy as np
         import torch
 
         def t(a):
-            return None if a is None else torch.from_numpy(a).to(device)
+            if a is None:
+                return None
+            if a.dtype == np.uint16:   # bf16 bit patterns travel as int16
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
 
         def qw(q):
             if q is None:

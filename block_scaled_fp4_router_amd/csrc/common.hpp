@@ -20,6 +20,7 @@ constexpr int kWave = 64;
 constexpr int kMXFP4 = 1;
 constexpr int kNVFP4 = 2;
 constexpr int kFP8 = 3;
+constexpr int kBF16 = 4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 

@@ -398,7 +398,8 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeA
   }
 }
 
-// ================================================ bf16 / FP8 kernels ======
+// ================================================ NVFP4 / FP8 / BF16 kernels
+// (BF16 weights go to the bf16 MFMA as they are.)
 // Per-lane weight slice of one 128-element K chunk (elements [32g, 32g+32)).
 struct WSlice4 {   // NVFP4: 16 bytes of codes + two E4M3 block scales
   uint4 c;
@@ -407,8 +408,12 @@ struct WSlice4 {   // NVFP4: 16 bytes of codes + two E4M3 block scales
 struct WSlice8 {   // FP8: 32 bytes of codes
   uint4 c0, c1;
 };
+struct WSlice16 {  // BF16: 32 values, 8 per MFMA step
+  uint4 c[4];
+};
 template <int WFMT> struct WSliceT { using type = WSlice4; };
 template <> struct WSliceT<kFP8> { using type = WSlice8; };
+template <> struct WSliceT<kBF16> { using type = WSlice16; };
 
 template <int WFMT>
 __device__ __forceinline__ typename WSliceT<WFMT>::type load_wslice(const QW& w, size_t row, int K, int kb) {
@@ -417,6 +422,10 @@ __device__ __forceinline__ typename WSliceT<WFMT>::type load_wslice(const QW& w,
     const uint8_t* p = w.codes + row * K + kb;
     s.c0 = load16(p);
     s.c1 = load16(p + 16);
+  } else if constexpr (WFMT == kBF16) {
+    const uint8_t* p = w.codes + (row * K + kb) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.c[i] = load16(p + 16 * i);
   } else {
     s.c = load16(w.codes + row * (K / 2) + kb / 2);
     s.sc = *reinterpret_cast<const uint16_t*>(w.scales + row * (K / 16) + kb / 16);
@@ -491,6 +500,8 @@ __device__ __forceinline__ void mma_batch(const typename WSliceT<WFMT>::type* ws
         bf16x8 bw;
         if constexpr (WFMT == kFP8)
           bw = fp8_bf16(ws[u], st);
+        else if constexpr (WFMT == kBF16)
+          bw = __builtin_bit_cast(bf16x8, ws[u].c[st]);
         else
           bw = nvfp4_bf16(ws[u], st);
         const bf16x8 av = valid ? __builtin_bit_cast(bf16x8, lds16(row, r, kb / 8 + st)) : bf16x8{};
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   }
 
   // this lane's weight row's multiplier (and the activation scale)
-  float f = row_scale(w, e, j < 8 ? i0 + j : I + i0 + (j - 8));
+  float f = WFMT == kBF16 ? 1.0f : row_scale(w, e, j < 8 ? i0 + j : I + i0 + (j - 8));
   if constexpr (FP8ACT) f *= scale_from_amax(a.amax_x);
   uint16_t* h = shared ? a.hs : a.h;
   float mx = 0.f;
@@ -604,7 +615,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
       ws[u] = load_wslice<WFMT>(w, wrow, K, min(kc0 + u * 128, K - 128) + g * 32);
     mma_batch<WFMT, FP8ACT, true, NB>(ws, kc0, K, g, hsm, 2 * K, j, aval, sh, acc);
   }
-  const float f = row_scale(w, e, n0 + j) * sh;
+  const float f = (WFMT == kBF16 ? 1.0f : row_scale(w, e, n0 + j)) * sh;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int slot = 4 * g + r;
@@ -704,7 +715,7 @@ static hipError_t run_gateup_mx(const DecodeArgs& a, hipStream_t s) {
 
 template <int WFMT, bool FP8ACT, int WPB>
 static hipError_t run_gateup(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NB = WFMT == kFP8 ? 8 : 16;
+  constexpr int NB = WFMT == kBF16 ? 4 : WFMT == kFP8 ? 8 : 16;
   const int imax = a.Is > a.I ? a.Is : a.I;
   const size_t lds = static_cast<size_t>(decode_rows(a.T)) * (FP8ACT ? a.H : 2 * a.H);
   dim3 grid((imax / 8 + WPB - 1) / WPB, a.nb_routed + a.nb_shared);
@@ -733,7 +744,7 @@ static hipError_t run_down_mx(const DecodeArgs& a, hipStream_t s) {
 
 template <int WFMT, bool FP8ACT>
 static hipError_t run_down(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NB = WFMT == kFP8 ? 4 : 8;
+  constexpr int NB = WFMT == kBF16 ? 2 : WFMT == kFP8 ? 4 : 8;
   const int kmax = a.Is > a.I ? a.Is : a.I;
   const size_t lds = static_cast<size_t>(decode_rows(a.T)) * 2 * kmax;
   dim3 grid(decode_down_tiles(a.H), a.nb_routed + a.nb_shared);
@@ -754,6 +765,9 @@ hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
     case kFP8:
       if (fp8act) return small ? run_gateup<kFP8, true, 1>(a, s) : run_gateup<kFP8, true, 4>(a, s);
       return small ? run_gateup<kFP8, false, 1>(a, s) : run_gateup<kFP8, false, 4>(a, s);
+    case kBF16:
+      if (fp8act) return hipErrorInvalidValue;
+      return small ? run_gateup<kBF16, false, 1>(a, s) : run_gateup<kBF16, false, 4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -764,6 +778,7 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
     case kMXFP4: return run_down_mx(a, s);
     case kNVFP4: return run_down<kNVFP4, false>(a, s);
     case kFP8: return fp8act ? run_down<kFP8, true>(a, s) : run_down<kFP8, false>(a, s);
+    case kBF16: return fp8act ? hipErrorInvalidValue : run_down<kBF16, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -127,8 +127,10 @@ ftmoe_status check_qweight(const ftmoe_qweight& q, const char* name, int fmt, in
   }
   if (q.row_scales != 0 && q.row_scales != 1)
     return fail(FTMOE_ERR_INVALID_ARG, "%s.row_scales=%d is neither 0 nor 1", name, q.row_scales);
-  if (q.row_scales && fmt == FTMOE_W_MXFP4)
-    return fail(FTMOE_ERR_INVALID_ARG, "%s.row_scales: MXFP4 has no fp32 multipliers", name);
+  if (q.row_scales && (fmt == FTMOE_W_MXFP4 || fmt == FTMOE_W_BF16))
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.row_scales: the format has no fp32 multipliers", name);
+  if (q.packed && fmt == FTMOE_W_BF16)
+    return fail(FTMOE_ERR_INVALID_ARG, "%s.packed: BF16 experts have no packed layout", name);
   if (q.reserved != 0) return fail(FTMOE_ERR_INVALID_ARG, "%s.reserved=%d is not 0", name, q.reserved);
   if (q.packed && (reinterpret_cast<uintptr_t>(q.packed) & 255u))
     return fail(FTMOE_ERR_INVALID_ARG, "%s.packed is not 256-byte aligned", name);
@@ -156,7 +158,7 @@ ftmoe_status check_layer(const ftmoe_layer* L) {
   if (!L->router_w) return fail(FTMOE_ERR_INVALID_ARG, "router_w is NULL");
   if (!aligned16(L->router_w)) return fail(FTMOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
   const int fmt = L->gate_up.fmt;
-  if (fmt != FTMOE_W_MXFP4 && fmt != FTMOE_W_NVFP4 && fmt != FTMOE_W_FP8_E4M3)
+  if (fmt != FTMOE_W_MXFP4 && fmt != FTMOE_W_NVFP4 && fmt != FTMOE_W_FP8_E4M3 && fmt != FTMOE_W_BF16)
     return fail(FTMOE_ERR_INVALID_ARG, "gate_up.fmt=%d is not an ftmoe_wfmt", fmt);
   if (L->act == FTMOE_ACT_FP8_PER_TENSOR && fmt != FTMOE_W_FP8_E4M3)
     return fail(FTMOE_ERR_UNSUPPORTED, "FP8 per-tensor activations need FP8 weights");
@@ -633,7 +635,8 @@ ftmoe_status ftmoe_packed_size(const ftmoe_qweight* w, int32_t role, size_t* byt
   if (role != FTMOE_ROLE_GATE_UP && role != FTMOE_ROLE_DOWN)
     return fail(FTMOE_ERR_INVALID_ARG, "role=%d is not an ftmoe_role", role);
   if (w->fmt != FTMOE_W_MXFP4 && w->fmt != FTMOE_W_NVFP4 && w->fmt != FTMOE_W_FP8_E4M3)
-    return fail(FTMOE_ERR_INVALID_ARG, "fmt=%d is not an ftmoe_wfmt", w->fmt);
+    return fail(w->fmt == FTMOE_W_BF16 ? FTMOE_ERR_UNSUPPORTED : FTMOE_ERR_INVALID_ARG,
+                "fmt=%d has no packed layout", w->fmt);
   if (w->num_experts < 1 || w->num_experts > kMaxExperts || w->n < 1 || w->k < 128 || w->k % 128 ||
       w->k > kMaxDim || w->n > 2 * kMaxDim || (role == FTMOE_ROLE_GATE_UP && w->n % 256))
     return fail(FTMOE_ERR_UNSUPPORTED, "matrix set [%d][%d][%d] has no packed layout", w->num_experts, w->n, w->k);

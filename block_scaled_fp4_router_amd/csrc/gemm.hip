@@ -59,7 +59,7 @@ int gemm_block_m(int T, int k, int E, int wfmt, bool a8) {
   // Small experts (few rows each) waste less padding with 64-row blocks; FP8
   // weight stages are twice as wide, and MXFP8 activation stages half as
   // wide, so both always use 128-row blocks (whole DMA chunks per wave).
-  if (wfmt == kFP8 || a8) return 128;
+  if (wfmt == kFP8 || wfmt == kBF16 || a8) return 128;
   return static_cast<long long>(T) * k >= 192LL * E ? 128 : 64;
 }
 
@@ -67,15 +67,17 @@ template <int WFMT, bool FP8ACT, int BM>
 struct Cfg {
   static constexpr int kWM = BM / 64;                  // waves along rows
   static constexpr int kWN = kGemmWaves / kWM;         // waves along columns
-  static constexpr int kNT = BM == 128 ? 4 : 2;        // 32-column MFMA tiles per wave
+  // 32-column MFMA tiles per wave (BF16 weight stages are 4x as wide as
+  // FP4's, so their tile has half the columns)
+  static constexpr int kNT = WFMT == kBF16 ? 2 : BM == 128 ? 4 : 2;
   static constexpr int kBN = 32 * kNT * kWN;           // weight rows per workgroup
   static constexpr int kAV = FP8ACT ? 4 : 8;           // 16-byte vectors per activation row and stage
   static constexpr int kARowB = 16 * kAV;
-  static constexpr int kBRowB = WFMT == kFP8 ? 64 : 32;  // weight bytes per row and stage
+  static constexpr int kBRowB = WFMT == kBF16 ? 128 : WFMT == kFP8 ? 64 : 32;  // weight bytes per row and stage
   static constexpr int kBV = kBRowB / 16;
   static constexpr int kABytes = BM * kARowB;
   static constexpr int kBBytes = kBN * kBRowB;
-  static constexpr bool kScales = WFMT != kFP8;        // FP4: one scale dword per weight row and stage
+  static constexpr bool kScales = WFMT == kMXFP4 || WFMT == kNVFP4;   // FP4: one scale dword per weight row and stage
   static constexpr int kSBytes = kScales ? 4 * kBN : 0;
   // MXFP4: split E4M3 activations (a row's stage = 64 hi + 64 lo bytes), or
   // with FP8ACT the MXFP8 form (64 bytes), and one E8M0 scale dword per
@@ -354,6 +356,35 @@ __device__ __forceinline__ void frag_read_a2(uint32_t vA0, uint32_t vA1, u32x4& 
       : "v"(vA0), "v"(vA1), "n"(OFF));
 }
 
+// BF16 weights (and activations), 2 column tiles: four vectors per operand
+// row, one per MFMA step, at per-lane offsets (the swizzle differs per step).
+template <int OB1, int OAM>
+__device__ __forceinline__ void frag_read_bf16w_2(const uint32_t (&vB)[4], const uint32_t (&vA)[4], u32x4 (&b)[8],
+                                                  u32x4 (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %17\n"
+      "ds_read_b128 %2, %18\n"
+      "ds_read_b128 %3, %19\n"
+      "ds_read_b128 %4, %16 offset:%24\n"
+      "ds_read_b128 %5, %17 offset:%24\n"
+      "ds_read_b128 %6, %18 offset:%24\n"
+      "ds_read_b128 %7, %19 offset:%24\n"
+      "ds_read_b128 %8, %20\n"
+      "ds_read_b128 %9, %21\n"
+      "ds_read_b128 %10, %22\n"
+      "ds_read_b128 %11, %23\n"
+      "ds_read_b128 %12, %20 offset:%25\n"
+      "ds_read_b128 %13, %21 offset:%25\n"
+      "ds_read_b128 %14, %22 offset:%25\n"
+      "ds_read_b128 %15, %23 offset:%25\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]),
+        "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(vB[0]), "v"(vB[1]), "v"(vB[2]), "v"(vB[3]), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1),
+        "n"(OAM));
+}
+
 // FP8 weights and activations, 4 column tiles: two vectors per operand row.
 template <int OB1, int OB2, int OB3, int OAM>
 __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
@@ -526,7 +557,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // ---- DMA side: the tile whose stages are being fetched ----
   // 32-bit per-lane offsets from uniform bases (one expert's matrix < 4 GiB)
   const size_t wrows = static_cast<size_t>(GATEUP ? 2 * N : N);
-  const uint32_t wrow_bytes = WFMT == kFP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
+  const uint32_t wrow_bytes = WFMT == kBF16 ? 2u * static_cast<uint32_t>(K)
+                              : WFMT == kFP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
   // Weight stages come from the row-major matrices, or from the packed tile
   // layout, where a stage of this tile is one contiguous run: codes in LDS
   // order, then (FP4) one scale dword per tile row.
@@ -678,10 +710,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // through immediate offsets of the same read instructions.
   const int RB = Rt[0] + j, RA = arow0 + j;
   const uint32_t brow = C::kABytes + RB * C::kBRowB, arow = RA * C::kARowB;
-  uint32_t bo[2], ao[4];
+  uint32_t bo[4], ao[4];
   const uint32_t so = C::kABytes + C::kBBytes + 4 * RB;
   const uint32_t sao = C::kABytes + C::kBBytes + C::kSBytes + 4 * RA;
-  if constexpr (WFMT != kFP8) {
+  if constexpr (WFMT == kBF16) {
+    // K [32g + 8t, 32g + 8t + 8) of a row at MFMA step t, as for the activations
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) bo[tt] = brow + 16 * swz<C::kBV>(RB, 4 * g + tt);
+  } else if constexpr (WFMT != kFP8) {
     bo[0] = bo[1] = brow + 16 * swz<C::kBV>(RB, g);
   } else if constexpr (FP8ACT) {
     bo[0] = brow + 16 * swz<C::kBV>(RB, g);
@@ -713,7 +749,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   constexpr int kD2 = GATEUP ? kHalf : 64;
   constexpr int kD3 = GATEUP ? kHalf + 32 : 96;
   constexpr int kOAM = 32 * C::kARowB;
-  constexpr int kBVec = WFMT == kFP8 ? 2 * NT : NT;
+  constexpr int kBVec = WFMT == kBF16 ? 4 * NT : WFMT == kFP8 ? 2 * NT : NT;
   constexpr int kAVec = FP8ACT ? 4 : 8;
 
   f32x16 acc[2][NT];
@@ -736,6 +772,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       else
         frag_read_mx_2<kD1 * C::kBRowB, kD1 * 4, kOAM, 32 * 4>(base + bo[0], base + so, base + sao, vA, bv, scw, asw,
                                                                av);
+    } else if constexpr (WFMT == kBF16) {
+      static_assert(NT == 2, "BF16 weight tiles");
+      const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
+      const uint32_t vB[4] = {base + bo[0], base + bo[1], base + bo[2], base + bo[3]};
+      frag_read_bf16w_2<kD1 * C::kBRowB, kOAM>(vB, vA, bv, av);
     } else if constexpr (WFMT != kFP8) {
       const uint32_t vA[4] = {base + ao[0], base + ao[1], base + ao[2], base + ao[3]};
       if constexpr (NT == 4)
@@ -793,7 +834,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
           bf16x8 bt;
-          if constexpr (WFMT == kFP8)
+          if constexpr (WFMT == kBF16)
+            bt = __builtin_bit_cast(bf16x8, to_u4(bv[4 * ct + tt]));
+          else if constexpr (WFMT == kFP8)
             bt = weight_bf16<WFMT>(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]), 0, tt);
           else
             bt = weight_bf16<WFMT>(to_u4(bv[ct]), to_u4(bv[ct]), scw[ct] >> sh, tt);
@@ -1016,8 +1059,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       for (int u = 0; u < NT / 2; ++u) {
         const int col = tile_col(nt, Rt[u] + j);   // gate column of this lane
         // multipliers of its gate row and of the matching up row
-        const float fg = wact ? row_scale(w, e, col) * fa : 0.f;
-        const float fu = wact ? row_scale(w, e, N + col) * fa : 0.f;
+        const float fg = WFMT == kBF16 ? 1.0f : wact ? row_scale(w, e, col) * fa : 0.f;
+        const float fu = WFMT == kBF16 ? 1.0f : wact ? row_scale(w, e, N + col) * fa : 0.f;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -1036,7 +1079,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       float fc[NT];   // multiplier of each of this lane's output columns
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) fc[ct] = 1.0f;
-      if constexpr (WFMT != kMXFP4) {
+      if constexpr (WFMT == kNVFP4 || WFMT == kFP8) {
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) fc[ct] = wact ? row_scale(w, e, c0 + 32 * ct) * fa : 0.f;
       }
@@ -1108,6 +1151,9 @@ static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
     case kFP8:
       if (bm != 128) return hipErrorInvalidValue;
       return fp8act ? run<kFP8, true, 128, GATEUP>(ga, s) : run<kFP8, false, 128, GATEUP>(ga, s);
+    case kBF16:
+      if (bm != 128 || fp8act || ga.w.packed) return hipErrorInvalidValue;
+      return run<kBF16, false, 128, GATEUP>(ga, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -60,17 +60,21 @@ typedef enum {
   FTMOE_ERR_HIP = 4           /* HIP runtime reported an error             */
 } ftmoe_status;
 
-/* Expert weight formats (FreeToken README, "Broad MoE & Ecosystem Support").
+/* Expert weight formats (FreeToken README, "Broad MoE & Ecosystem Support":
+ * MXFP4, NVFP4, FP8 and BF16).
  *  MXFP4: OCP Microscaling v1.0.  E2M1 codes, two per byte (element 2i in the
  *         low nibble), one E8M0 scale byte (2^(s-127)) per 32 elements along K.
  *  NVFP4: E2M1 codes as above, one E4M3FN scale byte per 16 elements along K,
  *         and one fp32 multiplier per matrix: w = e2m1 * e4m3(s_blk) * g.
  *  FP8:   one E4M3FN (OCP: bias 7, max 448, no inf) byte per element and one
- *         fp32 multiplier per matrix: w = e4m3 * g.                       */
+ *         fp32 multiplier per matrix: w = e4m3 * g.
+ *  BF16:  one bf16 per element (codes hold [E][N][K] 16-bit patterns), no
+ *         scales; bf16 activations only; no packed prefill layout.        */
 typedef enum {
   FTMOE_W_MXFP4 = 1,
   FTMOE_W_NVFP4 = 2,
-  FTMOE_W_FP8_E4M3 = 3
+  FTMOE_W_FP8_E4M3 = 3,
+  FTMOE_W_BF16 = 4
 } ftmoe_wfmt;
 
 /* Activation format fed to the expert GEMMs.  FP8_PER_TENSOR is the W8A8
@@ -107,11 +111,11 @@ typedef enum {
 } ftmoe_path;
 
 /* One stacked set of expert matrices, [E][N][K], K contiguous.
- *  codes:         FP4: [E][N][K/2] bytes.  FP8: [E][N][K] bytes.
- *  block_scales:  MXFP4: [E][N][K/32] E8M0.  NVFP4: [E][N][K/16] E4M3.  FP8: NULL.
+ *  codes:         FP4: [E][N][K/2] bytes.  FP8: [E][N][K] bytes.  BF16: [E][N][K] bf16.
+ *  block_scales:  MXFP4: [E][N][K/32] E8M0.  NVFP4: [E][N][K/16] E4M3.  FP8, BF16: NULL.
  *  tensor_scales: NVFP4, FP8: fp32 dequantisation multipliers, [E] (one per
  *                 matrix) or, with row_scales = 1, [E][N] (one per matrix
- *                 row: row-wise scaling).  MXFP4: NULL.
+ *                 row: row-wise scaling).  MXFP4, BF16: NULL.
  * A fused projection whose parts were quantised with separate per-tensor
  * scales (the FreeToken commit message on FP8 projections: gate and up of a
  * gate_up matrix, each with its own scale) is passed with row_scales = 1 and

@@ -234,6 +234,8 @@ CONFIGS = {
     # the c4 layer with its Zipf router bias taking part in the selection only
     "c4-selbias": LayerConfig("c4-selbias", (16384,), 4096, 128, 8, 1536, "fp8", act="fp8", zipf_s=1.1,
                               bias_mode="select", seed=4),
+    # the c2 layer's shape with BF16 experts
+    "c2-bf16": LayerConfig("c2-bf16", (4096,), 2048, 128, 8, 768, "bf16", seed=1),
     # the c1 / c2 layers (same weights) with MXFP8 activations (W4A8)
     "c1-w4a8": LayerConfig("c1-w4a8", (1, 8), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),
     "c2-w4a8": LayerConfig("c2-w4a8", (4096,), 2048, 128, 8, 768, "mxfp4", act="mxfp8", seed=1),

@@ -143,6 +143,25 @@ def test_weight_shape_and_format_validation():
 
 
 @needs_lib
+def test_bf16_experts_validation():
+    d = good_layer()
+    d.gate_up = _qw(ft.W_BF16, 8, 256, 256)
+    d.down = _qw(ft.W_BF16, 8, 256, 128)
+    assert _ws_status(d)[0] == ft.OK
+    d.gate_up.row_scales = 1                       # no fp32 multipliers
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    d.gate_up.row_scales = 0
+    d.act = ft.ACT_FP8_PER_TENSOR                  # bf16 activations only
+    assert _ws_status(d)[0] == ft.ERR_UNSUPPORTED
+    d.act = ft.ACT_BF16
+    d.gate_up.packed = FAKE                        # no packed layout
+    assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert ft.load().ftmoe_packed_size(ctypes.byref(_qw(ft.W_BF16, 8, 256, 256)), ft.ROLE_GATE_UP,
+                                       ctypes.byref(n)) == ft.ERR_UNSUPPORTED
+
+
+@needs_lib
 def test_row_scale_flag_validation():
     d = good_layer()
     d.gate_up.row_scales = 1                       # MXFP4 has no fp32 multipliers

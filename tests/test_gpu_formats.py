@@ -24,6 +24,8 @@ LAYERS = {
     "f8row": (256, 8, 2, 256, "fp8", "fp8", 0, {"scale_mode": "row"}),
     "f8part": (256, 8, 2, 128, "fp8", "bf16", 0, {"scale_mode": "part"}),
     "nvrow": (256, 8, 2, 128, "nvfp4", "bf16", 128, {"scale_mode": "row"}),
+    # BF16 experts (with a shared expert)
+    "bf16w": (256, 8, 2, 256, "bf16", "bf16", 128),
     # Zipf router bias used for the selection only
     "mxsel": (384, 16, 4, 256, "mxfp4", "bf16", 0, {"zipf_s": 1.1, "zipf_ratio": 2.5, "bias_mode": "select"}),
 }
@@ -33,6 +35,8 @@ _cache = {}
 
 
 def layer(name, packed=False):
+    if packed and LAYERS[name][4] == "bf16":
+        pytest.skip("BF16 experts have no packed layout")
     key = (name, packed)
     if key not in _cache:
         H, E, k, I, fmt, act, Is = LAYERS[name][:7]
