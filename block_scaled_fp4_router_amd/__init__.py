@@ -38,7 +38,9 @@ EXPORTS = (
     "ftmoe_workspace_size", "ftmoe_align_max_padded", "ftmoe_align_workspace_size", "ftmoe_route",
     "ftmoe_align", "ftmoe_experts_forward", "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor",
     "ftmoe_timing_enable", "ftmoe_timing_collect", "ftmoe_status_string", "ftmoe_last_error", "ftmoe_version",
-    "ftmoe_packed_size", "ftmoe_pack_qweight",
+    "ftmoe_packed_size", "ftmoe_pack_qweight", "ftmoe_cache_pool_size", "ftmoe_cache_create",
+    "ftmoe_cache_destroy", "ftmoe_cache_plan", "ftmoe_cache_workspace_size", "ftmoe_cache_forward",
+    "ftmoe_cache_stats",
 )
 ROLE_GATE_UP, ROLE_DOWN = 0, 1
 
@@ -105,8 +107,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_timing_enable.restype = None
     lib.ftmoe_timing_collect.argtypes = [i32, ctypes.c_char_p, P(ctypes.c_double), P(i64)]
     lib.ftmoe_timing_collect.restype = i32
+    lib.ftmoe_cache_pool_size.argtypes = [P(LayerDesc), i32, P(sz)]
+    lib.ftmoe_cache_create.argtypes = [P(LayerDesc), P(QWeightDesc), P(QWeightDesc), i32, vp, sz, P(vp)]
+    lib.ftmoe_cache_destroy.argtypes = [vp]
+    lib.ftmoe_cache_destroy.restype = None
+    lib.ftmoe_cache_plan.argtypes = [vp, vp, i32, vp, vp]
+    lib.ftmoe_cache_workspace_size.argtypes = [vp, i32, P(sz)]
+    lib.ftmoe_cache_forward.argtypes = [vp, vp, i32, vp, sz, vp, vp, vp, vp]
+    lib.ftmoe_cache_stats.argtypes = [vp, P(i64), P(i64), P(i64), P(i64)]
     for name in ("ftmoe_workspace_size", "ftmoe_route", "ftmoe_align", "ftmoe_experts_forward",
-                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight"):
+                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight",
+                 "ftmoe_cache_pool_size", "ftmoe_cache_create", "ftmoe_cache_plan", "ftmoe_cache_workspace_size",
+                 "ftmoe_cache_forward", "ftmoe_cache_stats"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -307,6 +319,84 @@ def forward(layer: DeviceLayer, x, T: int, ws, y, topk_ids=None, topk_w=None, st
     d = desc if desc is not None else layer.desc()
     _check(load().ftmoe_forward(ctypes.byref(d), _ptr(x), T, _ptr(ws), ws.numel(), _ptr(y), _ptr(topk_ids),
                                 _ptr(topk_w), _stream(stream)))
+
+
+class ExpertCache:
+    """An HBM pool of ``slots`` expert slots over routed experts kept in host
+    memory (ftmoe_cache_*).  ``layer`` is a DeviceLayer whose router and
+    shared expert are used (its routed experts are not); ``host_gate_up``
+    and ``host_down`` are DeviceQWeight-like holders of host tensors (pinned
+    for asynchronous copies)."""
+
+    def __init__(self, layer: DeviceLayer, host_gate_up: "DeviceQWeight", host_down: "DeviceQWeight", slots: int,
+                 device="cuda"):
+        import torch
+        lib = load()
+        self.layer, self.host_gate_up, self.host_down, self.slots = layer, host_gate_up, host_down, slots
+        self._desc = layer.desc()
+        n = ctypes.c_size_t(0)
+        _check(lib.ftmoe_cache_pool_size(ctypes.byref(self._desc), slots, ctypes.byref(n)))
+        self.pool = torch.empty(max(256, n.value), dtype=torch.uint8, device=device)
+        self._hgu, self._hdn = host_gate_up.desc(), host_down.desc()
+        h = ctypes.c_void_p(0)
+        _check(lib.ftmoe_cache_create(ctypes.byref(self._desc), ctypes.byref(self._hgu), ctypes.byref(self._hdn),
+                                      slots, _ptr(self.pool), self.pool.numel(), ctypes.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def from_host(cls, lay, slots: int, device="cuda", path="auto") -> "ExpertCache":
+        """From a generator layer: router and shared expert on the device, the
+        routed experts in pinned host memory."""
+        import numpy as np
+        import torch
+
+        def pinned(a):
+            if a is None:
+                return None
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+
+        def hq(q):
+            return DeviceQWeight(q.fmt, q.num_experts, q.n, q.k, pinned(q.codes), pinned(q.block_scales),
+                                 pinned(q.tensor_scales))
+
+        return cls(DeviceLayer.from_host(lay, device, path=path), hq(lay.gate_up), hq(lay.down), slots, device)
+
+    def plan(self, experts):
+        """The residency policy alone (host): (slot per expert, miss flags)."""
+        import numpy as np
+        e = np.ascontiguousarray(experts, dtype=np.int32)
+        sl = np.zeros(len(e), np.int32)
+        miss = np.zeros(len(e), np.int32)
+        _check(load().ftmoe_cache_plan(self.handle, e.ctypes.data, len(e), sl.ctypes.data, miss.ctypes.data))
+        return sl, miss
+
+    def workspace(self, T: int, device="cuda"):
+        import torch
+        n = ctypes.c_size_t(0)
+        _check(load().ftmoe_cache_workspace_size(self.handle, T, ctypes.byref(n)))
+        return torch.empty(max(256, n.value), dtype=torch.uint8, device=device)
+
+    def forward(self, x, T: int, ws, y, topk_ids=None, topk_w=None, stream=None) -> None:
+        _check(load().ftmoe_cache_forward(self.handle, _ptr(x), T, _ptr(ws), ws.numel(), _ptr(y), _ptr(topk_ids),
+                                          _ptr(topk_w), _stream(stream)))
+
+    def stats(self) -> dict:
+        v = [ctypes.c_int64(0) for _ in range(4)]
+        _check(load().ftmoe_cache_stats(self.handle, *[ctypes.byref(t) for t in v]))
+        return dict(zip(("hits", "misses", "bytes_copied", "passes"), (t.value for t in v)))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            load().ftmoe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def quantize_fp8_per_tensor(x, n: int, q, scale, ws, stream=None) -> None:

@@ -282,10 +282,12 @@ __global__ __launch_bounds__(64 * kGateWaves) void decode_gateup_mx_kernel(Decod
   const int I = shared ? a.Is : a.I;
   const int c0 = blockIdx.x * 8 * kGateWaves;
   if (c0 >= I) return;
-  const int e = shared ? 0 : a.block_expert[b];
-  if (e < 0) return;
-  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const int ex = shared ? 0 : a.block_expert[b];
+  if (ex < 0) return;
   const QW& w = shared ? a.sgu : a.gu;
+  const int e = expert_slot(w, ex);   // slot of its matrices
+  if (e < 0) return;                  // served by another pass
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const int H = a.H, nch = H / 128;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int i0 = c0 + wave * 8;
@@ -358,10 +360,12 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_mx_kernel(DecodeA
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int b = blockIdx.y;
   const bool shared = b >= a.nb_routed;
-  const int e = shared ? 0 : a.block_expert[b];
-  if (e < 0) return;
-  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const int ex = shared ? 0 : a.block_expert[b];
+  if (ex < 0) return;
   const QW& w = shared ? a.sdn : a.dn;
+  const int e = expert_slot(w, ex);   // slot of its matrices
+  if (e < 0) return;                  // served by another pass
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const int K = shared ? a.Is : a.I;
   const int H = a.H, nch = K / 128;
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -517,10 +521,12 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ float red[16];
   const int b = blockIdx.y;
   const bool shared = b >= a.nb_routed;
-  const int e = shared ? 0 : a.block_expert[b];
-  if (e < 0) return;
-  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const int ex = shared ? 0 : a.block_expert[b];
+  if (ex < 0) return;
   const QW& w = shared ? a.sgu : a.gu;
+  const int e = expert_slot(w, ex);   // slot of its matrices
+  if (e < 0) return;                  // served by another pass
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const int I = shared ? a.Is : a.I;
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -581,10 +587,12 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
   extern __shared__ __attribute__((aligned(16))) uint8_t hsm[];
   const int b = blockIdx.y;
   const bool shared = b >= a.nb_routed;
-  const int e = shared ? 0 : a.block_expert[b];
-  if (e < 0) return;
-  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const int ex = shared ? 0 : a.block_expert[b];
+  if (ex < 0) return;
   const QW& w = shared ? a.sdn : a.dn;
+  const int e = expert_slot(w, ex);   // slot of its matrices
+  if (e < 0) return;                  // served by another pass
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
   const int K = shared ? a.Is : a.I;
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = lane_id();

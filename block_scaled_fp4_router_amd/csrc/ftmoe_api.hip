@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <new>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -284,7 +285,7 @@ Plan make_plan(const ftmoe_layer* L, int T) {
 }
 
 QW to_qw(const ftmoe_qweight& q) {
-  QW w;
+  QW w{};
   w.fmt = q.fmt;
   w.n = q.n;
   w.k = q.k;
@@ -356,8 +357,21 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
   return FTMOE_OK;
 }
 
+// Expert passes over an expert-slot pool: pass i runs the routed gate_up and
+// down of the experts that table i maps to a slot (the others' blocks exit at
+// once); before(i) is called on the host first (it enqueues that pass's
+// copies into the pool).  The shared expert runs in pass 0; align, the
+// activation preparation and the combine run once.
+struct Passes {
+  int n = 1;
+  const int32_t* const* tables = nullptr;   // n device tables [E], or NULL: one pass, no table
+  ftmoe_status (*before)(void* ctx, int i) = nullptr;
+  void* ctx = nullptr;
+};
+
 ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, const int32_t* ids, const float* w,
-                             const float* sg, const Plan& p, void* ws, uint16_t* y, bool aligned, hipStream_t s) {
+                             const float* sg, const Plan& p, void* ws, uint16_t* y, bool aligned, hipStream_t s,
+                             const Passes& passes = Passes{}) {
   const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
   const bool fp8act = L->act == FTMOE_ACT_FP8_PER_TENSOR;
   const bool shared = L->shared_inter > 0;
@@ -446,9 +460,15 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     a.w = w;
     a.sg = shared ? sg : nullptr;
     a.y = y;
-    FT_HIP(timed("decode_gateup", s, [&] { return launch_decode_gateup(a, s); }), "decode gate_up launch");
-    if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
-    FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(a, s); }), "decode down launch");
+    for (int i = 0; i < passes.n; ++i) {
+      if (passes.before) FT_TRY(passes.before(passes.ctx, i));
+      if (passes.tables) a.gu.slot_of = a.dn.slot_of = passes.tables[i];
+      a.nb_shared = i == 0 ? p.nb_shared : 0;
+      FT_HIP(timed("decode_gateup", s, [&] { return launch_decode_gateup(a, s); }), "decode gate_up launch");
+      if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
+      FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(a, s); }), "decode down launch");
+    }
+    a.nb_shared = p.nb_shared;
     FT_HIP(timed("combine", s, [&] { return launch_decode_combine(a, s); }), "combine launch");
     return FTMOE_OK;
   }
@@ -488,9 +508,6 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
            "x split launch");
   }
   uint8_t* hgsc = p.mx_gemm ? at<uint8_t>(ws, p.hgsc) : nullptr;
-  FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gu, rr, xa, H, I, h, hgsc, ahs, s); }),
-         "gate_up GEMM launch");
-  if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
   GemmAct ha{};
   ha.bf16 = h;
   ha.amax = ah;
@@ -499,14 +516,22 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     ha.split_sc = hgsc;
     ha.mx8 = p.a8;
   }
-  if (fp8act) {
-    uint8_t* hq = at<uint8_t>(ws, p.hq);
-    FT_HIP(timed("quant_h", s,
-                 [&] { return launch_quant_fp8(h, static_cast<int64_t>(p.P) * I, ah, hq, nullptr, s); }),
-           "quantise launch");
-    ha.q = hq;
+  for (int i = 0; i < passes.n; ++i) {
+    if (passes.before) FT_TRY(passes.before(passes.ctx, i));
+    QW gup = gu, dnp = dn;
+    if (passes.tables) gup.slot_of = dnp.slot_of = passes.tables[i];
+    FT_HIP(timed("gemm_gateup", s, [&] { return launch_gemm_gateup(gup, rr, xa, H, I, h, hgsc, ahs, s); }),
+           "gate_up GEMM launch");
+    if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
+    if (fp8act) {
+      uint8_t* hq = at<uint8_t>(ws, p.hq);
+      FT_HIP(timed("quant_h", s,
+                   [&] { return launch_quant_fp8(h, static_cast<int64_t>(p.P) * I, ah, hq, nullptr, s); }),
+             "quantise launch");
+      ha.q = hq;
+    }
+    FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dnp, rr, ha, H, I, o, s); }), "down GEMM launch");
   }
-  FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dn, rr, ha, H, I, o, s); }), "down GEMM launch");
   if (shared) {
     GemmAct xs = xa;
     xs.q = nullptr;
@@ -532,6 +557,146 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),
          "combine launch");
   return FTMOE_OK;
+}
+
+// ---- expert-slot pool ----
+// Bytes of one expert's matrices in each array of a matrix set.
+struct SetBytes {
+  size_t codes = 0, scales = 0, ts = 0;
+};
+
+SetBytes set_bytes(const ftmoe_qweight& q) {
+  SetBytes b;
+  const size_t nk = static_cast<size_t>(q.n) * q.k;
+  switch (q.fmt) {
+    case FTMOE_W_MXFP4: b.codes = nk / 2; b.scales = nk / 32; break;
+    case FTMOE_W_NVFP4: b.codes = nk / 2; b.scales = nk / 16; b.ts = 4; break;
+    case FTMOE_W_FP8_E4M3: b.codes = nk; b.ts = 4; break;
+    default: b.codes = 2 * nk; break;   // BF16
+  }
+  if (b.ts && q.row_scales) b.ts = 4 * static_cast<size_t>(q.n);
+  return b;
+}
+
+// Pool regions: gate_up codes, scales, multipliers, then down's, each
+// [slots][per-expert bytes] and 256-byte aligned.
+struct PoolLayout {
+  SetBytes gu, dn;
+  size_t gu_codes = 0, gu_scales = 0, gu_ts = 0, dn_codes = 0, dn_scales = 0, dn_ts = 0, total = 0;
+};
+
+PoolLayout pool_layout(const ftmoe_qweight& gu, const ftmoe_qweight& dn, int slots) {
+  PoolLayout pl;
+  pl.gu = set_bytes(gu);
+  pl.dn = set_bytes(dn);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  pl.gu_codes = take(pl.gu.codes * slots);
+  pl.gu_scales = take(pl.gu.scales * slots);
+  pl.gu_ts = take(pl.gu.ts * slots);
+  pl.dn_codes = take(pl.dn.codes * slots);
+  pl.dn_scales = take(pl.dn.scales * slots);
+  pl.dn_ts = take(pl.dn.ts * slots);
+  pl.total = off;
+  return pl;
+}
+
+}  // namespace
+
+// Residency state of one layer (the C ABI's opaque ftmoe_cache).
+struct ftmoe_cache {
+  ftmoe_layer layer{};          // gate_up and down point into the pool
+  ftmoe_qweight host_gu{}, host_dn{};
+  int slots = 0, E = 0;
+  PoolLayout pl;
+  uint8_t* pool = nullptr;
+  std::vector<int> slot_expert, expert_slot;   // -1: empty / not resident
+  std::vector<int64_t> last_use;               // per slot; -1: never
+  int64_t clock = 0, hits = 0, misses = 0, bytes = 0, passes = 0;
+  // per-call state
+  std::vector<int32_t> ids_host;
+  std::vector<int32_t> tables;                 // [passes][E] slot of each expert, -1 if not in the pass
+  std::vector<std::vector<int>> copy_e, copy_s;   // per pass: experts to copy and their slots
+  hipStream_t stream = nullptr;
+};
+
+namespace {
+
+// The LRU policy (see ftmoe_cache_plan).
+ftmoe_status cache_plan(ftmoe_cache* c, const int32_t* experts, int n, int32_t* out_slot, int32_t* out_miss) {
+  if (n > c->slots)
+    return fail(FTMOE_ERR_UNSUPPORTED, "%d experts do not fit %d slots", n, c->slots);
+  std::vector<char> seen(c->E, 0), needed(c->slots, 0);
+  for (int i = 0; i < n; ++i) {
+    const int e = experts[i];
+    if (e < 0 || e >= c->E) return fail(FTMOE_ERR_INVALID_ARG, "expert %d outside [0, %d)", e, c->E);
+    if (seen[e]) return fail(FTMOE_ERR_INVALID_ARG, "expert %d listed twice", e);
+    seen[e] = 1;
+    if (c->expert_slot[e] >= 0) needed[c->expert_slot[e]] = 1;
+  }
+  // free slots in least-recently-used order (never used first, then by age, then by index)
+  std::vector<int> cand;
+  for (int sl = 0; sl < c->slots; ++sl)
+    if (!needed[sl]) cand.push_back(sl);
+  std::stable_sort(cand.begin(), cand.end(), [&](int a, int b) { return c->last_use[a] < c->last_use[b]; });
+  size_t next = 0;
+  ++c->clock;
+  for (int i = 0; i < n; ++i) {
+    const int e = experts[i];
+    int sl = c->expert_slot[e];
+    const bool miss = sl < 0;
+    if (miss) {
+      sl = cand[next++];
+      if (c->slot_expert[sl] >= 0) c->expert_slot[c->slot_expert[sl]] = -1;
+      c->slot_expert[sl] = e;
+      c->expert_slot[e] = sl;
+      ++c->misses;
+    } else {
+      ++c->hits;
+    }
+    c->last_use[sl] = c->clock;
+    if (out_slot) out_slot[i] = sl;
+    if (out_miss) out_miss[i] = miss ? 1 : 0;
+  }
+  return FTMOE_OK;
+}
+
+// Copies of pass i: each missing expert's gate_up and down arrays, host -> its slot.
+ftmoe_status cache_copy_pass(void* ctx, int i) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  const PoolLayout& pl = c->pl;
+  auto copy = [&](size_t dst_off, const void* src, size_t bytes) -> hipError_t {
+    if (bytes == 0) return hipSuccess;
+    c->bytes += static_cast<int64_t>(bytes);
+    return hipMemcpyAsync(c->pool + dst_off, src, bytes, hipMemcpyHostToDevice, c->stream);
+  };
+  for (size_t m = 0; m < c->copy_e[i].size(); ++m) {
+    const size_t e = static_cast<size_t>(c->copy_e[i][m]), sl = static_cast<size_t>(c->copy_s[i][m]);
+    const uint8_t* gc = static_cast<const uint8_t*>(c->host_gu.codes);
+    const uint8_t* gs = static_cast<const uint8_t*>(c->host_gu.block_scales);
+    const uint8_t* gt = reinterpret_cast<const uint8_t*>(c->host_gu.tensor_scales);
+    const uint8_t* dc = static_cast<const uint8_t*>(c->host_dn.codes);
+    const uint8_t* ds = static_cast<const uint8_t*>(c->host_dn.block_scales);
+    const uint8_t* dt = reinterpret_cast<const uint8_t*>(c->host_dn.tensor_scales);
+    FT_HIP(copy(pl.gu_codes + sl * pl.gu.codes, gc + e * pl.gu.codes, pl.gu.codes), "expert copy");
+    if (pl.gu.scales) FT_HIP(copy(pl.gu_scales + sl * pl.gu.scales, gs + e * pl.gu.scales, pl.gu.scales), "expert copy");
+    if (pl.gu.ts) FT_HIP(copy(pl.gu_ts + sl * pl.gu.ts, gt + e * pl.gu.ts, pl.gu.ts), "expert copy");
+    FT_HIP(copy(pl.dn_codes + sl * pl.dn.codes, dc + e * pl.dn.codes, pl.dn.codes), "expert copy");
+    if (pl.dn.scales) FT_HIP(copy(pl.dn_scales + sl * pl.dn.scales, ds + e * pl.dn.scales, pl.dn.scales), "expert copy");
+    if (pl.dn.ts) FT_HIP(copy(pl.dn_ts + sl * pl.dn.ts, dt + e * pl.dn.ts, pl.dn.ts), "expert copy");
+  }
+  return FTMOE_OK;
+}
+
+// The most passes a step can need, and the workspace of ftmoe_cache_forward.
+int cache_max_passes(const ftmoe_cache* c) { return (c->E + c->slots - 1) / c->slots; }
+
+size_t cache_ws_bytes(const ftmoe_cache* c, const Plan& p) {
+  return up256(p.total) + up256(static_cast<size_t>(cache_max_passes(c)) * c->E * 4);
 }
 
 }  // namespace
@@ -730,5 +895,158 @@ const char* ftmoe_status_string(ftmoe_status st) {
 const char* ftmoe_last_error(void) { return g_last_error.c_str(); }
 
 int32_t ftmoe_version(void) { return 100; }
+
+ftmoe_status ftmoe_cache_pool_size(const ftmoe_layer* layer, int32_t slots, size_t* bytes) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  if (slots < 1 || slots > layer->num_experts)
+    return fail(FTMOE_ERR_INVALID_ARG, "slots=%d outside [1, num_experts=%d]", slots, layer->num_experts);
+  if (!bytes) return fail(FTMOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = pool_layout(layer->gate_up, layer->down, slots).total;
+  return FTMOE_OK;
+}
+
+ftmoe_status ftmoe_cache_create(const ftmoe_layer* layer, const ftmoe_qweight* host_gate_up,
+                                const ftmoe_qweight* host_down, int32_t slots, void* pool, size_t pool_bytes,
+                                ftmoe_cache** cache) {
+  g_last_error.clear();
+  if (!cache || !host_gate_up || !host_down) return fail(FTMOE_ERR_INVALID_ARG, "NULL argument");
+  *cache = nullptr;
+  FT_TRY(check_layer(layer));
+  const int E = layer->num_experts;
+  if (slots < 1 || slots > E) return fail(FTMOE_ERR_INVALID_ARG, "slots=%d outside [1, num_experts=%d]", slots, E);
+  const int fmt = layer->gate_up.fmt;
+  FT_TRY(check_qweight(*host_gate_up, "host_gate_up", fmt, E, 2 * layer->inter, layer->hidden));
+  FT_TRY(check_qweight(*host_down, "host_down", fmt, E, layer->hidden, layer->inter));
+  if (host_gate_up->packed || host_down->packed)
+    return fail(FTMOE_ERR_INVALID_ARG, "host experts have no packed layout");
+  const PoolLayout pl = pool_layout(*host_gate_up, *host_down, slots);
+  if (!pool || (reinterpret_cast<uintptr_t>(pool) & 255u))
+    return fail(FTMOE_ERR_INVALID_ARG, "pool must be non-NULL and 256-byte aligned");
+  if (pool_bytes < pl.total)
+    return fail(FTMOE_ERR_INVALID_ARG, "pool holds %zu bytes, %zu needed", pool_bytes, pl.total);
+  ftmoe_cache* c = new (std::nothrow) ftmoe_cache;
+  if (!c) return fail(FTMOE_ERR_INVALID_ARG, "out of host memory");
+  c->layer = *layer;
+  c->host_gu = *host_gate_up;
+  c->host_dn = *host_down;
+  c->slots = slots;
+  c->E = E;
+  c->pl = pl;
+  c->pool = static_cast<uint8_t*>(pool);
+  auto pooled = [&](const ftmoe_qweight& h, size_t codes, size_t scales, size_t ts) {
+    ftmoe_qweight q = h;
+    q.codes = c->pool + codes;
+    q.block_scales = h.block_scales ? c->pool + scales : nullptr;
+    q.tensor_scales = h.tensor_scales ? reinterpret_cast<const float*>(c->pool + ts) : nullptr;
+    q.packed = nullptr;
+    return q;
+  };
+  c->layer.gate_up = pooled(*host_gate_up, pl.gu_codes, pl.gu_scales, pl.gu_ts);
+  c->layer.down = pooled(*host_down, pl.dn_codes, pl.dn_scales, pl.dn_ts);
+  c->slot_expert.assign(slots, -1);
+  c->expert_slot.assign(E, -1);
+  c->last_use.assign(slots, -1);
+  *cache = c;
+  return FTMOE_OK;
+}
+
+void ftmoe_cache_destroy(ftmoe_cache* cache) { delete cache; }
+
+ftmoe_status ftmoe_cache_plan(ftmoe_cache* cache, const int32_t* experts, int32_t n, int32_t* out_slot,
+                              int32_t* out_miss) {
+  g_last_error.clear();
+  if (!cache || (n > 0 && !experts) || n < 0) return fail(FTMOE_ERR_INVALID_ARG, "bad arguments");
+  return cache_plan(cache, experts, n, out_slot, out_miss);
+}
+
+ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, size_t* bytes) {
+  g_last_error.clear();
+  if (!cache || !bytes) return fail(FTMOE_ERR_INVALID_ARG, "NULL argument");
+  FT_TRY(check_tokens(T));
+  *bytes = cache_ws_bytes(cache, make_plan(&cache->layer, T));
+  return FTMOE_OK;
+}
+
+ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                                 uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(FTMOE_ERR_INVALID_ARG, "cache is NULL");
+  const ftmoe_layer* L = &c->layer;
+  FT_TRY(check_tokens(T));
+  if (T == 0) return FTMOE_OK;
+  if (!x || !y) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  const Plan p = make_plan(L, T);
+  const size_t need = cache_ws_bytes(c, p);
+  if (ws_bytes < need)
+    return fail(FTMOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+  FT_TRY(check_ws(p, ws, ws_bytes));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = c->E, k = L->top_k;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
+  float* sg = at<float>(ws, p.sg);
+  const bool fused_align = p.decode && p.small_route;
+  FT_TRY(enqueue_route(L, x, T, p, ws, ids, w, sg, fused_align, s));
+
+  // the step's distinct experts, resident ones first
+  const size_t n_ids = static_cast<size_t>(T) * k;
+  c->ids_host.resize(n_ids);
+  FT_HIP(hipMemcpyAsync(c->ids_host.data(), ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
+  FT_HIP(hipStreamSynchronize(s), "routing copy");
+  std::vector<char> used(E, 0);
+  for (size_t i = 0; i < n_ids; ++i) used[c->ids_host[i]] = 1;
+  std::vector<int> order;
+  for (int e = 0; e < E; ++e)
+    if (used[e] && c->expert_slot[e] >= 0) order.push_back(e);
+  for (int e = 0; e < E; ++e)
+    if (used[e] && c->expert_slot[e] < 0) order.push_back(e);
+  const int n = static_cast<int>(order.size());
+  const int npass = std::max(1, (n + c->slots - 1) / c->slots);
+  if (npass > 1 && L->act == FTMOE_ACT_FP8_PER_TENSOR)
+    return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations need all %d experts of the step in %d slots", n,
+                c->slots);
+
+  // plan every pass (the copies of pass i are enqueued after the kernels of pass i - 1)
+  c->tables.assign(static_cast<size_t>(npass) * E, -1);
+  c->copy_e.assign(npass, {});
+  c->copy_s.assign(npass, {});
+  std::vector<int32_t> sl(c->slots), miss(c->slots);
+  for (int i = 0; i < npass; ++i) {
+    const int a = i * c->slots, m = std::min(n, a + c->slots) - a;
+    FT_TRY(cache_plan(c, order.data() + a, m, sl.data(), miss.data()));
+    for (int q = 0; q < m; ++q) {
+      c->tables[static_cast<size_t>(i) * E + order[a + q]] = sl[q];
+      if (miss[q]) {
+        c->copy_e[i].push_back(order[a + q]);
+        c->copy_s[i].push_back(sl[q]);
+      }
+    }
+  }
+  int32_t* tables = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + up256(p.total));
+  FT_HIP(hipMemcpyAsync(tables, c->tables.data(), c->tables.size() * 4, hipMemcpyHostToDevice, s), "table copy");
+  std::vector<const int32_t*> tptr(npass);
+  for (int i = 0; i < npass; ++i) tptr[i] = tables + static_cast<size_t>(i) * E;
+  c->stream = s;
+  c->passes += npass;
+  Passes passes;
+  passes.n = npass;
+  passes.tables = tptr.data();
+  passes.before = cache_copy_pass;
+  passes.ctx = c;
+  return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, passes);
+}
+
+ftmoe_status ftmoe_cache_stats(const ftmoe_cache* cache, int64_t* hits, int64_t* misses, int64_t* bytes_copied,
+                               int64_t* passes) {
+  g_last_error.clear();
+  if (!cache) return fail(FTMOE_ERR_INVALID_ARG, "cache is NULL");
+  if (hits) *hits = cache->hits;
+  if (misses) *misses = cache->misses;
+  if (bytes_copied) *bytes_copied = cache->bytes;
+  if (passes) *passes = cache->passes;
+  return FTMOE_OK;
+}
 
 }  // extern "C"

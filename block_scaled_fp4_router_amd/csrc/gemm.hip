@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     dnext = 0;
   };
 
-  // ---- compute side: the tile whose MFMA work runs ----
+  // ---- compute side: the tile whose MFMA work runs (ce: its matrix slot) ----
   int cb = 0, cnt = 0, ce = 0, cflat = 0, nvalid = 0;
   bool wact = false, rows_ok[2] = {false, false};
   auto enter = [&](int b, int nt, int e, int nv, int flat) {
@@ -636,12 +636,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     if (!tile_bnt(0, b, nt)) return;
     const int e = sid ? rows.block_expert[b] : 0;
     if (e < 0) return;
+    const int slot = expert_slot(w, e);   // slot of its matrices (< 0: served by another pass)
+    if (slot < 0) return;
     auto fsid = [&](int r) -> int { return sid ? sid[b * BM + r] : 0; };
-    set_sources(b, nt, e, fsid);
+    set_sources(b, nt, slot, fsid);
     dlive = true;
     int flat = 0;
     if constexpr (!GATEUP) flat = sid ? sid[b * BM + arow0 + lane] : b * BM + arow0 + lane;
-    enter(b, nt, e, block_rows(rows, b, e, BM), flat);
+    enter(b, nt, slot, block_rows(rows, b, e, BM), flat);
   }
   // the tile after the DMA tile: block, column tile, expert (uniform)
   int nb = 0, nnt = 0, ne = -1;
@@ -662,6 +664,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     if (PERSIST && ne >= 0) {
       ++dk;
       const int k = dk;
+      // (persistent launches have no slot table: the slot is the expert)
       set_sources(nb, nnt, ne, [&](int r) -> int { return sid ? meta_row(k, r) : 0; });
       qb = nb;
       qnt = nnt;
@@ -1125,7 +1128,8 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
   // longer and whose registers are all in use, run one tile per workgroup.)
   constexpr int kAhead = C::kAScales && FP8ACT ? C::kRing : C::kRing - 1;
   if constexpr (!GATEUP) {
-    if (ga.K / kStageK >= kAhead) {
+    // (not with an expert-slot table: tiles of experts outside the call are skipped one tile per workgroup)
+    if (ga.K / kStageK >= kAhead && !ga.w.slot_of) {
       int dev = 0, ncu = 0;
       if (hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)

@@ -37,14 +37,19 @@ hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipSt
 
 // Device view of one stacked packed matrix set [E][N][K].
 struct QW {
-  int fmt;                     // kMXFP4 | kNVFP4 | kFP8
-  int n, k;
-  const uint8_t* codes;        // fp4: [E][N][K/2]; fp8: [E][N][K]
-  const uint8_t* scales;       // mxfp4 [E][N][K/32]; nvfp4 [E][N][K/16]; fp8 unused
-  const float* tscale;         // nvfp4 / fp8: [E], or [E][N] with rowsc; mxfp4 unused
-  const uint8_t* packed;       // optional: the same matrices in the prefill tile layout, or NULL
-  int rowsc;                   // tscale holds one multiplier per matrix row
+  int fmt = 0;                 // kMXFP4 | kNVFP4 | kFP8 | kBF16
+  int n = 0, k = 0;
+  const uint8_t* codes = nullptr;   // fp4: [E][N][K/2]; fp8: [E][N][K]; bf16: [E][N][K] x 2 bytes
+  const uint8_t* scales = nullptr;  // mxfp4 [E][N][K/32]; nvfp4 [E][N][K/16]; fp8 / bf16 unused
+  const float* tscale = nullptr;    // nvfp4 / fp8: [E], or [E][N] with rowsc; mxfp4 unused
+  const uint8_t* packed = nullptr;  // optional: the same matrices in the prefill tile layout, or NULL
+  int rowsc = 0;                    // tscale holds one multiplier per matrix row
+  const int32_t* slot_of = nullptr; // optional [E]: the matrix slot holding expert e, < 0 if none (NULL: slot e)
 };
+
+// Slot of expert e's matrices (an expert-slot pool), or < 0 when this call
+// does not serve it.
+__device__ __forceinline__ int expert_slot(const QW& w, int e) { return w.slot_of ? w.slot_of[e] : e; }
 
 // fp32 multiplier of row `row` of expert e's matrix (NVFP4 / FP8).
 __device__ __forceinline__ float row_scale(const QW& w, int e, int row) {

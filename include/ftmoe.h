@@ -250,6 +250,65 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
                            void* ws, size_t ws_bytes, uint16_t* y,
                            int32_t* topk_ids_out, float* topk_w_out, void* stream);
 
+/* ---- Expert residency: an HBM slot pool over experts kept in host memory ----
+ * The FreeToken README ("About", its runtime features) lists an LRU cache of
+ * experts held in GPU memory, and the atomicmilkshake fork README ("Verified
+ * on my hardware") runs with the routed experts in host memory.  Here the
+ * routed experts of one layer live in host memory (caller-owned, preferably
+ * pinned, so that the copies are asynchronous); a device pool of `slots`
+ * expert slots (gate_up and down of one expert each, in the layer's format)
+ * holds the ones last used.  The router, the shared expert and everything
+ * else stay in device memory as in a plain layer.  The cache object is host
+ * memory the library allocates (ftmoe_cache_destroy frees it); the pool is
+ * device memory the caller provides.  A cache is used by one thread at a
+ * time.                                                                   */
+typedef struct ftmoe_cache ftmoe_cache;
+
+/* Device bytes of a pool of `slots` expert slots for `layer` (slots >= 1;
+ * 256-byte aligned regions).                                             */
+ftmoe_status ftmoe_cache_pool_size(const ftmoe_layer* layer, int32_t slots, size_t* bytes);
+
+/* Creates the residency state for `layer` (its gate_up and down are not
+ * used), whose routed experts are `host_gate_up` and `host_down` (HOST
+ * pointers, same layout and format as in a layer, no packed layout).
+ * `pool`: device memory of ftmoe_cache_pool_size bytes, 256-byte aligned.
+ * All slots start empty.  The descriptors are copied.                   */
+ftmoe_status ftmoe_cache_create(const ftmoe_layer* layer, const ftmoe_qweight* host_gate_up,
+                                const ftmoe_qweight* host_down, int32_t slots, void* pool, size_t pool_bytes,
+                                ftmoe_cache** cache);
+void ftmoe_cache_destroy(ftmoe_cache* cache);
+
+/* The residency policy (host only, no device work): for the n distinct
+ * experts one step needs (each in [0, E), distinct), gives each a slot:
+ * a resident expert keeps its slot (a hit); a missing one (a miss, out_miss
+ * = 1, to be copied) takes the least recently used slot that this step does
+ * not need, evicting its expert.  Every expert of the step then counts as
+ * used now.  FTMOE_ERR_UNSUPPORTED if n > slots (nothing changes).       */
+ftmoe_status ftmoe_cache_plan(ftmoe_cache* cache, const int32_t* experts, int32_t n, int32_t* out_slot,
+                              int32_t* out_miss);
+
+/* Workspace bytes of ftmoe_cache_forward for T tokens.                    */
+ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, size_t* bytes);
+
+/* The layer forward with the routed experts served from the pool.  Routes
+ * on `stream`, copies the routing to the host and waits for it (this entry
+ * point synchronises `stream` once), then takes the step's distinct experts
+ * in passes of at most `slots`, experts already resident first: each pass
+ * is planned as above, its missing experts are copied host -> pool on
+ * `stream`, and the pass's gate_up and down run on the pool; the combine
+ * follows the last pass.  Layers with per-tensor FP8 activations need one
+ * pass (their h scale spans every expert): FTMOE_ERR_UNSUPPORTED if the
+ * step needs more experts than there are slots.  Arguments as in
+ * ftmoe_forward; the outputs equal ftmoe_forward's on a layer whose
+ * experts are in device memory.                                           */
+ftmoe_status ftmoe_cache_forward(ftmoe_cache* cache, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                                 uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
+/* Counters since creation: slot hits and misses (experts copied), bytes
+ * copied host -> pool, and passes run.  Any output may be NULL.          */
+ftmoe_status ftmoe_cache_stats(const ftmoe_cache* cache, int64_t* hits, int64_t* misses, int64_t* bytes_copied,
+                               int64_t* passes);
+
 /* Per-tensor E4M3 activation quantiser used by FTMOE_ACT_FP8_PER_TENSOR,
  * exposed for testing: scale[0] = amax(|x|)/448 (1 if amax is 0, fp32) and
  * q = E4M3(x / scale) rounded to nearest even and saturated to +-448.

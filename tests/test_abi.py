@@ -271,3 +271,77 @@ def test_layer_rejects_misaligned_packed_weights():
     d = good_layer()
     d.gate_up.packed = FAKE + 16
     assert _ws_status(d)[0] == ft.ERR_INVALID_ARG
+
+
+# ---- expert residency: the LRU policy (host only) ----
+def _cache(slots, E=8):
+    d = good_layer()
+    d.num_experts = E
+    d.gate_up = _qw(ft.W_MXFP4, E, 256, 256)
+    d.down = _qw(ft.W_MXFP4, E, 256, 128)
+    lib = ft.load()
+    n = ctypes.c_size_t(0)
+    assert lib.ftmoe_cache_pool_size(ctypes.byref(d), slots, ctypes.byref(n)) == ft.OK
+    # 256-aligned regions; per slot: gate_up 256*256/2 + 256*256/32, down 256*128/2 + 256*128/32
+    assert n.value == slots * (256 * 256 // 2) + slots * (256 * 256 // 32) + slots * (256 * 128 // 2) + \
+        slots * (256 * 128 // 32)
+    h = ctypes.c_void_p(0)
+    gu, dn = _qw(ft.W_MXFP4, E, 256, 256), _qw(ft.W_MXFP4, E, 256, 128)
+    assert lib.ftmoe_cache_create(ctypes.byref(d), ctypes.byref(gu), ctypes.byref(dn), slots, FAKE, n.value,
+                                  ctypes.byref(h)) == ft.OK
+    return h
+
+
+class _LRU:
+    """The policy written out: hits keep their slot; misses take free slots by
+    (last use, slot index), never used first."""
+
+    def __init__(self, slots):
+        self.slot_of, self.exp_of, self.last, self.clock = {}, [None] * slots, [-1] * slots, 0
+
+    def plan(self, experts):
+        needed = {self.slot_of[e] for e in experts if e in self.slot_of}
+        free = sorted((s for s in range(len(self.exp_of)) if s not in needed), key=lambda s: (self.last[s], s))
+        self.clock += 1
+        out = []
+        for e in experts:
+            if e in self.slot_of:
+                s, miss = self.slot_of[e], 0
+            else:
+                s, miss = free.pop(0), 1
+                if self.exp_of[s] is not None:
+                    del self.slot_of[self.exp_of[s]]
+                self.exp_of[s], self.slot_of[e] = e, s
+            self.last[s] = self.clock
+            out.append((s, miss))
+        return out
+
+
+@needs_lib
+def test_cache_plan_is_lru():
+    import numpy as np
+    lib = ft.load()
+    h = _cache(slots=4, E=8)
+    model = _LRU(4)
+    rng = np.random.default_rng(4)
+    steps = [[0, 1, 2], [1, 3], [4, 5], [0, 6, 7, 1], [2], [2, 3, 4, 5]]
+    steps += [sorted(rng.choice(8, size=rng.integers(1, 5), replace=False).tolist()) for _ in range(40)]
+    hits = misses = 0
+    for st in steps:
+        e = np.array(st, np.int32)
+        sl, miss = np.zeros(len(e), np.int32), np.zeros(len(e), np.int32)
+        assert lib.ftmoe_cache_plan(h, e.ctypes.data, len(e), sl.ctypes.data, miss.ctypes.data) == ft.OK
+        ref = model.plan(st)
+        assert [(int(a), int(b)) for a, b in zip(sl, miss)] == ref
+        assert len(set(sl.tolist())) == len(sl)       # distinct slots within a step
+        hits += int((miss == 0).sum())
+        misses += int(miss.sum())
+    v = [ctypes.c_int64(0) for _ in range(4)]
+    assert lib.ftmoe_cache_stats(h, *[ctypes.byref(t) for t in v]) == ft.OK
+    assert (v[0].value, v[1].value) == (hits, misses)
+    # too many experts for the slots, a repeated expert, or one out of range: refused, state unchanged
+    for bad, status in (([0, 1, 2, 3, 4], ft.ERR_UNSUPPORTED), ([1, 1], ft.ERR_INVALID_ARG),
+                        ([9], ft.ERR_INVALID_ARG)):
+        e = np.array(bad, np.int32)
+        assert lib.ftmoe_cache_plan(h, e.ctypes.data, len(e), None, None) == status
+    lib.ftmoe_cache_destroy(h)
