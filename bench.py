@@ -78,6 +78,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="decode: oracle steps run until this much time")
+    ap.add_argument("--pool-slots", type=int, default=0,
+                    help="serve the routed experts from pinned host memory through an HBM pool of this many "
+                         "expert slots (ftmoe_cache_*); the rate then includes the host-to-device copies")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -95,10 +98,11 @@ def main() -> int:
     name, T, kind = WORKLOADS[args.workload]
     cfg = synth.CONFIGS[name]
     lay = synth.make_layer(name)
-    ring = args.ring or (4 if kind == "decode" else 1)
+    ring = args.ring or (4 if kind == "decode" and not args.pool_slots else 1)
     dev = "cuda"
     dlays = [ft.DeviceLayer.from_host(lay, dev, path=args.path) for _ in range(ring)]
-    if kind == "prefill" or args.path == "prefill":
+    pool = ft.ExpertCache.from_host(lay, args.pool_slots, dev, path=args.path) if args.pool_slots else None
+    if (kind == "prefill" or args.path == "prefill") and pool is None:
         # load-time step: the prefill GEMMs read their weight stages from the
         # packed tile layout (outside the timed region, like loading a model)
         for d in dlays:
@@ -132,15 +136,32 @@ def main() -> int:
     def step(i):
         ft.forward(dlays[i % ring], xs[i % nb], T, ws, y, ids, w, stream=stream, desc=descs[i % ring])
 
+    if pool is not None:
+        del dlays, descs
+        pws = pool.workspace(T)
+
+        def step(i):  # noqa: F811
+            pool.forward(xs[i % nb], T, pws, y, ids, w, stream=stream)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    pool_before = pool.stats() if pool is not None else None
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    pool_stats = None
+    if pool is not None:
+        st = pool.stats()
+        d = {key: st[key] - pool_before[key] for key in st}
+        pool_stats = {"slots": args.pool_slots, "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
+                      "copied_bytes_per_step": d["bytes_copied"] // args.steps,
+                      "passes_per_step": round(d["passes"] / args.steps, 3),
+                      "copy_GBs": round(d["bytes_copied"] / (t1 - t0) / 1e9, 2),
+                      "h2d_copy_GBs_measured": h2d_rate(torch, dev)}
     mean_bytes = float(np.mean([sel_bytes[i % nb] for i in range(args.steps)]))
 
     # Same steps again with per-kernel timing: events attached to each kernel's
@@ -197,6 +218,7 @@ def main() -> int:
         "config": {"workload": describe(cfg, T), "kind": kind, "tokens": T, "layer_copies_cycled": ring,
                    "token_batches_cycled": nb, "path": args.path,
                    "selected_expert_bytes_per_step": int(mean_bytes)},
+        **({"expert_pool": pool_stats} if pool_stats else {}),
         "roofline": roof,
         "kernel_avg_us": {k2: round(v, 3) for k2, v in sorted(kernel_us.items())},
     }
@@ -204,11 +226,25 @@ def main() -> int:
     traffic = measured_traffic(roof["kernel"], args.workload)
     if traffic is not None:
         roof["traffic"] = traffic
-    if not args.no_cpu_baseline:
+    if pool is not None:
+        out["config"]["workload"] += f", routed experts in pinned host memory through a {args.pool_slots}-slot HBM pool"
+    if not args.no_cpu_baseline and pool is None:
         out["cpu_baseline"] = cpu_baseline(lay, xs_host, kind, T, args.cpu_sample_tokens, sel_bytes,
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def h2d_rate(torch, dev, mib=256):
+    """GB/s of one plain pinned-host -> device copy of `mib` MiB (the link's rate, for context)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    return round((mib << 20) / (time.perf_counter() - t0) / 1e9, 2)
 
 
 PREFILL_SAMPLE = {"c2": 128, "c3": 64, "c4": 64, "c2-w4a8": 128, "c2-bf16": 128}

@@ -344,24 +344,35 @@ class ExpertCache:
         self.handle = h
 
     @classmethod
-    def from_host(cls, lay, slots: int, device="cuda", path="auto") -> "ExpertCache":
+    def from_host(cls, lay, slots: int, device="cuda", path="auto", pinned=True) -> "ExpertCache":
         """From a generator layer: router and shared expert on the device, the
-        routed experts in pinned host memory."""
+        routed experts only in host memory (pinned unless ``pinned`` is
+        False: the pool is then filled by staged DMA copies instead of the
+        fill kernel)."""
         import numpy as np
         import torch
 
-        def pinned(a):
+        def host(a):
             if a is None:
                 return None
             if a.dtype == np.uint16:
                 a = a.view(np.int16)
-            return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return t.pin_memory() if pinned else t.clone()
 
         def hq(q):
-            return DeviceQWeight(q.fmt, q.num_experts, q.n, q.k, pinned(q.codes), pinned(q.block_scales),
-                                 pinned(q.tensor_scales))
+            return DeviceQWeight(q.fmt, q.num_experts, q.n, q.k, host(q.codes), host(q.block_scales),
+                                 host(q.tensor_scales))
 
-        return cls(DeviceLayer.from_host(lay, device, path=path), hq(lay.gate_up), hq(lay.down), slots, device)
+        gu, dn = hq(lay.gate_up), hq(lay.down)
+
+        class _NoRouted:   # the layer without its routed experts, which stay on the host
+            def __getattr__(self, name):
+                return None if name in ("gate_up", "down") else getattr(lay, name)
+
+        dl = DeviceLayer.from_host(_NoRouted(), device, path=path)
+        dl.gate_up, dl.down = gu, dn   # descriptors only (the cache does not read a layer's routed experts)
+        return cls(dl, gu, dn, slots, device)
 
     def plan(self, experts):
         """The residency policy alone (host): (slot per expert, miss flags)."""

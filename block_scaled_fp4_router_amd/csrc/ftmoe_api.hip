@@ -359,13 +359,16 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
 
 // Expert passes over an expert-slot pool: pass i runs the routed gate_up and
 // down of the experts that table i maps to a slot (the others' blocks exit at
-// once); before(i) is called on the host first (it enqueues that pass's
-// copies into the pool).  The shared expert runs in pass 0; align, the
-// activation preparation and the combine run once.
+// once).  Host hooks: before(i) is called before pass i is enqueued (it makes
+// the stream wait for that pass's copies into the pool), after(i) right
+// after (it marks the pass done and starts the next pass's copies).  The
+// shared expert runs in pass 0; align, the activation preparation and the
+// combine run once.
 struct Passes {
   int n = 1;
   const int32_t* const* tables = nullptr;   // n device tables [E], or NULL: one pass, no table
   ftmoe_status (*before)(void* ctx, int i) = nullptr;
+  ftmoe_status (*after)(void* ctx, int i) = nullptr;
   void* ctx = nullptr;
 };
 
@@ -467,6 +470,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
       FT_HIP(timed("decode_gateup", s, [&] { return launch_decode_gateup(a, s); }), "decode gate_up launch");
       if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
       FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(a, s); }), "decode down launch");
+      if (passes.after) FT_TRY(passes.after(passes.ctx, i));
     }
     a.nb_shared = p.nb_shared;
     FT_HIP(timed("combine", s, [&] { return launch_decode_combine(a, s); }), "combine launch");
@@ -531,6 +535,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
       ha.q = hq;
     }
     FT_HIP(timed("gemm_down", s, [&] { return launch_gemm_down(dnp, rr, ha, H, I, o, s); }), "down GEMM launch");
+    if (passes.after) FT_TRY(passes.after(passes.ctx, i));
   }
   if (shared) {
     GemmAct xs = xa;
@@ -617,11 +622,29 @@ struct ftmoe_cache {
   std::vector<int> slot_expert, expert_slot;   // -1: empty / not resident
   std::vector<int64_t> last_use;               // per slot; -1: never
   int64_t clock = 0, hits = 0, misses = 0, bytes = 0, passes = 0;
+  // copies run on their own stream, ordered against the passes by events
+  hipStream_t copy_stream = nullptr;
+  std::vector<hipEvent_t> ev_copied, ev_done;  // per pass: its copies landed / its kernels ran
   // per-call state
   std::vector<int32_t> ids_host;
   std::vector<int32_t> tables;                 // [passes][E] slot of each expert, -1 if not in the pass
   std::vector<std::vector<int>> copy_e, copy_s;   // per pass: experts to copy and their slots
-  hipStream_t stream = nullptr;
+  std::vector<int> copy_after;                 // per pass: the last earlier pass that reads a slot it overwrites, or -1
+  hipStream_t stream = nullptr;                // the stream of the last call
+  bool called = false;
+  // device-visible addresses of the host arrays (pinned, mapped memory): the
+  // pool is then filled by one kernel per pass instead of one DMA per array
+  int zero_copy = -1;                          // -1: not probed yet; 0: DMA copies; 1: fill kernel
+  const uint8_t* dev_src[kFillArrays] = {};
+
+  ~ftmoe_cache() {
+    if (copy_stream) {
+      (void)hipStreamSynchronize(copy_stream);
+      (void)hipStreamDestroy(copy_stream);
+    }
+    for (hipEvent_t e : ev_copied) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ev_done) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -665,14 +688,42 @@ ftmoe_status cache_plan(ftmoe_cache* c, const int32_t* experts, int n, int32_t* 
   return FTMOE_OK;
 }
 
-// Copies of pass i: each missing expert's gate_up and down arrays, host -> its slot.
-ftmoe_status cache_copy_pass(void* ctx, int i) {
-  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+// Copies of pass i on the copy stream: each missing expert's gate_up and down
+// arrays, host -> its slot, after the last earlier pass that reads one of the
+// slots they overwrite; then the pass's "copied" event.
+ftmoe_status cache_copy_pass(ftmoe_cache* c, int i) {
+  if (c->copy_e[i].empty()) return FTMOE_OK;
+  const hipStream_t cs = c->copy_stream;
+  if (c->copy_after[i] >= 0) FT_HIP(hipStreamWaitEvent(cs, c->ev_done[c->copy_after[i]], 0), "copy stream wait");
   const PoolLayout& pl = c->pl;
+  if (c->zero_copy == 1) {
+    FillArgs fa{};
+    const size_t dst_off[kFillArrays] = {pl.gu_codes, pl.gu_scales, pl.gu_ts, pl.dn_codes, pl.dn_scales, pl.dn_ts};
+    const size_t per[kFillArrays] = {pl.gu.codes, pl.gu.scales, pl.gu.ts, pl.dn.codes, pl.dn.scales, pl.dn.ts};
+    size_t expert_bytes = 0;
+    for (int j = 0; j < kFillArrays; ++j) {
+      fa.src[j] = c->dev_src[j];
+      fa.dst[j] = c->pool + dst_off[j];
+      fa.bytes[j] = c->dev_src[j] ? static_cast<uint32_t>(per[j]) : 0u;
+      expert_bytes += fa.bytes[j];
+    }
+    const int n = static_cast<int>(c->copy_e[i].size());
+    for (int a = 0; a < n; a += kFillMax) {
+      fa.n = std::min(kFillMax, n - a);
+      for (int m = 0; m < fa.n; ++m) {
+        fa.e[m] = c->copy_e[i][a + m];
+        fa.s[m] = c->copy_s[i][a + m];
+      }
+      FT_HIP(launch_expert_fill(fa, cs), "pool fill launch");
+    }
+    c->bytes += static_cast<int64_t>(expert_bytes) * n;
+    FT_HIP(hipEventRecord(c->ev_copied[i], cs), "copy event");
+    return FTMOE_OK;
+  }
   auto copy = [&](size_t dst_off, const void* src, size_t bytes) -> hipError_t {
     if (bytes == 0) return hipSuccess;
     c->bytes += static_cast<int64_t>(bytes);
-    return hipMemcpyAsync(c->pool + dst_off, src, bytes, hipMemcpyHostToDevice, c->stream);
+    return hipMemcpyAsync(c->pool + dst_off, src, bytes, hipMemcpyHostToDevice, cs);
   };
   for (size_t m = 0; m < c->copy_e[i].size(); ++m) {
     const size_t e = static_cast<size_t>(c->copy_e[i][m]), sl = static_cast<size_t>(c->copy_s[i][m]);
@@ -689,11 +740,59 @@ ftmoe_status cache_copy_pass(void* ctx, int i) {
     if (pl.dn.scales) FT_HIP(copy(pl.dn_scales + sl * pl.dn.scales, ds + e * pl.dn.scales, pl.dn.scales), "expert copy");
     if (pl.dn.ts) FT_HIP(copy(pl.dn_ts + sl * pl.dn.ts, dt + e * pl.dn.ts, pl.dn.ts), "expert copy");
   }
+  FT_HIP(hipEventRecord(c->ev_copied[i], cs), "copy event");
   return FTMOE_OK;
 }
 
-// The most passes a step can need, and the workspace of ftmoe_cache_forward.
-int cache_max_passes(const ftmoe_cache* c) { return (c->E + c->slots - 1) / c->slots; }
+// Whether every host array has a device-visible address (pinned, mapped
+// memory) and fits the fill kernel's 32-bit per-expert sizes; else the pool
+// is filled by DMA copies.
+ftmoe_status cache_probe_zero_copy(ftmoe_cache* c) {
+  const void* host[kFillArrays] = {c->host_gu.codes, c->host_gu.block_scales, c->host_gu.tensor_scales,
+                                   c->host_dn.codes, c->host_dn.block_scales, c->host_dn.tensor_scales};
+  const size_t per[kFillArrays] = {c->pl.gu.codes, c->pl.gu.scales, c->pl.gu.ts,
+                                   c->pl.dn.codes, c->pl.dn.scales, c->pl.dn.ts};
+  bool ok = true;
+  for (int j = 0; j < kFillArrays; ++j) {
+    c->dev_src[j] = nullptr;
+    if (!host[j] || per[j] == 0) continue;
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(host[j]), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();   // not pinned and mapped: clear the error, use DMA copies
+      ok = false;
+      break;
+    }
+    if (per[j] % 4 || per[j] > 0xFFFFFFFFu) ok = false;
+    c->dev_src[j] = static_cast<const uint8_t*>(d);
+  }
+  c->zero_copy = ok ? 1 : 0;
+  return FTMOE_OK;
+}
+
+// Pass hooks: pass 0 starts its own copies; pass i waits for its copies; after
+// pass i is enqueued its "done" event is recorded and pass i + 1's copies
+// start, so they overlap pass i's kernels unless they evict what it reads.
+ftmoe_status cache_before_pass(void* ctx, int i) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  if (i == 0) FT_TRY(cache_copy_pass(c, 0));
+  if (!c->copy_e[i].empty()) FT_HIP(hipStreamWaitEvent(c->stream, c->ev_copied[i], 0), "pass wait");
+  return FTMOE_OK;
+}
+
+ftmoe_status cache_after_pass(void* ctx, int i) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  FT_HIP(hipEventRecord(c->ev_done[i], c->stream), "pass event");
+  if (i + 1 < static_cast<int>(c->copy_e.size())) FT_TRY(cache_copy_pass(c, i + 1));
+  return FTMOE_OK;
+}
+
+// Misses per pass when a step's experts do not all fit: half the pool, so
+// one pass's copies can land while the previous pass runs.
+int cache_group(const ftmoe_cache* c) { return std::max(1, c->slots / 2); }
+
+// The most passes a step can need (the resident experts, then the misses in
+// groups), and the workspace of ftmoe_cache_forward.
+int cache_max_passes(const ftmoe_cache* c) { return 1 + (c->E + cache_group(c) - 1) / cache_group(c); }
 
 size_t cache_ws_bytes(const ftmoe_cache* c, const Plan& p) {
   return up256(p.total) + up256(static_cast<size_t>(cache_max_passes(c)) * c->E * 4);
@@ -983,6 +1082,8 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
     return fail(FTMOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
   FT_TRY(check_ws(p, ws, ws_bytes));
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the previous call's passes, on another stream, may still read the pool
+  if (c->called && c->stream != s) FT_HIP(hipStreamSynchronize(c->stream), "previous stream");
   const int E = c->E, k = L->top_k;
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
   float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
@@ -990,50 +1091,87 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
   const bool fused_align = p.decode && p.small_route;
   FT_TRY(enqueue_route(L, x, T, p, ws, ids, w, sg, fused_align, s));
 
-  // the step's distinct experts, resident ones first
+  // the step's distinct experts: resident ones (hits), then the others
   const size_t n_ids = static_cast<size_t>(T) * k;
   c->ids_host.resize(n_ids);
   FT_HIP(hipMemcpyAsync(c->ids_host.data(), ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
   FT_HIP(hipStreamSynchronize(s), "routing copy");
   std::vector<char> used(E, 0);
   for (size_t i = 0; i < n_ids; ++i) used[c->ids_host[i]] = 1;
-  std::vector<int> order;
+  std::vector<int> hit, missing;
   for (int e = 0; e < E; ++e)
-    if (used[e] && c->expert_slot[e] >= 0) order.push_back(e);
-  for (int e = 0; e < E; ++e)
-    if (used[e] && c->expert_slot[e] < 0) order.push_back(e);
-  const int n = static_cast<int>(order.size());
-  const int npass = std::max(1, (n + c->slots - 1) / c->slots);
-  if (npass > 1 && L->act == FTMOE_ACT_FP8_PER_TENSOR)
-    return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations need all %d experts of the step in %d slots", n,
-                c->slots);
+    if (used[e]) (c->expert_slot[e] >= 0 ? hit : missing).push_back(e);
+  const int n = static_cast<int>(hit.size() + missing.size());
+  // Passes: with per-tensor FP8 activations all experts in one (their h
+  // scale spans every expert); otherwise the hits first, so that they run
+  // while the misses are copied, then the misses: in one pass when they fit
+  // beside the hits, else in groups of half the pool.
+  std::vector<std::vector<int>> groups;
+  if (L->act == FTMOE_ACT_FP8_PER_TENSOR) {
+    if (n > c->slots)
+      return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations need all %d experts of the step in %d slots",
+                  n, c->slots);
+    groups.emplace_back(hit);
+    groups[0].insert(groups[0].end(), missing.begin(), missing.end());
+  } else {
+    if (!hit.empty()) groups.push_back(hit);
+    const int m = static_cast<int>(missing.size());
+    const int g = n <= c->slots ? std::max(1, m) : cache_group(c);
+    for (int a = 0; a < m; a += g)
+      groups.emplace_back(missing.begin() + a, missing.begin() + std::min(m, a + g));
+    if (groups.empty()) groups.emplace_back();
+  }
+  const int npass = static_cast<int>(groups.size());
 
-  // plan every pass (the copies of pass i are enqueued after the kernels of pass i - 1)
+  // the copy stream, the fill mode and per-pass events (host resources of the cache, made once)
+  if (c->zero_copy < 0) FT_TRY(cache_probe_zero_copy(c));
+  if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+    c->copy_stream = nullptr;
+    return fail(FTMOE_ERR_HIP, "copy stream creation failed");
+  }
+  while (static_cast<int>(c->ev_done.size()) < npass) {
+    hipEvent_t a = nullptr, b = nullptr;
+    FT_HIP(hipEventCreateWithFlags(&a, hipEventDisableTiming), "event creation");
+    if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return fail(FTMOE_ERR_HIP, "event creation failed");
+    }
+    c->ev_copied.push_back(a);
+    c->ev_done.push_back(b);
+  }
+
+  // plan every pass; a pass's copies wait for the last earlier pass reading a slot they overwrite
   c->tables.assign(static_cast<size_t>(npass) * E, -1);
   c->copy_e.assign(npass, {});
   c->copy_s.assign(npass, {});
+  c->copy_after.assign(npass, -1);
+  std::vector<int> reader(c->slots, -1);   // last pass of this step that reads each slot
   std::vector<int32_t> sl(c->slots), miss(c->slots);
   for (int i = 0; i < npass; ++i) {
-    const int a = i * c->slots, m = std::min(n, a + c->slots) - a;
-    FT_TRY(cache_plan(c, order.data() + a, m, sl.data(), miss.data()));
+    const int m = static_cast<int>(groups[i].size());
+    FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data()));
     for (int q = 0; q < m; ++q) {
-      c->tables[static_cast<size_t>(i) * E + order[a + q]] = sl[q];
+      c->tables[static_cast<size_t>(i) * E + groups[i][q]] = sl[q];
       if (miss[q]) {
-        c->copy_e[i].push_back(order[a + q]);
+        c->copy_e[i].push_back(groups[i][q]);
         c->copy_s[i].push_back(sl[q]);
+        c->copy_after[i] = std::max(c->copy_after[i], reader[sl[q]]);
       }
     }
+    for (int q = 0; q < m; ++q) reader[sl[q]] = i;
   }
   int32_t* tables = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + up256(p.total));
   FT_HIP(hipMemcpyAsync(tables, c->tables.data(), c->tables.size() * 4, hipMemcpyHostToDevice, s), "table copy");
   std::vector<const int32_t*> tptr(npass);
   for (int i = 0; i < npass; ++i) tptr[i] = tables + static_cast<size_t>(i) * E;
   c->stream = s;
+  c->called = true;
   c->passes += npass;
   Passes passes;
   passes.n = npass;
   passes.tables = tptr.data();
-  passes.before = cache_copy_pass;
+  passes.before = cache_before_pass;
+  passes.after = cache_after_pass;
   passes.ctx = c;
   return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, passes);
 }

@@ -194,6 +194,23 @@ hipError_t launch_pack_weights(const QW& w, int E, bool gate_up, uint8_t* out, h
 // a8 the MXFP8 form xs [T][H] and the same scales.
 hipError_t launch_x_split_gemm(const uint16_t* x, int T, int H, uint8_t* xs, uint8_t* xsc, bool a8, hipStream_t s);
 
+// ---- expert-slot pool fills ----
+// Copies the arrays of n experts from host memory the device can read
+// (pinned, mapped) into their pool slots: for each array j, expert e[m]'s
+// bytes [e*bytes[j], (e+1)*bytes[j]) of src[j] go to dst[j] + s[m]*bytes[j].
+// One launch reads the PCIe link at its full rate where one DMA copy per
+// array would pay a fixed cost for each.
+constexpr int kFillArrays = 6;
+constexpr int kFillMax = 64;    // experts per launch
+struct FillArgs {
+  const uint8_t* src[kFillArrays];
+  uint8_t* dst[kFillArrays];
+  uint32_t bytes[kFillArrays];  // per expert; 0 = array absent; multiples of 4
+  int32_t n;
+  int32_t e[kFillMax], s[kFillMax];
+};
+hipError_t launch_expert_fill(const FillArgs& a, hipStream_t s);
+
 // ---- combine ----
 // y[t] = sum_j w[t,j] o[t*k+j] (+ sg[t] * sh[t]) -> bf16.
 hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H, const float* sg,

@@ -151,4 +151,57 @@ hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H
                 y);
 }
 
+// ------------------------------------------------- expert-slot pool fill ---
+// Work units of kFillUnit bytes of one array of one expert; 256 threads move
+// a unit as 16-byte words (4 in flight per thread) when the array's
+// per-expert size and both bases allow it, else as 4-byte words.
+constexpr uint32_t kFillUnit = 64u << 10;
+
+__global__ __launch_bounds__(256) void expert_fill_kernel(FillArgs a) {
+  uint32_t units[kFillArrays], per_expert = 0;
+#pragma unroll
+  for (int j = 0; j < kFillArrays; ++j) {
+    units[j] = (a.bytes[j] + kFillUnit - 1) / kFillUnit;
+    per_expert += units[j];
+  }
+  const uint32_t total = per_expert * static_cast<uint32_t>(a.n);
+  for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int m = static_cast<int>(u / per_expert);
+    uint32_t r = u % per_expert;
+    int j = 0;
+    while (r >= units[j]) r -= units[j++];
+    const size_t b = a.bytes[j];
+    const uint8_t* src = a.src[j] + static_cast<size_t>(a.e[m]) * b;
+    uint8_t* dst = a.dst[j] + static_cast<size_t>(a.s[m]) * b;
+    const uint32_t lo = r * kFillUnit, hi = min(static_cast<uint32_t>(b), lo + kFillUnit);
+    const bool vec = (b % 16 == 0) && ((reinterpret_cast<uintptr_t>(a.src[j]) | reinterpret_cast<uintptr_t>(a.dst[j])) % 16 == 0);
+    if (vec) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(src + lo);
+      uint4* d4 = reinterpret_cast<uint4*>(dst + lo);
+      const uint32_t n4 = (hi - lo) / 16;
+      for (uint32_t i = threadIdx.x; i < n4; i += 4 * 256) {
+        uint4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (i + q * 256 < n4) v[q] = s4[i + q * 256];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (i + q * 256 < n4) d4[i + q * 256] = v[q];
+      }
+    } else {
+      const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src + lo);
+      uint32_t* d1 = reinterpret_cast<uint32_t*>(dst + lo);
+      for (uint32_t i = threadIdx.x; i < (hi - lo) / 4; i += 256) d1[i] = s1[i];
+    }
+  }
+}
+
+hipError_t launch_expert_fill(const FillArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  // 64 workgroups keep enough reads in flight to fill the link and leave the
+  // other compute units to the kernels of the pass that overlaps the fill.
+  expert_fill_kernel<<<64, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace ftmoe

@@ -272,7 +272,12 @@ ftmoe_status ftmoe_cache_pool_size(const ftmoe_layer* layer, int32_t slots, size
  * used), whose routed experts are `host_gate_up` and `host_down` (HOST
  * pointers, same layout and format as in a layer, no packed layout).
  * `pool`: device memory of ftmoe_cache_pool_size bytes, 256-byte aligned.
- * All slots start empty.  The descriptors are copied.                   */
+ * All slots start empty.  The descriptors are copied.  Host only: the copy
+ * stream and events are made on the first ftmoe_cache_forward, which also
+ * asks HIP for device addresses of the host arrays: if every one is pinned
+ * and mapped (hipHostMalloc), one kernel per pass reads the missing experts
+ * straight from them (each array must then lie in one allocation),
+ * otherwise each array of each missing expert is one DMA copy.           */
 ftmoe_status ftmoe_cache_create(const ftmoe_layer* layer, const ftmoe_qweight* host_gate_up,
                                 const ftmoe_qweight* host_down, int32_t slots, void* pool, size_t pool_bytes,
                                 ftmoe_cache** cache);
@@ -292,15 +297,19 @@ ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, siz
 
 /* The layer forward with the routed experts served from the pool.  Routes
  * on `stream`, copies the routing to the host and waits for it (this entry
- * point synchronises `stream` once), then takes the step's distinct experts
- * in passes of at most `slots`, experts already resident first: each pass
- * is planned as above, its missing experts are copied host -> pool on
- * `stream`, and the pass's gate_up and down run on the pool; the combine
- * follows the last pass.  Layers with per-tensor FP8 activations need one
- * pass (their h scale spans every expert): FTMOE_ERR_UNSUPPORTED if the
- * step needs more experts than there are slots.  Arguments as in
- * ftmoe_forward; the outputs equal ftmoe_forward's on a layer whose
- * experts are in device memory.                                           */
+ * point synchronises `stream` once, and the previous call's stream if it
+ * was another), then runs the step's distinct experts in passes, each
+ * planned as above: first the resident ones (hits), then the missing ones,
+ * in one pass when they fit beside the hits, else in groups of half the
+ * pool.  A pass's copies (host -> pool) run on a copy stream the cache owns
+ * and overlap the previous pass's kernels, except where they evict a slot
+ * that an unfinished pass reads (then they wait for it); each pass's
+ * gate_up and down wait for their copies; the combine follows the last
+ * pass.  Layers with per-tensor FP8 activations run in one pass (their h
+ * scale spans every expert): FTMOE_ERR_UNSUPPORTED if the step needs more
+ * experts than there are slots.  Arguments as in ftmoe_forward; the
+ * outputs equal ftmoe_forward's on a layer whose experts are in device
+ * memory.  Call with the device current that was current at creation.   */
 ftmoe_status ftmoe_cache_forward(ftmoe_cache* cache, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
                                  uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
 

@@ -33,10 +33,66 @@ def cache_forward(cache, x_bits):
     return bf16_dev_to_f64(y), ids.cpu().numpy(), w.cpu().numpy()
 
 
+class _PoolModel:
+    """The residency policy the library documents, replayed on the host: per
+    step, the resident experts form the first pass and the missing ones
+    follow (one pass if they fit beside them, else groups of half the
+    pool; one pass of everything for per-tensor FP8 activations); each pass
+    gives a missing expert the least recently used slot the pass does not
+    need."""
+
+    def __init__(self, E, slots, fp8=False):
+        self.slots, self.fp8 = slots, fp8
+        self.slot_of = {}
+        self.owner = [-1] * slots
+        self.last = [-1] * slots
+        self.clock = 0
+        self.hits = self.misses = self.passes = 0
+
+    def _plan(self, group):
+        needed = {self.slot_of[e] for e in group if e in self.slot_of}
+        cand = sorted((s for s in range(self.slots) if s not in needed), key=lambda s: self.last[s])
+        self.clock += 1
+        nxt = 0
+        for e in group:
+            if e in self.slot_of:
+                self.hits += 1
+                s = self.slot_of[e]
+            else:
+                self.misses += 1
+                s = cand[nxt]
+                nxt += 1
+                if self.owner[s] >= 0:
+                    del self.slot_of[self.owner[s]]
+                self.owner[s] = e
+                self.slot_of[e] = s
+            self.last[s] = self.clock
+
+    def step(self, experts):
+        experts = sorted(int(e) for e in experts)
+        hit = [e for e in experts if e in self.slot_of]
+        miss = [e for e in experts if e not in self.slot_of]
+        if self.fp8:
+            groups = [hit + miss]
+        else:
+            groups = [hit] if hit else []
+            g = max(1, len(miss)) if len(experts) <= self.slots else max(1, self.slots // 2)
+            groups += [miss[a:a + g] for a in range(0, len(miss), g)]
+            groups = groups or [[]]
+        for grp in groups:
+            self._plan(grp)
+        self.passes += len(groups)
+
+    def stats(self):
+        return {"hits": self.hits, "misses": self.misses, "passes": self.passes}
+
+
 CASES = [
-    # name, layer, T, path, slots
+    # name, layer, T, path, slots[, host memory pinned]
     ("c1", None, 8, "decode", 64),
+    ("c1", None, 8, "decode", 12, False),
     ("c1", None, 8, "decode", 12),
+    ("c1", None, 8, "decode", 1),
     ("c1-w4a8", None, 8, "decode", 20),
     ("c1", None, 40, "prefill", 24),
     ("nvs", (256, 16, 4, 128, "nvfp4", "bf16", 128), 9, "decode", 5),
@@ -47,10 +103,10 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,shape,T,path,slots", CASES)
+@pytest.mark.parametrize("name,shape,T,path,slots,pinned", [c if len(c) == 6 else c + (True,) for c in CASES])
 @pytest.mark.timeout(600)
-def test_cache_forward_equals_device_layer(name, shape, T, path, slots):
-    say(f"expert cache {name} T={T} path={path} slots={slots}")
+def test_cache_forward_equals_device_layer(name, shape, T, path, slots, pinned):
+    say(f"expert cache {name} T={T} path={path} slots={slots} pinned={pinned}")
     if shape is None:
         lay, dlay = layer_pair(name)
     else:
@@ -58,29 +114,29 @@ def test_cache_forward_equals_device_layer(name, shape, T, path, slots):
         dlay = ft.DeviceLayer.from_host(lay, DEV)
     x = synth.make_tokens(lay, T, stream=T)
     ref_y, ref_ids, ref_w = run_forward(dlay, x, path)
-    cache = ft.ExpertCache.from_host(lay, slots, DEV, path=path)
+    cache = ft.ExpertCache.from_host(lay, slots, DEV, path=path, pinned=pinned)
     y, ids, w = cache_forward(cache, x)
     assert np.array_equal(ids, ref_ids) and np.array_equal(w, ref_w)
     assert np.array_equal(y, ref_y)
-    n = len(np.unique(ids))
-    st = cache.stats()
-    passes = -(-n // slots)
-    say(f"  distinct experts {n}, stats {st}")
-    assert st["passes"] == passes
-    assert st["hits"] + st["misses"] == n
-    assert st["misses"] == n   # a fresh pool
     per_expert = sum(t.numel() * t.element_size() for t in (cache.host_gate_up.codes, cache.host_gate_up.block_scales,
                                                            cache.host_gate_up.tensor_scales, cache.host_down.codes,
                                                            cache.host_down.block_scales,
                                                            cache.host_down.tensor_scales) if t is not None) // dlay.num_experts
-    assert st["bytes_copied"] == n * per_expert
-    # the same step again: everything that stayed resident is a hit
+    model = _PoolModel(dlay.num_experts, slots, fp8=lay.cfg.act == "fp8")
+    step = np.unique(ids)
+    model.step(step)
+    st = cache.stats()
+    say(f"  distinct experts {len(step)}, stats {st}, model {model.stats()}")
+    assert st == dict(model.stats(), bytes_copied=model.misses * per_expert)
+    # the same step again: the experts that stayed resident are hits and run first
     y2, ids2, _ = cache_forward(cache, x)
     assert np.array_equal(y2, ref_y)
+    model.step(step)
     st2 = cache.stats()
-    if passes == 1:
-        assert st2["misses"] == st["misses"] and st2["hits"] == st["hits"] + n
-        assert st2["bytes_copied"] == st["bytes_copied"]
+    say(f"  second step: stats {st2}")
+    assert st2 == dict(model.stats(), bytes_copied=model.misses * per_expert)
+    if len(step) <= slots:
+        assert st2["misses"] == st["misses"] and st2["passes"] == st["passes"] + 1
     cache.close()
 
 
