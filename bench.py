@@ -81,6 +81,9 @@ def main() -> int:
     ap.add_argument("--pool-slots", type=int, default=0,
                     help="serve the routed experts from pinned host memory through an HBM pool of this many "
                          "expert slots (ftmoe_cache_*); the rate then includes the host-to-device copies")
+    ap.add_argument("--host-threads", type=int, default=0,
+                    help="with --pool-slots: CPU-GPU co-execution, missing experts split between this many host "
+                         "threads and the pool by the calibrated cost model (ftmoe_cache_set_host_compute)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -102,6 +105,8 @@ def main() -> int:
     dev = "cuda"
     dlays = [ft.DeviceLayer.from_host(lay, dev, path=args.path) for _ in range(ring)]
     pool = ft.ExpertCache.from_host(lay, args.pool_slots, dev, path=args.path) if args.pool_slots else None
+    if pool is not None and args.host_threads:
+        pool.set_host_compute(args.host_threads)
     if (kind == "prefill" or args.path == "prefill") and pool is None:
         # load-time step: the prefill GEMMs read their weight stages from the
         # packed tile layout (outside the timed region, like loading a model)
@@ -147,6 +152,7 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
     pool_before = pool.stats() if pool is not None else None
+    host_before = pool.host_stats() if pool is not None else None
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -162,6 +168,14 @@ def main() -> int:
                       "passes_per_step": round(d["passes"] / args.steps, 3),
                       "copy_GBs": round(d["bytes_copied"] / (t1 - t0) / 1e9, 2),
                       "h2d_copy_GBs_measured": h2d_rate(torch, dev)}
+        if args.host_threads:
+            hs = pool.host_stats()
+            pool_stats["host_compute"] = {
+                "threads": args.host_threads, "experts_per_step": round((hs["experts"] - host_before["experts"]) /
+                                                                        args.steps, 3),
+                "rows_per_step": round((hs["rows"] - host_before["rows"]) / args.steps, 3),
+                "host_ms_per_step": round((hs["seconds"] - host_before["seconds"]) * 1e3 / args.steps, 4),
+                "cost_model": {"expert_s": hs["expert_s"], "row_s": hs["row_s"]}}
     mean_bytes = float(np.mean([sel_bytes[i % nb] for i in range(args.steps)]))
 
     # Same steps again with per-kernel timing: events attached to each kernel's

@@ -40,7 +40,7 @@ EXPORTS = (
     "ftmoe_timing_enable", "ftmoe_timing_collect", "ftmoe_status_string", "ftmoe_last_error", "ftmoe_version",
     "ftmoe_packed_size", "ftmoe_pack_qweight", "ftmoe_cache_pool_size", "ftmoe_cache_create",
     "ftmoe_cache_destroy", "ftmoe_cache_plan", "ftmoe_cache_workspace_size", "ftmoe_cache_forward",
-    "ftmoe_cache_stats",
+    "ftmoe_cache_stats", "ftmoe_cache_set_host_compute", "ftmoe_cache_host_stats", "ftmoe_host_expert_rows",
 )
 ROLE_GATE_UP, ROLE_DOWN = 0, 1
 
@@ -115,10 +115,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_cache_workspace_size.argtypes = [vp, i32, P(sz)]
     lib.ftmoe_cache_forward.argtypes = [vp, vp, i32, vp, sz, vp, vp, vp, vp]
     lib.ftmoe_cache_stats.argtypes = [vp, P(i64), P(i64), P(i64), P(i64)]
+    dbl = ctypes.c_double
+    lib.ftmoe_cache_set_host_compute.argtypes = [vp, i32, dbl, dbl, dbl]
+    lib.ftmoe_cache_host_stats.argtypes = [vp, P(i64), P(i64), P(dbl), P(dbl), P(dbl)]
+    lib.ftmoe_host_expert_rows.argtypes = [P(LayerDesc), vp, vp, vp, i32, vp, i32]
     for name in ("ftmoe_workspace_size", "ftmoe_route", "ftmoe_align", "ftmoe_experts_forward",
                  "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight",
                  "ftmoe_cache_pool_size", "ftmoe_cache_create", "ftmoe_cache_plan", "ftmoe_cache_workspace_size",
-                 "ftmoe_cache_forward", "ftmoe_cache_stats"):
+                 "ftmoe_cache_forward", "ftmoe_cache_stats", "ftmoe_cache_set_host_compute",
+                 "ftmoe_cache_host_stats", "ftmoe_host_expert_rows"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -398,6 +403,18 @@ class ExpertCache:
         _check(load().ftmoe_cache_stats(self.handle, *[ctypes.byref(t) for t in v]))
         return dict(zip(("hits", "misses", "bytes_copied", "passes"), (t.value for t in v)))
 
+    def set_host_compute(self, threads: int, expert_s: float = 0.0, row_s: float = -1.0,
+                         link_bytes_per_s: float = 0.0) -> None:
+        """CPU-GPU co-execution (ftmoe_cache_set_host_compute); expert_s <= 0
+        or row_s < 0 calibrates the host cost model."""
+        _check(load().ftmoe_cache_set_host_compute(self.handle, threads, expert_s, row_s, link_bytes_per_s))
+
+    def host_stats(self) -> dict:
+        i = [ctypes.c_int64(0) for _ in range(2)]
+        d = [ctypes.c_double(0) for _ in range(3)]
+        _check(load().ftmoe_cache_host_stats(self.handle, *[ctypes.byref(t) for t in i + d]))
+        return dict(zip(("experts", "rows", "seconds", "expert_s", "row_s"), [t.value for t in i + d]))
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             load().ftmoe_cache_destroy(self.handle)
@@ -408,6 +425,45 @@ class ExpertCache:
             self.close()
         except Exception:
             pass
+
+
+def host_expert_rows(lay, x_bits, tok, ex, threads: int = 4):
+    """The host half of co-execution alone (ftmoe_host_expert_rows), on a
+    generator layer in host memory: o [n][H] fp32 for token tok[r] through
+    routed expert ex[r]."""
+    import numpy as np
+    cfg = lay.cfg
+    keep = []
+
+    def arr(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a
+
+    def qd(q):
+        d = QWeightDesc()
+        d.fmt, d.num_experts, d.n, d.k = FMT_CODES[q.fmt], q.num_experts, q.n, q.k
+        d.codes = arr(q.codes).ctypes.data
+        bs, ts = arr(q.block_scales), arr(q.tensor_scales)
+        d.block_scales = bs.ctypes.data if bs is not None else None
+        d.tensor_scales = ts.ctypes.data if ts is not None else None
+        d.row_scales = 1 if ts is not None and ts.ndim == 2 else 0
+        return d
+
+    d = LayerDesc()
+    d.hidden, d.inter, d.num_experts, d.top_k = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
+    d.act, d.path = ACT_CODES[cfg.act], PATH_CODES["auto"]
+    d.router_w = arr(lay.router_w).ctypes.data
+    d.gate_up, d.down = qd(lay.gate_up), qd(lay.down)
+    x = arr(np.asarray(x_bits, dtype=np.uint16))
+    tok = arr(np.asarray(tok, dtype=np.int32))
+    ex = arr(np.asarray(ex, dtype=np.int32))
+    o = np.zeros((len(tok), cfg.hidden), np.float32)
+    _check(load().ftmoe_host_expert_rows(ctypes.byref(d), x.ctypes.data, tok.ctypes.data, ex.ctypes.data, len(tok),
+                                         o.ctypes.data, threads))
+    return o
 
 
 def quantize_fp8_per_tensor(x, n: int, q, scale, ws, stream=None) -> None:

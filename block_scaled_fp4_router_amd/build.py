@@ -27,6 +27,18 @@ HIPFLAGS = [
 ]
 
 
+# Host-only C++ (the host half of CPU-GPU co-execution): built by the host
+# compiler; functions that need AVX2/FMA carry their own target attribute.
+CXXFLAGS = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-pthread", "-I", os.path.join(ROOT, "include")]
+
+
+def cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), "/opt/rocm/llvm/bin/clang++"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("no host C++ compiler found")
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -35,15 +47,18 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [cxx(), *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        raise RuntimeError(f"compiler failed on {src}:\n{r.stderr}")
     return obj
 
 
@@ -64,7 +79,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

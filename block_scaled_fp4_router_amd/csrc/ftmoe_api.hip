@@ -4,6 +4,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
+#include <memory>
 #include <new>
 #include <cstdio>
 #include <string>
@@ -11,6 +13,7 @@
 
 #include "../../include/ftmoe.h"
 #include "common.hpp"
+#include "host_experts.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -369,6 +372,9 @@ struct Passes {
   const int32_t* const* tables = nullptr;   // n device tables [E], or NULL: one pass, no table
   ftmoe_status (*before)(void* ctx, int i) = nullptr;
   ftmoe_status (*after)(void* ctx, int i) = nullptr;
+  // after the last pass, before the combine: o is the expert output buffer,
+  // fp32 [T*k][H] (decode) or bf16 (prefill)
+  ftmoe_status (*before_combine)(void* ctx, void* o, bool fp32) = nullptr;
   void* ctx = nullptr;
 };
 
@@ -473,6 +479,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
       if (passes.after) FT_TRY(passes.after(passes.ctx, i));
     }
     a.nb_shared = p.nb_shared;
+    if (passes.before_combine) FT_TRY(passes.before_combine(passes.ctx, a.o32, true));
     FT_HIP(timed("combine", s, [&] { return launch_decode_combine(a, s); }), "combine launch");
     return FTMOE_OK;
   }
@@ -559,6 +566,7 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
                  [&] { return launch_gemm_down(to_qw(L->shared_down), rs, hsa, H, L->shared_inter, sh, s); }),
            "shared down GEMM launch");
   }
+  if (passes.before_combine) FT_TRY(passes.before_combine(passes.ctx, o, false));
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),
          "combine launch");
   return FTMOE_OK;
@@ -626,8 +634,8 @@ struct ftmoe_cache {
   hipStream_t copy_stream = nullptr;
   std::vector<hipEvent_t> ev_copied, ev_done;  // per pass: its copies landed / its kernels ran
   // per-call state
-  std::vector<int32_t> ids_host;
-  std::vector<int32_t> tables;                 // [passes][E] slot of each expert, -1 if not in the pass
+  int32_t* pin = nullptr;                      // pinned host words: the routing ids [T*k], then the
+  size_t pin_words = 0;                        // pass tables [passes][E] (slot of each expert, -1 if not in the pass)
   std::vector<std::vector<int>> copy_e, copy_s;   // per pass: experts to copy and their slots
   std::vector<int> copy_after;                 // per pass: the last earlier pass that reads a slot it overwrites, or -1
   hipStream_t stream = nullptr;                // the stream of the last call
@@ -636,12 +644,34 @@ struct ftmoe_cache {
   // pool is then filled by one kernel per pass instead of one DMA per array
   int zero_copy = -1;                          // -1: not probed yet; 0: DMA copies; 1: fill kernel
   const uint8_t* dev_src[kFillArrays] = {};
+  // host compute of missing experts (co-execution); cost model in seconds
+  std::unique_ptr<ftmoe_host::Pool> host_pool;
+  double host_expert_s = 0, host_row_s = 0, link_bps = 0;
+  bool host_adaptive = false;                  // calibrated model: rescaled by the measured host times
+  double host_scale = 1;                       // measured / modelled host time (running average)
+  double host_predicted = 0;                   // modelled host time of this call's host experts
+  int64_t host_experts = 0, host_rows = 0;
+  double host_seconds = 0;
+  // per-call host work: x [T][H] copied back, the rows' tokens, experts, flat ids, outputs
+  void* hx = nullptr;
+  size_t hx_bytes = 0;
+  hipEvent_t ev_x = nullptr;
+  std::vector<int32_t> h_tok, h_ex;
+  int32_t* h_flat = nullptr;                   // pinned [rows]
+  float* h_out = nullptr;                      // pinned [rows][H]
+  size_t h_rows_cap = 0;
+  int h_n = 0, h_T = 0;
 
   ~ftmoe_cache() {
     if (copy_stream) {
       (void)hipStreamSynchronize(copy_stream);
       (void)hipStreamDestroy(copy_stream);
     }
+    if (pin) (void)hipHostFree(pin);
+    if (hx) (void)hipHostFree(hx);
+    if (h_flat) (void)hipHostFree(h_flat);
+    if (h_out) (void)hipHostFree(h_out);
+    if (ev_x) (void)hipEventDestroy(ev_x);
     for (hipEvent_t e : ev_copied) (void)hipEventDestroy(e);
     for (hipEvent_t e : ev_done) (void)hipEventDestroy(e);
   }
@@ -744,6 +774,22 @@ ftmoe_status cache_copy_pass(ftmoe_cache* c, int i) {
   return FTMOE_OK;
 }
 
+// Grows the pinned host buffer to `words` (after the last call's work, which may read it, is done).
+ftmoe_status cache_host_buffer(ftmoe_cache* c, size_t words) {
+  if (words <= c->pin_words) return FTMOE_OK;
+  if (c->pin) {
+    if (c->called) FT_HIP(hipStreamSynchronize(c->stream), "previous stream");
+    (void)hipHostFree(c->pin);
+    c->pin = nullptr;
+    c->pin_words = 0;
+  }
+  void* p = nullptr;
+  FT_HIP(hipHostMalloc(&p, words * 4, hipHostMallocDefault), "pinned host buffer");
+  c->pin = static_cast<int32_t*>(p);
+  c->pin_words = words;
+  return FTMOE_OK;
+}
+
 // Whether every host array has a device-visible address (pinned, mapped
 // memory) and fits the fill kernel's 32-bit per-expert sizes; else the pool
 // is filled by DMA copies.
@@ -789,6 +835,85 @@ ftmoe_status cache_after_pass(void* ctx, int i) {
 // Misses per pass when a step's experts do not all fit: half the pool, so
 // one pass's copies can land while the previous pass runs.
 int cache_group(const ftmoe_cache* c) { return std::max(1, c->slots / 2); }
+
+ftmoe_host::Mat host_mat(const ftmoe_qweight& q) {
+  ftmoe_host::Mat m;
+  m.fmt = q.fmt;
+  m.n = q.n;
+  m.k = q.k;
+  m.codes = static_cast<const uint8_t*>(q.codes);
+  m.scales = static_cast<const uint8_t*>(q.block_scales);
+  m.tscale = q.tensor_scales;
+  m.rowsc = q.row_scales;
+  return m;
+}
+
+// Host-computed expert rows: wait for x on the host, compute, and scatter
+// the rows into the device path's o buffer (the passes run meanwhile).
+ftmoe_status cache_host_rows(void* ctx, void* o, bool fp32) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  if (c->h_n == 0) return FTMOE_OK;
+  const ftmoe_layer& L = c->layer;
+  FT_HIP(hipEventSynchronize(c->ev_x), "x copy");
+  const auto t0 = std::chrono::steady_clock::now();
+  const ftmoe_host::Mat gu = host_mat(c->host_gu), dn = host_mat(c->host_dn);
+  if (!ftmoe_host::expert_rows(*c->host_pool, gu, dn, L.hidden, L.inter, L.act == FTMOE_ACT_MXFP8,
+                               static_cast<const uint16_t*>(c->hx), c->h_tok.data(), c->h_ex.data(), c->h_n,
+                               c->h_out))
+    return fail(FTMOE_ERR_UNSUPPORTED, "host expert compute needs AVX2 and FMA");
+  const double took = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  c->host_seconds += took;
+  if (c->host_adaptive && c->host_predicted > 0)
+    c->host_scale = 0.7 * c->host_scale + 0.3 * c->host_scale * took / c->host_predicted;
+  void *rows = nullptr, *flat = nullptr;
+  FT_HIP(hipHostGetDevicePointer(&rows, c->h_out, 0), "host rows address");
+  FT_HIP(hipHostGetDevicePointer(&flat, c->h_flat, 0), "host rows address");
+  FT_HIP(launch_host_rows_scatter(static_cast<const float*>(rows), static_cast<const int32_t*>(flat), c->h_n,
+                                  L.hidden, fp32 ? static_cast<float*>(o) : nullptr,
+                                  fp32 ? nullptr : static_cast<uint16_t*>(o), c->stream),
+         "host rows scatter launch");
+  return FTMOE_OK;
+}
+
+// Pinned host buffer p of at least `bytes` (grown; the caller has made sure no device work reads the old one).
+ftmoe_status grow_pinned(void** p, size_t* cap, size_t bytes) {
+  if (bytes <= *cap) return FTMOE_OK;
+  if (*p) (void)hipHostFree(*p);
+  *p = nullptr;
+  *cap = 0;
+  FT_HIP(hipHostMalloc(p, bytes, hipHostMallocDefault), "pinned host buffer");
+  *cap = bytes;
+  return FTMOE_OK;
+}
+
+// The co-execution split (bandwidth-adaptive): the missing experts, fewest
+// routed rows first (then by index), go to the host while that shortens the
+// step: q minimises max(sum of host times of the first q, sum of link times
+// of the rest), host time = expert_s + rows * row_s, link time = bytes /
+// link rate; ties take the smaller q.  Returns q; `missing` is reordered.
+int host_split(ftmoe_cache* c, std::vector<int>& missing, const std::vector<int>& rows) {
+  c->host_predicted = 0;
+  if (!c->host_pool || missing.empty()) return 0;
+  std::stable_sort(missing.begin(), missing.end(), [&](int a, int b) { return rows[a] < rows[b]; });
+  const double bytes = static_cast<double>(c->pl.gu.codes + c->pl.gu.scales + c->pl.gu.ts + c->pl.dn.codes +
+                                           c->pl.dn.scales + c->pl.dn.ts);
+  const int m = static_cast<int>(missing.size());
+  double link_rest = m * bytes / c->link_bps, host = 0, best = link_rest;
+  int q_best = 0;
+  double host_best = 0;
+  for (int q = 1; q <= m; ++q) {
+    host += c->host_scale * (c->host_expert_s + rows[missing[q - 1]] * c->host_row_s);
+    link_rest -= bytes / c->link_bps;
+    const double t = std::max(host, link_rest);
+    if (t < best) {
+      best = t;
+      q_best = q;
+      host_best = host;
+    }
+  }
+  c->host_predicted = host_best;
+  return q_best;
+}
 
 // The most passes a step can need (the resident experts, then the misses in
 // groups), and the workspace of ftmoe_cache_forward.
@@ -1093,14 +1218,57 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
 
   // the step's distinct experts: resident ones (hits), then the others
   const size_t n_ids = static_cast<size_t>(T) * k;
-  c->ids_host.resize(n_ids);
-  FT_HIP(hipMemcpyAsync(c->ids_host.data(), ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
+  FT_TRY(cache_host_buffer(c, n_ids + static_cast<size_t>(cache_max_passes(c)) * E));
+  const int32_t* ids_host = c->pin;
+  FT_HIP(hipMemcpyAsync(c->pin, ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
   FT_HIP(hipStreamSynchronize(s), "routing copy");
   std::vector<char> used(E, 0);
-  for (size_t i = 0; i < n_ids; ++i) used[c->ids_host[i]] = 1;
+  for (size_t i = 0; i < n_ids; ++i) used[ids_host[i]] = 1;
   std::vector<int> hit, missing;
   for (int e = 0; e < E; ++e)
     if (used[e]) (c->expert_slot[e] >= 0 ? hit : missing).push_back(e);
+  // co-execution: some missing experts computed on the host instead of filled
+  c->h_n = 0;
+  if (c->host_pool) {
+    std::vector<int> rows(E, 0);
+    for (size_t i = 0; i < n_ids; ++i) ++rows[ids_host[i]];
+    const int q = host_split(c, missing, rows);
+    if (q > 0) {
+      std::vector<char> on_host(E, 0);
+      int nr = 0;
+      for (int i = 0; i < q; ++i) {
+        on_host[missing[i]] = 1;
+        nr += rows[missing[i]];
+      }
+      missing.erase(missing.begin(), missing.begin() + q);
+      std::sort(missing.begin(), missing.end());
+      size_t cap_f = c->h_rows_cap * 4, cap_o = c->h_rows_cap * 4 * static_cast<size_t>(L->hidden);
+      if (static_cast<size_t>(nr) > c->h_rows_cap) {
+        void* pf = c->h_flat;
+        void* po = c->h_out;
+        FT_TRY(grow_pinned(&pf, &cap_f, static_cast<size_t>(nr) * 4));
+        c->h_flat = static_cast<int32_t*>(pf);
+        FT_TRY(grow_pinned(&po, &cap_o, static_cast<size_t>(nr) * 4 * L->hidden));
+        c->h_out = static_cast<float*>(po);
+        c->h_rows_cap = nr;
+      }
+      c->h_tok.clear();
+      c->h_ex.clear();
+      for (size_t f = 0; f < n_ids; ++f)
+        if (on_host[ids_host[f]]) {
+          c->h_flat[c->h_n++] = static_cast<int32_t>(f);
+          c->h_tok.push_back(static_cast<int32_t>(f / k));
+          c->h_ex.push_back(ids_host[f]);
+        }
+      c->host_experts += q;
+      c->host_rows += nr;
+      // x back to the host for them, ahead of the passes on the stream
+      FT_TRY(grow_pinned(&c->hx, &c->hx_bytes, static_cast<size_t>(T) * L->hidden * 2));
+      if (!c->ev_x) FT_HIP(hipEventCreateWithFlags(&c->ev_x, hipEventDisableTiming), "event creation");
+      FT_HIP(hipMemcpyAsync(c->hx, x, static_cast<size_t>(T) * L->hidden * 2, hipMemcpyDeviceToHost, s), "x copy");
+      FT_HIP(hipEventRecord(c->ev_x, s), "x copy event");
+    }
+  }
   const int n = static_cast<int>(hit.size() + missing.size());
   // Passes: with per-tensor FP8 activations all experts in one (their h
   // scale spans every expert); otherwise the hits first, so that they run
@@ -1141,7 +1309,8 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
   }
 
   // plan every pass; a pass's copies wait for the last earlier pass reading a slot they overwrite
-  c->tables.assign(static_cast<size_t>(npass) * E, -1);
+  int32_t* tab_host = c->pin + n_ids;
+  std::fill(tab_host, tab_host + static_cast<size_t>(npass) * E, -1);
   c->copy_e.assign(npass, {});
   c->copy_s.assign(npass, {});
   c->copy_after.assign(npass, -1);
@@ -1151,7 +1320,7 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
     const int m = static_cast<int>(groups[i].size());
     FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data()));
     for (int q = 0; q < m; ++q) {
-      c->tables[static_cast<size_t>(i) * E + groups[i][q]] = sl[q];
+      tab_host[static_cast<size_t>(i) * E + groups[i][q]] = sl[q];
       if (miss[q]) {
         c->copy_e[i].push_back(groups[i][q]);
         c->copy_s[i].push_back(sl[q]);
@@ -1161,7 +1330,8 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
     for (int q = 0; q < m; ++q) reader[sl[q]] = i;
   }
   int32_t* tables = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + up256(p.total));
-  FT_HIP(hipMemcpyAsync(tables, c->tables.data(), c->tables.size() * 4, hipMemcpyHostToDevice, s), "table copy");
+  FT_HIP(hipMemcpyAsync(tables, tab_host, static_cast<size_t>(npass) * E * 4, hipMemcpyHostToDevice, s),
+         "table copy");
   std::vector<const int32_t*> tptr(npass);
   for (int i = 0; i < npass; ++i) tptr[i] = tables + static_cast<size_t>(i) * E;
   c->stream = s;
@@ -1172,8 +1342,82 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
   passes.tables = tptr.data();
   passes.before = cache_before_pass;
   passes.after = cache_after_pass;
+  passes.before_combine = cache_host_rows;
   passes.ctx = c;
   return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, passes);
+}
+
+ftmoe_status ftmoe_cache_set_host_compute(ftmoe_cache* c, int32_t threads, double expert_s, double row_s,
+                                          double link_bytes_per_s) {
+  g_last_error.clear();
+  if (!c) return fail(FTMOE_ERR_INVALID_ARG, "cache is NULL");
+  if (threads < 0 || threads > 256) return fail(FTMOE_ERR_INVALID_ARG, "threads=%d outside [0, 256]", threads);
+  if (threads == 0) {
+    c->host_pool.reset();
+    return FTMOE_OK;
+  }
+  if (c->layer.act == FTMOE_ACT_FP8_PER_TENSOR)
+    return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations span every expert: no host compute");
+  if (!ftmoe_host::cpu_supported()) return fail(FTMOE_ERR_UNSUPPORTED, "host expert compute needs AVX2 and FMA");
+  c->host_pool = std::make_unique<ftmoe_host::Pool>(threads);
+  c->link_bps = link_bytes_per_s > 0 ? link_bytes_per_s : 50e9;
+  c->host_scale = 1;
+  c->host_adaptive = !(expert_s > 0 && row_s >= 0);
+  if (!c->host_adaptive) {
+    c->host_expert_s = expert_s;
+    c->host_row_s = row_s;
+    return FTMOE_OK;
+  }
+  // calibration: expert 0 with 1 and with 65 rows of a constant token, best of two each (many rows
+  // make the dot products, not the weight decoding, the bound)
+  const int H = c->layer.hidden;
+  const ftmoe_host::Mat gu = host_mat(c->host_gu), dn = host_mat(c->host_dn);
+  std::vector<uint16_t> x(H, 0x3C00);   // bf16 0.0078125
+  constexpr int kRows = 65;
+  std::vector<int32_t> tok(kRows, 0), ex(kRows, 0);
+  std::vector<float> o(static_cast<size_t>(kRows) * H);
+  double t[2] = {1e30, 1e30};
+  for (int rep = 0; rep < 2; ++rep)
+    for (int v = 0; v < 2; ++v) {
+      const auto t0 = std::chrono::steady_clock::now();
+      ftmoe_host::expert_rows(*c->host_pool, gu, dn, H, c->layer.inter, c->layer.act == FTMOE_ACT_MXFP8, x.data(),
+                              tok.data(), ex.data(), v ? kRows : 1, o.data());
+      t[v] = std::min(t[v], std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count());
+    }
+  c->host_row_s = std::max(0.0, (t[1] - t[0]) / (kRows - 1));
+  c->host_expert_s = std::max(1e-7, t[0] - c->host_row_s);
+  return FTMOE_OK;
+}
+
+ftmoe_status ftmoe_cache_host_stats(const ftmoe_cache* c, int64_t* experts, int64_t* rows, double* seconds,
+                                    double* expert_s, double* row_s) {
+  g_last_error.clear();
+  if (!c) return fail(FTMOE_ERR_INVALID_ARG, "cache is NULL");
+  if (experts) *experts = c->host_experts;
+  if (rows) *rows = c->host_rows;
+  if (seconds) *seconds = c->host_seconds;
+  if (expert_s) *expert_s = c->host_expert_s * c->host_scale;
+  if (row_s) *row_s = c->host_row_s * c->host_scale;
+  return FTMOE_OK;
+}
+
+ftmoe_status ftmoe_host_expert_rows(const ftmoe_layer* layer, const uint16_t* x, const int32_t* tok,
+                                    const int32_t* ex, int32_t n, float* o, int32_t threads) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  if (n < 0 || threads < 1 || threads > 256) return fail(FTMOE_ERR_INVALID_ARG, "bad n or threads");
+  if (n > 0 && (!x || !tok || !ex || !o)) return fail(FTMOE_ERR_INVALID_ARG, "NULL argument");
+  if (layer->act == FTMOE_ACT_FP8_PER_TENSOR)
+    return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations span every expert: no host compute");
+  for (int i = 0; i < n; ++i)
+    if (ex[i] < 0 || ex[i] >= layer->num_experts || tok[i] < 0)
+      return fail(FTMOE_ERR_INVALID_ARG, "row %d: expert %d or token %d out of range", i, ex[i], tok[i]);
+  const ftmoe_host::Mat gu = host_mat(layer->gate_up), dn = host_mat(layer->down);
+  ftmoe_host::Pool pool(threads);
+  if (!ftmoe_host::expert_rows(pool, gu, dn, layer->hidden, layer->inter, layer->act == FTMOE_ACT_MXFP8, x, tok, ex,
+                               n, o))
+    return fail(FTMOE_ERR_UNSUPPORTED, "host expert compute needs AVX2 and FMA");
+  return FTMOE_OK;
 }
 
 ftmoe_status ftmoe_cache_stats(const ftmoe_cache* cache, int64_t* hits, int64_t* misses, int64_t* bytes_copied,

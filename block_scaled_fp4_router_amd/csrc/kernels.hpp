@@ -211,6 +211,12 @@ struct FillArgs {
 };
 hipError_t launch_expert_fill(const FillArgs& a, hipStream_t s);
 
+// Expert output rows computed on the host (device-readable host memory:
+// rows [n][H] fp32, flat row ids [n]) into the device path's o buffer:
+// fp32 o32 [T*k][H] (decode) or, with o32 NULL, bf16 o16 (nearest even).
+hipError_t launch_host_rows_scatter(const float* rows, const int32_t* flat, int n, int H, float* o32, uint16_t* o16,
+                                    hipStream_t s);
+
 // ---- combine ----
 // y[t] = sum_j w[t,j] o[t*k+j] (+ sg[t] * sh[t]) -> bf16.
 hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H, const float* sg,

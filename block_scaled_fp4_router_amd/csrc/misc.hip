@@ -204,4 +204,28 @@ hipError_t launch_expert_fill(const FillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------- host rows scatter ---
+__global__ __launch_bounds__(256) void host_rows_scatter_kernel(const float* __restrict__ rows,
+                                                                const int32_t* __restrict__ flat, int H,
+                                                                float* o32, uint16_t* o16) {
+  const int r = blockIdx.x;
+  const size_t f = static_cast<size_t>(flat[r]);
+  const float4* src = reinterpret_cast<const float4*>(rows + static_cast<size_t>(r) * H);
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    const float4 v = src[c];
+    if (o32) {
+      reinterpret_cast<float4*>(o32 + f * H)[c] = v;
+    } else {
+      reinterpret_cast<uint2*>(o16 + f * H)[c] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+  }
+}
+
+hipError_t launch_host_rows_scatter(const float* rows, const int32_t* flat, int n, int H, float* o32, uint16_t* o16,
+                                    hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  host_rows_scatter_kernel<<<n, 256, 0, s>>>(rows, flat, H, o32, o16);
+  return hipGetLastError();
+}
+
 }  // namespace ftmoe

@@ -318,6 +318,44 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* cache, const uint16_t* x, int32_t 
 ftmoe_status ftmoe_cache_stats(const ftmoe_cache* cache, int64_t* hits, int64_t* misses, int64_t* bytes_copied,
                                int64_t* passes);
 
+/* ---- CPU-GPU co-execution over the expert-slot pool ----
+ * The FreeToken README ("About", its runtime features) lists bandwidth-
+ * adaptive co-execution that splits MoE work between the host CPU and the
+ * GPU, without giving the policy.  With it enabled, ftmoe_cache_forward
+ * splits each step's missing experts (the hits always run on the GPU):
+ * taking them fewest routed rows first, the host computes the first q and
+ * the pool fills the rest, where q minimises the larger of the host's time
+ * (sum over its experts of expert_s + rows * row_s) and the link's (their
+ * bytes / link_bytes_per_s), the smaller q on ties.  The host computes
+ * from the host arrays while the GPU runs the passes.  It uses `threads`
+ * threads of its own and the calling thread, in fp32 with h rounded as the
+ * device path rounds it.  Its rows then go into the device's expert output
+ * buffer before the combine.  Host-computed experts count as neither hits
+ * nor misses and do not enter the pool.
+ * threads = 0 disables it.  expert_s <= 0 or row_s < 0 asks for
+ * calibration: expert 0 is timed here with 1 and 65 rows.  The model is
+ * then adaptive: after each step that computed experts on the host, it is
+ * rescaled toward the measured host time (a running average).
+ * link_bytes_per_s <= 0 means 50e9.  FTMOE_ERR_UNSUPPORTED for per-tensor
+ * FP8 activations (h's scale spans every expert) and on CPUs without AVX2
+ * and FMA.                                                               */
+ftmoe_status ftmoe_cache_set_host_compute(ftmoe_cache* cache, int32_t threads, double expert_s, double row_s,
+                                          double link_bytes_per_s);
+
+/* Counters of host-computed experts and rows, host compute seconds, and
+ * the cost model in use (adaptive scaling applied).  Any output may be
+ * NULL.                                                                   */
+ftmoe_status ftmoe_cache_host_stats(const ftmoe_cache* cache, int64_t* experts, int64_t* rows, double* seconds,
+                                    double* expert_s, double* row_s);
+
+/* The host half alone, with HOST pointers throughout.  Row r is token
+ * tok[r] of x [*][H] (bf16) through routed expert ex[r] of `layer`, whose
+ * gate_up and down are host arrays; the router and shared expert are not
+ * used.  o [n][H] fp32 = W_down h.  `threads` >= 1.  Exposed so that the
+ * arithmetic can be tested without a GPU; the device path never calls it. */
+ftmoe_status ftmoe_host_expert_rows(const ftmoe_layer* layer, const uint16_t* x, const int32_t* tok,
+                                    const int32_t* ex, int32_t n, float* o, int32_t threads);
+
 /* Per-tensor E4M3 activation quantiser used by FTMOE_ACT_FP8_PER_TENSOR,
  * exposed for testing: scale[0] = amax(|x|)/448 (1 if amax is 0, fp32) and
  * q = E4M3(x / scale) rounded to nearest even and saturated to +-448.

@@ -9,8 +9,9 @@ import numpy as np
 import pytest
 
 import block_scaled_fp4_router_amd as ft
+import oracle
 import synth
-from gpu_util import DEV, bf16_dev_to_f64, layer_pair, run_forward, say, to_dev_bf16
+from gpu_util import DEV, bf16_dev_to_f64, layer_pair, rel_fro, run_forward, say, to_dev_bf16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -147,5 +148,81 @@ def test_cache_refuses_fp8_per_tensor_layers_that_need_several_passes():
     cache = ft.ExpertCache.from_host(lay, 2, DEV, path="prefill")
     with pytest.raises(ft.FtmoeError) as err:
         cache_forward(cache, x)
+    assert err.value.status == ft.ERR_UNSUPPORTED
+    cache.close()
+
+
+# ------------------------------------------------------------ co-execution --
+HOST_CASES = [
+    # name, layer, T, path, slots, mode: "all" (every miss on the host), "none", "calibrated"
+    ("c1", None, 8, "decode", 12, "all"),
+    ("c1", None, 8, "decode", 12, "none"),
+    ("c1", None, 8, "decode", 24, "calibrated"),
+    ("c1-w4a8", None, 8, "decode", 20, "all"),
+    ("c1", None, 40, "prefill", 24, "all"),
+    ("nvs", (256, 16, 4, 128, "nvfp4", "bf16", 128), 70, "prefill", 5, "all"),
+    ("bf16", (256, 8, 2, 256, "bf16", "bf16", 0), 9, "decode", 3, "all"),
+]
+
+
+@pytest.mark.parametrize("name,shape,T,path,slots,mode", HOST_CASES)
+@pytest.mark.timeout(600)
+def test_cache_host_compute(name, shape, T, path, slots, mode):
+    """Missing experts computed on the host cores: the layer output stays
+    within 1e-2 of the device-only output (relative Frobenius; the host
+    sums in another order) and within the layer's tolerance of the oracle;
+    the routing is unchanged; the counters add up."""
+    say(f"expert cache + host compute {name} T={T} path={path} slots={slots} mode={mode}")
+    if shape is None:
+        lay, dlay = layer_pair(name)
+    else:
+        lay = _small(name, *shape)
+        dlay = ft.DeviceLayer.from_host(lay, DEV)
+    x = synth.make_tokens(lay, T, stream=T + 1)
+    ref_y, ref_ids, ref_w = run_forward(dlay, x, path)
+    cache = ft.ExpertCache.from_host(lay, slots, DEV, path=path)
+    if mode == "all":
+        cache.set_host_compute(4, expert_s=1e-12, row_s=0.0, link_bytes_per_s=1.0)
+    elif mode == "none":
+        cache.set_host_compute(4, expert_s=1e3, row_s=0.0)
+    else:
+        cache.set_host_compute(4)
+    hs0 = cache.host_stats()
+    say(f"  cost model {hs0}")
+    assert hs0["expert_s"] > 0 and hs0["row_s"] >= 0
+    for step in range(2):
+        y, ids, w = cache_forward(cache, x)
+        assert np.array_equal(ids, ref_ids) and np.array_equal(w, ref_w)
+        assert np.isfinite(y).all()
+        err = rel_fro(y, ref_y)
+        say(f"  step {step}: vs device-only {err:.2e}, pool {cache.stats()}, host {cache.host_stats()}")
+        assert err <= 1e-2
+        if mode == "none":
+            assert np.array_equal(y, ref_y)
+    hs, st = cache.host_stats(), cache.stats()
+    n = len(np.unique(ids))
+    if mode == "all":
+        # nothing is ever resident: every expert of both steps is computed on the host
+        assert hs["experts"] == 2 * n and hs["rows"] == 2 * ids.size
+        assert st["hits"] == 0 and st["misses"] == 0 and st["bytes_copied"] == 0
+    elif mode == "none":
+        assert hs["experts"] == 0 and hs["rows"] == 0
+    else:
+        assert hs["experts"] + st["hits"] + st["misses"] == 2 * n
+    tok = np.arange(T)
+    s_h = None
+    ref = oracle.forward_tokens(lay, x, tok, s_h=s_h)
+    err = rel_fro(y, ref)
+    say(f"  vs oracle {err:.2e}")
+    assert err <= (3e-2 if lay.cfg.act in ("fp8", "mxfp8") else 2e-2)
+    cache.close()
+
+
+@pytest.mark.timeout(300)
+def test_host_compute_refuses_fp8_per_tensor_layers():
+    lay = _small("f8a8", 256, 8, 2, 256, "fp8", "fp8", 0)
+    cache = ft.ExpertCache.from_host(lay, 8, DEV, path="decode")
+    with pytest.raises(ft.FtmoeError) as err:
+        cache.set_host_compute(2)
     assert err.value.status == ft.ERR_UNSUPPORTED
     cache.close()
