@@ -1192,10 +1192,28 @@ ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, siz
   return FTMOE_OK;
 }
 
+static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                                       uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
                                  uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
   g_last_error.clear();
   if (!c) return fail(FTMOE_ERR_INVALID_ARG, "cache is NULL");
+  const ftmoe_status st = cache_forward_impl(c, x, T, ws, ws_bytes, y, topk_ids_out, topk_w_out, stream);
+  if (st == FTMOE_ERR_HIP) {
+    // a runtime failure after planning may leave slots marked resident whose fills never ran: forget them all
+    // (finishing what was enqueued first, so that no fill lands in a slot after it is reassigned)
+    if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
+    if (c->called) (void)hipStreamSynchronize(c->stream);
+    std::fill(c->slot_expert.begin(), c->slot_expert.end(), -1);
+    std::fill(c->expert_slot.begin(), c->expert_slot.end(), -1);
+    std::fill(c->last_use.begin(), c->last_use.end(), -1);
+  }
+  return st;
+}
+
+static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                                       uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
   const ftmoe_layer* L = &c->layer;
   FT_TRY(check_tokens(T));
   if (T == 0) return FTMOE_OK;

@@ -309,7 +309,8 @@ ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, siz
  * scale spans every expert): FTMOE_ERR_UNSUPPORTED if the step needs more
  * experts than there are slots.  Arguments as in ftmoe_forward; the
  * outputs equal ftmoe_forward's on a layer whose experts are in device
- * memory.  Call with the device current that was current at creation.   */
+ * memory.  Call with the device current that was current at creation.
+ * After FTMOE_ERR_HIP the pool forgets what it held (every slot empty).   */
 ftmoe_status ftmoe_cache_forward(ftmoe_cache* cache, const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
                                  uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
 
