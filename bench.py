@@ -178,6 +178,17 @@ def main() -> int:
                 "cost_model": {"expert_s": hs["expert_s"], "row_s": hs["row_s"]}}
     mean_bytes = float(np.mean([sel_bytes[i % nb] for i in range(args.steps)]))
 
+    # Per-step durations (events on the stream around each step, no host
+    # synchronisation between steps): median and spread.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in evs])
+    step_pct = {q: round(float(np.percentile(per_step, v)), 5) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     # Same steps again with per-kernel timing: events attached to each kernel's
     # launch (recorded at its start and end), or bracketing a multi-kernel step.
     ft.timing_enable(True)
@@ -210,9 +221,13 @@ def main() -> int:
         unit_bytes = {"decode_gateup": gu_b * mean_unique + sgu_b,
                       "decode_down": dn_b * mean_unique + sdn_b}[dom]
         achieved = unit_bytes / (kernel_us[dom] * 1e-6) / 1e9
+        expert_us = kernel_us["decode_gateup"] + kernel_us["decode_down"]
+        # the expert kernels alone (one launch each per step; a pool runs several passes)
+        expert_rate = round(mean_bytes / (expert_us * 1e-6) / 1e9, 1) if pool is None else None
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_launch": int(unit_bytes), "avg_launch_us": round(kernel_us[dom], 3)}
+                "algorithmic_bytes_per_launch": int(unit_bytes), "avg_launch_us": round(kernel_us[dom], 3),
+                "expert_kernels_GBs": expert_rate}
     else:
         value = T / (ms * 1e-3)
         unit = "tokens/s"
@@ -233,6 +248,7 @@ def main() -> int:
                    "token_batches_cycled": nb, "path": args.path,
                    "selected_expert_bytes_per_step": int(mean_bytes)},
         **({"expert_pool": pool_stats} if pool_stats else {}),
+        "step_ms_percentiles": step_pct,
         "roofline": roof,
         "kernel_avg_us": {k2: round(v, 3) for k2, v in sorted(kernel_us.items())},
     }
