@@ -115,7 +115,8 @@ def test_forward_parity_full(name, T, path):
 
 
 @pytest.mark.parametrize("name,T,nsample", [("c2", 4096, 48), ("c3", 8192, 40), ("c4", 16384, 24),
-                                            ("c2-w4a8", 4096, 48), ("c2-bf16", 4096, 32)])
+                                            ("c2-w4a8", 4096, 48), ("c2-bf16", 4096, 32),
+                                            ("c0", 1 << 20, 32)])   # the largest batch the library takes
 @pytest.mark.timeout(900)
 def test_forward_parity_full_size_sampled(name, T, nsample):
     say(f"forward parity full size {name} T={T} (sample {nsample}), packed weights as the benchmark runs")
