@@ -592,13 +592,14 @@ SetBytes set_bytes(const ftmoe_qweight& q) {
 }
 
 // Pool regions: gate_up codes, scales, multipliers, then down's, each
-// [slots][per-expert bytes] and 256-byte aligned.
+// [slots][per-expert bytes], then the residency table [E] (slot of each
+// expert, -1 if none), each 256-byte aligned.
 struct PoolLayout {
   SetBytes gu, dn;
-  size_t gu_codes = 0, gu_scales = 0, gu_ts = 0, dn_codes = 0, dn_scales = 0, dn_ts = 0, total = 0;
+  size_t gu_codes = 0, gu_scales = 0, gu_ts = 0, dn_codes = 0, dn_scales = 0, dn_ts = 0, resid = 0, total = 0;
 };
 
-PoolLayout pool_layout(const ftmoe_qweight& gu, const ftmoe_qweight& dn, int slots) {
+PoolLayout pool_layout(const ftmoe_qweight& gu, const ftmoe_qweight& dn, int slots, int E) {
   PoolLayout pl;
   pl.gu = set_bytes(gu);
   pl.dn = set_bytes(dn);
@@ -614,6 +615,7 @@ PoolLayout pool_layout(const ftmoe_qweight& gu, const ftmoe_qweight& dn, int slo
   pl.dn_codes = take(pl.dn.codes * slots);
   pl.dn_scales = take(pl.dn.scales * slots);
   pl.dn_ts = take(pl.dn.ts * slots);
+  pl.resid = take(static_cast<size_t>(E) * 4);
   pl.total = off;
   return pl;
 }
@@ -656,6 +658,16 @@ struct ftmoe_cache {
   void* hx = nullptr;
   size_t hx_bytes = 0;
   hipEvent_t ev_x = nullptr;
+  // device residency table (in the pool) read by each step's first pass
+  bool resid_init = false;
+  int32_t* resid_host = nullptr;               // pinned [E]
+  hipEvent_t ev_ids = nullptr;                 // the routing ids have reached the host
+  // per-call pass state, completed by the first pass's hook
+  Passes run;
+  std::vector<const int32_t*> tptr;
+  int32_t* tables_dev = nullptr;               // workspace tables of passes 1..
+  size_t n_ids = 0;
+  int step_k = 0, step_T = 0;
   std::vector<int32_t> h_tok, h_ex;
   int32_t* h_flat = nullptr;                   // pinned [rows]
   float* h_out = nullptr;                      // pinned [rows][H]
@@ -668,6 +680,8 @@ struct ftmoe_cache {
       (void)hipStreamDestroy(copy_stream);
     }
     if (pin) (void)hipHostFree(pin);
+    if (resid_host) (void)hipHostFree(resid_host);
+    if (ev_ids) (void)hipEventDestroy(ev_ids);
     if (hx) (void)hipHostFree(hx);
     if (h_flat) (void)hipHostFree(h_flat);
     if (h_out) (void)hipHostFree(h_out);
@@ -915,6 +929,164 @@ int host_split(ftmoe_cache* c, std::vector<int>& missing, const std::vector<int>
   return q_best;
 }
 
+// The copy stream, per-pass events, the routing event and the pinned
+// residency table (host resources of the cache, made once).
+int cache_max_passes(const ftmoe_cache* c);
+int cache_group(const ftmoe_cache* c);
+ftmoe_status cache_host_resources(ftmoe_cache* c) {
+  if (c->zero_copy < 0) FT_TRY(cache_probe_zero_copy(c));
+  if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+    c->copy_stream = nullptr;
+    return fail(FTMOE_ERR_HIP, "copy stream creation failed");
+  }
+  if (!c->ev_ids) FT_HIP(hipEventCreateWithFlags(&c->ev_ids, hipEventDisableTiming), "event creation");
+  if (!c->ev_x) FT_HIP(hipEventCreateWithFlags(&c->ev_x, hipEventDisableTiming), "event creation");
+  if (!c->resid_host) {
+    void* p = nullptr;
+    FT_HIP(hipHostMalloc(&p, static_cast<size_t>(c->E) * 4, hipHostMallocDefault), "pinned host buffer");
+    c->resid_host = static_cast<int32_t*>(p);
+  }
+  const int np = cache_max_passes(c);
+  while (static_cast<int>(c->ev_done.size()) < np) {
+    hipEvent_t a = nullptr, b = nullptr;
+    FT_HIP(hipEventCreateWithFlags(&a, hipEventDisableTiming), "event creation");
+    if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return fail(FTMOE_ERR_HIP, "event creation failed");
+    }
+    c->ev_copied.push_back(a);
+    c->ev_done.push_back(b);
+  }
+  c->tptr.assign(np, nullptr);
+  return FTMOE_OK;
+}
+
+// Plans the step once its routing is on the host.  spec: the first pass
+// (the resident experts, on the device residency table) is already
+// enqueued, and the misses get passes 1..; else every pass is planned here,
+// pass 0 included.  Passes: the hits, then the misses (after the host's
+// share is taken out) in one pass when they fit beside the hits, else in
+// groups of half the pool; with per-tensor FP8 activations a single pass.
+ftmoe_status cache_plan_step(ftmoe_cache* c, bool spec) {
+  const ftmoe_layer* L = &c->layer;
+  const int E = c->E, k = c->step_k;
+  const size_t n_ids = c->n_ids;
+  FT_HIP(hipEventSynchronize(c->ev_ids), "routing copy");
+  const int32_t* ids_host = c->pin;
+  std::vector<int> rows(E, 0);
+  for (size_t i = 0; i < n_ids; ++i) ++rows[ids_host[i]];
+  std::vector<int> hit, missing;
+  for (int e = 0; e < E; ++e)
+    if (rows[e]) (c->expert_slot[e] >= 0 ? hit : missing).push_back(e);
+  // co-execution: some missing experts computed on the host instead of filled
+  c->h_n = 0;
+  const int q = host_split(c, missing, rows);
+  if (q > 0) {
+    std::vector<char> on_host(E, 0);
+    int nr = 0;
+    for (int i = 0; i < q; ++i) {
+      on_host[missing[i]] = 1;
+      nr += rows[missing[i]];
+    }
+    missing.erase(missing.begin(), missing.begin() + q);
+    std::sort(missing.begin(), missing.end());
+    if (static_cast<size_t>(nr) > c->h_rows_cap) {
+      size_t cap_f = c->h_rows_cap * 4, cap_o = c->h_rows_cap * 4 * static_cast<size_t>(L->hidden);
+      void* pf = c->h_flat;
+      void* po = c->h_out;
+      FT_TRY(grow_pinned(&pf, &cap_f, static_cast<size_t>(nr) * 4));
+      c->h_flat = static_cast<int32_t*>(pf);
+      FT_TRY(grow_pinned(&po, &cap_o, static_cast<size_t>(nr) * 4 * L->hidden));
+      c->h_out = static_cast<float*>(po);
+      c->h_rows_cap = nr;
+    }
+    c->h_tok.clear();
+    c->h_ex.clear();
+    for (size_t f = 0; f < n_ids; ++f)
+      if (on_host[ids_host[f]]) {
+        c->h_flat[c->h_n++] = static_cast<int32_t>(f);
+        c->h_tok.push_back(static_cast<int32_t>(f / k));
+        c->h_ex.push_back(ids_host[f]);
+      }
+    c->host_experts += q;
+    c->host_rows += nr;
+  }
+  const int n = static_cast<int>(hit.size() + missing.size());
+  std::vector<std::vector<int>> groups;
+  if (!spec) {
+    if (n > c->slots)
+      return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations need all %d experts of the step in %d slots",
+                  n, c->slots);
+    groups.emplace_back(hit);
+    groups[0].insert(groups[0].end(), missing.begin(), missing.end());
+  } else {
+    groups.push_back(hit);
+    const int m = static_cast<int>(missing.size());
+    const int g = n <= c->slots ? std::max(1, m) : cache_group(c);
+    for (int a = 0; a < m; a += g)
+      groups.emplace_back(missing.begin() + a, missing.begin() + std::min(m, a + g));
+  }
+  const int npass = static_cast<int>(groups.size());
+  // plan every pass; a pass's copies wait for the last earlier pass reading a slot they overwrite
+  c->copy_e.assign(npass, {});
+  c->copy_s.assign(npass, {});
+  c->copy_after.assign(npass, -1);
+  const int first = spec ? 1 : 0;   // passes whose tables go to the workspace
+  int32_t* tab_host = c->pin + n_ids;
+  std::fill(tab_host, tab_host + static_cast<size_t>(npass - first) * E, -1);
+  std::vector<int> reader(c->slots, -1);
+  std::vector<int32_t> sl(c->slots), miss(c->slots);
+  for (int i = 0; i < npass; ++i) {
+    const int m = static_cast<int>(groups[i].size());
+    FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data()));
+    for (int qq = 0; qq < m; ++qq) {
+      if (i >= first) tab_host[static_cast<size_t>(i - first) * E + groups[i][qq]] = sl[qq];
+      if (miss[qq]) {
+        c->copy_e[i].push_back(groups[i][qq]);
+        c->copy_s[i].push_back(sl[qq]);
+        c->copy_after[i] = std::max(c->copy_after[i], reader[sl[qq]]);
+      }
+    }
+    for (int qq = 0; qq < m; ++qq) reader[sl[qq]] = i;
+  }
+  if (npass > first)
+    FT_HIP(hipMemcpyAsync(c->tables_dev, tab_host, static_cast<size_t>(npass - first) * E * 4,
+                          hipMemcpyHostToDevice, c->stream),
+           "table copy");
+  for (int i = first; i < npass; ++i) c->tptr[i] = c->tables_dev + static_cast<size_t>(i - first) * E;
+  c->run.n = npass;
+  c->passes += npass;
+  return FTMOE_OK;
+}
+
+// Hooks of the speculative flow: pass 0 (the resident experts) has no
+// copies; its hook plans the rest and starts pass 1's copies.
+ftmoe_status cache_spec_before(void* ctx, int i) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  if (i > 0 && !c->copy_e[i].empty()) FT_HIP(hipStreamWaitEvent(c->stream, c->ev_copied[i], 0), "pass wait");
+  return FTMOE_OK;
+}
+
+ftmoe_status cache_spec_after(void* ctx, int i) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  FT_HIP(hipEventRecord(c->ev_done[i], c->stream), "pass event");
+  if (i == 0) FT_TRY(cache_plan_step(c, true));
+  if (i + 1 < c->run.n) FT_TRY(cache_copy_pass(c, i + 1));
+  return FTMOE_OK;
+}
+
+// Before the combine: the host rows, then the residency table the next
+// step's first pass reads (after every pass of this step on the stream).
+ftmoe_status cache_spec_combine(void* ctx, void* o, bool fp32) {
+  ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
+  FT_TRY(cache_host_rows(ctx, o, fp32));
+  for (int e = 0; e < c->E; ++e) c->resid_host[e] = c->expert_slot[e];
+  FT_HIP(hipMemcpyAsync(c->pool + c->pl.resid, c->resid_host, static_cast<size_t>(c->E) * 4, hipMemcpyHostToDevice,
+                        c->stream),
+         "residency table copy");
+  return FTMOE_OK;
+}
+
 // The most passes a step can need (the resident experts, then the misses in
 // groups), and the workspace of ftmoe_cache_forward.
 int cache_max_passes(const ftmoe_cache* c) { return 1 + (c->E + cache_group(c) - 1) / cache_group(c); }
@@ -1126,7 +1298,7 @@ ftmoe_status ftmoe_cache_pool_size(const ftmoe_layer* layer, int32_t slots, size
   if (slots < 1 || slots > layer->num_experts)
     return fail(FTMOE_ERR_INVALID_ARG, "slots=%d outside [1, num_experts=%d]", slots, layer->num_experts);
   if (!bytes) return fail(FTMOE_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = pool_layout(layer->gate_up, layer->down, slots).total;
+  *bytes = pool_layout(layer->gate_up, layer->down, slots, layer->num_experts).total;
   return FTMOE_OK;
 }
 
@@ -1144,7 +1316,7 @@ ftmoe_status ftmoe_cache_create(const ftmoe_layer* layer, const ftmoe_qweight* h
   FT_TRY(check_qweight(*host_down, "host_down", fmt, E, layer->hidden, layer->inter));
   if (host_gate_up->packed || host_down->packed)
     return fail(FTMOE_ERR_INVALID_ARG, "host experts have no packed layout");
-  const PoolLayout pl = pool_layout(*host_gate_up, *host_down, slots);
+  const PoolLayout pl = pool_layout(*host_gate_up, *host_down, slots, E);
   if (!pool || (reinterpret_cast<uintptr_t>(pool) & 255u))
     return fail(FTMOE_ERR_INVALID_ARG, "pool must be non-NULL and 256-byte aligned");
   if (pool_bytes < pl.total)
@@ -1208,6 +1380,7 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
     std::fill(c->slot_expert.begin(), c->slot_expert.end(), -1);
     std::fill(c->expert_slot.begin(), c->expert_slot.end(), -1);
     std::fill(c->last_use.begin(), c->last_use.end(), -1);
+    c->resid_init = false;   // the device residency table is rewritten on the next call
   }
   return st;
 }
@@ -1234,135 +1407,56 @@ static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_
   const bool fused_align = p.decode && p.small_route;
   FT_TRY(enqueue_route(L, x, T, p, ws, ids, w, sg, fused_align, s));
 
-  // the step's distinct experts: resident ones (hits), then the others
+  // host resources (made once), the routing ids on their way to the host
   const size_t n_ids = static_cast<size_t>(T) * k;
   FT_TRY(cache_host_buffer(c, n_ids + static_cast<size_t>(cache_max_passes(c)) * E));
-  const int32_t* ids_host = c->pin;
-  FT_HIP(hipMemcpyAsync(c->pin, ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
-  FT_HIP(hipStreamSynchronize(s), "routing copy");
-  std::vector<char> used(E, 0);
-  for (size_t i = 0; i < n_ids; ++i) used[ids_host[i]] = 1;
-  std::vector<int> hit, missing;
-  for (int e = 0; e < E; ++e)
-    if (used[e]) (c->expert_slot[e] >= 0 ? hit : missing).push_back(e);
-  // co-execution: some missing experts computed on the host instead of filled
-  c->h_n = 0;
-  if (c->host_pool) {
-    std::vector<int> rows(E, 0);
-    for (size_t i = 0; i < n_ids; ++i) ++rows[ids_host[i]];
-    const int q = host_split(c, missing, rows);
-    if (q > 0) {
-      std::vector<char> on_host(E, 0);
-      int nr = 0;
-      for (int i = 0; i < q; ++i) {
-        on_host[missing[i]] = 1;
-        nr += rows[missing[i]];
-      }
-      missing.erase(missing.begin(), missing.begin() + q);
-      std::sort(missing.begin(), missing.end());
-      size_t cap_f = c->h_rows_cap * 4, cap_o = c->h_rows_cap * 4 * static_cast<size_t>(L->hidden);
-      if (static_cast<size_t>(nr) > c->h_rows_cap) {
-        void* pf = c->h_flat;
-        void* po = c->h_out;
-        FT_TRY(grow_pinned(&pf, &cap_f, static_cast<size_t>(nr) * 4));
-        c->h_flat = static_cast<int32_t*>(pf);
-        FT_TRY(grow_pinned(&po, &cap_o, static_cast<size_t>(nr) * 4 * L->hidden));
-        c->h_out = static_cast<float*>(po);
-        c->h_rows_cap = nr;
-      }
-      c->h_tok.clear();
-      c->h_ex.clear();
-      for (size_t f = 0; f < n_ids; ++f)
-        if (on_host[ids_host[f]]) {
-          c->h_flat[c->h_n++] = static_cast<int32_t>(f);
-          c->h_tok.push_back(static_cast<int32_t>(f / k));
-          c->h_ex.push_back(ids_host[f]);
-        }
-      c->host_experts += q;
-      c->host_rows += nr;
-      // x back to the host for them, ahead of the passes on the stream
-      FT_TRY(grow_pinned(&c->hx, &c->hx_bytes, static_cast<size_t>(T) * L->hidden * 2));
-      if (!c->ev_x) FT_HIP(hipEventCreateWithFlags(&c->ev_x, hipEventDisableTiming), "event creation");
-      FT_HIP(hipMemcpyAsync(c->hx, x, static_cast<size_t>(T) * L->hidden * 2, hipMemcpyDeviceToHost, s), "x copy");
-      FT_HIP(hipEventRecord(c->ev_x, s), "x copy event");
-    }
-  }
-  const int n = static_cast<int>(hit.size() + missing.size());
-  // Passes: with per-tensor FP8 activations all experts in one (their h
-  // scale spans every expert); otherwise the hits first, so that they run
-  // while the misses are copied, then the misses: in one pass when they fit
-  // beside the hits, else in groups of half the pool.
-  std::vector<std::vector<int>> groups;
-  if (L->act == FTMOE_ACT_FP8_PER_TENSOR) {
-    if (n > c->slots)
-      return fail(FTMOE_ERR_UNSUPPORTED, "per-tensor FP8 activations need all %d experts of the step in %d slots",
-                  n, c->slots);
-    groups.emplace_back(hit);
-    groups[0].insert(groups[0].end(), missing.begin(), missing.end());
-  } else {
-    if (!hit.empty()) groups.push_back(hit);
-    const int m = static_cast<int>(missing.size());
-    const int g = n <= c->slots ? std::max(1, m) : cache_group(c);
-    for (int a = 0; a < m; a += g)
-      groups.emplace_back(missing.begin() + a, missing.begin() + std::min(m, a + g));
-    if (groups.empty()) groups.emplace_back();
-  }
-  const int npass = static_cast<int>(groups.size());
-
-  // the copy stream, the fill mode and per-pass events (host resources of the cache, made once)
-  if (c->zero_copy < 0) FT_TRY(cache_probe_zero_copy(c));
-  if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
-    c->copy_stream = nullptr;
-    return fail(FTMOE_ERR_HIP, "copy stream creation failed");
-  }
-  while (static_cast<int>(c->ev_done.size()) < npass) {
-    hipEvent_t a = nullptr, b = nullptr;
-    FT_HIP(hipEventCreateWithFlags(&a, hipEventDisableTiming), "event creation");
-    if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
-      (void)hipEventDestroy(a);
-      return fail(FTMOE_ERR_HIP, "event creation failed");
-    }
-    c->ev_copied.push_back(a);
-    c->ev_done.push_back(b);
-  }
-
-  // plan every pass; a pass's copies wait for the last earlier pass reading a slot they overwrite
-  int32_t* tab_host = c->pin + n_ids;
-  std::fill(tab_host, tab_host + static_cast<size_t>(npass) * E, -1);
-  c->copy_e.assign(npass, {});
-  c->copy_s.assign(npass, {});
-  c->copy_after.assign(npass, -1);
-  std::vector<int> reader(c->slots, -1);   // last pass of this step that reads each slot
-  std::vector<int32_t> sl(c->slots), miss(c->slots);
-  for (int i = 0; i < npass; ++i) {
-    const int m = static_cast<int>(groups[i].size());
-    FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data()));
-    for (int q = 0; q < m; ++q) {
-      tab_host[static_cast<size_t>(i) * E + groups[i][q]] = sl[q];
-      if (miss[q]) {
-        c->copy_e[i].push_back(groups[i][q]);
-        c->copy_s[i].push_back(sl[q]);
-        c->copy_after[i] = std::max(c->copy_after[i], reader[sl[q]]);
-      }
-    }
-    for (int q = 0; q < m; ++q) reader[sl[q]] = i;
-  }
-  int32_t* tables = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + up256(p.total));
-  FT_HIP(hipMemcpyAsync(tables, tab_host, static_cast<size_t>(npass) * E * 4, hipMemcpyHostToDevice, s),
-         "table copy");
-  std::vector<const int32_t*> tptr(npass);
-  for (int i = 0; i < npass; ++i) tptr[i] = tables + static_cast<size_t>(i) * E;
+  FT_TRY(cache_host_resources(c));
   c->stream = s;
   c->called = true;
-  c->passes += npass;
-  Passes passes;
-  passes.n = npass;
-  passes.tables = tptr.data();
-  passes.before = cache_before_pass;
-  passes.after = cache_after_pass;
-  passes.before_combine = cache_host_rows;
-  passes.ctx = c;
-  return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, passes);
+  c->n_ids = n_ids;
+  c->step_k = k;
+  c->step_T = T;
+  c->tables_dev = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + up256(p.total));
+  FT_HIP(hipMemcpyAsync(c->pin, ids, n_ids * 4, hipMemcpyDeviceToHost, s), "routing copy");
+  FT_HIP(hipEventRecord(c->ev_ids, s), "routing copy event");
+  c->h_n = 0;
+  c->run = Passes{};
+  c->run.ctx = c;
+  if (L->act == FTMOE_ACT_FP8_PER_TENSOR) {
+    // one pass of every expert of the step (the h scale spans them all), planned before it runs
+    FT_TRY(cache_plan_step(c, false));
+    c->run.before = cache_before_pass;
+    c->run.after = cache_after_pass;
+  } else {
+    // The first pass runs at once on the residency table of the last step:
+    // the step's resident experts run while the routing reaches the host;
+    // its hook then plans the misses (more passes) and the host rows.
+    if (c->host_pool) {   // x for the host rows, on the copy stream so that the first pass does not wait
+      FT_TRY(grow_pinned(&c->hx, &c->hx_bytes, static_cast<size_t>(T) * L->hidden * 2));
+      FT_HIP(hipStreamWaitEvent(c->copy_stream, c->ev_ids, 0), "copy stream wait");
+      FT_HIP(hipMemcpyAsync(c->hx, x, static_cast<size_t>(T) * L->hidden * 2, hipMemcpyDeviceToHost,
+                            c->copy_stream),
+             "x copy");
+      FT_HIP(hipEventRecord(c->ev_x, c->copy_stream), "x copy event");
+    }
+    int32_t* resid = reinterpret_cast<int32_t*>(c->pool + c->pl.resid);
+    if (!c->resid_init) {
+      std::fill(c->resid_host, c->resid_host + E, -1);
+      FT_HIP(hipMemcpyAsync(resid, c->resid_host, static_cast<size_t>(E) * 4, hipMemcpyHostToDevice, s),
+             "residency table copy");
+      c->resid_init = true;
+    }
+    c->tptr[0] = resid;
+    c->copy_e.assign(1, {});
+    c->copy_s.assign(1, {});
+    c->copy_after.assign(1, -1);
+    c->run.n = 1;
+    c->run.before = cache_spec_before;
+    c->run.after = cache_spec_after;
+    c->run.before_combine = cache_spec_combine;
+  }
+  c->run.tables = c->tptr.data();
+  return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, c->run);
 }
 
 ftmoe_status ftmoe_cache_set_host_compute(ftmoe_cache* c, int32_t threads, double expert_s, double row_s,

@@ -282,9 +282,10 @@ def _cache(slots, E=8):
     lib = ft.load()
     n = ctypes.c_size_t(0)
     assert lib.ftmoe_cache_pool_size(ctypes.byref(d), slots, ctypes.byref(n)) == ft.OK
-    # 256-aligned regions; per slot: gate_up 256*256/2 + 256*256/32, down 256*128/2 + 256*128/32
+    # 256-aligned regions; per slot: gate_up 256*256/2 + 256*256/32, down 256*128/2 + 256*128/32; then the
+    # residency table of E int32 rounded up to 256 bytes
     assert n.value == slots * (256 * 256 // 2) + slots * (256 * 256 // 32) + slots * (256 * 128 // 2) + \
-        slots * (256 * 128 // 32)
+        slots * (256 * 128 // 32) + (E * 4 + 255) // 256 * 256
     h = ctypes.c_void_p(0)
     gu, dn = _qw(ft.W_MXFP4, E, 256, 256), _qw(ft.W_MXFP4, E, 256, 128)
     assert lib.ftmoe_cache_create(ctypes.byref(d), ctypes.byref(gu), ctypes.byref(dn), slots, FAKE, n.value,

@@ -36,8 +36,9 @@ def cache_forward(cache, x_bits):
 
 class _PoolModel:
     """The residency policy the library documents, replayed on the host: per
-    step, the resident experts form the first pass and the missing ones
-    follow (one pass if they fit beside them, else groups of half the
+    step, the resident experts form the first pass (run at once on the
+    device's residency table, so it exists even when empty) and the missing
+    ones follow (one pass if they fit beside them, else groups of half the
     pool; one pass of everything for per-tensor FP8 activations); each pass
     gives a missing expert the least recently used slot the pass does not
     need."""
@@ -76,10 +77,9 @@ class _PoolModel:
         if self.fp8:
             groups = [hit + miss]
         else:
-            groups = [hit] if hit else []
+            groups = [hit]
             g = max(1, len(miss)) if len(experts) <= self.slots else max(1, self.slots // 2)
             groups += [miss[a:a + g] for a in range(0, len(miss), g)]
-            groups = groups or [[]]
         for grp in groups:
             self._plan(grp)
         self.passes += len(groups)
