@@ -104,7 +104,7 @@ struct Cfg {
 // kXcdChunk consecutive tiles (chunk c to XCD c % 8), so each XCD's L2 sees
 // runs of tiles of the same expert, while the empty tail of the padded block
 // list (the grid covers the largest possible one) is spread over all XCDs.
-constexpr int kXcdChunk = 16;
+constexpr int kXcdChunk = 32;
 __device__ __forceinline__ int logical_tile(int w) {
   const int x = w & 7, li = w >> 3;
   return ((li / kXcdChunk) * 8 + x) * kXcdChunk + li % kXcdChunk;
