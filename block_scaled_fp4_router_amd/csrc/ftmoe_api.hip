@@ -202,7 +202,7 @@ size_t up256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 struct Plan {
   bool decode = false;    // bandwidth-bound decode kernels
   bool small_route = false;  // router via H-sliced partials + fused top-k (T <= kDecodeMaxT)
-  int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0;
+  int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0, rsplit = 1;
   size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
          scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
          hsc = 0, hq = 0, xs = 0, xssc = 0, hgsc = 0, hssc = 0, total = 0;
@@ -236,10 +236,12 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   };
   const size_t tk = static_cast<size_t>(T) * k;
   const size_t obytes = p.decode ? 4 : 2;
-  if (p.small_route)
+  if (p.small_route) {
     p.part = take(static_cast<size_t>(p.S) * T * (E + 1) * 4);
-  else
-    p.logits = take(static_cast<size_t>(T) * (E + 1) * 4);
+  } else {
+    p.rsplit = router_splits_gemm(T, L->hidden, E + (L->shared_inter > 0 ? 1 : 0));
+    p.logits = take(static_cast<size_t>(p.rsplit) * T * (E + 1) * 4);
+  }
   p.ids = take(tk * 4);
   p.w = take(tk * 4);
   p.sg = take(static_cast<size_t>(T) * 4);
@@ -353,8 +355,8 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
          "router logits launch");
   FT_HIP(timed("topk", s,
                [&] {
-                 return launch_topk(logits, T, E, k, L->router_bias, L->router_bias_mode == FTMOE_BIAS_SELECT,
-                                    shared, ids, w, sg, s);
+                 return launch_topk(logits, p.rsplit, T, E, k, L->router_bias,
+                                    L->router_bias_mode == FTMOE_BIAS_SELECT, shared, ids, w, sg, s);
                }),
          "top-k launch");
   return FTMOE_OK;

@@ -76,11 +76,13 @@ struct Rows {
 };
 
 // ---- router ----
+// logits [S][T][E+1] fp32, S = router_splits_gemm(T, H, rows) K splits (rows = E + shared).
+int router_splits_gemm(int T, int H, int rows);
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
                                 const float* shared_gate_w, float* logits, hipStream_t s);
 // bias_select: the bias ranks the experts only; the weights are the softmax
 // of the selected logits without it.
-hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool bias_select,
+hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, const float* bias, bool bias_select,
                        bool has_shared, int32_t* ids, float* w, float* sgate, hipStream_t s);
 
 // ---- align ----

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
                                                                 const float* __restrict__ router_w, int E,
                                                                 const float* __restrict__ shared_gate_w,
                                                                 float* __restrict__ logits) {
+  // blockIdx.z: the K split; split z sums H range [z, z + 1) * H / gridDim.z into logits[z]
   __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
   const int rows = E + (shared_gate_w ? 1 : 0);
@@ -125,12 +126,15 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
   };
 
   f32x16 acc = {};
-  load(0);
-  for (int k0 = 0; k0 < H; k0 += kRK) {
+  const int kspan = H / static_cast<int>(gridDim.z), kbeg = static_cast<int>(blockIdx.z) * kspan;
+  const int kend = kbeg + kspan;
+  logits += static_cast<size_t>(blockIdx.z) * T * (E + 1);
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kRK) {
     __syncthreads();   // the previous stage's reads are done
     store();
     __syncthreads();
-    if (k0 + kRK < H) load(k0 + kRK);
+    if (k0 + kRK < kend) load(k0 + kRK);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
@@ -152,6 +156,17 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
   }
 }
 
+// K splits of the router GEMM: enough tiles to cover the compute units
+// (the top-k kernel adds the splits in order, so the logits stay
+// deterministic).
+int router_splits_gemm(int T, int H, int rows) {
+  if (T <= kGemvMaxT) return 1;
+  const long long tiles = static_cast<long long>((T + kRT - 1) / kRT) * ((rows + kRE - 1) / kRE);
+  int S = 1;
+  while (S < 4 && tiles * S < 256 && (H / kRK) % (2 * S) == 0) S *= 2;
+  return S;
+}
+
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
                                 const float* shared_gate_w, float* logits, hipStream_t s) {
   const int rows = E + (shared_gate_w ? 1 : 0);
@@ -164,7 +179,7 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
     else
       return launch(router_gemv_kernel<kGemvMaxT>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   } else {
-    dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE);
+    dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE, router_splits_gemm(T, H, rows));
     return launch(router_gemm_kernel, grid, dim3(kRThreads), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   }
 }
@@ -239,7 +254,7 @@ __device__ __forceinline__ float lanes_softmax(float l, int k) {
 }
 
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit, int T, int E, int k,
                                                    const float* __restrict__ bias, int bias_select, int has_shared,
                                                    int32_t* __restrict__ ids, float* __restrict__ w,
                                                    float* __restrict__ sgate) {
@@ -247,23 +262,29 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   const int lane = lane_id();
   const float* row = logits + static_cast<size_t>(t) * (E + 1);
+  const size_t split = static_cast<size_t>(T) * (E + 1);
+  auto logit = [&](int e) {   // the K splits added in order
+    float l = row[e];
+    for (int z = 1; z < nsplit; ++z) l += row[z * split + e];
+    return l;
+  };
   float v[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + i * kWave;
     v[i] = -__builtin_inff();
-    if (e < E) v[i] = row[e] + (bias ? bias[e] : 0.f);
+    if (e < E) v[i] = logit(e) + (bias ? bias[e] : 0.f);
   }
   int sel_i;
   float sel_w;
   wave_topk_softmax<SLOTS>(v, k, &sel_i, &sel_w);
-  if (bias && bias_select) sel_w = lanes_softmax(lane < k ? row[sel_i] : 0.f, k);
+  if (bias && bias_select) sel_w = lanes_softmax(lane < k ? logit(sel_i) : 0.f, k);
   if (lane < k) {
     ids[static_cast<size_t>(t) * k + lane] = sel_i;
     w[static_cast<size_t>(t) * k + lane] = sel_w;
   }
   if (has_shared && lane == 0) {
-    const float g = row[E];
+    const float g = logit(E);
     sgate[t] = 1.0f / (1.0f + expf(-g));
   }
 }
@@ -278,11 +299,11 @@ static hipError_t with_slots(int E, F&& f) {
   return f.template operator()<16>();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, const float* bias, bool bias_select,
+hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, const float* bias, bool bias_select,
                        bool has_shared, int32_t* ids, float* w, float* sgate, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   return with_slots(E, [&]<int SL>() {
-    return launch(topk_kernel<SL>, grid, dim3(256), 0, s, logits, T, E, k, bias, bias_select ? 1 : 0,
+    return launch(topk_kernel<SL>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, bias, bias_select ? 1 : 0,
                   has_shared ? 1 : 0, ids, w, sgate);
   });
 }
