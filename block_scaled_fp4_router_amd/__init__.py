@@ -35,7 +35,7 @@ BIAS_CODES = {"logits": BIAS_LOGITS, "select": BIAS_SELECT}
 
 # Every symbol include/ftmoe.h declares.
 EXPORTS = (
-    "ftmoe_workspace_size", "ftmoe_align_max_padded", "ftmoe_align_workspace_size", "ftmoe_route",
+    "ftmoe_workspace_bytes", "ftmoe_workspace_size", "ftmoe_align_max_padded", "ftmoe_align_workspace_size", "ftmoe_route",
     "ftmoe_align", "ftmoe_experts_forward", "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor",
     "ftmoe_timing_enable", "ftmoe_timing_collect", "ftmoe_status_string", "ftmoe_last_error", "ftmoe_version",
     "ftmoe_packed_size", "ftmoe_pack_qweight", "ftmoe_cache_pool_size", "ftmoe_cache_create",
@@ -87,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     P = ctypes.POINTER
     lib.ftmoe_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
+    lib.ftmoe_workspace_bytes.argtypes = [P(LayerDesc), i32]
+    lib.ftmoe_workspace_bytes.restype = sz
     lib.ftmoe_align_max_padded.argtypes = [i32, i32, i32, i32]
     lib.ftmoe_align_max_padded.restype = i32
     lib.ftmoe_align_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -285,6 +287,12 @@ def workspace_size(layer: DeviceLayer, T: int) -> int:
     d = layer.desc()
     _check(load().ftmoe_workspace_size(ctypes.byref(d), T, ctypes.byref(n)))
     return n.value
+
+
+def workspace_bytes(layer: DeviceLayer, T: int) -> int:
+    """ftmoe_workspace_bytes: the same query as workspace_size, 0 on bad arguments."""
+    d = layer.desc()
+    return load().ftmoe_workspace_bytes(ctypes.byref(d), T)
 
 
 def align_max_padded(T: int, k: int, E: int, block_m: int) -> int:

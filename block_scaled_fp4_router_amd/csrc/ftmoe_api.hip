@@ -633,9 +633,11 @@ struct ftmoe_cache {
   uint8_t* pool = nullptr;
   std::vector<int> slot_expert, expert_slot;   // -1: empty / not resident
   std::vector<int64_t> last_use;               // per slot; -1: never
+  std::vector<char> filled;                    // per slot: its expert's bytes are in it (or their copy is enqueued)
   int64_t clock = 0, hits = 0, misses = 0, bytes = 0, passes = 0;
   // copies run on their own stream, ordered against the passes by events
   hipStream_t copy_stream = nullptr;
+  hipStream_t x_stream = nullptr;              // device -> host copies of x for host-computed rows
   std::vector<hipEvent_t> ev_copied, ev_done;  // per pass: its copies landed / its kernels ran
   // per-call state
   int32_t* pin = nullptr;                      // pinned host words: the routing ids [T*k], then the
@@ -677,10 +679,11 @@ struct ftmoe_cache {
   int h_n = 0, h_T = 0;
 
   ~ftmoe_cache() {
-    if (copy_stream) {
-      (void)hipStreamSynchronize(copy_stream);
-      (void)hipStreamDestroy(copy_stream);
-    }
+    for (hipStream_t* st : {&copy_stream, &x_stream})
+      if (*st) {
+        (void)hipStreamSynchronize(*st);
+        (void)hipStreamDestroy(*st);
+      }
     if (pin) (void)hipHostFree(pin);
     if (resid_host) (void)hipHostFree(resid_host);
     if (ev_ids) (void)hipEventDestroy(ev_ids);
@@ -695,8 +698,15 @@ struct ftmoe_cache {
 
 namespace {
 
-// The LRU policy (see ftmoe_cache_plan).
-ftmoe_status cache_plan(ftmoe_cache* c, const int32_t* experts, int n, int32_t* out_slot, int32_t* out_miss) {
+// An expert whose bytes are in (or on their way to) its slot.
+bool resident(const ftmoe_cache* c, int e) { return c->expert_slot[e] >= 0 && c->filled[c->expert_slot[e]]; }
+
+// The LRU policy (see ftmoe_cache_plan).  `fill`: the caller enqueues the
+// copies of the misses (a forward); otherwise (a plan alone) the slots given
+// to missing experts stay unfilled, and a later forward copies into them.
+// A planned but unfilled expert keeps its slot and counts as a miss again.
+ftmoe_status cache_plan(ftmoe_cache* c, const int32_t* experts, int n, int32_t* out_slot, int32_t* out_miss,
+                        bool fill) {
   if (n > c->slots)
     return fail(FTMOE_ERR_UNSUPPORTED, "%d experts do not fit %d slots", n, c->slots);
   std::vector<char> seen(c->E, 0), needed(c->slots, 0);
@@ -717,12 +727,15 @@ ftmoe_status cache_plan(ftmoe_cache* c, const int32_t* experts, int n, int32_t* 
   for (int i = 0; i < n; ++i) {
     const int e = experts[i];
     int sl = c->expert_slot[e];
-    const bool miss = sl < 0;
-    if (miss) {
+    const bool miss = !resident(c, e);
+    if (sl < 0) {
       sl = cand[next++];
       if (c->slot_expert[sl] >= 0) c->expert_slot[c->slot_expert[sl]] = -1;
       c->slot_expert[sl] = e;
       c->expert_slot[e] = sl;
+    }
+    if (miss) {
+      c->filled[sl] = fill ? 1 : 0;
       ++c->misses;
     } else {
       ++c->hits;
@@ -937,10 +950,11 @@ int cache_max_passes(const ftmoe_cache* c);
 int cache_group(const ftmoe_cache* c);
 ftmoe_status cache_host_resources(ftmoe_cache* c) {
   if (c->zero_copy < 0) FT_TRY(cache_probe_zero_copy(c));
-  if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
-    c->copy_stream = nullptr;
-    return fail(FTMOE_ERR_HIP, "copy stream creation failed");
-  }
+  for (hipStream_t* st : {&c->copy_stream, &c->x_stream})
+    if (!*st && hipStreamCreateWithFlags(st, hipStreamNonBlocking) != hipSuccess) {
+      *st = nullptr;
+      return fail(FTMOE_ERR_HIP, "copy stream creation failed");
+    }
   if (!c->ev_ids) FT_HIP(hipEventCreateWithFlags(&c->ev_ids, hipEventDisableTiming), "event creation");
   if (!c->ev_x) FT_HIP(hipEventCreateWithFlags(&c->ev_x, hipEventDisableTiming), "event creation");
   if (!c->resid_host) {
@@ -979,7 +993,7 @@ ftmoe_status cache_plan_step(ftmoe_cache* c, bool spec) {
   for (size_t i = 0; i < n_ids; ++i) ++rows[ids_host[i]];
   std::vector<int> hit, missing;
   for (int e = 0; e < E; ++e)
-    if (rows[e]) (c->expert_slot[e] >= 0 ? hit : missing).push_back(e);
+    if (rows[e]) (resident(c, e) ? hit : missing).push_back(e);
   // co-execution: some missing experts computed on the host instead of filled
   c->h_n = 0;
   const int q = host_split(c, missing, rows);
@@ -1040,7 +1054,7 @@ ftmoe_status cache_plan_step(ftmoe_cache* c, bool spec) {
   std::vector<int32_t> sl(c->slots), miss(c->slots);
   for (int i = 0; i < npass; ++i) {
     const int m = static_cast<int>(groups[i].size());
-    FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data()));
+    FT_TRY(cache_plan(c, groups[i].data(), m, sl.data(), miss.data(), true));
     for (int qq = 0; qq < m; ++qq) {
       if (i >= first) tab_host[static_cast<size_t>(i - first) * E + groups[i][qq]] = sl[qq];
       if (miss[qq]) {
@@ -1082,7 +1096,7 @@ ftmoe_status cache_spec_after(void* ctx, int i) {
 ftmoe_status cache_spec_combine(void* ctx, void* o, bool fp32) {
   ftmoe_cache* c = static_cast<ftmoe_cache*>(ctx);
   FT_TRY(cache_host_rows(ctx, o, fp32));
-  for (int e = 0; e < c->E; ++e) c->resid_host[e] = c->expert_slot[e];
+  for (int e = 0; e < c->E; ++e) c->resid_host[e] = resident(c, e) ? c->expert_slot[e] : -1;
   FT_HIP(hipMemcpyAsync(c->pool + c->pl.resid, c->resid_host, static_cast<size_t>(c->E) * 4, hipMemcpyHostToDevice,
                         c->stream),
          "residency table copy");
@@ -1108,6 +1122,11 @@ ftmoe_status ftmoe_workspace_size(const ftmoe_layer* layer, int32_t T, size_t* b
   if (!bytes) return fail(FTMOE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = make_plan(layer, T).total;
   return FTMOE_OK;
+}
+
+size_t ftmoe_workspace_bytes(const ftmoe_layer* layer, int32_t T) {
+  size_t n = 0;
+  return ftmoe_workspace_size(layer, T, &n) == FTMOE_OK ? n : 0;
 }
 
 int32_t ftmoe_align_max_padded(int32_t T, int32_t k, int32_t E, int32_t block_m) {
@@ -1345,6 +1364,7 @@ ftmoe_status ftmoe_cache_create(const ftmoe_layer* layer, const ftmoe_qweight* h
   c->slot_expert.assign(slots, -1);
   c->expert_slot.assign(E, -1);
   c->last_use.assign(slots, -1);
+  c->filled.assign(slots, 0);
   *cache = c;
   return FTMOE_OK;
 }
@@ -1355,7 +1375,11 @@ ftmoe_status ftmoe_cache_plan(ftmoe_cache* cache, const int32_t* experts, int32_
                               int32_t* out_miss) {
   g_last_error.clear();
   if (!cache || (n > 0 && !experts) || n < 0) return fail(FTMOE_ERR_INVALID_ARG, "bad arguments");
-  return cache_plan(cache, experts, n, out_slot, out_miss);
+  FT_TRY(cache_plan(cache, experts, n, out_slot, out_miss, false));
+  // evicted experts are gone from their slots: the device residency table
+  // the next forward's first pass reads is rewritten from the host state
+  cache->resid_init = false;
+  return FTMOE_OK;
 }
 
 ftmoe_status ftmoe_cache_workspace_size(const ftmoe_cache* cache, int32_t T, size_t* bytes) {
@@ -1378,10 +1402,12 @@ ftmoe_status ftmoe_cache_forward(ftmoe_cache* c, const uint16_t* x, int32_t T, v
     // a runtime failure after planning may leave slots marked resident whose fills never ran: forget them all
     // (finishing what was enqueued first, so that no fill lands in a slot after it is reassigned)
     if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
+    if (c->x_stream) (void)hipStreamSynchronize(c->x_stream);
     if (c->called) (void)hipStreamSynchronize(c->stream);
     std::fill(c->slot_expert.begin(), c->slot_expert.end(), -1);
     std::fill(c->expert_slot.begin(), c->expert_slot.end(), -1);
     std::fill(c->last_use.begin(), c->last_use.end(), -1);
+    std::fill(c->filled.begin(), c->filled.end(), 0);
     c->resid_init = false;   // the device residency table is rewritten on the next call
   }
   return st;
@@ -1433,17 +1459,21 @@ static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_
     // The first pass runs at once on the residency table of the last step:
     // the step's resident experts run while the routing reaches the host;
     // its hook then plans the misses (more passes) and the host rows.
-    if (c->host_pool) {   // x for the host rows, on the copy stream so that the first pass does not wait
-      FT_TRY(grow_pinned(&c->hx, &c->hx_bytes, static_cast<size_t>(T) * L->hidden * 2));
-      FT_HIP(hipStreamWaitEvent(c->copy_stream, c->ev_ids, 0), "copy stream wait");
-      FT_HIP(hipMemcpyAsync(c->hx, x, static_cast<size_t>(T) * L->hidden * 2, hipMemcpyDeviceToHost,
-                            c->copy_stream),
+    if (c->host_pool) {
+      // x for the host rows, on a stream of its own: neither the first pass
+      // nor the pool fills (on the copy stream) queue behind it
+      const size_t xb = static_cast<size_t>(T) * L->hidden * 2;
+      // the last call's x copy may still be writing the buffer that grows
+      if (c->hx && xb > c->hx_bytes) FT_HIP(hipStreamSynchronize(c->x_stream), "x stream");
+      FT_TRY(grow_pinned(&c->hx, &c->hx_bytes, xb));
+      FT_HIP(hipStreamWaitEvent(c->x_stream, c->ev_ids, 0), "x stream wait");
+      FT_HIP(hipMemcpyAsync(c->hx, x, static_cast<size_t>(T) * L->hidden * 2, hipMemcpyDeviceToHost, c->x_stream),
              "x copy");
-      FT_HIP(hipEventRecord(c->ev_x, c->copy_stream), "x copy event");
+      FT_HIP(hipEventRecord(c->ev_x, c->x_stream), "x copy event");
     }
     int32_t* resid = reinterpret_cast<int32_t*>(c->pool + c->pl.resid);
     if (!c->resid_init) {
-      std::fill(c->resid_host, c->resid_host + E, -1);
+      for (int e = 0; e < E; ++e) c->resid_host[e] = resident(c, e) ? c->expert_slot[e] : -1;
       FT_HIP(hipMemcpyAsync(resid, c->resid_host, static_cast<size_t>(E) * 4, hipMemcpyHostToDevice, s),
              "residency table copy");
       c->resid_init = true;

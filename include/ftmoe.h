@@ -2,10 +2,12 @@
  * ftmoe.h -- routed Mixture-of-Experts layer forward over block-quantised
  * expert weights (MXFP4, NVFP4, FP8 E4M3) on AMD Instinct MI355X (gfx950).
  *
- * The FreeToken README ("About": an edge-native Mixture-of-Experts serving
- * engine; "Broad MoE & Ecosystem Support": MXFP4, NVFP4, FP8, BF16 formats)
- * names the layer and its weight formats but never writes its arithmetic.
- * This library computes the standard routed SwiGLU MoE layer:
+ * Sources: the FreeToken README.  Its "About" section presents the project
+ * as an engine that serves Mixture-of-Experts models on consumer hardware;
+ * its "Broad MoE & Ecosystem Support" item lists the MoE model families it
+ * runs and the expert weight formats MXFP4, NVFP4, FP8 and BF16.  Neither
+ * writes the layer's arithmetic down.  The reading taken here (the routed
+ * MoE layer of those model families, with SwiGLU experts) is:
  *
  *   l[t,e]   = x_t . W_r[e] + b[e]                       router GEMM
  *   ids_t    = k largest l[t,:], descending, ties -> lower expert index
@@ -192,7 +194,11 @@ ftmoe_status ftmoe_pack_qweight(const ftmoe_qweight* w, int32_t role, void* pack
 /* Bytes of workspace that ftmoe_forward / ftmoe_experts_forward /
  * ftmoe_route need for T tokens of this layer (T >= 0).  The workspace must
  * be 256-byte aligned; its contents need no initialisation and are
- * meaningless after a call.                                               */
+ * meaningless after a call.
+ *  ftmoe_workspace_bytes returns the size directly, or 0 when the layer or
+ *  T is invalid (ftmoe_last_error() says why; a valid query is never 0).
+ *  ftmoe_workspace_size is the same query with a status.                  */
+size_t ftmoe_workspace_bytes(const ftmoe_layer* layer, int32_t T);
 ftmoe_status ftmoe_workspace_size(const ftmoe_layer* layer, int32_t T, size_t* bytes);
 
 /* Capacity of the padded expert-sorted row list written by ftmoe_align:
@@ -204,7 +210,15 @@ int32_t ftmoe_align_max_padded(int32_t T, int32_t k, int32_t E, int32_t block_m)
 size_t ftmoe_align_workspace_size(int32_t T, int32_t k, int32_t E, int32_t block_m);
 
 /* Router: logits, softmax top-k with renormalised weights, and the shared
- * expert's sigmoid gate.
+ * expert's sigmoid gate (the first two lines of the layer arithmetic at the
+ * top of this file).  Source: FreeToken README, "Broad MoE & Ecosystem
+ * Support" (the MoE model families it serves); the pages give no formula.
+ * Reading: the routing of those families -- every token goes to the k
+ * experts of largest router logit, weighted by a softmax over those k
+ * logits, and a shared expert is gated by the sigmoid of the token's
+ * projection on a gate vector; logits accumulate in fp32 from the exact
+ * widening of bf16 x against fp32 W_r (never rounded to a narrower type),
+ * and ties go to the lower expert index.
  *  x           [T][H] bf16.
  *  topk_ids    [T][k] int32 out: experts by descending logit.
  *  topk_w      [T][k] fp32 out: softmax over the k selected logits.
@@ -216,7 +230,12 @@ ftmoe_status ftmoe_route(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
                          int32_t* topk_ids, float* topk_w, float* shared_gate,
                          void* stream);
 
-/* Token-to-expert alignment (count, prefix-sum, padded scatter).
+/* Token-to-expert alignment (count, prefix-sum, padded scatter): the
+ * grouping that lets each expert's routed rows run as one GEMM over whole
+ * blocks.  Source: FreeToken README, "About" (MoE serving); the pages do
+ * not describe the grouping.  Reading: a stable counting sort of the flat
+ * rows by expert, each expert's segment padded to a multiple of block_m,
+ * so that the result is unique.
  * Flat row i = t*k + j goes to expert topk_ids[i] (each in [0, E)).
  *  counts       [E]     rows per expert.
  *  offsets      [E+1]   exclusive prefix sum of counts rounded up to block_m.
@@ -234,7 +253,16 @@ ftmoe_status ftmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t 
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Experts given a routing: align, gate_up GEMM with fused SwiGLU, down GEMM,
- * weighted combine and the optional gated shared expert.
+ * weighted combine and the optional gated shared expert (lines 3-6 of the
+ * layer arithmetic at the top of this file).  Source: FreeToken README,
+ * "Broad MoE & Ecosystem Support" (MoE families whose experts are stored
+ * as MXFP4, NVFP4, FP8 or BF16 weights) and the FreeToken commit page of
+ * commit 58f4b9e (its message on FP8 projections with per-tensor
+ * activation scales, for FTMOE_ACT_FP8_PER_TENSOR); the pages give no
+ * formula.  Reading: SwiGLU experts with the gate rows first in gate_up,
+ * h = silu(gate) * up, the k expert outputs summed in ascending slot order,
+ * the gated shared expert added last, y rounded once to bf16; h may be
+ * rounded to bf16 between the GEMMs.
  *  topk_ids, topk_w  as written by ftmoe_route.
  *  shared_gate       [T] fp32 sigmoid gate, required iff shared_inter > 0.
  *  y                 [T][H] bf16 out (round to nearest even).             */
@@ -243,7 +271,9 @@ ftmoe_status ftmoe_experts_forward(const ftmoe_layer* layer, const uint16_t* x, 
                                    const float* shared_gate,
                                    void* ws, size_t ws_bytes, uint16_t* y, void* stream);
 
-/* The whole layer: ftmoe_route then ftmoe_experts_forward.
+/* The whole layer: ftmoe_route then ftmoe_experts_forward (the full layer
+ * arithmetic at the top of this file; sources and readings as for those
+ * two entry points).
  *  topk_ids_out / topk_w_out: optional [T][k] copies of the routing (NULL
  *  to keep it in the workspace only).                                    */
 ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
@@ -285,10 +315,14 @@ void ftmoe_cache_destroy(ftmoe_cache* cache);
 
 /* The residency policy (host only, no device work): for the n distinct
  * experts one step needs (each in [0, E), distinct), gives each a slot:
- * a resident expert keeps its slot (a hit); a missing one (a miss, out_miss
- * = 1, to be copied) takes the least recently used slot that this step does
- * not need, evicting its expert.  Every expert of the step then counts as
- * used now.  FTMOE_ERR_UNSUPPORTED if n > slots (nothing changes).       */
+ * an expert that holds a slot keeps it; another takes the least recently
+ * used slot that this step does not need, evicting its expert.  Every
+ * expert of the step then counts as used now.  out_miss = 0 (a hit) when
+ * the expert's bytes are in its slot, 1 (a miss) when they must be copied
+ * there.  This call copies nothing: the slots it gives stay unfilled, and
+ * the next ftmoe_cache_forward that routes to such an expert copies it
+ * (a miss then too); evicted experts are gone from the pool at once.
+ * FTMOE_ERR_UNSUPPORTED if n > slots (nothing changes).                  */
 ftmoe_status ftmoe_cache_plan(ftmoe_cache* cache, const int32_t* experts, int32_t n, int32_t* out_slot,
                               int32_t* out_miss);
 

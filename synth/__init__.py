@@ -21,3 +21,4 @@ from .layers import (  # noqa: F401
     e2m1_encode,
     e4m3_encode,
 )
+from .crafted import CRAFTED, WIDE, crafted_layer, crafted_tokens  # noqa: F401,E402

@@ -294,8 +294,11 @@ def _cache(slots, E=8):
 
 
 class _LRU:
-    """The policy written out: hits keep their slot; misses take free slots by
-    (last use, slot index), never used first."""
+    """The policy written out: an expert holding a slot keeps it; the others
+    take free slots by (last use, slot index), never used first.  A plan on
+    its own copies nothing, so every expert it lists still has to be copied
+    (a miss) until a forward fills its slot; the slots are the same either
+    way."""
 
     def __init__(self, slots):
         self.slot_of, self.exp_of, self.last, self.clock = {}, [None] * slots, [-1] * slots, 0
@@ -307,14 +310,14 @@ class _LRU:
         out = []
         for e in experts:
             if e in self.slot_of:
-                s, miss = self.slot_of[e], 0
+                s = self.slot_of[e]
             else:
-                s, miss = free.pop(0), 1
+                s = free.pop(0)
                 if self.exp_of[s] is not None:
                     del self.slot_of[self.exp_of[s]]
                 self.exp_of[s], self.slot_of[e] = e, s
             self.last[s] = self.clock
-            out.append((s, miss))
+            out.append((s, 1))
         return out
 
 
@@ -346,3 +349,68 @@ def test_cache_plan_is_lru():
         e = np.array(bad, np.int32)
         assert lib.ftmoe_cache_plan(h, e.ctypes.data, len(e), None, None) == status
     lib.ftmoe_cache_destroy(h)
+
+
+# The boundary's contract: the names and C signatures of the layer entry
+# points.  Two documented deviations add caller scratch to ftmoe_route and
+# ftmoe_align (the library never allocates device memory), marked "+ws".
+CONTRACT = {
+    "ftmoe_workspace_bytes": ("size_t", ["const ftmoe_layer*", "int32_t"]),
+    "ftmoe_align_max_padded": ("int32_t", ["int32_t", "int32_t", "int32_t", "int32_t"]),
+    "ftmoe_route": ("ftmoe_status", ["const ftmoe_layer*", "const uint16_t*", "int32_t", "+ws", "int32_t*",
+                                     "float*", "float*", "void*"]),
+    "ftmoe_align": ("ftmoe_status", ["const int32_t*", "int32_t", "int32_t", "int32_t", "int32_t", "int32_t*",
+                                     "int32_t*", "int32_t*", "int32_t*", "int32_t*", "+ws", "void*"]),
+    "ftmoe_experts_forward": ("ftmoe_status", ["const ftmoe_layer*", "const uint16_t*", "int32_t",
+                                               "const int32_t*", "const float*", "const float*", "void*", "size_t",
+                                               "uint16_t*", "void*"]),
+    "ftmoe_forward": ("ftmoe_status", ["const ftmoe_layer*", "const uint16_t*", "int32_t", "void*", "size_t",
+                                       "uint16_t*", "int32_t*", "float*", "void*"]),
+    "ftmoe_status_string": ("const char*", ["ftmoe_status"]),
+}
+
+
+def header_prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][A-Za-z0-9_ ]*?\s*\*?)\s*\b(ftmoe_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        ret = " ".join(m.group(1).replace("*", " * ").split()).replace(" *", "*")
+        params = []
+        for p in m.group(3).split(","):
+            p = " ".join(p.replace("*", " * ").split())
+            if not p or p == "void":
+                continue
+            words = p.split(" ")
+            # drop the parameter name (the last word unless it is part of the type)
+            if words[-1] not in ("*",) and len(words) > 1 and words[-1] not in ("int32_t", "size_t", "float"):
+                words = words[:-1]
+            params.append(" ".join(words).replace(" *", "*"))
+        out[m.group(2)] = (ret, params)
+    return out
+
+
+def test_contract_names_and_signatures():
+    protos = header_prototypes()
+    for name, (ret, params) in CONTRACT.items():
+        assert name in protos, name
+        got_ret, got = protos[name]
+        assert got_ret == ret, (name, got_ret)
+        want = []
+        for p in params:
+            want += ["void*", "size_t"] if p == "+ws" else [p]
+        assert got == want, (name, got)
+
+
+@needs_lib
+def test_workspace_bytes_matches_workspace_size():
+    lib = ft.load()
+    d = good_layer()
+    for T in (0, 1, 8, 16, 17, 4096):
+        n = ctypes.c_size_t(0)
+        assert lib.ftmoe_workspace_size(ctypes.byref(d), T, ctypes.byref(n)) == ft.OK
+        assert lib.ftmoe_workspace_bytes(ctypes.byref(d), T) == n.value > 0
+    assert lib.ftmoe_workspace_bytes(ctypes.byref(d), -1) == 0
+    assert lib.ftmoe_workspace_bytes(None, 4) == 0
+    d.hidden = 100
+    assert lib.ftmoe_workspace_bytes(ctypes.byref(d), 4) == 0
+    assert b"hidden" in lib.ftmoe_last_error()

@@ -226,3 +226,31 @@ def test_host_compute_refuses_fp8_per_tensor_layers():
         cache.set_host_compute(2)
     assert err.value.status == ft.ERR_UNSUPPORTED
     cache.close()
+
+
+@pytest.mark.parametrize("path,T", [("decode", 8), ("prefill", 40)])
+@pytest.mark.timeout(600)
+def test_plan_then_forward_equals_device_layer(path, T):
+    """A plan on its own (ftmoe_cache_plan) copies nothing: the experts it
+    places, and the ones it evicts, must not count as resident in the next
+    forward, whose output stays bit-equal to the device layer's."""
+    say(f"expert cache plan then forward c1 T={T} path={path}")
+    lay, dlay = layer_pair("c1")
+    xa = synth.make_tokens(lay, T, stream=41)
+    xb = synth.make_tokens(lay, T, stream=42)
+    cache = ft.ExpertCache.from_host(lay, 48, DEV, path=path)
+    ya, ids_a, _ = cache_forward(cache, xa)            # fills the pool with step a's experts
+    ref_b = run_forward(dlay, xb, path)
+    ids_b = ref_b[1]
+    # plan b's experts, and then a's again (evicting some of b's placements
+    # and re-placing a's resident experts), without any copy
+    eb = np.unique(ids_b)
+    ea = np.unique(ids_a)
+    cache.plan(eb[:40])
+    sl, miss = cache.plan(ea[:40])
+    assert miss.sum() >= 0
+    yb, idsb, wb = cache_forward(cache, xb)
+    assert np.array_equal(idsb, ids_b) and np.array_equal(wb, ref_b[2])
+    assert np.array_equal(yb, ref_b[0]), "pool forward after a plan differs from the device layer"
+    ya2, _, _ = cache_forward(cache, xa)
+    assert np.array_equal(ya2, ya)

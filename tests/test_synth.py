@@ -47,3 +47,26 @@ def test_bf16_rounding_is_nearest_even():
     assert back[1] == 1.0           # exact tie 1 + 2^-8 -> even (1.0)
     assert back[4] == 1.0
     assert back[2] == np.float32(1.0078125)  # a quarter ulp above rounds down
+
+
+def test_crafted_layers_cover_every_code():
+    """The edge-case layers hold what their names promise: every E8M0 scale
+    code 0..254, every non-negative finite E4M3 block scale 0..126, and all
+    254 finite E4M3 weight codes; their tokens are finite bf16 of the
+    intended sizes, and the top-k gap holds."""
+    from synth.crafted import crafted_layer, crafted_tokens
+    mx = crafted_layer("mx_e8m0")
+    assert set(np.unique(mx.gate_up.block_scales[0])) >= set(range(255))
+    nv = crafted_layer("nv_e4m3")
+    assert set(np.unique(nv.gate_up.block_scales)) == set(range(127))
+    f8 = crafted_layer("fp8_all")
+    assert set(np.unique(f8.gate_up.codes[0])) == set(range(256)) - {0x7F, 0xFF}
+    for lay, wide in ((mx, False), (nv, False), (f8, False), (crafted_layer("wide_mx"), True)):
+        x = crafted_tokens(lay, 9, wide=wide)
+        xf = synth.bf16_bits_to_f32(x)
+        assert np.isfinite(xf).all() and x.shape == (9, lay.cfg.hidden)
+        nz = np.abs(xf[xf != 0])
+        assert nz.min() >= 2.0 ** -126   # no bf16 subnormals
+    xw = synth.bf16_bits_to_f32(crafted_tokens(crafted_layer("wide_mx"), 64, wide=True))
+    blk = np.abs(xw.reshape(64, -1, 32))
+    assert np.median(blk.max(axis=2) / blk.min(axis=2)) > 2.0 ** 12   # wide range inside a 32-block
