@@ -76,18 +76,41 @@ __device__ __forceinline__ void fp4x8_to_bf16(uint32_t w, float scale, uint32_t 
   out[3] = __builtin_bit_cast(uint32_t, p3);
 }
 
-// Eight E2M1 nibbles times an arbitrary fp32 factor -> four bf16 pairs.
-// Used for NVFP4, whose E4M3 block scale is not a power of two: the product
-// of a 2-bit and a 4-bit significand fits bf16's 8 bits, so it is exact.
-__device__ __forceinline__ void fp4x8_to_bf16_mul(uint32_t w, float factor, uint32_t out[4]) {
-  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  out[0] = pack_bf16x2(v0[0] * factor, v0[1] * factor);
-  out[1] = pack_bf16x2(v1[0] * factor, v1[1] * factor);
-  out[2] = pack_bf16x2(v2[0] * factor, v2[1] * factor);
-  out[3] = pack_bf16x2(v3[0] * factor, v3[1] * factor);
+// Two fp32 values that are exactly representable in bf16 -> their bf16
+// pair, by the hardware conversion (one instruction; no rounding happens).
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
+  const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// The significand of an NVFP4 block scale s (decoded E4M3, finite) with its
+// sign, as an fp32 in [1, 2) (0 for a zero scale): s = 2^floor(log2|s|) times it.
+__device__ __forceinline__ float nv_scale_significand(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (b & 0x7FFFFFFFu) ? __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u) : 0.0f;
+}
+
+// Eight E2M1 nibbles times an NVFP4 block scale s -> four bf16 pairs, exactly.
+// The scaled conversion applies s's power of two (it reads only the exponent
+// field of its scale operand), one multiply its significand `sig`
+// (nv_scale_significand(s)); E2M1 has 2 significant bits and E4M3 4, so each
+// product fits bf16's 8 and the final conversion does not round.
+__device__ __forceinline__ void fp4x8_to_bf16_nv(uint32_t w, float s, float sig, uint32_t out[4]) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+  out[0] = pack_exact_bf16x2(v0[0] * sig, v0[1] * sig);
+  out[1] = pack_exact_bf16x2(v1[0] * sig, v1[1] * sig);
+  out[2] = pack_exact_bf16x2(v2[0] * sig, v2[1] * sig);
+  out[3] = pack_exact_bf16x2(v3[0] * sig, v3[1] * sig);
+}
+
+// Four E4M3 codes (one dword) -> two bf16 pairs, exactly (every E4M3 value is
+// a bf16 value).
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t out[2]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 // fp32 -> E4M3FN code: round to nearest even, saturate to +-448.  The

@@ -441,20 +441,18 @@ __device__ __forceinline__ typename WSliceT<WFMT>::type load_wslice(const QW& w,
 __device__ __forceinline__ bf16x8 nvfp4_bf16(const WSlice4& s, int st) {
   uint32_t o[4];
   const uint32_t word = st == 0 ? s.c.x : st == 1 ? s.c.y : st == 2 ? s.c.z : s.c.w;
-  fp4x8_to_bf16_mul(word, e4m3_to_f32((s.sc >> (st < 2 ? 0 : 8)) & 0xFF), o);
+  const float sc = e4m3_to_f32((s.sc >> (st < 2 ? 0 : 8)) & 0xFF);
+  fp4x8_to_bf16_nv(word, sc, nv_scale_significand(sc), o);
   return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 // bf16 operand (8 values) for MFMA step `st` (0..3) of an FP8 slice.
 __device__ __forceinline__ bf16x8 fp8_bf16(const WSlice8& s, int st) {
   const uint4 c = st < 2 ? s.c0 : s.c1;
-  const uint32_t w0 = (st & 1) ? c.z : c.x, w1 = (st & 1) ? c.w : c.y;
-  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
-  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
-  const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
-  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
-  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]),
-                                               pack_bf16x2(c2[0], c2[1]), pack_bf16x2(d[0], d[1])));
+  uint32_t o[4];
+  fp8x4_to_bf16((st & 1) ? c.z : c.x, o);
+  fp8x4_to_bf16((st & 1) ? c.w : c.y, o + 2);
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 __device__ __forceinline__ float scale_from_amax(const uint32_t* bits) {

@@ -442,21 +442,16 @@ __device__ __forceinline__ bf16x8 weight_bf16(const uint4& c0, const uint4& c1, 
   uint32_t o[4];
   if constexpr (WFMT == kFP8) {
     const uint4 c = t < 2 ? c0 : c1;
-    const uint32_t w0 = (t & 1) ? c.z : c.x, w1 = (t & 1) ? c.w : c.y;
-    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
-    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
-    const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
-    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
-    o[0] = pack_bf16x2(a[0], a[1]);
-    o[1] = pack_bf16x2(b[0], b[1]);
-    o[2] = pack_bf16x2(c2[0], c2[1]);
-    o[3] = pack_bf16x2(d[0], d[1]);
+    fp8x4_to_bf16((t & 1) ? c.z : c.x, o);
+    fp8x4_to_bf16((t & 1) ? c.w : c.y, o + 2);
   } else {
     const uint32_t word = t == 0 ? c0.x : t == 1 ? c0.y : t == 2 ? c0.z : c0.w;
-    if constexpr (WFMT == kMXFP4)
+    if constexpr (WFMT == kMXFP4) {
       fp4x8_to_bf16(word, e8m0_as_scale(sc & 0xFF), o);
-    else
-      fp4x8_to_bf16_mul(word, e4m3_to_f32((sc >> (t < 2 ? 0 : 8)) & 0xFF), o);
+    } else {
+      const float s = e4m3_to_f32((sc >> (t < 2 ? 0 : 8)) & 0xFF);
+      fp4x8_to_bf16_nv(word, s, nv_scale_significand(s), o);
+    }
   }
   return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
@@ -528,11 +523,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   // tile of a workgroup comes from its own XCD's chunks.  The sequence ends
   // at `total` or at the first block without an expert (the padding blocks
   // are at the end of the list).
+  // Within one expert's run of row blocks the (block, tile) pairs go tile by
+  // tile: t / ntile is a block of the expert that owns pair t (the run of an
+  // expert with nb blocks spans nb * ntile pairs), and the pair's place in
+  // that run gives the column tile and then the block.  A chunk of pairs on
+  // one XCD then holds a weight tile across many row blocks (reused from its
+  // L2) rather than every tile of a few blocks.
   auto tile_bnt = [&](int k, int& b, int& nt) -> bool {
     const int t = logical_tile(static_cast<int>(blockIdx.x) + k * static_cast<int>(gridDim.x));
-    b = t / ntile;
-    nt = t % ntile;
-    return t < total;
+    if (t >= total) return false;
+    int first = 0, nb = rows.num_blocks;
+    if (rows.sorted_ids) {
+      const int e = rows.block_expert[t / ntile];
+      if (e < 0) {   // padding blocks past the last expert's run: exits at once
+        b = t / ntile;
+        nt = t % ntile;
+        return true;
+      }
+      first = rows.offsets[e] / BM;
+      nb = rows.offsets[e + 1] / BM - first;
+    }
+    const int local = t - first * ntile;
+    nt = local / nb;
+    b = first + local % nb;
+    return true;
   };
   // The sorted row ids of a tile's block are copied into LDS (meta[k & 1]) by
   // wave 0 while the tile before it is fetched, so that no register holds
