@@ -41,6 +41,7 @@ EXPORTS = (
     "ftmoe_packed_size", "ftmoe_pack_qweight", "ftmoe_cache_pool_size", "ftmoe_cache_create",
     "ftmoe_cache_destroy", "ftmoe_cache_plan", "ftmoe_cache_workspace_size", "ftmoe_cache_forward",
     "ftmoe_cache_stats", "ftmoe_cache_set_host_compute", "ftmoe_cache_host_stats", "ftmoe_host_expert_rows",
+    "ftmoe_forward_noalloc",
 )
 ROLE_GATE_UP, ROLE_DOWN = 0, 1
 
@@ -97,6 +98,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ftmoe_experts_forward.argtypes = [P(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp, vp]
     lib.ftmoe_forward.argtypes = [P(LayerDesc), vp, i32, vp, sz, vp, vp, vp, vp]
+    lib.ftmoe_forward_noalloc.argtypes = [P(LayerDesc), vp, i32, vp, vp, vp, vp]
     lib.ftmoe_quantize_fp8_per_tensor.argtypes = [vp, i64, vp, vp, vp, sz, vp]
     lib.ftmoe_packed_size.argtypes = [P(QWeightDesc), i32, P(sz)]
     lib.ftmoe_pack_qweight.argtypes = [P(QWeightDesc), i32, vp, sz, vp]
@@ -122,7 +124,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ftmoe_cache_host_stats.argtypes = [vp, P(i64), P(i64), P(dbl), P(dbl), P(dbl)]
     lib.ftmoe_host_expert_rows.argtypes = [P(LayerDesc), vp, vp, vp, i32, vp, i32]
     for name in ("ftmoe_workspace_size", "ftmoe_route", "ftmoe_align", "ftmoe_experts_forward",
-                 "ftmoe_forward", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight",
+                 "ftmoe_forward", "ftmoe_forward_noalloc", "ftmoe_quantize_fp8_per_tensor", "ftmoe_packed_size", "ftmoe_pack_qweight",
                  "ftmoe_cache_pool_size", "ftmoe_cache_create", "ftmoe_cache_plan", "ftmoe_cache_workspace_size",
                  "ftmoe_cache_forward", "ftmoe_cache_stats", "ftmoe_cache_set_host_compute",
                  "ftmoe_cache_host_stats", "ftmoe_host_expert_rows"):
@@ -332,6 +334,14 @@ def forward(layer: DeviceLayer, x, T: int, ws, y, topk_ids=None, topk_w=None, st
     d = desc if desc is not None else layer.desc()
     _check(load().ftmoe_forward(ctypes.byref(d), _ptr(x), T, _ptr(ws), ws.numel(), _ptr(y), _ptr(topk_ids),
                                 _ptr(topk_w), _stream(stream)))
+
+
+def forward_noalloc(layer: DeviceLayer, x, T: int, y, topk_ids=None, topk_w=None, stream=None, desc=None) -> None:
+    """ftmoe_forward_noalloc: the layer forward on the library's own fixed
+    scratch (no workspace, nothing allocated)."""
+    d = desc if desc is not None else layer.desc()
+    _check(load().ftmoe_forward_noalloc(ctypes.byref(d), _ptr(x), T, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                        _stream(stream)))
 
 
 class ExpertCache:

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <chrono>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <cstdio>
 #include <string>
@@ -571,6 +572,46 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
   if (passes.before_combine) FT_TRY(passes.before_combine(passes.ctx, o, false));
   FT_HIP(timed("combine", s, [&] { return launch_combine(o, w, T, k, H, shared ? sg : nullptr, sh, y, s); }),
          "combine launch");
+  return FTMOE_OK;
+}
+
+// The whole layer on a checked workspace: route (with the fused top-k and
+// align of small decode batches), then the experts.
+ftmoe_status enqueue_forward(const ftmoe_layer* layer, const uint16_t* x, int T, const Plan& p, void* ws, uint16_t* y,
+                             int32_t* topk_ids_out, float* topk_w_out, hipStream_t s) {
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
+  float* sg = at<float>(ws, p.sg);
+  const bool fused_align = p.decode && p.small_route;
+  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, s));
+  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, s);
+}
+
+// ---- allocation-free forward: a fixed scratch array in device memory ----
+// The workspace of ftmoe_forward_noalloc is this file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// In host code its name is not a device address: the address is asked of
+// HIP once per device, with that device current, and only that address is
+// used.  Every call on one GPU shares the array (overlapping calls race);
+// the forward zeroes what must start at zero with kernels of its own.
+constexpr size_t kScratchBytes = static_cast<size_t>(32) << 20;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ftmoe_status device_scratch(void** out) {
+  int dev = 0;
+  FT_HIP(hipGetDevice(&dev), "current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FTMOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    FT_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return fail(FTMOE_ERR_HIP, "scratch address is not usable");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return FTMOE_OK;
 }
 
@@ -1202,13 +1243,32 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
   if (!aligned16(x) || !aligned16(y)) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   const Plan p = make_plan(layer, T);
   FT_TRY(check_ws(p, ws, ws_bytes));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
-  float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
-  float* sg = at<float>(ws, p.sg);
-  const bool fused_align = p.decode && p.small_route;
-  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, s));
-  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, s);
+  return enqueue_forward(layer, x, T, p, ws, y, topk_ids_out, topk_w_out, static_cast<hipStream_t>(stream));
+}
+
+ftmoe_status ftmoe_forward_noalloc(const ftmoe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  g_last_error.clear();
+  FT_TRY(check_layer(layer));
+  FT_TRY(check_tokens(T));
+  if (T == 0) return FTMOE_OK;
+  if (!x || !y) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(FTMOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  const Plan p = make_plan(layer, T);
+  if (p.total > kScratchBytes)
+    return fail(FTMOE_ERR_WORKSPACE,
+                "%d tokens of this layer need %zu bytes of scratch; the allocation-free forward has %zu (call "
+                "ftmoe_forward with a workspace instead)",
+                T, p.total, kScratchBytes);
+  void* ws = nullptr;
+  FT_TRY(device_scratch(&ws));
+  // no timing events either (they would be created on first use)
+  const bool timing = g_timing;
+  g_timing = false;
+  const ftmoe_status st = enqueue_forward(layer, x, T, p, ws, y, topk_ids_out, topk_w_out,
+                                          static_cast<hipStream_t>(stream));
+  g_timing = timing;
+  return st;
 }
 
 ftmoe_status ftmoe_packed_size(const ftmoe_qweight* w, int32_t role, size_t* bytes) {

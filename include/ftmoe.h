@@ -280,6 +280,21 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
                            void* ws, size_t ws_bytes, uint16_t* y,
                            int32_t* topk_ids_out, float* topk_w_out, void* stream);
 
+/* The whole layer as ftmoe_forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument, and no allocation of any kind.
+ * Its scratch is a fixed device array inside the library, 32 MiB, which
+ * every GPU the library runs on holds until the process ends (its address
+ * is looked up, not allocated, on the first call on each device).  Layers
+ * and token counts whose ftmoe_workspace_size exceeds 32 MiB return
+ * FTMOE_ERR_WORKSPACE (nothing enqueued): decode batches of every layer the
+ * library takes fit.  Every call on one GPU shares that scratch: calls on
+ * one GPU must not overlap (order them on one stream or synchronise), or
+ * they race.  Results equal ftmoe_forward's bit for bit.  Per-kernel timing
+ * is not recorded for these calls.                                        */
+ftmoe_status ftmoe_forward_noalloc(const ftmoe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* ---- Expert residency: an HBM slot pool over experts kept in host memory ----
  * The FreeToken README ("About", its runtime features) lists an LRU cache of
  * experts held in GPU memory, and the atomicmilkshake fork README ("Verified

@@ -414,3 +414,19 @@ def test_workspace_bytes_matches_workspace_size():
     d.hidden = 100
     assert lib.ftmoe_workspace_bytes(ctypes.byref(d), 4) == 0
     assert b"hidden" in lib.ftmoe_last_error()
+
+
+@needs_lib
+def test_noalloc_forward_rejects_what_its_scratch_cannot_hold():
+    """The allocation-free forward checks its fixed scratch before touching
+    the GPU: a batch whose workspace exceeds it is refused with a message."""
+    lib = ft.load()
+    d = good_layer()
+    n = ctypes.c_size_t(0)
+    T = 1 << 20
+    assert lib.ftmoe_workspace_size(ctypes.byref(d), T, ctypes.byref(n)) == ft.OK
+    assert n.value > 32 << 20
+    assert lib.ftmoe_forward_noalloc(ctypes.byref(d), FAKE, T, FAKE, None, None, None) == ft.ERR_WORKSPACE
+    assert b"scratch" in lib.ftmoe_last_error()
+    assert lib.ftmoe_forward_noalloc(ctypes.byref(d), None, 4, FAKE, None, None, None) == ft.ERR_INVALID_ARG
+    assert lib.ftmoe_forward_noalloc(ctypes.byref(d), FAKE, 0, FAKE, None, None, None) == ft.OK   # empty batch
