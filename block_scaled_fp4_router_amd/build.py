@@ -27,6 +27,9 @@ HIPFLAGS = [
 ]
 
 
+# Device-side code generation flags every HIP translation unit needs.
+HIPFLAGS_DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+
 # Host-only C++ (the host half of CPU-GPU co-execution): built by the host
 # compiler; functions that need AVX2/FMA carry their own target attribute.
 CXXFLAGS = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-pthread", "-I", os.path.join(ROOT, "include")]
@@ -90,8 +93,59 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+# Sanitizer builds of the host code (not the GPU kernels): every HIP source
+# compiled for the host only, the host C++ and the check program in
+# tests/host_check.cpp, each instrumented, linked into one executable that
+# runs without a GPU.  "address" is AddressSanitizer with
+# UndefinedBehaviorSanitizer, "thread" ThreadSanitizer.
+SANITIZERS = {"address": ["address", "undefined"], "thread": ["thread"]}
+
+
+def host_clang() -> str:
+    for c in (os.environ.get("FTMOE_HOST_CLANG"), "/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("no clang++ found for the sanitizer build")
+
+
+def build_host_check(kind: str, jobs: int | None = None) -> str:
+    """Builds _build/san-<kind>/host_check; returns its path."""
+    out = os.path.join(BUILD, f"san-{kind}")
+    os.makedirs(out, exist_ok=True)
+    san = [f"-fsanitize={x}" for x in SANITIZERS[kind]]
+    common = ["-O1", "-g", "-std=c++20", "-fPIC", "-fno-omit-frame-pointer", "-pthread", "-I", os.path.join(ROOT, "include")]
+    host_san = [f for x in san for f in ("-Xarch_host", x)]   # each sanitizer flag for the host compilation only
+    check = os.path.join(ROOT, "tests", "host_check.cpp")
+
+    def one(src: str) -> str:
+        obj = os.path.join(out, os.path.basename(src) + ".o")
+        if src.endswith(".hip"):
+            cmd = [hipcc(), *common, f"--offload-arch={ARCH}", *HIPFLAGS_DEVICE, *host_san, "-c", src, "-o", obj]
+        else:
+            cmd = [host_clang(), *common, *san, "-I", CSRC, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiler failed on {src}:\n{r.stderr}")
+        return obj
+
+    srcs = sources() + [check]
+    with ThreadPoolExecutor(jobs or min(len(srcs), 8)) as ex:
+        objs = list(ex.map(one, srcs))
+    exe = os.path.join(out, "host_check")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", *host_san, "-pthread", *objs, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--sanitize", choices=sorted(SANITIZERS), default=None,
+                    help="build the host-code check program under a sanitizer instead of the library")
     a = ap.parse_args()
-    build(a.jobs, verbose=True)
+    if a.sanitize:
+        print(build_host_check(a.sanitize, a.jobs))
+    else:
+        build(a.jobs, verbose=True)

@@ -92,9 +92,9 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   TimedLaunch t{name, pool_event(), pool_event(), pool_event(), pool_event()};
   if (!t.a || !t.b || !t.c || !t.d) return launch();
   kernel_events() = KernelEvents{t.a, t.b};
-  hipEventRecord(t.c, s);
+  (void)hipEventRecord(t.c, s);
   const hipError_t e = launch();
-  hipEventRecord(t.d, s);
+  (void)hipEventRecord(t.d, s);
   if (kernel_events().start) {   // not a single launch() kernel: time the stream span
     kernel_events() = KernelEvents{nullptr, nullptr};
     std::swap(t.a, t.c);
