@@ -637,29 +637,41 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
 
 // ============================================================ combine =====
 // y[t] = sum_j w[t,j] o[t*k+j] (ascending j) + sg[t] s[t], from the fp32
-// partial outputs; one thread per 4 columns.
+// partial outputs; one thread per 4 columns.  Every row's load is issued
+// before the sums (MAXK >= k rows, unrolled).
+template <int MAXK>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int per_row = a.H / 4;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.T * per_row) return;
   const int t = idx / per_row, c = (idx % per_row) * 4;
+  float4 v[MAXK];
+  float wj[MAXK];
+#pragma unroll
+  for (int jj = 0; jj < MAXK; ++jj) {
+    if (jj < a.k) {
+      const size_t r = static_cast<size_t>(t) * a.k + jj;
+      wj[jj] = a.w[r];
+      v[jj] = *reinterpret_cast<const float4*>(a.o32 + r * a.H + c);
+    }
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int jj = 0; jj < a.k; ++jj) {
-    const size_t r = static_cast<size_t>(t) * a.k + jj;
-    const float wj = a.w[r];
-    const float4 v = *reinterpret_cast<const float4*>(a.o32 + r * a.H + c);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+#pragma unroll
+  for (int jj = 0; jj < MAXK; ++jj) {
+    if (jj < a.k) {
+      acc.x = fmaf(wj[jj], v[jj].x, acc.x);
+      acc.y = fmaf(wj[jj], v[jj].y, acc.y);
+      acc.z = fmaf(wj[jj], v[jj].z, acc.z);
+      acc.w = fmaf(wj[jj], v[jj].w, acc.w);
+    }
   }
   if (a.sg) {
     const float gt = a.sg[t];
-    const float4 v = *reinterpret_cast<const float4*>(a.s32 + static_cast<size_t>(t) * a.H + c);
-    acc.x = fmaf(gt, v.x, acc.x);
-    acc.y = fmaf(gt, v.y, acc.y);
-    acc.z = fmaf(gt, v.z, acc.z);
-    acc.w = fmaf(gt, v.w, acc.w);
+    const float4 q = *reinterpret_cast<const float4*>(a.s32 + static_cast<size_t>(t) * a.H + c);
+    acc.x = fmaf(gt, q.x, acc.x);
+    acc.y = fmaf(gt, q.y, acc.y);
+    acc.z = fmaf(gt, q.z, acc.z);
+    acc.w = fmaf(gt, q.w, acc.w);
   }
   *reinterpret_cast<uint2*>(a.y + static_cast<size_t>(t) * a.H + c) =
       make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
@@ -791,7 +803,8 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   const int n = a.T * (a.H / 4);
-  return launch(decode_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a);
+  if (a.k <= 8) return launch(decode_combine_kernel<8>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+  return launch(decode_combine_kernel<16>, dim3((n + 255) / 256), dim3(256), 0, s, a);
 }
 
 }  // namespace ftmoe

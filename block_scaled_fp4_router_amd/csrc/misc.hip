@@ -105,6 +105,9 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, const uint32_t* amax_b
 // -------------------------------------------------------------- combine ---
 // One thread per 8 outputs: y[t, n:n+8] = sum_j w[t,j] o[t*k+j, n:n+8]
 // (+ sg[t] * sh[t, n:n+8]), fp32 sums in ascending j, bf16 nearest-even.
+// Every row's load is issued before the sums (MAXK >= k rows, unrolled), so
+// the k loads of a thread are in flight together.
+template <int MAXK>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o,
                                                       const float* __restrict__ w, int T, int k, int H,
                                                       const float* __restrict__ sg,
@@ -115,21 +118,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (idx >= static_cast<int64_t>(T) * per_row) return;
   const int t = static_cast<int>(idx / per_row);
   const int c = static_cast<int>(idx % per_row) * 8;
-  float acc[8] = {};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[static_cast<size_t>(t) * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(o + (static_cast<size_t>(t) * k + j) * H + c);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint4 v[MAXK];
+  float wj[MAXK];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wj, bf16_to_f32(u[i] & 0xFFFF), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      wj[j] = w[static_cast<size_t>(t) * k + j];
+      v[j] = *reinterpret_cast<const uint4*>(o + (static_cast<size_t>(t) * k + j) * H + c);
+    }
+  }
+  float acc[8] = {};
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wj[j], bf16_to_f32(u[i] & 0xFFFF), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj[j], bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+      }
     }
   }
   if (sg) {
     const float g = sg[t];
-    const uint4 v = *reinterpret_cast<const uint4*>(sh + static_cast<size_t>(t) * H + c);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    const uint4 q = *reinterpret_cast<const uint4*>(sh + static_cast<size_t>(t) * H + c);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] = fmaf(g, bf16_to_f32(u[i] & 0xFFFF), acc[2 * i]);
@@ -147,8 +160,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H, const float* sg,
                           const uint16_t* sh, uint16_t* y, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
-  return launch(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, o, w, T, k, H, sg, sh,
-                y);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (k <= 8) return launch(combine_kernel<8>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
+  return launch(combine_kernel<16>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
 }
 
 // ------------------------------------------------- expert-slot pool fill ---
