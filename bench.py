@@ -256,6 +256,11 @@ def prefill_roofline(res):
     return roof
 
 
+def progress(msg):
+    """One line on stderr per phase, so a long run is never silent."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +305,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    progress(f"measuring {args.workload}")
     res = measure(ft, torch, synth, args.workload, args.steps, args.warmup, args.path, args.ring, args.batches,
                   args.pool_slots, args.host_threads)
     cfg, T, kind = res["cfg"], res["T"], res["kind"]
@@ -335,6 +341,7 @@ def main() -> int:
     if kind == "decode" and args.workload == "c1" and not args.no_prefill and not args.pool_slots:
         prefill = {}
         for wl in PREFILL_LINE:
+            progress(f"measuring {wl}")
             r = measure(ft, torch, synth, wl, args.prefill_steps, args.prefill_warmup)
             pr = prefill_roofline(r)
             tr = measured_traffic(pr["kernel"], wl)
@@ -355,6 +362,7 @@ def main() -> int:
         out["prefill"] = prefill
 
     for dst, r in cpu_jobs:
+        progress(f"cpu baseline {r['cfg'].name} T={r['T']}")
         dst["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
