@@ -238,6 +238,29 @@ def decode_roofline(res):
     return roof
 
 
+def gateup_min_bytes(res):
+    """Bytes the routed gate_up GEMM must move at least: the gate_up matrices
+    of the experts that received rows, each token's activation row once, and
+    each (token, expert) row of h once, in the formats the kernel reads and
+    writes them (split E4M3 pairs + E8M0 scales for MXFP4, E4M3 (+ E8M0) for
+    FP8 and MXFP8 activations, bf16 otherwise; h of FP8 layers is written in
+    bf16 and quantised after the global maximum is known)."""
+    lay, cfg, T = res["lay"], res["cfg"], res["T"]
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    gu_b, dn_b = per_expert_bytes(lay.gate_up), per_expert_bytes(lay.down)
+    sh_b = (per_expert_bytes(lay.shared_gate_up) + per_expert_bytes(lay.shared_down)) if cfg.shared_inter else 0
+    n_experts = (res["mean_bytes"] - sh_b) / (gu_b + dn_b)
+    if cfg.fmt == "mxfp4" and cfg.act == "mxfp8":
+        x_row, h_row = H + H // 32, I + I // 32
+    elif cfg.fmt == "mxfp4":
+        x_row, h_row = 2 * H + H // 32, 2 * I + I // 32
+    elif cfg.act == "fp8":
+        x_row, h_row = H, 2 * I
+    else:
+        x_row, h_row = 2 * H, 2 * I
+    return gu_b * n_experts + T * x_row + T * k * h_row
+
+
 def prefill_roofline(res):
     cfg, T, ku = res["cfg"], res["T"], res["kernel_us"]
     H, I, k = cfg.hidden, cfg.inter, cfg.top_k
@@ -247,7 +270,7 @@ def prefill_roofline(res):
     peak = MFMA_PEAK_TFLOPS["fp8" if cfg.act in ("fp8", "mxfp8") else "bf16"]
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None, "algorithmic_flops_per_launch": flops,
-            "avg_launch_us": round(ku[dom], 3)}
+            "algorithmic_bytes_per_launch": int(gateup_min_bytes(res)), "avg_launch_us": round(ku[dom], 3)}
     if "gemm_down" in ku:
         # both routed GEMMs together (gate_up 2/3, down 1/3 of the flops)
         g = 3.0 * flops / 2.0 / ((ku[dom] + ku["gemm_down"]) * 1e-6) / 1e12
@@ -319,6 +342,7 @@ def main() -> int:
     if traffic is not None:
         roof["traffic"] = traffic["bytes"]
         roof["traffic_counters"] = traffic["counters"]
+        roof["traffic_dram"] = traffic["dram"]
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(res["ms"], 5), "higher_is_better": True, "scaling": "weak",
@@ -348,6 +372,7 @@ def main() -> int:
             if tr is not None:
                 pr["traffic"] = tr["bytes"]
                 pr["traffic_counters"] = tr["counters"]
+                pr["traffic_dram"] = tr["dram"]
             entry = {"workload": describe(r["cfg"], r["T"]), "value": round(r["T"] / (r["ms"] * 1e-3), 1),
                      "unit": "tokens/s", "ms_per_step": round(r["ms"], 5), "steps": args.prefill_steps,
                      "warmup": args.prefill_warmup,
@@ -441,10 +466,11 @@ def cpu_baseline(res, seconds):
 
 
 def measured_traffic(kernel, workload):
-    """Bytes per launch of `kernel` between the L2 and memory, from the
-    committed counter summary (read and write request bytes, scaled by a
-    known-size copy), or None when there is none or the kernel sources
-    changed since it was taken."""
+    """Bytes per launch of `kernel` between the L2 and memory (L2-miss bytes:
+    FETCH_SIZE + WRITE_SIZE) and the bytes of its requests to the memory
+    controllers (TCC_EA0_RDREQ_DRAM + WRREQ_DRAM), each scaled by a known-size
+    copy, from the committed counter summary; None when there is none or the
+    kernel sources changed since it was taken."""
     import re
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
@@ -453,9 +479,11 @@ def measured_traffic(kernel, workload):
     m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
     m_h = re.search(r"^source_sha256:\s*([0-9a-f]+)", text, re.M)
     m_c = re.search(r"^traffic_counters:\s*(.+)$", text, re.M)
+    m_d = re.search(r"^dram_bytes_per_launch:\s*(\d+)", text, re.M)
     if not m_b or not m_h or m_h.group(1) != kernel_source_sha():
         return None
-    return {"bytes": int(m_b.group(1)), "counters": m_c.group(1).strip() if m_c else "FETCH_SIZE + WRITE_SIZE"}
+    return {"bytes": int(m_b.group(1)), "counters": m_c.group(1).strip() if m_c else "FETCH_SIZE + WRITE_SIZE",
+            "dram": int(m_d.group(1)) if m_d else None}
 
 
 def kernel_source_sha():
