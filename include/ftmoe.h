@@ -287,8 +287,10 @@ ftmoe_status ftmoe_forward(const ftmoe_layer* layer, const uint16_t* x, int32_t 
  * every GPU the library runs on holds until the process ends (its address
  * is looked up, not allocated, on the first call on each device).  Layers
  * and token counts whose ftmoe_workspace_size exceeds 32 MiB return
- * FTMOE_ERR_WORKSPACE (nothing enqueued): decode batches of every layer the
- * library takes fit.  Every call on one GPU shares that scratch: calls on
+ * FTMOE_ERR_WORKSPACE (nothing enqueued): decode batches of up to 8 tokens
+ * fit at the largest shapes the library takes (hidden and intermediate
+ * 4096, 1024 experts, top-16: under 19 MiB), 16 tokens only at smaller
+ * ones (about 37 MiB there).  Every call on one GPU shares that scratch: calls on
  * one GPU must not overlap (order them on one stream or synchronise), or
  * they race.  Results equal ftmoe_forward's bit for bit.  Per-kernel timing
  * is not recorded for these calls.                                        */

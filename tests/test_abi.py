@@ -430,3 +430,26 @@ def test_noalloc_forward_rejects_what_its_scratch_cannot_hold():
     assert b"scratch" in lib.ftmoe_last_error()
     assert lib.ftmoe_forward_noalloc(ctypes.byref(d), None, 4, FAKE, None, None, None) == ft.ERR_INVALID_ARG
     assert lib.ftmoe_forward_noalloc(ctypes.byref(d), FAKE, 0, FAKE, None, None, None) == ft.OK   # empty batch
+
+
+@needs_lib
+@pytest.mark.parametrize("fmt,act", [("W_MXFP4", "ACT_BF16"), ("W_MXFP4", "ACT_MXFP8"), ("W_NVFP4", "ACT_BF16"),
+                                     ("W_FP8_E4M3", "ACT_FP8_PER_TENSOR"), ("W_BF16", "ACT_BF16")])
+def test_noalloc_scratch_holds_eight_token_decode_at_the_largest_shapes(fmt, act):
+    """The header's promise for the allocation-free forward: an 8-token
+    batch fits its 32 MiB scratch at hidden = intermediate = 4096, 1024
+    experts, top-16 (and a 16-token one there does not)."""
+    lib = ft.load()
+    H = I = 4096
+    E, k = 1024, 16
+    d = ft.LayerDesc()
+    d.hidden, d.inter, d.num_experts, d.top_k = H, I, E, k
+    d.act, d.path = getattr(ft, act), ft.PATH_AUTO
+    d.router_w, d.router_bias = FAKE, None
+    d.gate_up = _qw(getattr(ft, fmt), E, 2 * I, H)
+    d.down = _qw(getattr(ft, fmt), E, H, I)
+    assert 0 < lib.ftmoe_workspace_bytes(ctypes.byref(d), 8) <= 32 << 20
+    n16 = lib.ftmoe_workspace_bytes(ctypes.byref(d), 16)
+    assert n16 > 0
+    if n16 > 32 << 20:
+        assert lib.ftmoe_forward_noalloc(ctypes.byref(d), FAKE, 16, FAKE, None, None, None) == ft.ERR_WORKSPACE
