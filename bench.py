@@ -224,6 +224,10 @@ def decode_roofline(res):
     sdn_b = per_expert_bytes(lay.shared_down) if cfg.shared_inter else 0
     mean_unique = (res["mean_bytes"] - sgu_b - sdn_b) / (gu_b + dn_b)
     unit_bytes = {"decode_gateup": gu_b * mean_unique + sgu_b, "decode_down": dn_b * mean_unique + sdn_b}[dom]
+    if "pool" in res:
+        # through the pool a step runs its experts in several passes, each a
+        # launch over a part of them: the bytes of the average launch
+        unit_bytes /= max(1.0, res["pool"]["passes_per_step"])
     achieved = unit_bytes / (ku[dom] * 1e-6) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
