@@ -206,7 +206,7 @@ struct Plan {
   int BM = 0, P = 0, nblocks = 0, nb_shared = 0, shared_rows = 0, S = 0, tiles = 0, n_zero = 0, rsplit = 1;
   size_t logits = 0, part = 0, ids = 0, w = 0, sg = 0, counts = 0, offsets = 0, sorted = 0, bexp = 0, npad = 0,
          scal = 0, ascratch = 0, xq = 0, xhi = 0, xlo = 0, xsc = 0, h = 0, o = 0, hs = 0, s = 0, hhi = 0, hlo = 0,
-         hsc = 0, hq = 0, xs = 0, xssc = 0, hgsc = 0, hssc = 0, total = 0;
+         hsc = 0, hq = 0, xs = 0, xssc = 0, hgsc = 0, hssc = 0, rplanes = 0, total = 0;
   int hsc_pitch = 0;
   bool a8 = false;        // MXFP8 activations: single codes where MXFP4 otherwise splits
   bool mx_split = false;  // MXFP4 decode: activations travel as split E4M3 pairs (or MXFP8)
@@ -242,6 +242,7 @@ Plan make_plan(const ftmoe_layer* L, int T) {
   } else {
     p.rsplit = router_splits_gemm(T, L->hidden, E + (L->shared_inter > 0 ? 1 : 0));
     p.logits = take(static_cast<size_t>(p.rsplit) * T * (E + 1) * 4);
+    p.rplanes = take(router_planes_bytes(E, L->hidden, shared));
   }
   p.ids = take(tk * 4);
   p.w = take(tk * 4);
@@ -348,10 +349,17 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
     return FTMOE_OK;
   }
   float* logits = at<float>(ws, p.logits);
+  uint16_t* planes = at<uint16_t>(ws, p.rplanes);
+  FT_HIP(timed("router_split", s,
+               [&] {
+                 return launch_router_split(L->router_w, E, L->hidden, shared ? L->shared_gate_w : nullptr, planes,
+                                            s);
+               }),
+         "router split launch");
   FT_HIP(timed("router_logits", s,
                [&] {
                  return launch_router_logits(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
-                                             logits, s);
+                                             planes, logits, s);
                }),
          "router logits launch");
   FT_HIP(timed("topk", s,

@@ -78,8 +78,15 @@ struct Rows {
 // ---- router ----
 // logits [S][T][E+1] fp32, S = router_splits_gemm(T, H, rows) K splits (rows = E + shared).
 int router_splits_gemm(int T, int H, int rows);
+// Many tokens: the router GEMM reads the fp32 router rows (and the shared
+// gate vector as row E) split into three bf16 planes [3][rows][H], made by
+// launch_router_split into router_planes_bytes of scratch; few tokens read
+// router_w directly (planes may then be null).
+size_t router_planes_bytes(int E, int H, bool shared);
+hipError_t launch_router_split(const float* router_w, int E, int H, const float* shared_gate_w, uint16_t* planes,
+                               hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                const float* shared_gate_w, float* logits, hipStream_t s);
+                                const float* shared_gate_w, const uint16_t* planes, float* logits, hipStream_t s);
 // bias_select: the bias ranks the experts only; the weights are the softmax
 // of the selected logits without it.
 hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, const float* bias, bool bias_select,

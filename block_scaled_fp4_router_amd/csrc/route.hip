@@ -53,12 +53,13 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 // w3 = w - w1 - w2, which fits bf16 because each rounding leaves at most 8
 // significant bits fewer).  Each product x * w_i of a bf16 x is exact in
 // fp32 and the MFMA accumulates in fp32, so the logits keep fp32 accuracy.
+// The split is made once per call into three bf16 planes [3][rows][H] (every
+// token tile of the GEMM would otherwise convert the same weights again).
 // Workgroup: 64 tokens x 64 router rows, 4 waves of one 32 x 32 tile each;
 // K stages of 64 staged through LDS (rows of 128 bytes, XOR-swizzled).  The
-// global loads of stage k + 1 are issued before the MFMA work of stage k.
-// (Every workgroup re-reads its 64 fp32 router rows, so larger token tiles
-// would save L2 traffic, but T = 4096 then leaves CUs idle.)
-constexpr int kRT = 64, kRE = 64, kRK = 64, kRThreads = 256;
+// global loads run kRPF stages ahead of the MFMA work, each stage in its own
+// register set, so that their latency is covered by as many stages of work.
+constexpr int kRT = 64, kRE = 64, kRK = 64, kRThreads = 256, kRPF = 2;
 
 __device__ __forceinline__ int rswz(int r, int q) { return q ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
@@ -69,82 +70,112 @@ __device__ __forceinline__ void split3(float w, uint16_t& a, uint16_t& b, uint16
   c = f32_to_bf16(r1 - bf16_to_f32(b));
 }
 
+// planes[m][r][h], m = 0, 1, 2: the three terms of row r (r = E: the shared
+// gate vector); one thread per 8 consecutive elements.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ router_w, int E, int H,
+                                                           const float* __restrict__ shared_gate_w,
+                                                           uint16_t* __restrict__ planes) {
+  const int rows = E + (shared_gate_w ? 1 : 0);
+  const size_t n8 = static_cast<size_t>(rows) * H / 8;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const size_t el = 8 * i;
+  const int r = static_cast<int>(el / H), h = static_cast<int>(el % H);
+  const float* src = (r < E ? router_w + static_cast<size_t>(r) * H : shared_gate_w) + h;
+  const float4 v0 = *reinterpret_cast<const float4*>(src);
+  const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+  const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t p[3][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint16_t a0, b0, c0, a1, b1, c1;
+    split3(f[2 * q], a0, b0, c0);
+    split3(f[2 * q + 1], a1, b1, c1);
+    p[0][q] = a0 | (static_cast<uint32_t>(a1) << 16);
+    p[1][q] = b0 | (static_cast<uint32_t>(b1) << 16);
+    p[2][q] = c0 | (static_cast<uint32_t>(c1) << 16);
+  }
+  const size_t plane = static_cast<size_t>(rows) * H;
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+    *reinterpret_cast<uint4*>(planes + m * plane + el) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
+}
+
 __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                                const float* __restrict__ router_w, int E,
-                                                                const float* __restrict__ shared_gate_w,
-                                                                float* __restrict__ logits) {
+                                                                const uint16_t* __restrict__ planes, int E,
+                                                                int rows, float* __restrict__ logits) {
   // blockIdx.z: the K split; split z sums H range [z, z + 1) * H / gridDim.z into logits[z]
   __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
-  const int rows = E + (shared_gate_w ? 1 : 0);
   const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
   const int j = lane & 31, g = lane >> 5;
 
-  // staging: x row tid / 4, vectors 2 (tid % 4) and + 1 of its 128-byte stage
-  // row; W row tid / 4, 16 fp32 (vectors 2 (tid % 4) and + 1 of each bf16 plane)
-  const int xr = tid >> 2, xq = (tid & 3) * 2;
-  const int wr = tid >> 2, wq = (tid & 3) * 2;
-  const int t = t0 + xr, e = e0 + wr;
+  // staging: x row tid / 4 and W row tid / 4, vectors 2 (tid % 4) and + 1 of
+  // their 128-byte stage rows (of each of the three planes for W)
+  const int sr = tid >> 2, sq = (tid & 3) * 2;
+  const int t = t0 + sr, e = e0 + sr;
   const uint16_t* xrow = t < T ? x + static_cast<size_t>(t) * H : nullptr;
-  const float* wrow = e < E ? router_w + static_cast<size_t>(e) * H : (e == E ? shared_gate_w : nullptr);
+  const size_t plane = static_cast<size_t>(rows) * H;
+  const uint16_t* wrow = e < rows ? planes + static_cast<size_t>(e) * H : nullptr;
 
-  uint4 xv[2];
-  float4 wv[4];
-  auto load = [&](int k0) {
-    xv[0] = xv[1] = make_uint4(0, 0, 0, 0);
-    if (xrow) {
-      xv[0] = *reinterpret_cast<const uint4*>(xrow + k0 + xq * 8);
-      xv[1] = *reinterpret_cast<const uint4*>(xrow + k0 + xq * 8 + 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wv[i] = wrow ? *reinterpret_cast<const float4*>(wrow + k0 + wq * 8 + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  struct Stage {
+    uint4 x[2];
+    uint4 w[3][2];
   };
-  auto store = [&]() {
+  Stage st[kRPF];
+  auto load = [&](Stage& sg, int k0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(xs + xr * 128 + 16 * rswz(xr, xq + h)) = xv[h];
+    for (int h = 0; h < 2; ++h)
+      sg.x[h] = xrow ? *reinterpret_cast<const uint4*>(xrow + k0 + (sq + h) * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {   // bf16 vector wq + v: fp32 elements 8v .. 8v + 7 of the thread's 16
-      const float f[8] = {wv[2 * v].x, wv[2 * v].y, wv[2 * v].z, wv[2 * v].w,
-                          wv[2 * v + 1].x, wv[2 * v + 1].y, wv[2 * v + 1].z, wv[2 * v + 1].w};
-      uint32_t p[3][4];
+    for (int m = 0; m < 3; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint16_t a0, b0, c0, a1, b1, c1;
-        split3(f[2 * i], a0, b0, c0);
-        split3(f[2 * i + 1], a1, b1, c1);
-        p[0][i] = a0 | (static_cast<uint32_t>(a1) << 16);
-        p[1][i] = b0 | (static_cast<uint32_t>(b1) << 16);
-        p[2][i] = c0 | (static_cast<uint32_t>(c1) << 16);
-      }
-      const int off = wr * 128 + 16 * rswz(wr, wq + v);
+      for (int h = 0; h < 2; ++h)
+        sg.w[m][h] = wrow ? *reinterpret_cast<const uint4*>(wrow + m * plane + k0 + (sq + h) * 8)
+                          : make_uint4(0, 0, 0, 0);
+  };
+  auto store = [&](const Stage& sg) {
 #pragma unroll
-      for (int m = 0; m < 3; ++m) *reinterpret_cast<uint4*>(ws[m] + off) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
+    for (int h = 0; h < 2; ++h) {
+      const int off = sr * 128 + 16 * rswz(sr, sq + h);
+      *reinterpret_cast<uint4*>(xs + off) = sg.x[h];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) *reinterpret_cast<uint4*>(ws[m] + off) = sg.w[m][h];
     }
   };
 
   f32x16 acc = {};
   const int kspan = H / static_cast<int>(gridDim.z), kbeg = static_cast<int>(blockIdx.z) * kspan;
-  const int kend = kbeg + kspan;
+  const int ns = kspan / kRK;
   logits += static_cast<size_t>(blockIdx.z) * T * (E + 1);
-  load(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += kRK) {
-    __syncthreads();   // the previous stage's reads are done
-    store();
-    __syncthreads();
-    if (k0 + kRK < kend) load(k0 + kRK);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
-      const int ra = wt + j, rb = we + j;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + ra * 128 + 16 * rswz(ra, q)));
+  for (int u = 0; u < kRPF; ++u)
+    if (u < ns) load(st[u], kbeg + u * kRK);
+  // stage s uses register set s % kRPF; the loop is unrolled by kRPF so that
+  // every register set is named statically
+  for (int s0 = 0; s0 < ns; s0 += kRPF) {
 #pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const bf16x8 b =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ws[m] + rb * 128 + 16 * rswz(rb, q)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    for (int u = 0; u < kRPF; ++u) {
+      const int s = s0 + u;
+      if (s >= ns) break;
+      __syncthreads();   // the previous stage's reads are done
+      store(st[u]);
+      __syncthreads();
+      if (s + kRPF < ns) load(st[u], kbeg + (s + kRPF) * kRK);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
+        const int ra = wt + j, rb = we + j;
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + ra * 128 + 16 * rswz(ra, q)));
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          const bf16x8 b =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ws[m] + rb * 128 + 16 * rswz(rb, q)));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
       }
     }
   }
@@ -156,19 +187,30 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
   }
 }
 
-// K splits of the router GEMM: enough tiles to cover the compute units
-// (the top-k kernel adds the splits in order, so the logits stay
+// K splits of the router GEMM: enough workgroups for about four per compute
+// unit (the top-k kernel adds the splits in order, so the logits stay
 // deterministic).
 int router_splits_gemm(int T, int H, int rows) {
   if (T <= kGemvMaxT) return 1;
   const long long tiles = static_cast<long long>((T + kRT - 1) / kRT) * ((rows + kRE - 1) / kRE);
   int S = 1;
-  while (S < 4 && tiles * S < 256 && (H / kRK) % (2 * S) == 0) S *= 2;
+  while (S < 4 && tiles * S < 1024 && (H / kRK) % (2 * S) == 0) S *= 2;
   return S;
 }
 
+size_t router_planes_bytes(int E, int H, bool shared) {
+  return 3 * static_cast<size_t>(E + (shared ? 1 : 0)) * H * sizeof(uint16_t);
+}
+
+hipError_t launch_router_split(const float* router_w, int E, int H, const float* shared_gate_w, uint16_t* planes,
+                               hipStream_t s) {
+  const size_t n8 = static_cast<size_t>(E + (shared_gate_w ? 1 : 0)) * H / 8;
+  return launch(router_split_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, router_w, E, H,
+                shared_gate_w, planes);
+}
+
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                const float* shared_gate_w, float* logits, hipStream_t s) {
+                                const float* shared_gate_w, const uint16_t* planes, float* logits, hipStream_t s) {
   const int rows = E + (shared_gate_w ? 1 : 0);
   if (T <= kGemvMaxT) {
     dim3 grid((rows + 3) / 4);
@@ -180,7 +222,8 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
       return launch(router_gemv_kernel<kGemvMaxT>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   } else {
     dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE, router_splits_gemm(T, H, rows));
-    return launch(router_gemm_kernel, grid, dim3(kRThreads), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
+    if (!planes) return hipErrorInvalidValue;
+    return launch(router_gemm_kernel, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits);
   }
 }
 
