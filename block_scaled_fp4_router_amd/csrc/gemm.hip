@@ -182,6 +182,16 @@ __device__ __forceinline__ int lds_i32(uint32_t addr) {
   return v;
 }
 
+// Completes the LDS reads a fragment reader left in flight.  The vectors are
+// passed through the asm, so no use of them can be scheduled before the wait
+// and their registers stay allocated until it.
+__device__ __forceinline__ void frag_wait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void frag_wait2(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n" : "+v"(a), "+v"(b));
+}
+
 // FP4 weights, 4 column tiles: weight vectors, scale dwords, activation vectors.
 template <int OB1, int OB2, int OB3, int OS1, int OS2, int OS3, int OAM>
 __device__ __forceinline__ void frag_read_fp4_4(uint32_t vB, uint32_t vS, const uint32_t (&vA)[4], u32x4 (&b)[4],
@@ -231,7 +241,10 @@ __device__ __forceinline__ void frag_read_fp4_2(uint32_t vB, uint32_t vS, const 
 }
 
 // MXFP4 weights with split activations, 4 column tiles: as frag_read_fp4_4
-// plus the activation scale dwords of the wave's two row tiles.
+// plus the activation scale dwords of the wave's two row tiles.  The second
+// row tile's activation vectors (a[4..7], read last) may still be in flight
+// on return: frag_wait4 completes them before their first use, so the first
+// row tile's MFMAs run while they arrive.
 template <int OB1, int OB2, int OB3, int OS1, int OS2, int OS3, int OAM, int OAS>
 __device__ __forceinline__ void frag_read_mx_4(uint32_t vB, uint32_t vS, uint32_t vAS, const uint32_t (&vA)[4],
                                                u32x4 (&b)[4], uint32_t (&s)[4], uint32_t (&as)[2], u32x4 (&a)[8]) {
@@ -254,7 +267,7 @@ __device__ __forceinline__ void frag_read_mx_4(uint32_t vB, uint32_t vS, uint32_
       "ds_read_b128 %15, %22 offset:%31\n"
       "ds_read_b128 %16, %23 offset:%31\n"
       "ds_read_b128 %17, %24 offset:%31\n"
-      "s_waitcnt lgkmcnt(0)\n"
+      "s_waitcnt lgkmcnt(4)\n"
       : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]),
         "=&v"(as[0]), "=&v"(as[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
         "=&v"(a[6]), "=&v"(a[7])
@@ -262,7 +275,8 @@ __device__ __forceinline__ void frag_read_mx_4(uint32_t vB, uint32_t vS, uint32_
         "n"(OS1), "n"(OS2), "n"(OS3), "n"(OAM), "n"(OAS));
 }
 
-// MXFP4 weights with split activations, 2 column tiles.
+// MXFP4 weights with split activations, 2 column tiles (a[4..7] as for
+// frag_read_mx_4).
 template <int OB1, int OS1, int OAM, int OAS>
 __device__ __forceinline__ void frag_read_mx_2(uint32_t vB, uint32_t vS, uint32_t vAS, const uint32_t (&vA)[4],
                                                u32x4 (&b)[2], uint32_t (&s)[2], uint32_t (&as)[2], u32x4 (&a)[8]) {
@@ -281,7 +295,7 @@ __device__ __forceinline__ void frag_read_mx_2(uint32_t vB, uint32_t vS, uint32_
       "ds_read_b128 %11, %18 offset:%23\n"
       "ds_read_b128 %12, %19 offset:%23\n"
       "ds_read_b128 %13, %20 offset:%23\n"
-      "s_waitcnt lgkmcnt(0)\n"
+      "s_waitcnt lgkmcnt(4)\n"
       : "=&v"(b[0]), "=&v"(b[1]), "=&v"(s[0]), "=&v"(s[1]), "=&v"(as[0]), "=&v"(as[1]), "=&v"(a[0]), "=&v"(a[1]),
         "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
       : "v"(vB), "v"(vS), "v"(vAS), "v"(vA[0]), "v"(vA[1]), "v"(vA[2]), "v"(vA[3]), "n"(OB1), "n"(OS1), "n"(OAM),
@@ -386,6 +400,8 @@ __device__ __forceinline__ void frag_read_bf16w_2(const uint32_t (&vB)[4], const
 }
 
 // FP8 weights and activations, 4 column tiles: two vectors per operand row.
+// The second row tile's activation vectors (a[2], a[3], read last) may still
+// be in flight on return: frag_wait2 completes them before their first use.
 template <int OB1, int OB2, int OB3, int OAM>
 __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint32_t vA0, uint32_t vA1, u32x4 (&b)[8],
                                                 u32x4 (&a)[4]) {
@@ -402,7 +418,7 @@ __device__ __forceinline__ void frag_read_fp8_4(uint32_t vB0, uint32_t vB1, uint
       "ds_read_b128 %9, %15\n"
       "ds_read_b128 %10, %14 offset:%19\n"
       "ds_read_b128 %11, %15 offset:%19\n"
-      "s_waitcnt lgkmcnt(0)\n"
+      "s_waitcnt lgkmcnt(2)\n"
       : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
       : "v"(vB0), "v"(vB1), "v"(vA0), "v"(vA1), "n"(OB1), "n"(OB2), "n"(OB3), "n"(OAM));
 }
@@ -815,6 +831,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       const int sh = 16 * (s & 1) + 8 * g;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        if (m == 1) frag_wait4(av[4], av[5], av[6], av[7]);   // (unconditional: the reads are in flight)
         if (!rows_ok[m]) continue;
         const int sa = static_cast<int>(asw[m] >> sh);
         const i32x8 ah = u4x2(to_u4(av[4 * m]), to_u4(av[4 * m + 1]));
@@ -837,6 +854,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
       for (int ct = 0; ct < NT; ++ct) bq[ct] = u4x2(to_u4(bv[2 * ct]), to_u4(bv[2 * ct + 1]));
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        if (m == 1) frag_wait2(av[2], av[3]);   // (unconditional: the reads are in flight)
         if (!rows_ok[m]) continue;
         const i32x8 a = u4x2(to_u4(av[2 * m]), to_u4(av[2 * m + 1]));
 #pragma unroll
