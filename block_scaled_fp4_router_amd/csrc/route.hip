@@ -451,13 +451,21 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
     int has_shared,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ sgate, int32_t* counts, int32_t* offsets,
     int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, int P, uint32_t* zero_words, int n_zero) {
+  constexpr int kRowWaves = kDecodeMaxT * 16 / kWave;   // waves of routed rows (T * k <= 256)
+  constexpr int kFewRows = 32;
   __shared__ __attribute__((aligned(16))) int ids_s[kDecodeMaxT * 16];
   __shared__ int cnt[kAlignMaxE];
+  __shared__ int cntw[kRowWaves][kAlignMaxE];   // rows of each expert in each wave of 64 rows
   __shared__ int tmp[32];
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const int rows = E + (has_shared ? 1 : 0);
+  const int nw = (T * k + kWave - 1) / kWave;
   for (int i = tid; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
-  cnt[tid] = 0;
+  const bool few = T * k <= kFewRows;   // rank by a scan of the earlier rows
+  if (few)
+    cnt[tid] = 0;
+  else
+    for (int i = tid; i < nw * kAlignMaxE; i += blockDim.x) cntw[i / kAlignMaxE][i % kAlignMaxE] = 0;
   if (wv < T) {
     const int t = wv;
     float v[SLOTS];
@@ -489,23 +497,50 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
   if (P == 0) return;  // routing only
   __syncthreads();
   const int n = T * k;
-  for (int i = tid; i < n; i += blockDim.x) atomicAdd(&cnt[ids_s[i]], 1);
+  // Stable rank of row i among the earlier rows of its expert.  Up to
+  // kFewRows rows: counts by LDS atomics and the rank by a scan of the
+  // earlier rows.  More: wave rw takes rows [64 rw, 64 rw + 64), the lanes
+  // holding the same expert are found with one ballot per bit of the id,
+  // and the last lane of each group records the wave's count of that
+  // expert; rows of earlier waves are counted through those records.
+  int my_id = -1, rank_in = 0;
+  if (few) {
+    if (tid < n) {
+      my_id = ids_s[tid];
+      atomicAdd(&cnt[my_id], 1);
+      for (int j = 0; j < tid; ++j) rank_in += ids_s[j] == my_id;
+    }
+  } else if (wv < nw) {   // uniform per wave
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    my_id = tid < n ? ids_s[tid] : -1;
+    uint64_t peers = __ballot(my_id >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (my_id >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    rank_in = __popcll(peers & ((uint64_t{1} << lane) - 1));
+    if (my_id >= 0 && (peers >> lane) == 1) cntw[wv][my_id] = __popcll(peers);
+  }
   __syncthreads();
-  const int c = tid < E ? cnt[tid] : 0;
+  int c = 0;
+  if (tid < E) {
+    if (few)
+      c = cnt[tid];
+    else
+      for (int w = 0; w < nw; ++w) c += cntw[w][tid];
+  }
   int off, total;
   finish_layout(tid, E, c, kDecodeBM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off,
                 &total);
-  if (tid < E) cnt[tid] = off;   // the counts are no longer needed: reuse as segment starts
+  if (tid < E) cnt[tid] = off;   // segment starts
   __syncthreads();
-  // row i goes after the earlier rows of its expert (stable counting sort)
-  if (tid < n) {
-    const int id = ids_s[tid];
-    int rank = 0;
-    for (int j0 = 0; j0 < tid; j0 += 4) {
-      const int4 v = *reinterpret_cast<const int4*>(&ids_s[j0]);
-      rank += (v.x == id) + (j0 + 1 < tid && v.y == id) + (j0 + 2 < tid && v.z == id) + (j0 + 3 < tid && v.w == id);
-    }
-    sorted_ids[cnt[id] + rank] = tid;
+  if (my_id >= 0) {
+    int before = 0;
+    if (!few)
+      for (int w = 0; w < wv; ++w) before += cntw[w][my_id];
+    sorted_ids[cnt[my_id] + before + rank_in] = tid;
   }
 }
 
