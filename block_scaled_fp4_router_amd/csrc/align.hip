@@ -9,7 +9,7 @@
 //
 // Small tables (n <= kAlignSmallN) use one workgroup.  Larger ones use three
 // kernels: per-chunk histograms, one scan over (chunk, expert), and a
-// per-chunk stable scatter where a wave ranks equal experts with lane reads.
+// per-chunk stable scatter where waves rank equal experts with ballots.
 #include <algorithm>
 
 #include "align_dev.hpp"
@@ -87,7 +87,11 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
 // Exclusive prefix of the per-chunk histograms over chunks, per expert, plus
 // the layout.  The 1024 threads are split into parts = 1024 / E groups of E
 // (one thread per expert and part); each part owns a contiguous range of
-// chunks, so the histogram is read with many loads in flight.
+// chunks.  A thread loads up to kScanCache of its histogram entries at once
+// and keeps them in registers for the second pass, so the histogram is read
+// once, with all loads in flight together.
+constexpr int kScanCache = 40;
+
 __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, int P, int nchunks,
                                                           int32_t* __restrict__ hist, int32_t* counts,
                                                           int32_t* offsets, int32_t* sorted_ids,
@@ -101,18 +105,16 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, 
   const bool worker = p < parts;
   const int per = (nchunks + parts - 1) / parts;
   const int c0 = min(nchunks, p * per), c1 = min(nchunks, c0 + per);
+  const int ncached = min(c1 - c0, kScanCache);
   // 1. each part's sum
+  int v[kScanCache];
   int sum = 0;
   if (worker) {
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[static_cast<size_t>(c + u) * E + e];
+    for (int u = 0; u < kScanCache; ++u) v[u] = u < ncached ? hist[static_cast<size_t>(c0 + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
-    }
-    for (; c < c1; ++c) sum += hist[static_cast<size_t>(c) * E + e];
+    for (int u = 0; u < kScanCache; ++u) sum += v[u];
+    for (int c = c0 + kScanCache; c < c1; ++c) sum += hist[static_cast<size_t>(c) * E + e];
     part_base[tid] = sum;
   }
   __syncthreads();
@@ -120,9 +122,9 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, 
   int total_e = 0;
   if (tid < E) {
     for (int q = 0; q < parts; ++q) {
-      const int v = part_base[q * E + tid];
+      const int x = part_base[q * E + tid];
       part_base[q * E + tid] = total_e;
-      total_e += v;
+      total_e += x;
     }
   }
   __syncthreads();
@@ -135,42 +137,49 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, 
   // 4. every (chunk, expert) entry becomes the expert's first slot for that chunk
   if (worker) {
     int base = exp_off[e] + part_base[tid];
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[static_cast<size_t>(c + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        hist[static_cast<size_t>(c + u) * E + e] = base;
+    for (int u = 0; u < kScanCache; ++u) {
+      if (u < ncached) {
+        hist[static_cast<size_t>(c0 + u) * E + e] = base;
         base += v[u];
       }
     }
-    for (; c < c1; ++c) {
-      const int v = hist[static_cast<size_t>(c) * E + e];
+    for (int c = c0 + kScanCache; c < c1; ++c) {
+      const int x = hist[static_cast<size_t>(c) * E + e];
       hist[static_cast<size_t>(c) * E + e] = base;
-      base += v;
+      base += x;
     }
   }
 }
 
-// One wave per chunk: rows are taken 64 at a time in index order; a row's
-// slot is its expert's running position plus the number of earlier lanes in
-// the group with the same expert (found with one ballot per id bit).
-__global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                           const int32_t* __restrict__ hist,
-                                                           int32_t* __restrict__ sorted_ids) {
+// Four waves per chunk.  The chunk's rows are taken 256 at a time in index
+// order, wave w on rows [64 w, 64 w + 64) of each group.  Within a wave the
+// lanes with the same expert are found with one ballot per bit of the id;
+// the last lane of each such group records the wave's count of that expert,
+// so a row's slot is its expert's running position, plus the rows of that
+// expert in the earlier waves of the group, plus the earlier lanes of its
+// own group.  The records are cleared by the lanes that wrote them.
+constexpr int kScatterWaves = 4;
+
+__global__ __launch_bounds__(64 * kScatterWaves) void align_scatter_kernel(const int32_t* __restrict__ ids, int n,
+                                                                           int E, const int32_t* __restrict__ hist,
+                                                                           int32_t* __restrict__ sorted_ids) {
   __shared__ int run[kAlignMaxE];
+  __shared__ int wcnt[kScatterWaves][kAlignMaxE];
   const int c = blockIdx.x;
-  const int lane = lane_id();
-  for (int e = lane; e < E; e += kWave) run[e] = hist[static_cast<size_t>(c) * E + e];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    run[e] = hist[static_cast<size_t>(c) * E + e];
+#pragma unroll
+    for (int w = 0; w < kScatterWaves; ++w) wcnt[w][e] = 0;
+  }
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt = (uint64_t{1} << lane) - 1, gt = ~lt & ~(uint64_t{1} << lane);
+  const uint64_t lt = (uint64_t{1} << lane) - 1;
   __syncthreads();
   const int i0 = c * kAlignChunk, i1 = min(n, i0 + kAlignChunk);
-  for (int g = i0; g < i1; g += kWave) {
-    const int i = g + lane;
+  for (int g = i0; g < i1; g += 64 * kScatterWaves) {
+    const int i = g + 64 * wave + lane;
     int id = i < i1 ? ids[i] : -1;
     if (static_cast<unsigned>(id) >= static_cast<unsigned>(E)) id = -1;  // ignored, as in the count
     const bool valid = id >= 0;
@@ -181,15 +190,30 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
       peers &= bit ? bal : ~bal;
     }
     const int rank = __popcll(peers & lt);
-    const bool last = (peers & gt) == 0;
-    int pos = 0;
-    if (valid) pos = run[id] + rank;
+    const bool last = valid && (peers >> lane) == 1;
+    if (last) wcnt[wave][id] = __popcll(peers);
     __syncthreads();
+    int before = 0, group = 0;
     if (valid) {
-      sorted_ids[pos] = i;
-      if (last) run[id] = pos + 1;
+#pragma unroll
+      for (int w = 0; w < kScatterWaves; ++w) {
+        const int x = wcnt[w][id];
+        before += w < wave ? x : 0;
+        group += x;
+      }
+      sorted_ids[run[id] + before + rank] = i;
     }
     __syncthreads();
+    // the last wave holding the expert advances its running position; each
+    // record is cleared by the lane that wrote it
+    if (last) {
+      bool later = false;
+#pragma unroll
+      for (int w = 0; w < kScatterWaves; ++w) later |= w > wave && wcnt[w][id] != 0;
+      if (!later) run[id] += group;
+    }
+    __syncthreads();
+    if (last) wcnt[wave][id] = 0;
   }
 }
 
@@ -217,7 +241,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int32_t
   align_hist_kernel<<<nchunks, 256, 0, s>>>(ids, n, E, hist, zero_words, n_zero);
   align_scan_kernel<<<1, 1024, 0, s>>>(n, E, BM, P, nchunks, hist, counts, offsets, sorted_ids,
                                        block_expert, num_padded);
-  align_scatter_kernel<<<nchunks, 64, 0, s>>>(ids, n, E, hist, sorted_ids);
+  align_scatter_kernel<<<nchunks, 64 * kScatterWaves, 0, s>>>(ids, n, E, hist, sorted_ids);
   return hipGetLastError();
 }
 
