@@ -62,6 +62,9 @@ __device__ __forceinline__ float fp8_scale_from_amax(uint32_t bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
+// NT: the source is read with the non-temporal hint (large sources, read
+// once: the bf16 h of the FP8 layers).
+template <bool NT>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                         const uint32_t* __restrict__ amax_bits,
                                                         uint8_t* __restrict__ q, float* scale_out) {
@@ -70,7 +73,13 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
   const int64_t i0 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (i0 == 0 && scale_out) *scale_out = s;
   for (int64_t i = i0; i < n8; i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    uint4 v;
+    if constexpr (NT) {
+      const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + i);
+      v = make_uint4(u.x, u.y, u.z, u.w);
+    } else {
+      v = reinterpret_cast<const uint4*>(x)[i];
+    }
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2];
 #pragma unroll
@@ -97,17 +106,26 @@ hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* amax_bits, h
   return launch(amax_bf16_kernel, dim3(elementwise_grid(n / 8, 512)), dim3(256), 0, s, x, n, amax_bits);
 }
 
+// Sources larger than this are read with the non-temporal hint (measured
+// faster once they exceed the Infinity Cache, slightly slower below it).
+constexpr int64_t kStreamNtBytes = int64_t{192} << 20;
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, const uint32_t* amax_bits, uint8_t* q,
                             float* scale_out, hipStream_t s) {
-  return launch(quant_fp8_kernel, dim3(elementwise_grid(n / 8)), dim3(256), 0, s, x, n, amax_bits, q, scale_out);
+  const dim3 grid(elementwise_grid(n / 8));
+  if (n * static_cast<int64_t>(sizeof(uint16_t)) > kStreamNtBytes)
+    return launch(quant_fp8_kernel<true>, grid, dim3(256), 0, s, x, n, amax_bits, q, scale_out);
+  return launch(quant_fp8_kernel<false>, grid, dim3(256), 0, s, x, n, amax_bits, q, scale_out);
 }
 
 // -------------------------------------------------------------- combine ---
 // One thread per 8 outputs: y[t, n:n+8] = sum_j w[t,j] o[t*k+j, n:n+8]
 // (+ sg[t] * sh[t, n:n+8]), fp32 sums in ascending j, bf16 nearest-even.
 // Every row's load is issued before the sums (MAXK >= k rows, unrolled), so
-// the k loads of a thread are in flight together.
-template <int MAXK>
+// the k loads of a thread are in flight together.  NT: the expert outputs
+// are read with the non-temporal hint (each is read once; measured 20%
+// faster when they exceed the Infinity Cache, slightly slower below it).
+template <int MAXK, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o,
                                                       const float* __restrict__ w, int T, int k, int H,
                                                       const float* __restrict__ sg,
@@ -124,7 +142,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int j = 0; j < MAXK; ++j) {
     if (j < k) {
       wj[j] = w[static_cast<size_t>(t) * k + j];
-      v[j] = *reinterpret_cast<const uint4*>(o + (static_cast<size_t>(t) * k + j) * H + c);
+      const uint16_t* src = o + (static_cast<size_t>(t) * k + j) * H + c;
+      if constexpr (NT) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        v[j] = make_uint4(q.x, q.y, q.z, q.w);
+      } else {
+        v[j] = *reinterpret_cast<const uint4*>(src);
+      }
     }
   }
   float acc[8] = {};
@@ -161,8 +185,12 @@ hipError_t launch_combine(const uint16_t* o, const float* w, int T, int k, int H
                           const uint16_t* sh, uint16_t* y, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  if (k <= 8) return launch(combine_kernel<8>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
-  return launch(combine_kernel<16>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
+  const bool nt = static_cast<int64_t>(T) * k * H * static_cast<int64_t>(sizeof(uint16_t)) > kStreamNtBytes;
+  if (k <= 8)
+    return nt ? launch(combine_kernel<8, true>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y)
+              : launch(combine_kernel<8, false>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
+  return nt ? launch(combine_kernel<16, true>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y)
+            : launch(combine_kernel<16, false>, grid, dim3(256), 0, s, o, w, T, k, H, sg, sh, y);
 }
 
 // ------------------------------------------------- expert-slot pool fill ---
