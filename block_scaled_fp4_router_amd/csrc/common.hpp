@@ -153,12 +153,12 @@ __device__ __forceinline__ void mx_split_pair(float a, float b, uint32_t* hi2, u
   *lo2 = f32x2_to_e4m3x2((a - dh[0]) * 16.0f, (b - dh[1]) * 16.0f);
 }
 
-// Splits one 32-block of bf16 values (4 vectors of 8) into 32 hi codes, 32
-// lo codes (16-byte aligned destinations, global or LDS) and the scale code.
-__device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi, uint8_t* lo, uint8_t* sc) {
+// Largest magnitude of the bf16 values in n vectors of 8.
+template <int N>
+__device__ __forceinline__ float bf16_amax(const uint4 (&v)[N]) {
   float amax = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < N; ++q) {
     const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -166,11 +166,18 @@ __device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi,
       amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[i] >> 16)));
     }
   }
+  return amax;
+}
+
+// Half of a 32-block (16 bf16 values, 2 vectors of 8) in the split form, given
+// the maximum over the whole block: 16 hi codes, 16 lo codes; returns the
+// block's scale code.
+__device__ __forceinline__ uint32_t mx_split_half(const uint4 (&v)[2], float amax, uint4& hi, uint4& lo) {
   const uint32_t code = mx_split_scale_code(amax);
   const float inv = mx_inv_scale(code);
-  uint32_t hw[8], lw[8];
+  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
@@ -181,10 +188,23 @@ __device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi,
       lw[2 * q + i / 2] = l0 | (l1 << 16);
     }
   }
-  reinterpret_cast<uint4*>(hi)[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-  reinterpret_cast<uint4*>(hi)[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-  reinterpret_cast<uint4*>(lo)[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-  reinterpret_cast<uint4*>(lo)[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  return code;
+}
+
+// Splits one 32-block of bf16 values (4 vectors of 8) into 32 hi codes, 32
+// lo codes (16-byte aligned destinations, global or LDS) and the scale code.
+__device__ __forceinline__ void mx_split_block(const uint4 (&v)[4], uint8_t* hi, uint8_t* lo, uint8_t* sc) {
+  const float amax = bf16_amax(v);
+  const uint4 a[2] = {v[0], v[1]}, b[2] = {v[2], v[3]};
+  uint4 h0, l0, h1, l1;
+  const uint32_t code = mx_split_half(a, amax, h0, l0);
+  mx_split_half(b, amax, h1, l1);
+  reinterpret_cast<uint4*>(hi)[0] = h0;
+  reinterpret_cast<uint4*>(hi)[1] = h1;
+  reinterpret_cast<uint4*>(lo)[0] = l0;
+  reinterpret_cast<uint4*>(lo)[1] = l1;
   *sc = static_cast<uint8_t>(code);
 }
 
@@ -199,24 +219,14 @@ __device__ __forceinline__ uint32_t mxfp8_scale_code(float amax) {
   return static_cast<uint32_t>(ebits > 8 ? ebits - 8 : 0);
 }
 
-// Converts one 32-block of bf16 values (4 vectors of 8) to 32 E4M3 codes
-// (16-byte aligned destination, global or LDS) and the scale code.
-__device__ __forceinline__ void mxfp8_block(const uint4 (&v)[4], uint8_t* q, uint8_t* sc) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[c] & 0xFFFF)));
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[c] >> 16)));
-    }
-  }
+// Half of a 32-block (16 bf16 values) as E4M3 codes under the block's scale,
+// given the maximum over the whole block; returns the scale code.
+__device__ __forceinline__ uint32_t mxfp8_half(const uint4 (&v)[2], float amax, uint4& q) {
   const uint32_t code = mxfp8_scale_code(amax);
   const float inv = mx_inv_scale(code);
-  uint32_t o[8];
+  uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     const uint32_t p0 = f32x2_to_e4m3x2(bf16_to_f32(w[0] & 0xFFFF) * inv, bf16_to_f32(w[0] >> 16) * inv);
     const uint32_t p1 = f32x2_to_e4m3x2(bf16_to_f32(w[1] & 0xFFFF) * inv, bf16_to_f32(w[1] >> 16) * inv);
@@ -225,8 +235,20 @@ __device__ __forceinline__ void mxfp8_block(const uint4 (&v)[4], uint8_t* q, uin
     o[2 * i] = p0 | (p1 << 16);
     o[2 * i + 1] = p2 | (p3 << 16);
   }
-  reinterpret_cast<uint4*>(q)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  reinterpret_cast<uint4*>(q)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  q = make_uint4(o[0], o[1], o[2], o[3]);
+  return code;
+}
+
+// Converts one 32-block of bf16 values (4 vectors of 8) to 32 E4M3 codes
+// (16-byte aligned destination, global or LDS) and the scale code.
+__device__ __forceinline__ void mxfp8_block(const uint4 (&v)[4], uint8_t* q, uint8_t* sc) {
+  const float amax = bf16_amax(v);
+  const uint4 a[2] = {v[0], v[1]}, b[2] = {v[2], v[3]};
+  uint4 q0, q1;
+  const uint32_t code = mxfp8_half(a, amax, q0);
+  mxfp8_half(b, amax, q1);
+  reinterpret_cast<uint4*>(q)[0] = q0;
+  reinterpret_cast<uint4*>(q)[1] = q1;
   *sc = static_cast<uint8_t>(code);
 }
 

@@ -320,9 +320,11 @@ ftmoe_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
 
 // Router.  With `align` (decode plans with few tokens) the fused top-k kernel
 // also writes the block alignment and clears the per-call counters, so the
-// experts stage can skip its own align launch.
+// experts stage can skip its own align launch.  With `gemm_x` (prefill plans
+// with MXFP4 experts) the router GEMM also writes x in the form the expert
+// GEMMs read, so the experts stage can skip its x conversion.
 ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const Plan& p, void* ws, int32_t* ids,
-                           float* w, float* sg, bool align, hipStream_t s) {
+                           float* w, float* sg, bool align, bool gemm_x, hipStream_t s) {
   const bool shared = L->shared_inter > 0;
   const int E = L->num_experts, k = L->top_k;
   if (p.small_route) {
@@ -359,7 +361,8 @@ ftmoe_status enqueue_route(const ftmoe_layer* L, const uint16_t* x, int T, const
   FT_HIP(timed("router_logits", s,
                [&] {
                  return launch_router_logits(x, T, L->hidden, L->router_w, E, shared ? L->shared_gate_w : nullptr,
-                                             planes, logits, s);
+                                             planes, logits, gemm_x ? at<uint8_t>(ws, p.xs) : nullptr,
+                                             gemm_x ? at<uint8_t>(ws, p.xssc) : nullptr, p.a8, s);
                }),
          "router logits launch");
   FT_HIP(timed("topk", s,
@@ -390,8 +393,8 @@ struct Passes {
 };
 
 ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, const int32_t* ids, const float* w,
-                             const float* sg, const Plan& p, void* ws, uint16_t* y, bool aligned, hipStream_t s,
-                             const Passes& passes = Passes{}) {
+                             const float* sg, const Plan& p, void* ws, uint16_t* y, bool aligned, bool x_ready,
+                             hipStream_t s, const Passes& passes = Passes{}) {
   const int E = L->num_experts, k = L->top_k, H = L->hidden, I = L->inter;
   const bool fp8act = L->act == FTMOE_ACT_FP8_PER_TENSOR;
   const bool shared = L->shared_inter > 0;
@@ -523,11 +526,13 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     xa.split = at<uint8_t>(ws, p.xs);
     xa.split_sc = at<uint8_t>(ws, p.xssc);
     xa.mx8 = p.a8;
-    FT_HIP(timed("x_split", s,
-                 [&] {
-                   return launch_x_split_gemm(x, T, H, at<uint8_t>(ws, p.xs), at<uint8_t>(ws, p.xssc), p.a8, s);
-                 }),
-           "x split launch");
+    if (!x_ready) {   // the router of this call did not write it
+      FT_HIP(timed("x_split", s,
+                   [&] {
+                     return launch_x_split_gemm(x, T, H, at<uint8_t>(ws, p.xs), at<uint8_t>(ws, p.xssc), p.a8, s);
+                   }),
+             "x split launch");
+    }
   }
   uint8_t* hgsc = p.mx_gemm ? at<uint8_t>(ws, p.hgsc) : nullptr;
   GemmAct ha{};
@@ -591,8 +596,9 @@ ftmoe_status enqueue_forward(const ftmoe_layer* layer, const uint16_t* x, int T,
   float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
   float* sg = at<float>(ws, p.sg);
   const bool fused_align = p.decode && p.small_route;
-  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, s));
-  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, s);
+  const bool gemm_x = !p.small_route && (p.mx_gemm || p.mx_gemm_shared);
+  FT_TRY(enqueue_route(layer, x, T, p, ws, ids, w, sg, fused_align, gemm_x, s));
+  return enqueue_experts(layer, x, T, ids, w, sg, p, ws, y, fused_align, gemm_x, s);
 }
 
 // ---- allocation-free forward: a fixed scratch array in device memory ----
@@ -1202,7 +1208,8 @@ ftmoe_status ftmoe_route(const ftmoe_layer* layer, const uint16_t* x, int32_t T,
     return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
   const Plan p = make_plan(layer, T);
   FT_TRY(check_ws(p, ws, ws_bytes));
-  return enqueue_route(layer, x, T, p, ws, topk_ids, topk_w, shared_gate, false, static_cast<hipStream_t>(stream));
+  return enqueue_route(layer, x, T, p, ws, topk_ids, topk_w, shared_gate, false, false,
+                       static_cast<hipStream_t>(stream));
 }
 
 ftmoe_status ftmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m, int32_t* counts,
@@ -1237,7 +1244,7 @@ ftmoe_status ftmoe_experts_forward(const ftmoe_layer* layer, const uint16_t* x, 
     return fail(FTMOE_ERR_INVALID_ARG, "the layer has a shared expert: shared_gate must be non-NULL");
   const Plan p = make_plan(layer, T);
   FT_TRY(check_ws(p, ws, ws_bytes));
-  return enqueue_experts(layer, x, T, topk_ids, topk_w, shared_gate, p, ws, y, false,
+  return enqueue_experts(layer, x, T, topk_ids, topk_w, shared_gate, p, ws, y, false, false,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -1501,7 +1508,8 @@ static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_
   float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
   float* sg = at<float>(ws, p.sg);
   const bool fused_align = p.decode && p.small_route;
-  FT_TRY(enqueue_route(L, x, T, p, ws, ids, w, sg, fused_align, s));
+  const bool gemm_x = !p.small_route && (p.mx_gemm || p.mx_gemm_shared);
+  FT_TRY(enqueue_route(L, x, T, p, ws, ids, w, sg, fused_align, gemm_x, s));
 
   // host resources (made once), the routing ids on their way to the host
   const size_t n_ids = static_cast<size_t>(T) * k;
@@ -1556,7 +1564,7 @@ static ftmoe_status cache_forward_impl(ftmoe_cache* c, const uint16_t* x, int32_
     c->run.before_combine = cache_spec_combine;
   }
   c->run.tables = c->tptr.data();
-  return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, s, c->run);
+  return enqueue_experts(L, x, T, ids, w, sg, p, ws, y, fused_align, gemm_x, s, c->run);
 }
 
 ftmoe_status ftmoe_cache_set_host_compute(ftmoe_cache* c, int32_t threads, double expert_s, double row_s,

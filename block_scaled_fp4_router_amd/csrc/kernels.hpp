@@ -85,8 +85,11 @@ int router_splits_gemm(int T, int H, int rows);
 size_t router_planes_bytes(int E, int H, bool shared);
 hipError_t launch_router_split(const float* router_w, int E, int H, const float* shared_gate_w, uint16_t* planes,
                                hipStream_t s);
+// With xs (many tokens only) the GEMM also writes x for MXFP4 expert GEMMs:
+// split E4M3 pairs, or MXFP8 codes with a8, and E8M0 scales (xssc).
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                const float* shared_gate_w, const uint16_t* planes, float* logits, hipStream_t s);
+                                const float* shared_gate_w, const uint16_t* planes, float* logits, uint8_t* xs,
+                                uint8_t* xssc, bool a8, hipStream_t s);
 // bias_select: the bias ranks the experts only; the weights are the softmax
 // of the selected logits without it.
 hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, const float* bias, bool bias_select,

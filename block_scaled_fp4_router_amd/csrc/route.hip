@@ -101,9 +101,17 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     *reinterpret_cast<uint4*>(planes + m * plane + el) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
 }
 
+// With xout (MXFP4 experts) the workgroups of the first router-row tile also
+// write x in the form the expert GEMMs read, from the x stages they load
+// anyway: split E4M3 pairs ([T][2H], per 64 elements 64 hi then 64 lo codes)
+// or, with a8, MXFP8 codes ([T][H]), and the E8M0 scales [T][H / 32].  A
+// thread holds half of a 32-block; the other half is in lane ^ 1.
+template <bool XOUT>
 __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                                 const uint16_t* __restrict__ planes, int E,
-                                                                int rows, float* __restrict__ logits) {
+                                                                int rows, float* __restrict__ logits,
+                                                                uint8_t* __restrict__ xout, uint8_t* __restrict__ xsc_out,
+                                                                int a8) {
   // blockIdx.z: the K split; split z sums H range [z, z + 1) * H / gridDim.z into logits[z]
   __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
@@ -146,6 +154,27 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
     }
   };
 
+  const bool split_x = XOUT && blockIdx.y == 0;   // uniform per workgroup
+  auto split_stage = [&](const Stage& sg, int k0) {
+    float m = bf16_amax(sg.x);
+    m = __builtin_fmaxf(m, __shfl_xor(m, 1, kWave));
+    if (!xrow) return;
+    const int e0 = k0 + 8 * sq;   // the thread's 16 elements; its 32-block is e0 / 32
+    uint32_t code;
+    if (a8) {
+      uint4 q;
+      code = mxfp8_half(sg.x, m, q);
+      *reinterpret_cast<uint4*>(xout + static_cast<size_t>(t) * H + e0) = q;
+    } else {
+      uint4 hi, lo;
+      code = mx_split_half(sg.x, m, hi, lo);
+      uint8_t* dst = xout + static_cast<size_t>(t) * (2 * H) + (e0 / 64) * 128 + (e0 % 64);
+      *reinterpret_cast<uint4*>(dst) = hi;
+      *reinterpret_cast<uint4*>(dst + 64) = lo;
+    }
+    if ((sq & 2) == 0) xsc_out[static_cast<size_t>(t) * (H / 32) + e0 / 32] = static_cast<uint8_t>(code);
+  };
+
   f32x16 acc = {};
   const int kspan = H / static_cast<int>(gridDim.z), kbeg = static_cast<int>(blockIdx.z) * kspan;
   const int ns = kspan / kRK;
@@ -162,6 +191,8 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
       if (s >= ns) break;
       __syncthreads();   // the previous stage's reads are done
       store(st[u]);
+      if constexpr (XOUT)
+        if (split_x) split_stage(st[u], kbeg + s * kRK);
       __syncthreads();
       if (s + kRPF < ns) load(st[u], kbeg + (s + kRPF) * kRK);
 #pragma unroll
@@ -210,7 +241,8 @@ hipError_t launch_router_split(const float* router_w, int E, int H, const float*
 }
 
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* router_w, int E,
-                                const float* shared_gate_w, const uint16_t* planes, float* logits, hipStream_t s) {
+                                const float* shared_gate_w, const uint16_t* planes, float* logits, uint8_t* xs,
+                                uint8_t* xssc, bool a8, hipStream_t s) {
   const int rows = E + (shared_gate_w ? 1 : 0);
   if (T <= kGemvMaxT) {
     dim3 grid((rows + 3) / 4);
@@ -223,7 +255,11 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
   } else {
     dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE, router_splits_gemm(T, H, rows));
     if (!planes) return hipErrorInvalidValue;
-    return launch(router_gemm_kernel, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits);
+    if (xs)
+      return launch(router_gemm_kernel<true>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits, xs,
+                    xssc, a8 ? 1 : 0);
+    return launch(router_gemm_kernel<false>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits, xs, xssc,
+                  0);
   }
 }
 
