@@ -193,6 +193,35 @@ def test_experts_forward_with_given_routing():
     assert rel_fro(bf16_dev_to_f64(y), ref["y"]) <= 2e-2
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,T", [("c0", 300), ("c1", 200), ("c1-w4a8", 64), ("c3", 40)])
+def test_forward_equals_route_then_experts_forward_prefill(name, T):
+    """On the prefill kernels, ftmoe_forward (whose router GEMM also writes the
+    split or MXFP8 x of MXFP4 layers) equals ftmoe_route followed by
+    ftmoe_experts_forward (which converts x with its own kernel) bit for
+    bit: both conversions implement the same block rule."""
+    say(f"forward == route + experts_forward, prefill kernels, {name} T={T}")
+    lay, dlay = layer_pair(name)
+    pl = dlay.with_path("prefill")
+    x = synth.make_tokens(lay, T, stream=5)
+    xd = to_dev_bf16(x)
+    k = dlay.top_k
+    ws = ft.alloc_workspace(pl, T)
+    y1 = torch.empty((T, dlay.hidden), dtype=torch.int16, device=DEV)
+    ids1 = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w1 = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ft.forward(pl, xd, T, ws, y1, ids1, w1)
+    ids2 = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w2 = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    sg = torch.empty((T,), dtype=torch.float32, device=DEV) if dlay.shared_inter else None
+    ft.route(pl, xd, T, ws, ids2, w2, sg)
+    y2 = torch.empty((T, dlay.hidden), dtype=torch.int16, device=DEV)
+    ft.experts_forward(pl, xd, T, ids2, w2, sg, ws, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and torch.equal(w1, w2)
+    assert torch.equal(y1, y2)
+
+
 # ---------------------------------------------------------- FP8 quantiser --
 @pytest.mark.timeout(300)
 def test_fp8_quantiser_bit_exact():
