@@ -66,13 +66,17 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------- large table ---
+// Per-chunk histograms; the workgroups also fill sorted_ids [0, P) with the
+// sentinel n (the scatter overwrites the routed rows' entries), so that the
+// one-workgroup scan writes no padding.
 __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                         int32_t* __restrict__ hist,
-                                                         uint32_t* zero_words, int n_zero) {
+                                                         int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
+                                                         int P, uint32_t* zero_words, int n_zero) {
   __shared__ int cnt[kAlignMaxE];
   const int c = blockIdx.x;
   if (c == 0)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
+  for (int i = c * blockDim.x + threadIdx.x; i < P; i += gridDim.x * blockDim.x) sorted_ids[i] = n;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   const int i0 = c * kAlignChunk, i1 = min(n, i0 + kAlignChunk);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int n, int E, int BM, 
   // 3. layout (thread e = expert e)
   int off, total;
   finish_layout(tid, E, tid < E ? total_e : 0, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded,
-                tmp, &off, &total);
+                tmp, &off, &total, false);
   if (tid < E) exp_off[tid] = off;
   __syncthreads();
   // 4. every (chunk, expert) entry becomes the expert's first slot for that chunk
@@ -238,7 +242,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int32_t
   }
   const int nchunks = (n + kAlignChunk - 1) / kAlignChunk;
   int32_t* hist = static_cast<int32_t*>(scratch);
-  align_hist_kernel<<<nchunks, 256, 0, s>>>(ids, n, E, hist, zero_words, n_zero);
+  align_hist_kernel<<<nchunks, 256, 0, s>>>(ids, n, E, hist, sorted_ids, P, zero_words, n_zero);
   align_scan_kernel<<<1, 1024, 0, s>>>(n, E, BM, P, nchunks, hist, counts, offsets, sorted_ids,
                                        block_expert, num_padded);
   align_scatter_kernel<<<nchunks, 64 * kScatterWaves, 0, s>>>(ids, n, E, hist, sorted_ids);
