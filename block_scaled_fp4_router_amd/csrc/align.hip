@@ -38,6 +38,9 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
   __shared__ int tmp[32];
   const int e = threadIdx.x;
   for (int i = e; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
+  // every sorted slot starts as the sentinel (coalesced); the routed rows'
+  // slots are overwritten at the end, after several barriers
+  for (int i = e; i < P; i += blockDim.x) sorted_ids[i] = n;
   cnt[e] = 0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) ids_s[i] = ids[i];
   __syncthreads();
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
   __syncthreads();
   const int c = e < E ? cnt[e] : 0;
   int off, total;
-  finish_layout(e, E, c, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off, &total);
+  finish_layout(e, E, c, BM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off, &total, false);
   if (e < E) cnt[e] = off;   // the counts are no longer needed: reuse as segment starts
   __syncthreads();
   // row i goes after the earlier rows of its expert (stable counting sort);

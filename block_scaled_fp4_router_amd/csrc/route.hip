@@ -497,6 +497,9 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
   const int rows = E + (has_shared ? 1 : 0);
   const int nw = (T * k + kWave - 1) / kWave;
   for (int i = tid; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
+  // every sorted slot starts as the sentinel (coalesced); the routed rows'
+  // slots are overwritten at the end, after several barriers
+  for (int i = tid; i < P; i += blockDim.x) sorted_ids[i] = T * k;
   const bool few = T * k <= kFewRows;   // rank by a scan of the earlier rows
   if (few)
     cnt[tid] = 0;
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(1024) void topk_align_decode_kernel(
   }
   int off, total;
   finish_layout(tid, E, c, kDecodeBM, n, P, counts, offsets, sorted_ids, block_expert, num_padded, tmp, &off,
-                &total);
+                &total, false);
   if (tid < E) cnt[tid] = off;   // segment starts
   __syncthreads();
   if (my_id >= 0) {
