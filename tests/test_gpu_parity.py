@@ -66,7 +66,9 @@ def _random_ids(T, k, E, seed, skew=None):
                                            (37, 3, 5, 8, None), (300, 4, 16, 1, None), (4096, 8, 128, 64, None),
                                            (16384, 8, 128, 64, 1.1), (16384, 8, 128, 128, 1.1),
                                            (8192, 10, 512, 64, None),
-                                           (129, 16, 16, 64, None), (2000, 1, 1, 128, None)])
+                                           (129, 16, 16, 64, None), (2000, 1, 1, 128, None),
+                                           # more chunks per scan thread than it keeps in registers
+                                           (65536, 8, 128, 128, 1.1), (3000, 16, 1024, 64, None)])
 @pytest.mark.timeout(300)
 def test_align_parity(T, k, E, BM, skew):
     say(f"align parity T={T} k={k} E={E} BM={BM}")
