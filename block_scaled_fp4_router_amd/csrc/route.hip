@@ -55,11 +55,21 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 // fp32 and the MFMA accumulates in fp32, so the logits keep fp32 accuracy.
 // The split is made once per call into three bf16 planes [3][rows][H] (every
 // token tile of the GEMM would otherwise convert the same weights again).
-// Workgroup: 64 tokens x 64 router rows, 4 waves of one 32 x 32 tile each;
-// K stages of 64 staged through LDS (rows of 128 bytes, XOR-swizzled).  The
-// global loads run kRPF stages ahead of the MFMA work, each stage in its own
-// register set, so that their latency is covered by as many stages of work.
-constexpr int kRT = 64, kRE = 64, kRK = 64, kRThreads = 256, kRPF = 2;
+// Workgroup: RT tokens x 64 router rows, 4 waves of RT / 2 tokens x 32 rows
+// each (RT = 128: two 32 x 32 tiles per wave sharing the weight fragments,
+// so every weight fragment read from LDS feeds two MFMAs; RT = 64, for token
+// counts that would leave CUs idle, one); K stages of 64 staged through LDS
+// (rows of 128 bytes, XOR-swizzled).  The global loads of the next stage are
+// issued before the current stage's MFMA work, and several workgroups share
+// each CU, so their latency is covered.
+constexpr int kRE = 64, kRK = 64, kRThreads = 256;
+
+// Token tile of the router GEMM for T tokens and `rows` router rows: 128
+// when that still gives 256 tiles, else 64.
+int router_token_tile(int T, int rows) {
+  const long long t128 = static_cast<long long>((T + 127) / 128) * ((rows + kRE - 1) / kRE);
+  return t128 >= 256 ? 128 : 64;
+}
 
 __device__ __forceinline__ int rswz(int r, int q) { return q ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
@@ -101,54 +111,59 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     *reinterpret_cast<uint4*>(planes + m * plane + el) = make_uint4(p[m][0], p[m][1], p[m][2], p[m][3]);
 }
 
-// With xout (MXFP4 experts) the workgroups of the first router-row tile also
+// With XOUT (MXFP4 experts) the workgroups of the first router-row tile also
 // write x in the form the expert GEMMs read, from the x stages they load
 // anyway: split E4M3 pairs ([T][2H], per 64 elements 64 hi then 64 lo codes)
 // or, with a8, MXFP8 codes ([T][H]), and the E8M0 scales [T][H / 32].  A
-// thread holds half of a 32-block; the other half is in lane ^ 1.
-template <bool XOUT>
+// thread stages one 32-block of x per stage (RT = 128) or half of one, the
+// other half being in lane ^ 1 (RT = 64).
+template <int RT, bool XOUT>
 __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                                 const uint16_t* __restrict__ planes, int E,
                                                                 int rows, float* __restrict__ logits,
                                                                 uint8_t* __restrict__ xout, uint8_t* __restrict__ xsc_out,
                                                                 int a8) {
   // blockIdx.z: the K split; split z sums H range [z, z + 1) * H / gridDim.z into logits[z]
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kRT * 128];
+  constexpr int MW = RT / 64;    // 32-token tiles per wave
+  constexpr int XV = RT / 32;    // x vectors a thread stages per stage
+  __shared__ __attribute__((aligned(16))) uint8_t xs[RT * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ws[3][kRE * 128];
-  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
+  const int t0 = blockIdx.x * RT, e0 = blockIdx.y * kRE;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
+  const int wt = (wave & 1) * 32 * MW, we = (wave >> 1) * 32;
   const int j = lane & 31, g = lane >> 5;
 
-  // staging: x row tid / 4 and W row tid / 4, vectors 2 (tid % 4) and + 1 of
-  // their 128-byte stage rows (of each of the three planes for W)
-  const int sr = tid >> 2, sq = (tid & 3) * 2;
-  const int t = t0 + sr, e = e0 + sr;
+  // staging: x row tid / (8 / XV), vectors XV (tid % (8 / XV)) .. + XV - 1;
+  // W row tid / 4, vectors 2 (tid % 4) and + 1 of each of the three planes
+  const int xr = tid / (8 / XV), xq = (tid % (8 / XV)) * XV;
+  const int wr = tid >> 2, wq = (tid & 3) * 2;
+  const int t = t0 + xr, e = e0 + wr;
   const uint16_t* xrow = t < T ? x + static_cast<size_t>(t) * H : nullptr;
   const size_t plane = static_cast<size_t>(rows) * H;
   const uint16_t* wrow = e < rows ? planes + static_cast<size_t>(e) * H : nullptr;
 
   struct Stage {
-    uint4 x[2];
+    uint4 x[XV];
     uint4 w[3][2];
   };
-  Stage st[kRPF];
+  Stage st;
   auto load = [&](Stage& sg, int k0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      sg.x[h] = xrow ? *reinterpret_cast<const uint4*>(xrow + k0 + (sq + h) * 8) : make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < XV; ++h)
+      sg.x[h] = xrow ? *reinterpret_cast<const uint4*>(xrow + k0 + (xq + h) * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        sg.w[m][h] = wrow ? *reinterpret_cast<const uint4*>(wrow + m * plane + k0 + (sq + h) * 8)
+        sg.w[m][h] = wrow ? *reinterpret_cast<const uint4*>(wrow + m * plane + k0 + (wq + h) * 8)
                           : make_uint4(0, 0, 0, 0);
   };
   auto store = [&](const Stage& sg) {
 #pragma unroll
+    for (int h = 0; h < XV; ++h) *reinterpret_cast<uint4*>(xs + xr * 128 + 16 * rswz(xr, xq + h)) = sg.x[h];
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int off = sr * 128 + 16 * rswz(sr, sq + h);
-      *reinterpret_cast<uint4*>(xs + off) = sg.x[h];
+      const int off = wr * 128 + 16 * rswz(wr, wq + h);
 #pragma unroll
       for (int m = 0; m < 3; ++m) *reinterpret_cast<uint4*>(ws[m] + off) = sg.w[m][h];
     }
@@ -156,65 +171,75 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
 
   const bool split_x = XOUT && blockIdx.y == 0;   // uniform per workgroup
   auto split_stage = [&](const Stage& sg, int k0) {
-    float m = bf16_amax(sg.x);
-    m = __builtin_fmaxf(m, __shfl_xor(m, 1, kWave));
-    if (!xrow) return;
-    const int e0 = k0 + 8 * sq;   // the thread's 16 elements; its 32-block is e0 / 32
-    uint32_t code;
-    if (a8) {
-      uint4 q;
-      code = mxfp8_half(sg.x, m, q);
-      *reinterpret_cast<uint4*>(xout + static_cast<size_t>(t) * H + e0) = q;
-    } else {
-      uint4 hi, lo;
-      code = mx_split_half(sg.x, m, hi, lo);
-      uint8_t* dst = xout + static_cast<size_t>(t) * (2 * H) + (e0 / 64) * 128 + (e0 % 64);
-      *reinterpret_cast<uint4*>(dst) = hi;
-      *reinterpret_cast<uint4*>(dst + 64) = lo;
+    const int e0 = k0 + 8 * xq;   // the thread's elements start here; its 32-block is e0 / 32
+    if constexpr (XV == 4) {
+      if (!xrow) return;
+      uint8_t* sc = xsc_out + static_cast<size_t>(t) * (H / 32) + e0 / 32;
+      if (a8) {
+        mxfp8_block(sg.x, xout + static_cast<size_t>(t) * H + e0, sc);
+      } else {
+        uint8_t* hi = xout + static_cast<size_t>(t) * (2 * H) + (e0 / 64) * 128 + (e0 % 64);
+        mx_split_block(sg.x, hi, hi + 64, sc);
+      }
+    } else {   // half a block: the block maximum from lane ^ 1 (every lane joins)
+      float m = bf16_amax(sg.x);
+      m = __builtin_fmaxf(m, __shfl_xor(m, 1, kWave));
+      if (!xrow) return;
+      uint32_t code;
+      if (a8) {
+        uint4 q;
+        code = mxfp8_half(sg.x, m, q);
+        *reinterpret_cast<uint4*>(xout + static_cast<size_t>(t) * H + e0) = q;
+      } else {
+        uint4 hi, lo;
+        code = mx_split_half(sg.x, m, hi, lo);
+        uint8_t* dst = xout + static_cast<size_t>(t) * (2 * H) + (e0 / 64) * 128 + (e0 % 64);
+        *reinterpret_cast<uint4*>(dst) = hi;
+        *reinterpret_cast<uint4*>(dst + 64) = lo;
+      }
+      if ((xq & 2) == 0) xsc_out[static_cast<size_t>(t) * (H / 32) + e0 / 32] = static_cast<uint8_t>(code);
     }
-    if ((sq & 2) == 0) xsc_out[static_cast<size_t>(t) * (H / 32) + e0 / 32] = static_cast<uint8_t>(code);
   };
 
-  f32x16 acc = {};
+  f32x16 acc[MW] = {};
   const int kspan = H / static_cast<int>(gridDim.z), kbeg = static_cast<int>(blockIdx.z) * kspan;
   const int ns = kspan / kRK;
   logits += static_cast<size_t>(blockIdx.z) * T * (E + 1);
+  if (ns > 0) load(st, kbeg);
+  for (int s = 0; s < ns; ++s) {
+    __syncthreads();   // the previous stage's reads are done
+    store(st);
+    if constexpr (XOUT)
+      if (split_x) split_stage(st, kbeg + s * kRK);
+    __syncthreads();
+    if (s + 1 < ns) load(st, kbeg + (s + 1) * kRK);
 #pragma unroll
-  for (int u = 0; u < kRPF; ++u)
-    if (u < ns) load(st[u], kbeg + u * kRK);
-  // stage s uses register set s % kRPF; the loop is unrolled by kRPF so that
-  // every register set is named statically
-  for (int s0 = 0; s0 < ns; s0 += kRPF) {
+    for (int ks = 0; ks < 4; ++ks) {
+      const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
+      const int rb = we + j;
+      bf16x8 a[MW];
 #pragma unroll
-    for (int u = 0; u < kRPF; ++u) {
-      const int s = s0 + u;
-      if (s >= ns) break;
-      __syncthreads();   // the previous stage's reads are done
-      store(st[u]);
-      if constexpr (XOUT)
-        if (split_x) split_stage(st[u], kbeg + s * kRK);
-      __syncthreads();
-      if (s + kRPF < ns) load(st[u], kbeg + (s + kRPF) * kRK);
+      for (int m = 0; m < MW; ++m) {
+        const int ra = wt + 32 * m + j;
+        a[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + ra * 128 + 16 * rswz(ra, q)));
+      }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int q = 2 * ks + g;   // 8 bf16 of K group g of step ks
-        const int ra = wt + j, rb = we + j;
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + ra * 128 + 16 * rswz(ra, q)));
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 b =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ws[p] + rb * 128 + 16 * rswz(rb, q)));
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-          const bf16x8 b =
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ws[m] + rb * 128 + 16 * rswz(rb, q)));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-        }
+        for (int m = 0; m < MW; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b, acc[m], 0, 0, 0);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tt = t0 + wt + 8 * (r >> 2) + 4 * g + (r & 3);
-    const int ee = e0 + we + j;
-    if (tt < T && ee < rows) logits[static_cast<size_t>(tt) * (E + 1) + ee] = acc[r];
+  for (int m = 0; m < MW; ++m) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = t0 + wt + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int ee = e0 + we + j;
+      if (tt < T && ee < rows) logits[static_cast<size_t>(tt) * (E + 1) + ee] = acc[m][r];
+    }
   }
 }
 
@@ -223,7 +248,8 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(const uint16_t* 
 // deterministic).
 int router_splits_gemm(int T, int H, int rows) {
   if (T <= kGemvMaxT) return 1;
-  const long long tiles = static_cast<long long>((T + kRT - 1) / kRT) * ((rows + kRE - 1) / kRE);
+  const int rt = router_token_tile(T, rows);
+  const long long tiles = static_cast<long long>((T + rt - 1) / rt) * ((rows + kRE - 1) / kRE);
   int S = 1;
   while (S < 4 && tiles * S < 1024 && (H / kRK) % (2 * S) == 0) S *= 2;
   return S;
@@ -253,13 +279,17 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* ro
     else
       return launch(router_gemv_kernel<kGemvMaxT>, grid, dim3(256), 0, s, x, T, H, router_w, E, shared_gate_w, logits);
   } else {
-    dim3 grid((T + kRT - 1) / kRT, (rows + kRE - 1) / kRE, router_splits_gemm(T, H, rows));
     if (!planes) return hipErrorInvalidValue;
-    if (xs)
-      return launch(router_gemm_kernel<true>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits, xs,
-                    xssc, a8 ? 1 : 0);
-    return launch(router_gemm_kernel<false>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits, xs, xssc,
-                  0);
+    const int rt = router_token_tile(T, rows);
+    const dim3 grid((T + rt - 1) / rt, (rows + kRE - 1) / kRE, router_splits_gemm(T, H, rows));
+    auto go = [&]<int RT>() {
+      if (xs)
+        return launch(router_gemm_kernel<RT, true>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits,
+                      xs, xssc, a8 ? 1 : 0);
+      return launch(router_gemm_kernel<RT, false>, grid, dim3(kRThreads), 0, s, x, T, H, planes, E, rows, logits, xs,
+                    xssc, 0);
+    };
+    return rt == 128 ? go.template operator()<128>() : go.template operator()<64>();
   }
 }
 
