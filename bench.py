@@ -300,8 +300,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="leave out the prefill configurations the default decode line carries")
-    ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=100)
+    ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="decode: oracle steps run until this much time")
     ap.add_argument("--pool-slots", type=int, default=0,
                     help="serve the routed experts from pinned host memory through an HBM pool of this many "
