@@ -26,9 +26,11 @@ def tol_for(name):
 
 
 # ------------------------------------------------------------------ route --
+# (c3 at 8155 and c2 at 16300 tokens: 128-token router tiles with a ragged
+# last tile; for c2 and c2-w4a8 the router also writes the split or MXFP8 x)
 @pytest.mark.parametrize("name,T", [("c0", 16), ("c1", 1), ("c1", 8), ("c2", 4096), ("c3", 1), ("c3", 8192),
                                     ("c4", 16384), ("c1", 17), ("c3", 33), ("c4-selbias", 1), ("c4-selbias", 8),
-                                    ("c4-selbias", 16384)])
+                                    ("c4-selbias", 16384), ("c3", 8155), ("c2", 16300), ("c2-w4a8", 16300)])
 @pytest.mark.timeout(600)
 def test_route_parity(name, T):
     say(f"route parity {name} T={T}")
@@ -196,12 +198,16 @@ def test_experts_forward_with_given_routing():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,T", [("c0", 300), ("c1", 200), ("c1-w4a8", 64), ("c3", 40)])
+@pytest.mark.parametrize("name,T", [("c0", 300), ("c1", 200), ("c1-w4a8", 64), ("c3", 40), ("c2", 16300),
+                                    ("c2-w4a8", 16300)])
 def test_forward_equals_route_then_experts_forward_prefill(name, T):
     """On the prefill kernels, ftmoe_forward (whose router GEMM also writes the
     split or MXFP8 x of MXFP4 layers) equals ftmoe_route followed by
     ftmoe_experts_forward (which converts x with its own kernel) bit for
-    bit: both conversions implement the same block rule."""
+    bit: both conversions implement the same block rule.  (At 16300 tokens
+    the router runs 128-token tiles, where a thread converts a whole
+    32-block; at the smaller counts 64-token tiles, where two lanes share
+    one.)"""
     say(f"forward == route + experts_forward, prefill kernels, {name} T={T}")
     lay, dlay = layer_pair(name)
     pl = dlay.with_path("prefill")
