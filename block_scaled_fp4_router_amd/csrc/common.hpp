@@ -146,27 +146,45 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t code) {
 }
 
 // hi and lo E4M3 codes of two adjacent values already divided by the scale.
+// Such values lie in (-256, 256): the scale code is at least floor(log2
+// amax) - 7, and its lower clamp only makes them smaller.  The lo input,
+// 16 (a - hi), is at most 16 times half an E4M3 step at 128..256, i.e. 128.
+// Neither conversion can therefore leave E4M3's range (448), and the
+// hardware's nearest-even conversion needs no clamp in front of it.
 __device__ __forceinline__ void mx_split_pair(float a, float b, uint32_t* hi2, uint32_t* lo2) {
-  const uint32_t h = f32x2_to_e4m3x2(a, b);
+  const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false));
   const f32x2 dh = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 1.0f, false);
   *hi2 = h;
-  *lo2 = f32x2_to_e4m3x2((a - dh[0]) * 16.0f, (b - dh[1]) * 16.0f);
+  *lo2 = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32((a - dh[0]) * 16.0f, (b - dh[1]) * 16.0f, 0, false));
 }
 
-// Largest magnitude of the bf16 values in n vectors of 8.
+// The same for four adjacent values, codes packed as one dword each (the
+// second conversion of each writes the upper half of the first's dword).
+__device__ __forceinline__ void mx_split_quad(float a0, float a1, float a2, float a3, uint32_t& hi4, uint32_t& lo4) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, h, true);
+  const f32x2 d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<uint32_t>(h), 1.0f, false);
+  const f32x2 d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<uint32_t>(h), 1.0f, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32((a0 - d01[0]) * 16.0f, (a1 - d01[1]) * 16.0f, 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32((a2 - d23[0]) * 16.0f, (a3 - d23[1]) * 16.0f, l, true);
+  hi4 = static_cast<uint32_t>(h);
+  lo4 = static_cast<uint32_t>(l);
+}
+
+// Largest magnitude of the bf16 values in n vectors of 8.  With the sign bit
+// cleared, the bits of finite bf16 values order as their magnitudes, so the
+// maximum is taken on the 16-bit patterns, two per packed integer max.
 template <int N>
 __device__ __forceinline__ float bf16_amax(const uint4 (&v)[N]) {
-  float amax = 0.f;
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
 #pragma unroll
   for (int q = 0; q < N; ++q) {
     const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[i] & 0xFFFF)));
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(w[i] >> 16)));
-    }
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
   }
-  return amax;
+  return bf16_to_f32(m.x > m.y ? m.x : m.y);
 }
 
 // Half of a 32-block (16 bf16 values, 2 vectors of 8) in the split form, given
@@ -180,13 +198,10 @@ __device__ __forceinline__ uint32_t mx_split_half(const uint4 (&v)[2], float ama
   for (int q = 0; q < 2; ++q) {
     const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-      uint32_t h0, l0, h1, l1;
-      mx_split_pair(bf16_to_f32(w[i] & 0xFFFF) * inv, bf16_to_f32(w[i] >> 16) * inv, &h0, &l0);
-      mx_split_pair(bf16_to_f32(w[i + 1] & 0xFFFF) * inv, bf16_to_f32(w[i + 1] >> 16) * inv, &h1, &l1);
-      hw[2 * q + i / 2] = h0 | (h1 << 16);
-      lw[2 * q + i / 2] = l0 | (l1 << 16);
-    }
+    for (int i = 0; i < 4; i += 2)
+      mx_split_quad(bf16_to_f32(w[i] & 0xFFFF) * inv, bf16_to_f32(w[i] >> 16) * inv,
+                    bf16_to_f32(w[i + 1] & 0xFFFF) * inv, bf16_to_f32(w[i + 1] >> 16) * inv, hw[2 * q + i / 2],
+                    lw[2 * q + i / 2]);
   }
   hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
