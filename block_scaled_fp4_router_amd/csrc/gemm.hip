@@ -112,15 +112,18 @@ __device__ __forceinline__ int logical_tile(int w) {
 
 // Position of vector q in an LDS row of V 16-byte vectors (V = 8, 4 or 2).
 // A fragment read takes one vector from each of 32 consecutive rows; the XOR
-// pattern puts every 8 and every 16 consecutive rows of it on distinct
-// 16-byte bank groups, so the read is conflict-free whether the LDS serves 8
-// or 16 lanes of a 128-bit read per cycle.
+// pattern spreads them over the LDS banks.  The patterns were checked with
+// the LDS bank-conflict counter (SQ_LDS_BANK_CONFLICT against
+// SQ_LDS_IDX_ACTIVE) on the GEMMs that use them: none for V = 8 and V = 2.
+// For the 64-byte rows (V = 4) q ^ ((r >> 2) & 3) measured no conflicts,
+// where q ^ (((r >> 1) ^ (r >> 3)) & 3) measured one conflict cycle per access
+// and q ^ (r & 3) three.
 template <int V>
 __device__ __forceinline__ int swz(int r, int q) {
   if constexpr (V == 8)
     return q ^ ((r & 7) ^ ((r >> 3) & 1));
   else if constexpr (V == 4)
-    return q ^ (((r >> 1) ^ (r >> 3)) & 3);
+    return q ^ ((r >> 2) & 3);
   else
     return q ^ (((r >> 2) ^ (r >> 3)) & 1);
 }
