@@ -2,8 +2,13 @@
 //
 // A workgroup is 8 waves over one (row block, column tile): BM token rows of
 // one expert (BM = 128 or 64) times a tile of the expert's weight rows.  Each
-// wave owns a 64 x 64 output tile (2 x 2 MFMA tiles of 32 x 32); the waves are
-// laid out BM/64 along rows and 8 / (BM/64) along columns.
+// wave owns a 64 x 64 output tile (2 x 2 MFMA tiles of 32 x 32), or 64 x 128
+// (2 x 4) with 128-row blocks; the waves are laid out BM/64 along rows and
+// 8 / (BM/64) along columns.  NVFP4 gate_up launches with 64-row blocks and
+// enough tiles to fill the chip twice take 64 x 128 wave tiles too: the
+// workgroup then spans two 512-row weight tiles (1024 weight rows), and each
+// activation fragment read from LDS, as well as each activation stage
+// fetched, serves twice the columns.
 //   gate_up: a wave's two column tiles are 32 gate rows and the 32 matching up
 //            rows, so h = silu(gate) * up is formed in registers;
 //   down:    a wave's two column tiles are 64 consecutive output columns.
@@ -63,14 +68,21 @@ int gemm_block_m(int T, int k, int E, int wfmt, bool a8) {
   return static_cast<long long>(T) * k >= 192LL * E ? 128 : 64;
 }
 
-template <int WFMT, bool FP8ACT, int BM>
+template <int WFMT, bool FP8ACT, int BM, bool WIDE = false>
 struct Cfg {
   static constexpr int kWM = BM / 64;                  // waves along rows
   static constexpr int kWN = kGemmWaves / kWM;         // waves along columns
+  // WIDE (NVFP4 gate_up with 64-row blocks): each wave takes 4 column tiles,
+  // so a workgroup covers two 512-row weight tiles and every activation
+  // fragment it reads feeds twice the MFMAs
+  static constexpr bool kWide = WIDE;
+  static_assert(!WIDE || (WFMT == kNVFP4 && BM == 64), "wide tiles: NVFP4, 64-row blocks");
   // 32-column MFMA tiles per wave (BF16 weight stages are 4x as wide as
   // FP4's, so their tile has half the columns)
-  static constexpr int kNT = WFMT == kBF16 ? 2 : BM == 128 ? 4 : 2;
+  static constexpr int kNT = WFMT == kBF16 ? 2 : (BM == 128 || kWide) ? 4 : 2;
   static constexpr int kBN = 32 * kNT * kWN;           // weight rows per workgroup
+  static constexpr int kSub = kWide ? 2 : 1;           // packed weight tiles per workgroup tile
+  static constexpr int kTileW = kBN / kSub;            // rows of one packed tile
   static constexpr int kAV = FP8ACT ? 4 : 8;           // 16-byte vectors per activation row and stage
   static constexpr int kARowB = 16 * kAV;
   static constexpr int kBRowB = WFMT == kBF16 ? 128 : WFMT == kFP8 ? 64 : 32;  // weight bytes per row and stage
@@ -92,10 +104,11 @@ struct Cfg {
   static constexpr int kChunks = (kABytes + kBBytes) / 1024;
   static constexpr int kChunksPerWave = kChunks / kGemmWaves;
   static_assert(kChunks % kGemmWaves == 0, "every wave issues the same number of DMA instructions");
-  static constexpr int kScaleRowsPerWave = kBN / kGemmWaves;   // one 4-byte DMA instruction per wave
-  static_assert(kScaleRowsPerWave <= 64, "scale rows per wave");
+  static constexpr int kScaleRowsPerWave = kBN / kGemmWaves;
+  static constexpr int kScaleInstr = (kScaleRowsPerWave + 63) / 64;   // 4-byte DMA instructions per wave and stage
+  static_assert(kScaleRowsPerWave <= 64 || kScaleRowsPerWave == 128, "scale rows per wave");
   static constexpr int kARowsPerWave = BM / kGemmWaves;   // activation scale rows per wave
-  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? 1 : 0) + (kAScales ? 1 : 0);
+  static constexpr int kVmPerStage = kChunksPerWave + (kScales ? kScaleInstr : 0) + (kAScales ? 1 : 0);
   static_assert(kVmPerStage * (kRing - 2) < 64, "vmcnt range");
 };
 
@@ -492,9 +505,9 @@ struct GemmArgs {
   uint32_t* amax_slots;      // gate_up with FP8 activations: partial maxima of |h|
 };
 
-template <int WFMT, bool FP8ACT, int BM, bool GATEUP, bool PERSIST>
+template <int WFMT, bool FP8ACT, int BM, bool GATEUP, bool PERSIST, bool WIDE = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
-  using C = Cfg<WFMT, FP8ACT, BM>;
+  using C = Cfg<WFMT, FP8ACT, BM, WIDE>;
   constexpr int NT = C::kNT;
   // MXFP8 activations: fragments of the next stage are read while the
   // current stage's MFMAs run (two register sets)
@@ -513,15 +526,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   const int j = lane & 31, g = lane >> 5;
   const int ns = K / kStageK;
 
-  // weight row (within the expert's matrix) of tile row R of column tile nt, or -1 past N
+  // weight row (within the expert's matrix) of tile row R of column tile nt,
+  // or -1 past N.  A tile of kSub packed tiles holds them one after another
+  // (gate_up: each packed tile pairs its gate rows with the matching up rows).
   auto tile_col = [&](int nt, int R) -> int {
+    if constexpr (C::kSub > 1) {
+      nt = C::kSub * nt + R / C::kTileW;
+      R %= C::kTileW;
+    }
     if constexpr (GATEUP) {
-      const int half = C::kBN / 2;
+      const int half = C::kTileW / 2;
       const int c = nt * half + (R < half ? R : R - half);
       if (c >= N) return -1;
       return R < half ? c : N + c;
     } else {
-      const int c = nt * C::kBN + R;
+      const int c = nt * C::kTileW + R;
       return c < N ? c : -1;
     }
   };
@@ -530,9 +549,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   int Rt[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
-    if constexpr (GATEUP)
-      Rt[ct] = (ct < NT / 2 ? 0 : C::kBN / 2) + 32 * (wn * (NT / 2) + ct % (NT / 2));
-    else
+    if constexpr (GATEUP) {
+      constexpr int kWps = C::kWN / C::kSub;   // waves per packed tile
+      Rt[ct] = (wn / kWps) * C::kTileW + (ct < NT / 2 ? 0 : C::kTileW / 2) + 32 * ((wn % kWps) * (NT / 2) + ct % (NT / 2));
+    } else
       Rt[ct] = 32 * (wn * NT + ct);
   }
 
@@ -603,13 +623,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   const uint8_t* sbase = nullptr;   // its block scales
   uint32_t src[C::kChunksPerWave];
   uint32_t soff = 0, aoff = 0;      // this lane's block-scale and activation-scale offsets
+  uint32_t soff2 = 0;               // (second scale row group, kScaleInstr == 2)
+  // packed tiles per expert matrix, and the distance between consecutive ones
+  const int ptiles = C::kSub == 1 ? ntile : GATEUP ? (N + C::kTileW / 2 - 1) / (C::kTileW / 2) : (N + C::kTileW - 1) / C::kTileW;
+  const uint32_t ptile_bytes = static_cast<uint32_t>(ns) * kPackStage;
   int dnext = 0;        // next stage of the DMA tile
   bool dlive = false;   // the DMA tile exists (else stages are refetched into buffers nobody reads)
   // sources of tile k (block b, column tile nt, expert e); f(r) gives the
   // sorted id of tile row r
   auto set_sources = [&](int b, int nt, int e, auto f) {
-    wbase = packed ? w.packed + (static_cast<size_t>(e) * ntile + nt) * ns * kPackStage
+    wbase = packed ? w.packed + (static_cast<size_t>(e) * ptiles + C::kSub * nt) * ns * kPackStage
                    : w.codes + static_cast<size_t>(e) * wrows * wrow_bytes;
+    // packed tile q of the workgroup tile (past the matrix's last: its first, unused)
+    auto sub_off = [&](int q) -> uint32_t {
+      if constexpr (C::kSub == 1) return 0u;
+      return C::kSub * nt + q < ptiles ? q * ptile_bytes : 0u;
+    };
 #pragma unroll
     for (int i = 0; i < C::kChunksPerWave; ++i) {
       const int c = wave + kGemmWaves * i;
@@ -621,7 +650,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
         const int v = (c - C::kAChunks) * 64 + lane;
         const int R = v / C::kBV, q = swz<C::kBV>(R, v % C::kBV);
         const int col = tile_col(nt, R);
-        src[i] = packed ? 16u * static_cast<uint32_t>(v) : static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
+        constexpr int kSubV = C::kTileW * C::kBV;   // 16-byte vectors of one packed tile's stage
+        src[i] = packed ? sub_off(v / kSubV) + 16u * static_cast<uint32_t>(v % kSubV)
+                        : static_cast<uint32_t>(col < 0 ? 0 : col) * wrow_bytes + 16 * q;
       }
     }
     // Block scales: lanes l < kScaleRowsPerWave of wave w fetch the scale
@@ -630,13 +661,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     // picked at use).
     if constexpr (C::kScales) {
       const int R = wave * C::kScaleRowsPerWave + (lane < C::kScaleRowsPerWave ? lane : 0);
+      const int R2 = R + 64;   // second instruction's row (kScaleInstr == 2)
       if (packed) {
         sbase = wbase;
-        soff = C::kBBytes + 4 * R;
+        soff = sub_off(R / C::kTileW) + C::kTileW * C::kBRowB + 4 * (R % C::kTileW);
+        if constexpr (C::kScaleInstr == 2) soff2 = sub_off(R2 / C::kTileW) + C::kTileW * C::kBRowB + 4 * (R2 % C::kTileW);
       } else {
         const int col = tile_col(nt, R);
         sbase = w.scales + static_cast<size_t>(e) * wrows * spitch;
         soff = static_cast<uint32_t>(col < 0 ? 0 : col) * spitch;
+        if constexpr (C::kScaleInstr == 2) {
+          const int col2 = tile_col(nt, R2);
+          soff2 = static_cast<uint32_t>(col2 < 0 ? 0 : col2) * spitch;
+        }
       }
     }
     // Activation scales (MXFP4): lanes l < kARowsPerWave of wave w fetch the
@@ -727,11 +764,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
     }
     if constexpr (C::kScales) {
       if (lane < C::kScaleRowsPerWave) dma4(sbase + soff, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave);
+      if constexpr (C::kScaleInstr == 2)
+        dma4(sbase + soff2, buf + C::kABytes + C::kBBytes + wave * 4 * C::kScaleRowsPerWave + 256);
       // row-major MXFP4: stages 2m and 2m + 1 share the dword at 4m
-      if (packed)
-        soff += adv ? kPackStage : 0;
-      else
-        soff += adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0;
+      const uint32_t sadv = packed ? (adv ? kPackStage : 0) : (adv && (WFMT == kNVFP4 || (cur_stage & 1)) ? 4 : 0);
+      soff += sadv;
+      if constexpr (C::kScaleInstr == 2) soff2 += sadv;
     }
     if constexpr (C::kAScales) {
       if (lane < C::kARowsPerWave)
@@ -781,9 +819,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
   }
   // tile-row distances of this wave's column tiles from the first
   constexpr int kHalf = C::kBN / 2;
-  constexpr int kD1 = GATEUP ? (NT == 4 ? 32 : kHalf) : 32;
-  constexpr int kD2 = GATEUP ? kHalf : 64;
-  constexpr int kD3 = GATEUP ? kHalf + 32 : 96;
+  constexpr int kUpD = C::kTileW / 2;   // gate_up: tile rows from a gate row to its up row
+  constexpr int kD1 = GATEUP ? (NT == 4 ? 32 : kUpD) : 32;
+  constexpr int kD2 = GATEUP ? kUpD : 64;
+  constexpr int kD3 = GATEUP ? kUpD + 32 : 96;
   constexpr int kOAM = 32 * C::kARowB;
   constexpr int kBVec = WFMT == kBF16 ? 4 * NT : WFMT == kFP8 ? 2 * NT : NT;
   constexpr int kAVec = FP8ACT ? 4 : 8;
@@ -1145,9 +1184,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs ga) {
 }
 
 // ------------------------------------------------------------ launches ----
-template <int WFMT, bool FP8ACT, int BM, bool GATEUP>
+template <int WFMT, bool FP8ACT, int BM, bool GATEUP, bool WIDE = false>
 static hipError_t run(const GemmArgs& ga, hipStream_t s) {
-  using C = Cfg<WFMT, FP8ACT, BM>;
+  using C = Cfg<WFMT, FP8ACT, BM, WIDE>;
   const int ntile = GATEUP ? (ga.N + C::kBN / 2 - 1) / (C::kBN / 2) : (ga.N + C::kBN - 1) / C::kBN;
   const int total = ga.rows.num_blocks * ntile;
   if (total == 0) return hipSuccess;
@@ -1173,7 +1212,15 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
       return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP, true>, dim3(grid), dim3(kGemmThreads), 0, s, ga);
     }
   }
-  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP, false>, dim3(grid), dim3(kGemmThreads), 0, s, ga);
+  return launch(gemm_kernel<WFMT, FP8ACT, BM, GATEUP, false, WIDE>, dim3(grid), dim3(kGemmThreads), 0, s, ga);
+}
+
+// Compute units of the current device (0 if the query fails).
+static int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return ncu;
 }
 
 template <bool GATEUP>
@@ -1186,7 +1233,16 @@ static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
       return bm == 128 ? run<kMXFP4, false, 128, GATEUP>(ga, s) : run<kMXFP4, false, 64, GATEUP>(ga, s);
     case kNVFP4:
       if (fp8act) return hipErrorInvalidValue;
-      return bm == 128 ? run<kNVFP4, false, 128, GATEUP>(ga, s) : run<kNVFP4, false, 64, GATEUP>(ga, s);
+      if (bm == 128) return run<kNVFP4, false, 128, GATEUP>(ga, s);
+      if constexpr (GATEUP) {
+        // wide tiles once they still give every CU two (the shared expert's
+        // dense rows alone would leave half the chip idle)
+        const long long wide_tiles = static_cast<long long>(ga.rows.num_blocks) *
+                                     ((ga.N + Cfg<kNVFP4, false, 64, true>::kBN / 2 - 1) / (Cfg<kNVFP4, false, 64, true>::kBN / 2));
+        const int ncu = device_cus();
+        if (ncu > 0 && wide_tiles >= 2LL * ncu) return run<kNVFP4, false, 64, true, true>(ga, s);
+      }
+      return run<kNVFP4, false, 64, GATEUP>(ga, s);
     case kFP8:
       if (bm != 128) return hipErrorInvalidValue;
       return fp8act ? run<kFP8, true, 128, GATEUP>(ga, s) : run<kFP8, false, 128, GATEUP>(ga, s);
@@ -1257,9 +1313,9 @@ hipError_t launch_gemm_down(const QW& w, const Rows& rows, const GemmAct& h, int
 // row R's vector swz(R, p)), then for FP4 one scale dword per tile row (MXFP4:
 // the dword of the stage pair; NVFP4: the stage's).  Rows past N are zero.
 constexpr int kTileRows = 512;
-static_assert(Cfg<kMXFP4, false, 128>::kBN == kTileRows && Cfg<kMXFP4, false, 64>::kBN == kTileRows &&
-                  Cfg<kMXFP4, true, 128>::kBN == kTileRows &&
-                  Cfg<kNVFP4, false, 64>::kBN == kTileRows && Cfg<kFP8, true, 128>::kBN == kTileRows,
+static_assert(Cfg<kMXFP4, false, 128>::kTileW == kTileRows && Cfg<kMXFP4, false, 64>::kTileW == kTileRows &&
+                  Cfg<kMXFP4, true, 128>::kTileW == kTileRows && Cfg<kNVFP4, false, 128>::kTileW == kTileRows &&
+                  Cfg<kNVFP4, false, 64>::kTileW == kTileRows && Cfg<kFP8, true, 128>::kTileW == kTileRows,
               "one packed layout serves every tile configuration");
 
 int packed_tiles(int n, bool gate_up) {
