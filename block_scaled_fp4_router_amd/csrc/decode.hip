@@ -580,6 +580,84 @@ __global__ __launch_bounds__(64 * WPB) void decode_gateup_kernel(DecodeArgs a) {
   if constexpr (FP8ACT) wg_amax_to_slots(mx, a.amax_slots, red);
 }
 
+// One- and two-token batches: the KS waves of a workgroup share one group of
+// 16 weight rows (8 gate + 8 up) and split it along K, so the step's stream
+// is carried by KS times as many waves and each wave's dequantisation and
+// MFMA chain is 1/KS as long.  The partial sums meet in LDS and are added in
+// wave order (fixed, so the result does not depend on timing).
+template <int WFMT, bool FP8ACT, int NB, int KS>
+__global__ __launch_bounds__(64 * KS) void decode_gateup_ks_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  __shared__ f32x4 part[KS][kWave];
+  const int b = blockIdx.y;
+  const bool shared = b >= a.nb_routed;
+  const int ex = shared ? 0 : a.block_expert[b];
+  if (ex < 0) return;
+  const QW& w = shared ? a.sgu : a.gu;
+  const int e = expert_slot(w, ex);   // slot of its matrices
+  if (e < 0) return;                  // served by another pass
+  const int p0 = (shared ? b - a.nb_routed : b) * kDecodeBM;
+  const int I = shared ? a.Is : a.I;
+  const int H = a.H;
+  if (static_cast<int>(blockIdx.x) * 8 >= I) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int i0 = blockIdx.x * 8;
+  const int j = lane & 15, g = lane >> 4;
+  const size_t wrow = static_cast<size_t>(e) * (2 * I) + (j < 8 ? i0 + j : I + i0 + (j - 8));
+  const int row_bytes = FP8ACT ? H : 2 * H;
+  const int kq = H / KS, k0 = wave * kq, k1 = k0 + kq;   // this wave's K range (multiples of 128)
+
+  const int raw = slot_fetch(a, b, shared);
+  typename WSliceT<WFMT>::type ws[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) ws[u] = load_wslice<WFMT>(w, wrow, H, min(k0 + u * 128, k1 - 128) + g * 32);
+  __builtin_amdgcn_sched_barrier(0);
+  const LaneSlot ls = slot_decode(a, shared, p0, raw);
+  const int count = __popcll(__ballot(ls.valid && lane < kDecodeBM));
+  dma_rows(xs, count, row_bytes / 16, [&](int r) -> const void* {
+    const size_t t = static_cast<size_t>(__shfl(ls.tok, r, kWave));
+    return FP8ACT ? a.xq + t * H : reinterpret_cast<const uint8_t*>(a.x + t * H);
+  });
+  __syncthreads();
+
+  const bool aval = j < count;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mma_batch<WFMT, FP8ACT, false, NB>(ws, k0, k1, g, xs, row_bytes, j, aval, 1.0f, acc);
+  for (int kc0 = k0 + NB * 128; kc0 < k1; kc0 += NB * 128) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) ws[u] = load_wslice<WFMT>(w, wrow, H, min(kc0 + u * 128, k1 - 128) + g * 32);
+    mma_batch<WFMT, FP8ACT, false, NB>(ws, kc0, k1, g, xs, row_bytes, j, aval, 1.0f, acc);
+  }
+  if (wave > 0) part[wave][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int q = 1; q < KS; ++q) {
+    const f32x4 p = part[q][lane];
+    acc[0] += p[0];
+    acc[1] += p[1];
+    acc[2] += p[2];
+    acc[3] += p[3];
+  }
+
+  float f = WFMT == kBF16 ? 1.0f : row_scale(w, e, j < 8 ? i0 + j : I + i0 + (j - 8));
+  if constexpr (FP8ACT) f *= scale_from_amax(a.amax_x);
+  uint16_t* h = shared ? a.hs : a.h;
+  float mx = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float val = acc[r] * f;
+    const float up = __shfl_xor(val, 8, kWave);
+    const int slot = 4 * g + r;
+    if (j < 8 && slot < count) {
+      const float v = swiglu(val, up);
+      h[static_cast<size_t>(p0 + slot) * I + i0 + j] = f32_to_bf16(v);
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+    }
+  }
+  if constexpr (FP8ACT) wave_amax_to_slots(mx, a.amax_slots);
+}
+
 template <int WFMT, bool FP8ACT, int NB>
 __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t hsm[];
@@ -771,21 +849,35 @@ static hipError_t run_down(const DecodeArgs& a, hipStream_t s) {
   return launch(decode_down_kernel<WFMT, FP8ACT, NB>, grid, dim3(64 * kDownWaves), lds, s, a);
 }
 
-// bf16 / FP8 gate_up: one-token batches touch few experts, so single-wave
-// workgroups spread them over every CU; larger batches share each LDS token
-// copy among 4 waves.
+// One- and two-token batches touch few experts: each group of 16 weight rows
+// is split along K over the 4 waves of a workgroup when H allows it (else one
+// wave per group), so the stream is spread over every CU; larger batches
+// share each LDS token copy among 4 waves on different row groups.
+template <int WFMT, bool FP8ACT>
+static hipError_t run_gateup_small(const DecodeArgs& a, hipStream_t s) {
+  if (a.H % (4 * 128)) return run_gateup<WFMT, FP8ACT, 1>(a, s);
+  constexpr int KS = 4;
+  constexpr int NB = 4;   // K chunks in flight per wave: a quarter of H = 2048
+  const int imax = a.Is > a.I ? a.Is : a.I;
+  const size_t lds = static_cast<size_t>(decode_rows(a.T)) * (FP8ACT ? a.H : 2 * a.H);
+  dim3 grid(imax / 8, a.nb_routed + a.nb_shared);
+  const hipError_t e = allow_lds(decode_gateup_ks_kernel<WFMT, FP8ACT, NB, KS>, lds);
+  if (e != hipSuccess) return e;
+  return launch(decode_gateup_ks_kernel<WFMT, FP8ACT, NB, KS>, grid, dim3(64 * KS), lds, s, a);
+}
+
 hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s) {
   const bool fp8act = a.xq != nullptr;
   const bool small = a.T <= 2;
   switch (a.gu.fmt) {
     case kMXFP4: return run_gateup_mx(a, s);
-    case kNVFP4: return small ? run_gateup<kNVFP4, false, 1>(a, s) : run_gateup<kNVFP4, false, 4>(a, s);
+    case kNVFP4: return small ? run_gateup_small<kNVFP4, false>(a, s) : run_gateup<kNVFP4, false, 4>(a, s);
     case kFP8:
-      if (fp8act) return small ? run_gateup<kFP8, true, 1>(a, s) : run_gateup<kFP8, true, 4>(a, s);
-      return small ? run_gateup<kFP8, false, 1>(a, s) : run_gateup<kFP8, false, 4>(a, s);
+      if (fp8act) return small ? run_gateup_small<kFP8, true>(a, s) : run_gateup<kFP8, true, 4>(a, s);
+      return small ? run_gateup_small<kFP8, false>(a, s) : run_gateup<kFP8, false, 4>(a, s);
     case kBF16:
       if (fp8act) return hipErrorInvalidValue;
-      return small ? run_gateup<kBF16, false, 1>(a, s) : run_gateup<kBF16, false, 4>(a, s);
+      return small ? run_gateup_small<kBF16, false>(a, s) : run_gateup<kBF16, false, 4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
