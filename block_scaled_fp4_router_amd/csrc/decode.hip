@@ -713,6 +713,65 @@ __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(DecodeArgs
   }
 }
 
+// ============================================ one token: down + combine ====
+// A one-token step routes its k rows to k distinct experts, one row per block.
+// For MXFP4 experts one workgroup then takes 16 output columns of every block
+// at once: wave b streams block b's 16 weight rows (the shared expert's block
+// last) against the block's split h row, the 16 fp32 outputs of each block
+// meet in LDS, and wave 0 adds them exactly as the combine kernel does
+// (ascending j, then the gated shared expert), so the step needs no separate
+// combine launch and gives the same bits as down followed by combine.  (The
+// formats dequantised in registers are VALU-bound here: with every block's
+// conversion on half as many CUs the fused launch took as long as the two.)
+constexpr int kFusedMaxBlocks = 16;   // waves per workgroup
+
+// y[n0 .. n0 + 15] of the token from the blocks' outputs ob[block][column].
+__device__ __forceinline__ void combine_one_token(const DecodeArgs& a, const float (*ob)[16], const int* blk_of,
+                                                  int n0) {
+  const int lane = lane_id();
+  if (threadIdx.x >= 16) return;
+  float acc = 0.f;
+  for (int jj = 0; jj < a.k; ++jj) acc = fmaf(a.w[jj], ob[blk_of[jj]][lane], acc);
+  if (a.sg) acc = fmaf(a.sg[0], ob[a.nb_routed][lane], acc);
+  a.y[n0 + lane] = f32_to_bf16(acc);
+}
+
+template <int NB, bool PACK, bool A8>
+__global__ __launch_bounds__(64 * kFusedMaxBlocks) void decode_down_combine1_mx_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float ob[kFusedMaxBlocks][16];
+  __shared__ int blk_of[kFusedMaxBlocks];
+  const int nbl = a.nb_routed + a.nb_shared;
+  const int b = threadIdx.x >> 6, lane = lane_id();   // one wave per block
+  const bool shared = b >= a.nb_routed;
+  const int ex = shared ? 0 : a.block_expert[b];
+  const bool live = ex >= 0;
+  const QW& w = shared ? a.sdn : a.dn;
+  const int e = live ? expert_slot(w, ex) : 0;
+  const int K = a.I, H = a.H, nch = K / 128;   // (the shared expert has the same K)
+  const int n0 = blockIdx.x * 16;
+  const int j = lane & 15, g = lane >> 4;
+  const size_t wrow = static_cast<size_t>(e) * H + n0 + j;
+  const uint8_t* codes = w.codes + wrow * (K / 2);
+  const uint8_t* scales = w.scales + wrow * (K / 32);
+  MxW<NB, PACK> wt;
+  if (live) mx_wload(wt, codes, scales, 0, nch, g);
+  const int flat = live && !shared ? a.sorted_ids[b * kDecodeBM] : -1;
+  __builtin_amdgcn_sched_barrier(0);
+  // the h row of every block (slot 0 of block r is h row 16 r, the shared
+  // expert's rows following the routed ones) -> LDS row r
+  const MxRows m = mx_rows<A8>(smem, K, a.hsc_pitch, nbl);
+  dma_split_rows(smem, nbl, K, a.hsc_pitch, a.hhi, A8 ? nullptr : a.hlo, a.hsc,
+                 [](int r) { return r * kDecodeBM; });
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) mx_row_dot<NB, PACK, A8>(wt, codes, scales, m, b, j == 0, nch, g, acc);
+  if (g == 0) ob[b][j] = live ? acc[0] : 0.f;   // column n0 + j of the block's slot 0
+  if (flat >= 0 && lane == 0) blk_of[flat] = b;
+  __syncthreads();
+  combine_one_token(a, ob, blk_of, n0);
+}
+
 // ============================================================ combine =====
 // y[t] = sum_j w[t,j] o[t*k+j] (ascending j) + sg[t] s[t], from the fp32
 // partial outputs; one thread per 4 columns.  Every row's load is issued
@@ -891,6 +950,29 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
     case kBF16: return fp8act ? hipErrorInvalidValue : run_down<kBF16, false>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool decode_fused_one_token(const DecodeArgs& a) {
+  const int nbl = a.nb_routed + a.nb_shared;
+  return a.T == 1 && a.dn.fmt == kMXFP4 && nbl <= kFusedMaxBlocks && (a.nb_shared == 0 || a.Is == a.I) &&
+         a.H % 16 == 0 && !a.dn.slot_of;
+}
+
+template <bool PACK, bool A8>
+static hipError_t run_down_combine1_mx(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NB = 8;
+  const int nbl = a.nb_routed + a.nb_shared;
+  const size_t lds = mx_rows_bytes<A8>(a.I, a.hsc_pitch, nbl);
+  const hipError_t e = allow_lds(decode_down_combine1_mx_kernel<NB, PACK, A8>, lds);
+  if (e != hipSuccess) return e;
+  return launch(decode_down_combine1_mx_kernel<NB, PACK, A8>, dim3(a.H / 16), dim3(64 * nbl), lds, s, a);
+}
+
+hipError_t launch_decode_down_combine1(const DecodeArgs& a, hipStream_t s) {
+  if (!decode_fused_one_token(a)) return hipErrorInvalidValue;
+  const bool pack = (a.I / 128) % 4 == 0;
+  if (a.a8) return pack ? run_down_combine1_mx<true, true>(a, s) : run_down_combine1_mx<false, true>(a, s);
+  return pack ? run_down_combine1_mx<true, false>(a, s) : run_down_combine1_mx<false, false>(a, s);
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {

@@ -483,12 +483,19 @@ ftmoe_status enqueue_experts(const ftmoe_layer* L, const uint16_t* x, int T, con
     a.w = w;
     a.sg = shared ? sg : nullptr;
     a.y = y;
+    // a one-token step in one pass runs down and combine as one launch
+    const bool fused = passes.n == 1 && !passes.tables && !passes.before_combine && decode_fused_one_token(a);
     for (int i = 0; i < passes.n; ++i) {
       if (passes.before) FT_TRY(passes.before(passes.ctx, i));
       if (passes.tables) a.gu.slot_of = a.dn.slot_of = passes.tables[i];
       a.nb_shared = i == 0 ? p.nb_shared : 0;
       FT_HIP(timed("decode_gateup", s, [&] { return launch_decode_gateup(a, s); }), "decode gate_up launch");
       if (fp8act) FT_HIP(timed("amax_h", s, [&] { return launch_amax_fold(ahs, ah, s); }), "amax fold launch");
+      if (fused) {
+        FT_HIP(timed("decode_down", s, [&] { return launch_decode_down_combine1(a, s); }),
+               "decode down + combine launch");
+        return FTMOE_OK;
+      }
       FT_HIP(timed("decode_down", s, [&] { return launch_decode_down(a, s); }), "decode down launch");
       if (passes.after) FT_TRY(passes.after(passes.ctx, i));
     }

@@ -172,6 +172,10 @@ hipError_t launch_decode_gateup(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
 // y = routed rows summed in ascending slot order j, then the gated shared expert.
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
+// One-token steps of MXFP4 layers: down and combine in one launch (same
+// results as the two); decode_fused_one_token tells whether the step qualifies.
+bool decode_fused_one_token(const DecodeArgs& a);
+hipError_t launch_decode_down_combine1(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill experts (grouped GEMMs on MFMA) ----
 // Rows per block of the prefill GEMMs for a layer routing T*k rows over E experts.
