@@ -4,11 +4,11 @@
 // one expert (BM = 128 or 64) times a tile of the expert's weight rows.  Each
 // wave owns a 64 x 64 output tile (2 x 2 MFMA tiles of 32 x 32), or 64 x 128
 // (2 x 4) with 128-row blocks; the waves are laid out BM/64 along rows and
-// 8 / (BM/64) along columns.  NVFP4 launches (gate_up and down) with 64-row
-// blocks and enough tiles to fill the chip twice take 64 x 128 wave tiles
-// too: the workgroup then spans two 512-row weight tiles (1024 weight rows),
-// and each activation fragment read from LDS, as well as each activation
-// stage fetched, serves twice the columns.
+// 8 / (BM/64) along columns.  NVFP4 gate_up launches with 64-row blocks and
+// enough tiles to fill the chip twice take 64 x 128 wave tiles too: the
+// workgroup then spans two 512-row weight tiles (1024 weight rows), and each
+// activation fragment read from LDS, as well as each activation stage
+// fetched, serves twice the columns.
 //   gate_up: a wave's two column tiles are 32 gate rows and the 32 matching up
 //            rows, so h = silu(gate) * up is formed in registers;
 //   down:    a wave's two column tiles are 64 consecutive output columns.
@@ -1199,10 +1199,9 @@ static hipError_t run(const GemmArgs& ga, hipStream_t s) {
   // current one's last; that needs at least as many stages per tile as are
   // fetched ahead (else one workgroup per tile).
   // (The down GEMMs run this way; the gate_up GEMMs, whose epilogue is
-  // longer and whose registers are all in use, run one tile per workgroup,
-  // and so do the wide NVFP4 down GEMMs: made persistent they spill.)
+  // longer and whose registers are all in use, run one tile per workgroup.)
   constexpr int kAhead = C::kAScales && FP8ACT ? C::kRing : C::kRing - 1;
-  if constexpr (!GATEUP && !WIDE) {
+  if constexpr (!GATEUP) {
     // (not with an expert-slot table: tiles of experts outside the call are skipped one tile per workgroup)
     if (ga.K / kStageK >= kAhead && !ga.w.slot_of) {
       int dev = 0, ncu = 0;
@@ -1235,15 +1234,13 @@ static hipError_t dispatch(const GemmArgs& ga, bool fp8act, hipStream_t s) {
     case kNVFP4:
       if (fp8act) return hipErrorInvalidValue;
       if (bm == 128) return run<kNVFP4, false, 128, GATEUP>(ga, s);
-      {
+      if constexpr (GATEUP) {
         // wide tiles once they still give every CU two (the shared expert's
-        // dense rows alone would leave half the chip idle); the wide down
-        // GEMM runs one tile per workgroup
-        constexpr int kWideBN = Cfg<kNVFP4, false, 64, true>::kBN;
-        const int cols = GATEUP ? kWideBN / 2 : kWideBN;
-        const long long wide_tiles = static_cast<long long>(ga.rows.num_blocks) * ((ga.N + cols - 1) / cols);
+        // dense rows alone would leave half the chip idle)
+        const long long wide_tiles = static_cast<long long>(ga.rows.num_blocks) *
+                                     ((ga.N + Cfg<kNVFP4, false, 64, true>::kBN / 2 - 1) / (Cfg<kNVFP4, false, 64, true>::kBN / 2));
         const int ncu = device_cus();
-        if (ncu > 0 && wide_tiles >= 2LL * ncu) return run<kNVFP4, false, 64, GATEUP, true>(ga, s);
+        if (ncu > 0 && wide_tiles >= 2LL * ncu) return run<kNVFP4, false, 64, true, true>(ga, s);
       }
       return run<kNVFP4, false, 64, GATEUP>(ga, s);
     case kFP8:
