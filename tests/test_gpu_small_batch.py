@@ -4,7 +4,8 @@ multiple of 512) and the single launch of down and combine for one-token
 MXFP4 steps (with a shared expert of the routed experts' width, and with
 MXFP8 activations).  Expected values come from the oracle.  A token's output
 must also not depend on whether it is decoded alone or beside a second token
-(one launch instead of two, the same arithmetic), bit for bit."""
+(one launch instead of two, the same arithmetic), bit for bit, and the
+one-token MXFP4 step must indeed run without a separate combine launch."""
 import numpy as np
 import pytest
 
@@ -69,3 +70,24 @@ def test_token_alone_equals_token_in_pair(name):
     assert np.array_equal(ids1[0], ids2[0])
     assert np.array_equal(w1[0], w2[0])
     assert np.array_equal(y1[0], y2[0])
+
+
+# which launches a step makes: one-token MXFP4 steps run down and combine as
+# one launch; other steps keep the separate combine
+@pytest.mark.parametrize("name,T,combine", [("mxsh", 1, False), ("mx8sh", 1, False), ("mxsh", 2, True),
+                                            ("nvw", 1, True)])
+@pytest.mark.timeout(300)
+def test_one_token_launches(name, T, combine):
+    say(f"launches of a decode step {name} T={T}")
+    lay, dlay = layer(name)
+    x = synth.make_tokens(lay, T, stream=60)
+    ft.timing_collect()
+    ft.timing_enable(True)
+    try:
+        run_forward(dlay, x, "decode")
+        torch.cuda.synchronize()
+        kern = ft.timing_collect()
+    finally:
+        ft.timing_enable(False)
+    assert "decode_down" in kern and "decode_gateup" in kern
+    assert ("combine" in kern) == combine
